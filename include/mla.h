@@ -1,0 +1,211 @@
+/*
+ * mla.h — C ABI of libmla.so: Multi-head Latent Attention (MLA) decode on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * What is computed.  For every sequence b of a batch, one query token (the
+ * newest one) attends over the sequence's cached tokens j = 0..T_b-1 with n_h
+ * heads.  The cache keeps per token only the joint KV latent c^KV_j (width d_c)
+ * and the shared, already rotated RoPE key k^R_j (width d_h^R)
+ * [DeepSeek-V2 explainer (一文通透DeepSeek-V2) §2.2.1 and §2.2.2].  Keys and
+ * values of head i are W^UK_i c^KV_j and W^UV_i c^KV_j, and the score is
+ *     s_{i,j} = ([q^C_i; q^R_i] . [W^UK_i c^KV_j; k^R_j]) * softmax_scale,
+ * softmax_scale = 1/sqrt(d_h + d_h^R)  [deepseek(2)——deepseek 關鍵技術, §1 MLA].
+ * By associativity W^UK_i moves to the query side and W^UV_i past the softmax
+ * [DeepSeek-V2 explainer §2.2.2; V3 interview notes (Deepseek系列从v3到R易背面经版),
+ * section MLA]:
+ *     q_lat_i = (W^UK_i)^T q^C_i                                   mla_absorb_q
+ *     o_lat_i = sum_j softmax_j(s_{i,.}) c^KV_j, with
+ *               s_{i,j} = (q_lat_i . c^KV_j + q^R_i . k^R_j) * scale  mla_decode (+ mla_merge_splits)
+ *     o_i     = W^UV_i o_lat_i                                     mla_out_proj
+ * and [o_1; ...; o_nh] is the input of the output projection W^O.
+ *
+ * Conventions for every entry point.
+ *  - Tensor pointers are DEVICE pointers owned by the caller; dense, row-major,
+ *    16-byte aligned.  The library allocates no device memory.  Pointers to
+ *    mla_dims_t / mla_paged_cache_t / mla_partition_t structs are HOST pointers,
+ *    read during the call only.
+ *  - `stream` is a hipStream_t passed as void* (NULL = default stream).  Calls
+ *    enqueue kernels and return; they do not synchronise.
+ *  - Validation happens before anything is enqueued: on MLA_ERR_* nothing was
+ *    launched and no device memory was touched.  A failed launch returns
+ *    MLA_ERR_HIP.  No C++ exception crosses the ABI.
+ *  - Heads are stacked in order: head i of a [.., n_h*d_h] matrix owns rows
+ *    i*d_h .. (i+1)*d_h-1 ([deepseek(2) 關鍵技術] §1 stacked notation).
+ *  - LSE values are natural-log sum-exp of the scaled scores.
+ *
+ * Fast paths (MFMA kernels): n_h = 128, d_c = 512, d_h^R = 64, d_h = 128,
+ * page_size = 64, bf16 queries/weights, bf16 or fp8 cache.  Other shapes and
+ * dtypes (e.g. the fp32 tiny case) run on generic VALU kernels with fp32
+ * arithmetic, limited to d_c <= 1024, d_h^R <= 256, d_h <= 1024.
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = 1,   /* null pointer, non-positive size, inconsistent sizes */
+  MLA_ERR_UNSUPPORTED = 2,   /* valid but not implemented (dtype combination, size limit) */
+  MLA_ERR_ALIGNMENT = 3,     /* a tensor pointer is not 16-byte aligned */
+  MLA_ERR_WORKSPACE = 4,     /* workspace missing or smaller than mla_decode_workspace_size */
+  MLA_ERR_HIP = 5            /* the HIP runtime reported an error (launch or device query) */
+} mla_status_t;
+
+typedef enum {
+  MLA_F32 = 0,
+  MLA_BF16 = 1,
+  MLA_FP8_E4M3 = 2           /* OCP E4M3FN (finite max 448); cache only */
+} mla_dtype_t;
+
+/* n_h, d_h, d_h^R, d_c. */
+typedef struct {
+  int32_t n_heads;
+  int32_t d_head;
+  int32_t d_rope;
+  int32_t d_latent;
+} mla_dims_t;
+
+/*
+ * Paged latent cache [DeepSeek-V2 explainer §2.2.2: only c^KV and k^R are cached;
+ * §2.1.1 names paged KV memory].  Token t of sequence b sits in page
+ * block_table[b * max_pages_per_seq + t / page_size], slot t % page_size, as
+ * the row [c^KV_t (d_latent) | k^R_t (d_rope)].
+ *   kv:      [num_pages, page_size, d_latent + d_rope] elements of `dtype`.
+ *   scales:  fp8 only: [num_pages, page_size, ceil((d_latent + d_rope)/128)] fp32,
+ *            one per token per 128-channel group; a stored value is code * scale
+ *            (the 1x128 per-token-group FP8 format of the V3 notes, section
+ *            F8量化策略).  NULL for other dtypes.
+ *   block_table: [batch, max_pages_per_seq] int32; only the first
+ *            ceil(seq_lens[b]/page_size) entries of a row are read, each must be
+ *            in [0, num_pages).
+ *   seq_lens: [batch] int32, 0 <= seq_lens[b] <= max_pages_per_seq * page_size.
+ * Slots past a sequence's length are never read (they may hold NaN).
+ */
+typedef struct {
+  const void* kv;
+  const float* scales;
+  mla_dtype_t dtype;
+  int32_t page_size;
+  int32_t num_pages;
+  const int32_t* block_table;
+  int32_t max_pages_per_seq;
+  const int32_t* seq_lens;
+} mla_paged_cache_t;
+
+/*
+ * How mla_decode divides the tokens of the batch into work items.
+ *   split_tokens > 0: sequence b is cut into ceil(T_b / split_tokens) chunks
+ *       [s*split_tokens, min((s+1)*split_tokens, T_b)); split_tokens must be a
+ *       multiple of page_size.  Chunk s of sequence b uses workspace slot
+ *       b * S + s, S = ceil(max_pages_per_seq * page_size / split_tokens).
+ *   split_tokens == 0, num_parts == 0: one work item per sequence, no workspace.
+ *   split_tokens == 0, num_parts > 0: the pages of all sequences, taken in
+ *       sequence order, are divided into min(num_parts, total pages) contiguous,
+ *       equal (+-1 page) parts; part w's share of sequence b uses workspace slot
+ *       w + b.  num_parts < 0 means "the device's compute-unit count".
+ * A sequence covered by a single work item receives its final o_lat / lse
+ * directly from mla_decode; the others (and empty sequences) receive them from
+ * mla_merge_splits.
+ */
+typedef struct {
+  int32_t split_tokens;
+  int32_t num_parts;
+} mla_partition_t;
+
+/* Human-readable name of a status code (static storage). */
+const char* mla_status_string(mla_status_t status);
+
+/* Build description: target, kernels compiled in. */
+const char* mla_build_info(void);
+
+/*
+ * q_lat[b, i, :] = (W^UK_i)^T q_nope[b, i, :]   ([DeepSeek-V2 explainer §2.2.2]
+ * absorption of W^UK into the query side).
+ *   q_nope: [batch, n_h, d_h] (q_dt);  w_uk: [n_h * d_h, d_c] (w_dt) = W^UK as on
+ *   the pages;  q_lat: [batch, n_h, d_c] (out_dt).  fp32 accumulation.
+ *   q_dt, w_dt, out_dt in {MLA_F32, MLA_BF16}.
+ */
+mla_status_t mla_absorb_q(const mla_dims_t* dims, int32_t batch,
+                          const void* q_nope, mla_dtype_t q_dt,
+                          const void* w_uk, mla_dtype_t w_dt,
+                          void* q_lat, mla_dtype_t out_dt, void* stream);
+
+/*
+ * Workspace needed by mla_decode / mla_merge_splits for a partition: fp32 split
+ * partials o_part [num_slots, n_h, d_c] at offset 0, then fp32 lse_part
+ * [num_slots, n_h] at offset mla_lse_part_offset(...).  *bytes = 0 when the
+ * partition never splits.  num_parts < 0 needs a current HIP device.
+ */
+mla_status_t mla_decode_workspace_size(const mla_dims_t* dims, int32_t batch,
+                                       int32_t max_pages_per_seq, int32_t page_size,
+                                       const mla_partition_t* part,
+                                       size_t* bytes, int32_t* num_slots);
+
+/* Byte offset of lse_part inside the workspace for num_slots slots. */
+size_t mla_lse_part_offset(const mla_dims_t* dims, int32_t num_slots);
+
+/*
+ * Attention of each sequence's query over its paged cache, absorbed form
+ * (scores against c^KV and k^R, output in latent space; [deepseek(2) 關鍵技術] §1
+ * with [DeepSeek-V2 explainer] §2.2.2 absorption).
+ *   q_lat: [batch, n_h, d_c], q_pe: [batch, n_h, d_rope] (RoPE already applied),
+ *       both q_dt (MLA_F32, or MLA_BF16).
+ *   softmax_scale: multiplies every score, normally 1/sqrt(d_h + d_rope).
+ *   o_lat: [batch, n_h, d_c] (o_dt in {MLA_F32, MLA_BF16}); lse: [batch, n_h]
+ *       fp32 or NULL.  Written for sequences covered by one work item.
+ *   workspace: see mla_decode_workspace_size; may be NULL when it is 0 bytes.
+ * The cache must be f32 with f32 queries, or bf16 / fp8 with bf16 queries.
+ */
+mla_status_t mla_decode(const mla_dims_t* dims, int32_t batch,
+                        const void* q_lat, const void* q_pe, mla_dtype_t q_dt,
+                        const mla_paged_cache_t* cache, float softmax_scale,
+                        const mla_partition_t* part,
+                        void* workspace, size_t workspace_bytes,
+                        void* o_lat, mla_dtype_t o_dt, float* lse, void* stream);
+
+/*
+ * Log-sum-exp merge of split partials: for each sequence split over several
+ * work items, lse = log sum_s exp(lse_s) and o_lat = sum_s exp(lse_s - lse) o_s.
+ * Sequences with no tokens get o_lat = 0 and lse = -inf.  Sequences covered by
+ * one work item are left untouched.  Arguments must match the mla_decode call
+ * whose partials are merged; seq_lens is the cache's device array.
+ */
+mla_status_t mla_merge_splits(const mla_dims_t* dims, int32_t batch,
+                              const int32_t* seq_lens, int32_t page_size,
+                              int32_t max_pages_per_seq, const mla_partition_t* part,
+                              const void* workspace, size_t workspace_bytes,
+                              void* o_lat, mla_dtype_t o_dt, float* lse, void* stream);
+
+/*
+ * o_heads[b, i*d_h + k] = sum_c W^UV[i*d_h + k, c] o_lat[b, i, c]  (W^UV applied
+ * after attention, [DeepSeek-V2 explainer §2.2.2]).
+ *   o_lat: [batch, n_h, d_c] (o_dt);  w_uv: [n_h * d_h, d_c] (w_dt);
+ *   o_heads: [batch, n_h * d_h] (out_dt).  fp32 accumulation.
+ */
+mla_status_t mla_out_proj(const mla_dims_t* dims, int32_t batch,
+                          const void* o_lat, mla_dtype_t o_dt,
+                          const void* w_uv, mla_dtype_t w_dt,
+                          void* o_heads, mla_dtype_t out_dt, void* stream);
+
+/*
+ * Host helper (no device access): for host copies of seq_lens, the workspace
+ * slots that hold sequence b's partials: slots part_first[b] .. part_first[b] +
+ * part_count[b] - 1.  part_count[b] == 1 means mla_decode writes the final
+ * output directly; 0 means the sequence is empty.  num_parts must be >= 0.
+ */
+mla_status_t mla_partition_host(const int32_t* seq_lens_host, int32_t batch,
+                                int32_t page_size, int32_t max_pages_per_seq,
+                                const mla_partition_t* part,
+                                int32_t* part_first, int32_t* part_count);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

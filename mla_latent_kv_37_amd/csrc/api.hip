@@ -1,0 +1,314 @@
+// C ABI of libmla (include/mla.h): argument validation, partition resolution,
+// dtype/shape dispatch and kernel launches.  Nothing here allocates device
+// memory; every check runs before the first launch.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "kernels.cuh"
+
+namespace {
+
+using namespace mla;
+
+constexpr int kGenMaxLatent = 1024;
+constexpr int kGenMaxRow = 1280;
+constexpr int kGenMaxHead = 1024;
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool is_v2(const mla_dims_t* d) {
+  return d->n_heads == 128 && d->d_latent == 512 && d->d_rope == 64;
+}
+
+mla_status_t check_dims(const mla_dims_t* d) {
+  if (d == nullptr) return MLA_ERR_INVALID_ARG;
+  if (d->n_heads < 1 || d->d_head < 1 || d->d_rope < 0 || d->d_latent < 1) return MLA_ERR_INVALID_ARG;
+  return MLA_OK;
+}
+
+bool valid_dtype(mla_dtype_t t) { return t == MLA_F32 || t == MLA_BF16 || t == MLA_FP8_E4M3; }
+
+// Resolve a partition into kernel parameters, item and slot counts.
+mla_status_t resolve(const mla_dims_t* dims, int32_t batch, int32_t max_pages, int32_t page_size,
+                     const mla_partition_t* part, PartParams* pp, int* n_items, int* n_slots) {
+  if (batch < 0 || max_pages < 1 || page_size < 1) return MLA_ERR_INVALID_ARG;
+  PartParams p{};
+  p.page_size = page_size;
+  p.batch = batch;
+  const int split = part ? part->split_tokens : 0;
+  const int parts = part ? part->num_parts : 0;
+  if (split < 0) return MLA_ERR_INVALID_ARG;
+  if (split > 0) {
+    if (split % page_size != 0) return MLA_ERR_INVALID_ARG;
+    const int64_t max_tokens = int64_t(max_pages) * page_size;
+    p.mode = PART_FIXED;
+    p.split_tokens = split;
+    p.fixed_slots = int((max_tokens + split - 1) / split);
+    *n_items = batch * p.fixed_slots;
+    *n_slots = *n_items;
+  } else if (parts == 0) {
+    p.mode = PART_WHOLE;
+    *n_items = batch;
+    *n_slots = 0;
+  } else {
+    int w = parts;
+    if (w < 0) {
+      int dev = 0;
+      if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_HIP;
+      if (hipDeviceGetAttribute(&w, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return MLA_ERR_HIP;
+      if (w < 1) return MLA_ERR_HIP;
+    }
+    p.mode = PART_BALANCED;
+    p.num_parts = w;
+    *n_items = w;
+    *n_slots = w + batch;
+  }
+  (void)dims;
+  *pp = p;
+  return MLA_OK;
+}
+
+struct WsLayout {
+  size_t o_part, lse_part, meta, total;
+};
+
+WsLayout ws_layout(const mla_dims_t* d, int n_slots, int batch, bool balanced) {
+  WsLayout L{};
+  if (n_slots == 0) return L;
+  L.o_part = 0;
+  L.lse_part = align256(size_t(n_slots) * d->n_heads * d->d_latent * sizeof(float));
+  L.meta = L.lse_part + align256(size_t(n_slots) * d->n_heads * sizeof(float));
+  L.total = L.meta + (balanced ? align256(size_t(2) * batch * sizeof(int32_t)) : 0);
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(mla_status_t s) {
+  switch (s) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_INVALID_ARG: return "MLA_ERR_INVALID_ARG: null pointer, bad size or inconsistent arguments";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: dtype combination or size not implemented";
+    case MLA_ERR_ALIGNMENT: return "MLA_ERR_ALIGNMENT: tensor pointer not 16-byte aligned";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE: workspace missing or too small";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP: HIP runtime error";
+  }
+  return "unknown mla_status_t";
+}
+
+const char* mla_build_info(void) {
+  return "libmla gfx950: absorb(v2 mfma, generic), decode(v2 bf16 mfma paired-wave, generic f32/bf16/fp8), "
+         "merge, out_proj(v2 mfma, generic)";
+}
+
+mla_status_t mla_absorb_q(const mla_dims_t* dims, int32_t batch, const void* q_nope, mla_dtype_t q_dt,
+                          const void* w_uk, mla_dtype_t w_dt, void* q_lat, mla_dtype_t out_dt, void* stream) {
+  if (mla_status_t s = check_dims(dims)) return s;
+  if (batch < 0) return MLA_ERR_INVALID_ARG;
+  if (!q_nope || !w_uk || !q_lat) return MLA_ERR_INVALID_ARG;
+  for (mla_dtype_t t : {q_dt, w_dt, out_dt})
+    if (t != MLA_F32 && t != MLA_BF16) return valid_dtype(t) ? MLA_ERR_UNSUPPORTED : MLA_ERR_INVALID_ARG;
+  if (!aligned16(q_nope) || !aligned16(w_uk) || !aligned16(q_lat)) return MLA_ERR_ALIGNMENT;
+  if (batch == 0) return MLA_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (is_v2(dims) && dims->d_head == 128 && q_dt == MLA_BF16 && w_dt == MLA_BF16 && out_dt == MLA_BF16) {
+    e = launch_absorb_v2(q_nope, w_uk, q_lat, batch, st);
+  } else {
+    if (dims->d_head > kGenMaxHead) return MLA_ERR_UNSUPPORTED;
+    e = launch_absorb_generic(q_nope, q_dt, w_uk, w_dt, q_lat, out_dt, batch, dims->n_heads, dims->d_head,
+                              dims->d_latent, st);
+  }
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status_t mla_decode_workspace_size(const mla_dims_t* dims, int32_t batch, int32_t max_pages_per_seq,
+                                       int32_t page_size, const mla_partition_t* part, size_t* bytes,
+                                       int32_t* num_slots) {
+  if (mla_status_t s = check_dims(dims)) return s;
+  if (!bytes) return MLA_ERR_INVALID_ARG;
+  PartParams pp;
+  int n_items = 0, n_slots = 0;
+  if (mla_status_t s = resolve(dims, batch, max_pages_per_seq, page_size, part, &pp, &n_items, &n_slots)) return s;
+  *bytes = ws_layout(dims, n_slots, batch, pp.mode == PART_BALANCED).total;
+  if (num_slots) *num_slots = n_slots;
+  return MLA_OK;
+}
+
+size_t mla_lse_part_offset(const mla_dims_t* dims, int32_t num_slots) {
+  if (dims == nullptr || num_slots <= 0) return 0;
+  return align256(size_t(num_slots) * dims->n_heads * dims->d_latent * sizeof(float));
+}
+
+mla_status_t mla_decode(const mla_dims_t* dims, int32_t batch, const void* q_lat, const void* q_pe,
+                        mla_dtype_t q_dt, const mla_paged_cache_t* cache, float softmax_scale,
+                        const mla_partition_t* part, void* workspace, size_t workspace_bytes, void* o_lat,
+                        mla_dtype_t o_dt, float* lse, void* stream) {
+  if (mla_status_t s = check_dims(dims)) return s;
+  if (!cache || !q_lat || !o_lat || (dims->d_rope > 0 && !q_pe)) return MLA_ERR_INVALID_ARG;
+  if (!cache->kv || !cache->block_table || !cache->seq_lens) return MLA_ERR_INVALID_ARG;
+  if (!valid_dtype(q_dt) || !valid_dtype(o_dt) || !valid_dtype(cache->dtype)) return MLA_ERR_INVALID_ARG;
+  if (cache->num_pages < 1 || cache->page_size < 1 || cache->max_pages_per_seq < 1) return MLA_ERR_INVALID_ARG;
+  if (!(softmax_scale > 0.f) || softmax_scale == INFINITY) return MLA_ERR_INVALID_ARG;
+  if (cache->dtype == MLA_FP8_E4M3 && !cache->scales) return MLA_ERR_INVALID_ARG;
+  // supported combinations: f32 cache with f32 queries; bf16/fp8 cache with bf16 queries
+  if (cache->dtype == MLA_F32 ? q_dt != MLA_F32 : q_dt != MLA_BF16) return MLA_ERR_UNSUPPORTED;
+  if (o_dt == MLA_FP8_E4M3) return MLA_ERR_UNSUPPORTED;
+  if (!aligned16(q_lat) || (q_pe && !aligned16(q_pe)) || !aligned16(cache->kv) || !aligned16(o_lat))
+    return MLA_ERR_ALIGNMENT;
+  PartParams pp;
+  int n_items = 0, n_slots = 0;
+  if (mla_status_t s = resolve(dims, batch, cache->max_pages_per_seq, cache->page_size, part, &pp, &n_items, &n_slots))
+    return s;
+  const WsLayout L = ws_layout(dims, n_slots, batch, pp.mode == PART_BALANCED);
+  if (L.total > 0 && (workspace == nullptr || workspace_bytes < L.total)) return MLA_ERR_WORKSPACE;
+  if (L.total > 0 && !aligned16(workspace)) return MLA_ERR_ALIGNMENT;
+  if (batch == 0 || n_items == 0) return MLA_OK;
+  char* ws = static_cast<char*>(workspace);
+  float* o_part = L.total ? reinterpret_cast<float*>(ws + L.o_part) : nullptr;
+  float* lse_part = L.total ? reinterpret_cast<float*>(ws + L.lse_part) : nullptr;
+  int32_t* meta = (L.total && pp.mode == PART_BALANCED) ? reinterpret_cast<int32_t*>(ws + L.meta) : nullptr;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+
+  const bool fast = is_v2(dims) && cache->page_size == 64 && q_dt == MLA_BF16 && cache->dtype == MLA_BF16;
+  hipError_t e;
+  if (fast) {
+    V2DecodeArgs a{};
+    a.q_lat = static_cast<const uint16_t*>(q_lat);
+    a.q_pe = static_cast<const uint16_t*>(q_pe);
+    a.kv = cache->kv;
+    a.block_table = cache->block_table;
+    a.seq_lens = cache->seq_lens;
+    a.max_pages = cache->max_pages_per_seq;
+    a.n_items = n_items;
+    a.scale_log2 = softmax_scale * kLog2e;
+    a.pp = pp;
+    a.o_part = o_part;
+    a.lse_part = lse_part;
+    a.meta = meta;
+    a.o_lat = o_lat;
+    a.o_dt = o_dt;
+    a.lse = lse;
+    e = launch_decode_v2(a, st);
+  } else {
+    if (dims->d_latent > kGenMaxLatent || dims->d_latent + dims->d_rope > kGenMaxRow) return MLA_ERR_UNSUPPORTED;
+    GenericDecodeArgs a{};
+    a.q_lat = q_lat;
+    a.q_pe = q_pe;
+    a.q_dt = q_dt;
+    a.kv = cache->kv;
+    a.scales = cache->scales;
+    a.kv_dt = cache->dtype;
+    a.block_table = cache->block_table;
+    a.seq_lens = cache->seq_lens;
+    a.max_pages = cache->max_pages_per_seq;
+    a.n_heads = dims->n_heads;
+    a.d_rope = dims->d_rope;
+    a.d_latent = dims->d_latent;
+    a.scale = softmax_scale;
+    a.pp = pp;
+    a.o_part = o_part;
+    a.lse_part = lse_part;
+    a.meta = meta;
+    a.o_lat = o_lat;
+    a.o_dt = o_dt;
+    a.lse = lse;
+    e = launch_decode_generic(a, n_items, st);
+  }
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status_t mla_merge_splits(const mla_dims_t* dims, int32_t batch, const int32_t* seq_lens, int32_t page_size,
+                              int32_t max_pages_per_seq, const mla_partition_t* part, const void* workspace,
+                              size_t workspace_bytes, void* o_lat, mla_dtype_t o_dt, float* lse, void* stream) {
+  if (mla_status_t s = check_dims(dims)) return s;
+  if (!seq_lens || !o_lat) return MLA_ERR_INVALID_ARG;
+  if (o_dt != MLA_F32 && o_dt != MLA_BF16) return valid_dtype(o_dt) ? MLA_ERR_UNSUPPORTED : MLA_ERR_INVALID_ARG;
+  if (!aligned16(o_lat)) return MLA_ERR_ALIGNMENT;
+  PartParams pp;
+  int n_items = 0, n_slots = 0;
+  if (mla_status_t s = resolve(dims, batch, max_pages_per_seq, page_size, part, &pp, &n_items, &n_slots)) return s;
+  const WsLayout L = ws_layout(dims, n_slots, batch, pp.mode == PART_BALANCED);
+  if (L.total > 0 && (workspace == nullptr || workspace_bytes < L.total)) return MLA_ERR_WORKSPACE;
+  if (batch == 0) return MLA_OK;
+  const char* ws = static_cast<const char*>(workspace);
+  MergeArgs a{};
+  a.seq_lens = seq_lens;
+  a.pp = pp;
+  a.n_heads = dims->n_heads;
+  a.d_latent = dims->d_latent;
+  a.o_part = L.total ? reinterpret_cast<const float*>(ws + L.o_part) : nullptr;
+  a.lse_part = L.total ? reinterpret_cast<const float*>(ws + L.lse_part) : nullptr;
+  a.meta = (L.total && pp.mode == PART_BALANCED) ? reinterpret_cast<const int32_t*>(ws + L.meta) : nullptr;
+  a.o_lat = o_lat;
+  a.o_dt = o_dt;
+  a.lse = lse;
+  const hipError_t e = launch_merge(a, batch, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status_t mla_out_proj(const mla_dims_t* dims, int32_t batch, const void* o_lat, mla_dtype_t o_dt, const void* w_uv,
+                          mla_dtype_t w_dt, void* o_heads, mla_dtype_t out_dt, void* stream) {
+  if (mla_status_t s = check_dims(dims)) return s;
+  if (batch < 0 || !o_lat || !w_uv || !o_heads) return MLA_ERR_INVALID_ARG;
+  for (mla_dtype_t t : {o_dt, w_dt, out_dt})
+    if (t != MLA_F32 && t != MLA_BF16) return valid_dtype(t) ? MLA_ERR_UNSUPPORTED : MLA_ERR_INVALID_ARG;
+  if (!aligned16(o_lat) || !aligned16(w_uv) || !aligned16(o_heads)) return MLA_ERR_ALIGNMENT;
+  if (batch == 0) return MLA_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (is_v2(dims) && dims->d_head == 128 && w_dt == MLA_BF16 && out_dt == MLA_BF16) {
+    e = launch_outproj_v2(o_lat, o_dt == MLA_F32, w_uv, o_heads, batch, st);
+  } else {
+    if (dims->d_latent > kGenMaxLatent) return MLA_ERR_UNSUPPORTED;
+    e = launch_outproj_generic(o_lat, o_dt, w_uv, w_dt, o_heads, out_dt, batch, dims->n_heads, dims->d_head,
+                               dims->d_latent, st);
+  }
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status_t mla_partition_host(const int32_t* seq_lens_host, int32_t batch, int32_t page_size,
+                                int32_t max_pages_per_seq, const mla_partition_t* part, int32_t* part_first,
+                                int32_t* part_count) {
+  if (batch < 0 || (batch > 0 && (!seq_lens_host || !part_first || !part_count))) return MLA_ERR_INVALID_ARG;
+  if (part && part->num_parts < 0 && part->split_tokens == 0) return MLA_ERR_INVALID_ARG;
+  mla_dims_t d{1, 1, 0, 1};
+  PartParams pp;
+  int n_items = 0, n_slots = 0;
+  if (mla_status_t s = resolve(&d, batch, max_pages_per_seq, page_size, part, &pp, &n_items, &n_slots)) return s;
+  int64_t P = 0;
+  for (int b = 0; b < batch; ++b) {
+    if (seq_lens_host[b] < 0 || int64_t(seq_lens_host[b]) > int64_t(max_pages_per_seq) * page_size)
+      return MLA_ERR_INVALID_ARG;
+    P += ceil_div(seq_lens_host[b], page_size);
+  }
+  const int64_t W = pp.mode == PART_BALANCED ? (pp.num_parts < P ? pp.num_parts : P) : 0;
+  int64_t S = 0;
+  for (int b = 0; b < batch; ++b) {
+    const int T = seq_lens_host[b];
+    const int np = ceil_div(T, page_size);
+    if (T == 0) {
+      part_first[b] = -1;
+      part_count[b] = 0;
+    } else if (pp.mode == PART_WHOLE) {
+      part_first[b] = -1;
+      part_count[b] = 1;
+    } else if (pp.mode == PART_FIXED) {
+      part_first[b] = b * pp.fixed_slots;
+      part_count[b] = ceil_div(T, pp.split_tokens);
+    } else {
+      const int wf = part_of_page(S, P, W), wl = part_of_page(S + np - 1, P, W);
+      part_first[b] = wf + b;
+      part_count[b] = wl - wf + 1;
+    }
+    S += np;
+  }
+  return MLA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,135 @@
+// Enumeration of the (sequence, token range) segments a work item processes.
+//
+// Three partitions (mla_partition_t):
+//   whole:    item b = sequence b.
+//   fixed:    item b*S + s = tokens [s*L, min((s+1)*L, T_b)) of sequence b.
+//   balanced: the pages of all sequences, in sequence order, are cut into
+//             W = min(num_parts, total pages) contiguous parts; item w takes
+//             pages [floor(w*P/W), floor((w+1)*P/W)) and may span sequences.
+//             Item w's share of sequence b uses slot w + b (unique because both
+//             w and b grow along the page stream).  The item holding a
+//             sequence's first page records w in meta[b]; the one holding its
+//             last page records w in meta[B + b], so the merge knows the slots.
+#pragma once
+
+#include "mla_common.cuh"
+
+namespace mla {
+
+// Inclusive scan of `v` over the block; `scratch` holds blockDim.x ints.  Also
+// returns the block total.  All threads must call it.
+__device__ __forceinline__ int block_inclusive_scan(int v, int* scratch, int* total) {
+  const int tid = threadIdx.x, n = blockDim.x;
+  scratch[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < n; off <<= 1) {
+    int add = tid >= off ? scratch[tid - off] : 0;
+    __syncthreads();
+    scratch[tid] += add;
+    __syncthreads();
+  }
+  int incl = scratch[tid];
+  *total = scratch[n - 1];
+  __syncthreads();
+  return incl;
+}
+
+// Iterates over the segments of one work item, in order:
+//   SegmentIter it; it.init(pp, seq_lens, item, scratch, meta);
+//   Segment sg; while (it.next(sg)) { ... }
+// `scratch` must hold blockDim.x + 4 ints of LDS and is free again once init()
+// returns.  All threads of the block must call init() and next() together; the
+// results are uniform across the block.
+struct SegmentIter {
+  PartParams pp;
+  const int32_t* seq_lens;
+  int32_t* meta;
+  int item;
+  int b;          // next sequence to look at
+  int64_t S;      // its first global page (balanced)
+  int64_t p0, p1; // the item's page range (balanced)
+  bool done;
+
+  __device__ __forceinline__ void init(const PartParams& pp_, const int32_t* __restrict__ seq_lens_, int item_,
+                                       int* scratch, int32_t* meta_) {
+    pp = pp_; seq_lens = seq_lens_; meta = meta_; item = item_;
+    done = false; b = 0; S = 0; p0 = p1 = 0;
+    if (pp.mode != PART_BALANCED) return;
+    const int B = pp.batch, page = pp.page_size;
+    const int tid = threadIdx.x, nt = blockDim.x;
+    int local = 0;
+    for (int i = tid; i < B; i += nt) local += ceil_div(max(seq_lens[i], 0), page);
+    int P = 0;
+    block_inclusive_scan(local, scratch, &P);
+    const int W = min(pp.num_parts, P);
+    if (P == 0 || item >= W) { done = true; return; }
+    p0 = part_start(item, P, W);
+    p1 = part_start(item + 1, P, W);
+    int* found = scratch + nt;  // [b_lo, S_lo]
+    if (tid == 0) { found[0] = -1; found[1] = 0; }
+    __syncthreads();
+    int offset = 0;
+    for (int base = 0; base < B; base += nt) {
+      const int i = base + tid;
+      const int np = i < B ? ceil_div(max(seq_lens[i], 0), page) : 0;
+      int tot = 0;
+      const int incl = block_inclusive_scan(np, scratch, &tot);
+      const int excl = incl - np;
+      if (i < B && np > 0 && offset + excl <= p0 && p0 < offset + incl) { found[0] = i; found[1] = offset + excl; }
+      offset += tot;
+      __syncthreads();
+      if (found[0] >= 0) break;
+    }
+    b = __builtin_amdgcn_readfirstlane(found[0]);
+    S = __builtin_amdgcn_readfirstlane(found[1]);
+    __syncthreads();
+    if (b < 0) done = true;
+  }
+
+  __device__ __forceinline__ bool next(Segment& sg) {
+    if (done) return false;
+    const int B = pp.batch, page = pp.page_size;
+    if (pp.mode == PART_WHOLE) {
+      done = true;
+      if (item >= B) return false;
+      const int T = seq_lens[item];
+      if (T <= 0) return false;
+      sg = Segment{item, 0, T, -1, true};
+      return true;
+    }
+    if (pp.mode == PART_FIXED) {
+      done = true;
+      const int bb = item / pp.fixed_slots, sp = item % pp.fixed_slots;
+      if (bb >= B) return false;
+      const int T = seq_lens[bb];
+      const int n = ceil_div(T, pp.split_tokens);
+      if (sp >= n) return false;
+      sg = Segment{bb, sp * pp.split_tokens, min(T, (sp + 1) * pp.split_tokens), item, n == 1};
+      return true;
+    }
+    while (b < B && S < p1) {
+      const int T = max(seq_lens[b], 0);
+      const int np = ceil_div(T, page);
+      const int64_t Sb = S;
+      const int bb = b;
+      S += np;
+      ++b;
+      if (np == 0) continue;
+      const int64_t lo = Sb > p0 ? Sb : p0, hi = Sb + np < p1 ? Sb + np : p1;
+      sg.b = bb;
+      sg.t0 = int(lo - Sb) * page;
+      sg.t1 = min(T, int(hi - Sb) * page);
+      sg.slot = item + bb;
+      sg.whole = (Sb >= p0) && (Sb + np <= p1);
+      if (meta != nullptr && threadIdx.x == 0) {
+        if (Sb >= p0) meta[bb] = item;
+        if (Sb + np <= p1) meta[B + bb] = item;
+      }
+      return true;
+    }
+    done = true;
+    return false;
+  }
+};
+
+}  // namespace mla

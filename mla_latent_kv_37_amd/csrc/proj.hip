@@ -1,0 +1,177 @@
+// The two per-head weight products around the decode:
+//   absorb:   q_lat[b,i,:] = (W^UK_i)^T q^C[b,i,:]      (W^UK moved to the query side)
+//   out proj: o[b, i*d_h:(i+1)*d_h] = W^UV_i o_lat[b,i,:] (W^UV applied after attention)
+// [DeepSeek-V2 explainer] §2.2.2 (W^UK absorbed on the query side, W^UV on the
+// output side); head i owns rows i*d_h..(i+1)*d_h-1 of W^UK and W^UV.
+//
+// Both are weight-streaming products (each weight element is used B times), so
+// they are bound by HBM; the V2-shape kernels run them on MFMA so the matrix
+// work stays far below the time to stream the 16.8 MB weight.
+#include "kernels.cuh"
+
+namespace mla {
+
+// ---------------------------------------------------------------------------
+// generic VALU kernels (any widths), one workgroup per (b, head)
+// ---------------------------------------------------------------------------
+constexpr int kProjThreads = 256;
+
+__global__ __launch_bounds__(kProjThreads) void absorb_generic_kernel(
+    const void* q, mla_dtype_t q_dt, const void* w, mla_dtype_t w_dt, void* out, mla_dtype_t o_dt,
+    int n_heads, int d_head, int d_latent) {
+  __shared__ float qs[1024];
+  const int b = blockIdx.x, i = blockIdx.y;
+  const int64_t qrow = (int64_t(b) * n_heads + i) * d_head;
+  for (int k = threadIdx.x; k < d_head; k += kProjThreads) qs[k] = load_any(q, qrow + k, q_dt);
+  __syncthreads();
+  const int64_t wrow0 = int64_t(i) * d_head;
+  for (int c = threadIdx.x; c < d_latent; c += kProjThreads) {
+    float acc = 0.f;
+    for (int k = 0; k < d_head; ++k) acc += qs[k] * load_any(w, (wrow0 + k) * d_latent + c, w_dt);
+    store_any(out, (int64_t(b) * n_heads + i) * d_latent + c, acc, o_dt);
+  }
+}
+
+__global__ __launch_bounds__(kProjThreads) void outproj_generic_kernel(
+    const void* o, mla_dtype_t o_dt, const void* w, mla_dtype_t w_dt, void* out, mla_dtype_t out_dt,
+    int n_heads, int d_head, int d_latent) {
+  __shared__ float os[1024];
+  const int b = blockIdx.x, i = blockIdx.y;
+  const int64_t orow = (int64_t(b) * n_heads + i) * d_latent;
+  for (int c = threadIdx.x; c < d_latent; c += kProjThreads) os[c] = load_any(o, orow + c, o_dt);
+  __syncthreads();
+  for (int k = threadIdx.x; k < d_head; k += kProjThreads) {
+    const int64_t wrow = (int64_t(i) * d_head + k) * d_latent;
+    float acc = 0.f;
+    for (int c = 0; c < d_latent; ++c) acc += load_any(w, wrow + c, w_dt) * os[c];
+    store_any(out, int64_t(b) * n_heads * d_head + int64_t(i) * d_head + k, acc, out_dt);
+  }
+}
+
+hipError_t launch_absorb_generic(const void* q, mla_dtype_t q_dt, const void* w, mla_dtype_t w_dt, void* out,
+                                 mla_dtype_t o_dt, int batch, int n_heads, int d_head, int d_latent, hipStream_t st) {
+  absorb_generic_kernel<<<dim3(batch, n_heads), kProjThreads, 0, st>>>(q, q_dt, w, w_dt, out, o_dt, n_heads, d_head,
+                                                                      d_latent);
+  return hipGetLastError();
+}
+
+hipError_t launch_outproj_generic(const void* o, mla_dtype_t o_dt, const void* w, mla_dtype_t w_dt, void* out,
+                                  mla_dtype_t out_dt, int batch, int n_heads, int d_head, int d_latent,
+                                  hipStream_t st) {
+  outproj_generic_kernel<<<dim3(batch, n_heads), kProjThreads, 0, st>>>(o, o_dt, w, w_dt, out, out_dt, n_heads,
+                                                                       d_head, d_latent);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// V2 shapes (d_h = 128, d_c = 512), bf16, v_mfma_f32_32x32x16_bf16
+// ---------------------------------------------------------------------------
+constexpr int kPH = 128, kPL = 512;
+
+// absorb, computed transposed: q_lat^T [cols x batch] = W^T [cols x k] . q^T [k x batch].
+// Workgroup (head i, 128-column block): the W^UK block [128 k x 128 cols] is
+// staged in LDS (row pitch 288 B so a 4-row transposing read hits distinct
+// banks); wavefront w owns columns 32w..32w+31 and loops over 32-row batch tiles.
+constexpr int kWPitch = 144;  // bf16 elements per staged row
+
+__global__ __launch_bounds__(256) void absorb_v2_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ w,
+                                                        uint16_t* __restrict__ out, int batch) {
+  __shared__ __attribute__((aligned(16))) uint16_t ws[kPH * kWPitch];
+  const int i = blockIdx.x, cb = blockIdx.y * 128;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5;
+  // stage W^UK[i*128 + k][cb .. cb+127]: 128 rows x 16 chunks of 16 B
+  for (int e = tid; e < kPH * 16; e += 256) {
+    const int k = e >> 4, ch = e & 15;
+    const uint4 v = *reinterpret_cast<const uint4*>(w + (int64_t(i) * kPH + k) * kPL + cb + ch * 8);
+    *reinterpret_cast<uint4*>(ws + k * kWPitch + ch * 8) = v;
+  }
+  __syncthreads();
+  // transposing read: lane (group g = lane/16, j = lane%16) -> row kbase + j/4, cols 16(g&1) + 4(j&3)
+  const int g = lane >> 4, j = lane & 15;
+  const uint16_t MLA_LDS* wl = (const uint16_t MLA_LDS*)ws;
+  const int col_l = wave * 32 + 16 * (g & 1) + 4 * (j & 3);
+  for (int bt = 0; bt < batch; bt += 32) {
+    const int bq = bt + (lane & 31);
+    f32x16 acc = {};
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const int r0 = 16 * kk + 8 * h + (j >> 2);
+      s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 MLA_LDS*)(wl + r0 * kWPitch + col_l));
+      s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 MLA_LDS*)(wl + (r0 + 4) * kWPitch + col_l));
+      typedef short s16x8 __attribute__((ext_vector_type(8)));
+      s16x8 av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      bf16x8 bv = {};
+      if (bq < batch) bv = *reinterpret_cast<const bf16x8*>(q + (int64_t(bq) * kPH + i) * kPH + 16 * kk + 8 * h);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), bv, acc, 0, 0, 0);
+    }
+    // D[col][b]: lane has b = lane%32, cols 8(r/4) + 4h + r%4 of the wave's 32 columns
+    if (bq < batch) {
+      uint16_t* o = out + (int64_t(bq) * kPH + i) * kPL + cb + wave * 32 + 4 * h;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (__bf16)acc[4 * q4 + e];
+        *reinterpret_cast<bf16x4*>(o + 8 * q4) = v;
+      }
+    }
+  }
+}
+
+// out proj, computed transposed: o^T [k x batch] = W^UV_i [k x c] . o_lat^T [c x batch].
+// Both operands are read straight from global memory (c is contiguous in both).
+// Workgroup (head i, 32-row batch tile); wavefront w owns rows k = 32w..32w+31.
+template <bool OF32>
+__global__ __launch_bounds__(256) void outproj_v2_kernel(const void* __restrict__ o_lat, const uint16_t* __restrict__ w,
+                                                         uint16_t* __restrict__ out, int batch) {
+  const int i = blockIdx.x, bt = blockIdx.y * 32;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5;
+  const int krow = wave * 32 + (lane & 31);
+  const int bq = bt + (lane & 31);
+  const bf16x8* wr = reinterpret_cast<const bf16x8*>(w + (int64_t(i) * kPH + krow) * kPL);
+  f32x16 acc = {};
+#pragma unroll 8
+  for (int kk = 0; kk < kPL / 16; ++kk) {
+    const bf16x8 av = wr[2 * kk + h];
+    bf16x8 bv = {};
+    if (bq < batch) {
+      if (OF32) {
+        const float* op = static_cast<const float*>(o_lat) + (int64_t(bq) * kPH + i) * kPL + 16 * kk + 8 * h;
+        const f32x4 x0 = *reinterpret_cast<const f32x4*>(op), x1 = *reinterpret_cast<const f32x4*>(op + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { bv[e] = (__bf16)x0[e]; bv[4 + e] = (__bf16)x1[e]; }
+      } else {
+        bv = reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(o_lat) + (int64_t(bq) * kPH + i) * kPL)[2 * kk + h];
+      }
+    }
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
+  }
+  if (bq < batch) {
+    uint16_t* o = out + int64_t(bq) * kPH * kPH + int64_t(i) * kPH + wave * 32 + 4 * h;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      bf16x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (__bf16)acc[4 * q4 + e];
+      *reinterpret_cast<bf16x4*>(o + 8 * q4) = v;
+    }
+  }
+}
+
+hipError_t launch_absorb_v2(const void* q, const void* w, void* out, int batch, hipStream_t st) {
+  absorb_v2_kernel<<<dim3(kPH, kPL / 128), 256, 0, st>>>(static_cast<const uint16_t*>(q),
+                                                          static_cast<const uint16_t*>(w),
+                                                          static_cast<uint16_t*>(out), batch);
+  return hipGetLastError();
+}
+
+hipError_t launch_outproj_v2(const void* o_lat, bool o_f32, const void* w, void* out, int batch, hipStream_t st) {
+  dim3 grid(kPH, ceil_div(batch, 32));
+  if (o_f32)
+    outproj_v2_kernel<true><<<grid, 256, 0, st>>>(o_lat, static_cast<const uint16_t*>(w), static_cast<uint16_t*>(out), batch);
+  else
+    outproj_v2_kernel<false><<<grid, 256, 0, st>>>(o_lat, static_cast<const uint16_t*>(w), static_cast<uint16_t*>(out), batch);
+  return hipGetLastError();
+}
+
+}  // namespace mla
