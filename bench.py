@@ -1,0 +1,389 @@
+#!/usr/bin/env python3
+"""MLA decode benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload ragged|long|fp8|v2b1]
+
+A step is one full MLA decode step over the batch: mla_absorb_q -> mla_decode ->
+mla_merge_splits -> mla_out_proj, every input already resident in HBM.  The
+default workload is the ragged batch (B=64, cache lengths uniform in
+[1024, 8192], DeepSeek-V2 shapes, bf16 paged cache, pages in random order).
+Inputs are rotated over --copies full copies so that successive steps do not
+find their cache in the 256 MB Infinity Cache.
+
+Prints one JSON line with the contract fields plus `roofline` (the decode
+kernel's algorithmic bytes per launch / its mean launch time, HIP events on the
+launch stream) and `cpu_baseline` (the float64 oracle on a bounded sample).
+
+Helper modes for the rocprofv3 summaries kept in profiles/:
+    python bench.py --summarize-stats DIR OUT.md      (kernel-trace --stats)
+    python bench.py --summarize-pmc FETCH_DIR WRITE_DIR COPY_BYTES OUT.json OUT.md
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MLA decode KV-tokens/s + achieved TB/s & % roofline, 128 heads, d_c=512"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix
+N_H, D_H, D_R, D_C = 128, 128, 64, 512
+ROW_BYTES_BF16 = (D_C + D_R) * 2
+DECODE_SRC = os.path.join(ROOT, "mla_latent_kv_37_amd", "csrc", "decode_v2.hip")
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "decode_traffic.json")
+
+WORKLOADS = {
+    # name: (synth config id, description, partition (split_tokens, num_parts))
+    "ragged": (3, "v2_bf16_ragged_b64_t1024-8192", (0, -1)),
+    "long": (4, "v2_bf16_long_b4_t131072_split4096", (4096, 0)),
+    "fp8": (5, "v2_fp8_b32_t16384", (0, -1)),
+    "v2b1": (2, "v2_bf16_b1_t4096", (0, -1)),
+}
+
+
+def decode_source_hash() -> str:
+    return hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()[:16]
+
+
+# ---------------------------------------------------------------------------
+# algorithmic bytes / flops (what the method must move / compute)
+# ---------------------------------------------------------------------------
+
+def algorithmic(lens, cache_dtype: str):
+    """Bytes and flops of one decode step and of the decode kernel alone.
+
+    Per cached token: the row [c^KV | k^R] (1152 B bf16; 576 B + 5 fp32 scales
+    for fp8) and 2*n_h*(d_c+d_r) + 2*n_h*d_c flops.  Per query: q^C, q^R in,
+    q_lat/o_lat intermediates excluded, o_heads out; weights W^UK, W^UV once.
+    The decode kernel alone: cache rows + its inputs q_lat, q_pe + its output
+    o_lat (bf16) and lse; block table and lengths.
+    """
+    B = len(lens)
+    T = sum(lens)
+    pages = sum((t + 63) // 64 for t in lens)
+    row = ROW_BYTES_BF16 if cache_dtype == "bf16" else (D_C + D_R) + 4 * 5
+    cache = T * row
+    meta = pages * 4 + B * 4
+    q_in = B * N_H * (D_H + D_R) * 2
+    weights = 2 * N_H * D_H * D_C * 2
+    out = B * N_H * D_H * 2
+    flops_tok = 2 * N_H * (D_C + D_R) + 2 * N_H * D_C
+    step_flops = T * flops_tok + 2 * 2 * B * N_H * D_H * D_C
+    decode_bytes = cache + meta + B * N_H * (D_C + D_R) * 2 + B * N_H * (D_C * 2 + 4)
+    return {
+        "step_bytes": cache + meta + q_in + weights + out,
+        "step_flops": step_flops,
+        "decode_bytes": decode_bytes,
+        "decode_flops": T * flops_tok,
+        "cache_bytes": cache,
+    }
+
+
+# ---------------------------------------------------------------------------
+# inputs
+# ---------------------------------------------------------------------------
+
+def make_inputs(config_id: int, copies: int, device="cuda"):
+    import numpy as np
+    import torch
+    import synth
+    import mla_latent_kv_37_amd as mk
+    inp = synth.direct_inputs_for(config_id)
+    w = inp["workload"]
+    lens = inp["lens"]
+    words, scales = [], []
+    for r in inp["rows"]:
+        wd, sc = synth.store_rows(r, w.cache_dtype)
+        words.append(wd)
+        scales.append(sc)
+    del inp["rows"]
+    maxp = max((t + 63) // 64 for t in lens)
+    sets = []
+    for c in range(copies):
+        cache = synth.build_paged(words, w.cache_dtype, synth.rng_for(config_id, synth.S_PERM + 10 * c),
+                                  scales_per_seq=scales if w.cache_dtype == "fp8" else None, spare_pages=0,
+                                  max_pages=maxp)
+        dc = mk.upload_cache(cache.kv, cache.block_table, cache.seq_lens, w.cache_dtype, 64, cache.scales, device)
+        del cache
+
+        def t(x):
+            return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(device).to(torch.bfloat16)
+
+        sets.append(dict(cache=dc, q_nope=t(inp["q_nope"]), q_pe=t(inp["q_pe"]), W_UK=t(inp["W_UK"]),
+                         W_UV=t(inp["W_UV"])))
+    return w, lens, sets
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample of the same workload
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(config_id: int, budget_s: float = 15.0):
+    import numpy as np
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 0) for p in threadpool_info()), default=0)
+    except Exception:
+        threads = 0
+    cores = threads or len(os.sched_getaffinity(0))
+    w = synth.workload(config_id)
+    tokens = 0
+    elapsed = 0.0
+    nseq = 0
+    for b in range(len(w.lens)):
+        inp = synth.direct_inputs_for(config_id, lens=[w.lens[b]])
+        rows = inp["rows"][0]
+        if w.cache_dtype == "bf16":
+            from oracle.storage import bf16_bits_to_f64
+            rows = bf16_bits_to_f64(synth.to_bf16_bits(rows))
+        else:
+            rows = rows.astype(np.float64)
+        t0 = time.perf_counter()
+        oracle.attend(inp["q_nope"][0], inp["q_pe"][0], rows[:, :D_C], rows[:, D_C:], inp["W_UK"], inp["W_UV"])
+        elapsed += time.perf_counter() - t0
+        tokens += w.lens[b]
+        nseq += 1
+        if elapsed >= budget_s:
+            break
+    return {"value": tokens / elapsed, "unit": "KV-tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"oracle.attend (float64, non-absorbed, all {N_H} heads) on the first {nseq} sequences "
+                      f"({tokens} cached tokens) of the same workload; {elapsed:.1f} s"}
+
+
+# ---------------------------------------------------------------------------
+# GPU timing
+# ---------------------------------------------------------------------------
+
+def run(args):
+    import torch
+    import mla_latent_kv_37_amd as mk
+    cid, wname, (split, parts) = WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    mk._lib.load()
+    w, lens, sets = make_inputs(cid, args.copies)
+    maxp = sets[0]["cache"].max_pages
+    step = mk.DecodeStep(N_H, D_H, D_R, D_C, len(lens), maxp, 64, split, parts)
+    scale = 1.0 / math.sqrt(D_H + D_R)
+    stream = torch.cuda.current_stream()
+
+    def one(i, ev=None):
+        s = sets[i % len(sets)]
+        if ev is not None:
+            ev[0].record(stream)
+        step.absorb(s["q_nope"], s["W_UK"])
+        if ev is not None:
+            ev[1].record(stream)
+        mk.decode(step.d, step.q_lat, s["q_pe"], s["cache"].desc, scale, step.part, step.workspace, step.o_lat,
+                  step.lse)
+        if ev is not None:
+            ev[2].record(stream)
+        mk.merge_splits(step.d, s["cache"].seq_lens, 64, maxp, step.part, step.workspace, step.o_lat, step.lse)
+        if ev is not None:
+            ev[3].record(stream)
+        step.project(s["W_UV"])
+        if ev is not None:
+            ev[4].record(stream)
+
+    for i in range(args.warmup):
+        one(i)
+    torch.cuda.synchronize()
+    # timed region: exactly K steps; per-kernel events on the launch stream
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        one(args.warmup + i, evs[i] if args.kernel_events else None)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+    per_kernel = None
+    if args.kernel_events:
+        names = ["absorb", "decode", "merge", "out_proj"]
+        per_kernel = {n: sum(e[k].elapsed_time(e[k + 1]) for e in evs) / args.steps for k, n in enumerate(names)}
+    alg = algorithmic(lens, w.cache_dtype)
+    T = sum(lens)
+    value = T * args.steps / (total_ms * 1e-3)
+    res = {
+        "metric": METRIC, "value": value, "unit": "KV-tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wname, "batch": len(lens), "sum_cache_tokens": T, "cache_dtype": w.cache_dtype,
+                   "heads": N_H, "d_latent": D_C, "d_rope": D_R, "page_size": 64,
+                   "partition": {"split_tokens": split, "num_parts": parts}, "input_copies": args.copies,
+                   "parallelism": "single GPU"},
+    }
+    step_s = ms_per_step * 1e-3
+    res["query_tokens_per_s"] = len(lens) / step_s
+    res["step_TBps"] = alg["step_bytes"] / step_s / 1e12
+    res["step_roofline"] = {
+        "hbm_us": alg["step_bytes"] / (HBM_PEAK_GBS * 1e9) * 1e6,
+        "mfma_us": alg["step_flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12) * 1e6,
+    }
+    roof_us = max(res["step_roofline"].values())
+    res["step_roofline"]["frac_of_min_roof"] = roof_us / (ms_per_step * 1e3)
+    if per_kernel:
+        res["kernel_ms"] = per_kernel
+        dec_s = per_kernel["decode"] * 1e-3
+        ach = alg["decode_bytes"] / dec_s / 1e9
+        traffic = None
+        if os.path.exists(TRAFFIC_JSON):
+            tj = json.load(open(TRAFFIC_JSON))
+            if tj.get("decode_source_sha") == decode_source_hash() and tj.get("workload") == wname:
+                traffic = tj.get("decode_bytes_per_launch")
+        res["roofline"] = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": ach / HBM_PEAK_GBS, "traffic": traffic,
+                           "kernel": "decode_v2_bf16_kernel", "algorithmic_bytes_per_launch": alg["decode_bytes"],
+                           "mean_launch_ms": per_kernel["decode"],
+                           "mfma_frac": alg["decode_flops"] / dec_s / (MFMA_BF16_PEAK_TFLOPS * 1e12)}
+    res["wall_s_timed"] = wall
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cid, args.cpu_budget)
+    return res
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3 summaries
+# ---------------------------------------------------------------------------
+
+def _db(d):
+    hits = sorted(glob.glob(os.path.join(d, "**", "*results.db"), recursive=True))
+    if not hits:
+        raise SystemExit(f"no rocprofv3 results database under {d}")
+    import sqlite3
+    return sqlite3.connect(hits[-1])
+
+
+def _short(name: str) -> str:
+    name = name.split("(")[0]
+    for pre in ("void ", "mla::"):
+        name = name.replace(pre, "")
+    return name[:60]
+
+
+def summarize_stats(d, out_md, cmd=""):
+    """Per-kernel call count and duration from a `rocprofv3 --kernel-trace --stats` run."""
+    con = _db(d)
+    rows = list(con.execute("select name, total_calls, total_duration, average, percentage from top_kernels"))
+    mins = {}
+    for name, lo, hi in con.execute("select name, min(duration), max(duration) from kernels "
+                                    "group by name"):
+        mins[name] = (lo, hi)
+    lines = ["# Kernel time summary (rocprofv3 --kernel-trace --stats)", "", f"Command: `{cmd}`", "",
+             "| kernel | calls | total us | mean us | min us | max us | % |", "|---|---|---|---|---|---|---|"]
+    for name, calls, tot, avg, pct in rows:
+        lo, hi = mins.get(name, (0, 0))
+        lines.append(f"| {_short(name)} | {calls} | {tot:.1f} | {avg:.2f} | {lo / 1e3:.2f} | {hi / 1e3:.2f} | "
+                     f"{pct:.1f} |")
+    open(out_md, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def _pmc_per_kernel(d, counter):
+    con = _db(d)
+    vals = {}
+    for name, v in con.execute("select kernel_name, value from counters_collection where counter_name = ?",
+                               (counter,)):
+        vals.setdefault(_short(name), []).append(float(v))
+    return vals
+
+
+def summarize_pmc(fetch_dir, write_dir, copy_bytes, out_json, out_md, cmd=""):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the decode kernel, scaled by
+    what the same counters read for a plain device copy of known size."""
+    import statistics
+    copy_bytes = int(copy_bytes)
+    fetch = _pmc_per_kernel(fetch_dir, "FETCH_SIZE")
+    write = _pmc_per_kernel(write_dir, "WRITE_SIZE")
+    print("kernels seen:", sorted(fetch))
+
+    def pick(vals, key):
+        ks = [k for k in vals if key in k]
+        return ks[0] if ks else None
+
+    # the calibration copy is the largest dispatch of the runtime copy kernel
+    f_copy = max(fetch[pick(fetch, "copyBuffer")]) * 1024 / copy_bytes
+    w_copy = max(write[pick(write, "copyBuffer")]) * 1024 / copy_bytes
+    f_dec = statistics.median(fetch[pick(fetch, "decode_v2")]) * 1024 / f_copy
+    w_dec = statistics.median(write[pick(write, "decode_v2")]) * 1024 / w_copy
+    others = {}
+    for k in ("merge_kernel", "absorb_v2", "outproj_v2"):
+        kf, kw = pick(fetch, k), pick(write, k)
+        if kf and kw:
+            others[k] = {"fetch_bytes": statistics.median(fetch[kf]) * 1024 / f_copy,
+                         "write_bytes": statistics.median(write[kw]) * 1024 / w_copy}
+    res = {"workload": WORKLOADS["ragged"][1], "decode_source_sha": decode_source_hash(),
+           "copy_bytes": copy_bytes, "fetch_factor": f_copy, "write_factor": w_copy,
+           "decode_fetch_bytes": f_dec, "decode_write_bytes": w_dec, "decode_bytes_per_launch": f_dec + w_dec,
+           "other_kernels": others, "command": cmd}
+    json.dump(res, open(out_json, "w"), indent=2)
+    lines = ["# HBM traffic per dispatch (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)", "",
+             f"Commands: `{cmd}`", "",
+             f"- calibration: the runtime's device copy of {copy_bytes} B; FETCH_SIZE reads "
+             f"{f_copy:.4f} KiB per KiB copied and WRITE_SIZE {w_copy:.4f}; all figures below are divided by "
+             "these factors",
+             f"- decode kernel (decode_v2_bf16_kernel, source sha256[:16] {res['decode_source_sha']}): "
+             f"fetched {f_dec / 1e6:.2f} MB, written {w_dec / 1e6:.2f} MB, total {(f_dec + w_dec) / 1e6:.2f} MB "
+             "per launch"]
+    for k, v in others.items():
+        lines.append(f"- {k}: fetched {v['fetch_bytes'] / 1e6:.2f} MB, written {v['write_bytes'] / 1e6:.2f} MB")
+    open(out_md, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def copy_calibration(nbytes: int, reps: int = 3):
+    """A plain device-to-device copy of known size (the runtime's copy kernel) whose
+    counter readings scale the decode kernel's HBM counters."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").normal_()
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="ragged", choices=sorted(WORKLOADS))
+    ap.add_argument("--copies", type=int, default=2)
+    ap.add_argument("--no-kernel-events", dest="kernel_events", action="store_false")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
+    ap.add_argument("--summarize-stats", nargs=2, metavar=("DIR", "OUT_MD"))
+    ap.add_argument("--summarize-pmc", nargs=5, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_BYTES", "OUT_JSON", "OUT_MD"))
+    ap.add_argument("--cmd", default="")
+    args = ap.parse_args()
+    if args.summarize_stats:
+        return summarize_stats(*args.summarize_stats, cmd=args.cmd)
+    if args.summarize_pmc:
+        return summarize_pmc(*args.summarize_pmc, cmd=args.cmd)
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the MLA decode path here is single-GPU (no sharding, no "
+              "collectives); use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+    res = run(args)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
