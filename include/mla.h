@@ -108,7 +108,8 @@ typedef struct {
  *   split_tokens == 0, num_parts > 0: the pages of all sequences, taken in
  *       sequence order, are divided into min(num_parts, total pages) contiguous,
  *       equal (+-1 page) parts; part w's share of sequence b uses workspace slot
- *       w + b.  num_parts < 0 means "the device's compute-unit count".
+ *       w + b.  num_parts < 0 means "chosen by the library to fill the
+ *       current device once": its compute-unit count.
  * A sequence covered by a single work item receives its final o_lat / lse
  * directly from mla_decode; the others (and empty sequences) receive them from
  * mla_merge_splits.

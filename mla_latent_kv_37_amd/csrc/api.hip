@@ -32,7 +32,7 @@ mla_status_t check_dims(const mla_dims_t* d) {
 bool valid_dtype(mla_dtype_t t) { return t == MLA_F32 || t == MLA_BF16 || t == MLA_FP8_E4M3; }
 
 // Resolve a partition into kernel parameters, item and slot counts.
-mla_status_t resolve(const mla_dims_t* dims, int32_t batch, int32_t max_pages, int32_t page_size,
+mla_status_t resolve(const mla_dims_t* /*dims*/, int32_t batch, int32_t max_pages, int32_t page_size,
                      const mla_partition_t* part, PartParams* pp, int* n_items, int* n_slots) {
   if (batch < 0 || max_pages < 1 || page_size < 1) return MLA_ERR_INVALID_ARG;
   PartParams p{};
@@ -56,17 +56,18 @@ mla_status_t resolve(const mla_dims_t* dims, int32_t batch, int32_t max_pages, i
   } else {
     int w = parts;
     if (w < 0) {
-      int dev = 0;
+      // library default: fill the device once (one workgroup per compute unit)
+      int dev = 0, cus = 0;
       if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_HIP;
-      if (hipDeviceGetAttribute(&w, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return MLA_ERR_HIP;
-      if (w < 1) return MLA_ERR_HIP;
+      if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return MLA_ERR_HIP;
+      if (cus < 1) return MLA_ERR_HIP;
+      w = cus;
     }
     p.mode = PART_BALANCED;
     p.num_parts = w;
     *n_items = w;
     *n_slots = w + batch;
   }
-  (void)dims;
   *pp = p;
   return MLA_OK;
 }

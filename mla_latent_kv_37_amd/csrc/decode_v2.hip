@@ -9,28 +9,33 @@
 //   O^T [512 x heads]   += V^T [512 x tokens] . P^T [tokens x heads]
 //
 // Work decomposition.  A work item is a list of (sequence, token range)
-// segments (partition.cuh).  Two workgroups serve each work item, one per half
-// of the heads (64 heads each); their ids are spaced by 8 so both land on the
-// same XCD and the second read of every cache line is served by that XCD's L2.
-// Inside a workgroup the 4 wavefronts form two pairs; a pair owns 32 heads.
-// Wavefront (pair p, half d) multiplies the row dims [288d, 288d+288) for the
-// scores and owns output columns [256d, 256d+256).  The pair adds its two fp32
-// partial score blocks through LDS, both members run the (identical) softmax,
-// and each accumulates its 256 columns.  Per wavefront that is 72 registers of
-// query and 128 of accumulator, and every staged byte is read from LDS once per
-// head group.
+// segments (partition.cuh); one workgroup of 8 wavefronts (2 per SIMD, so one
+// wavefront's memory and LDS waits are covered by the other's matrix work)
+// serves one work item for all 128 heads.  The wavefronts form 4 pairs; pair p
+// owns heads 32p..32p+31 and its two members sit on the same SIMD.  Member d
+// multiplies half of the 576 row dims for the scores (latent dims
+// [256d, 256d+256) plus RoPE dims [32d, 32d+32)) and owns output columns
+// [256d, 256d+256).  The pair adds its two fp32 partial score blocks through
+// LDS, both members run the (identical) softmax, and each accumulates its 256
+// columns.  Per wavefront that is 64 registers of query (the RoPE part of the
+// query is read from LDS) and 128 of accumulator, which fits two wavefronts per
+// SIMD.
 //
-// Data movement.  32-token tiles (36,864 B) are staged in LDS, triple-buffered,
-// by buffer loads that write LDS directly (16 B per lane).  The descriptor's
-// size is the tile's valid bytes, so rows past the end of a sequence read as
-// zeros (their scores are masked to -inf, and a zero value row keeps 0 * v
-// finite even when the slot holds NaN).  LDS tile layout is chunk-major: the
-// 16-byte chunk c (8 bf16) of token row t sits at c*512 + (t ^ 4*(c&1))*16.  A
-// load instruction fills two chunk columns, a K fragment (32 rows of one chunk)
-// is 512 contiguous bytes, the row XOR on odd chunks puts the two chunks a
-// transposing V read touches (4 rows x 32 B) on disjoint banks, and every LDS
-// address is a per-lane base plus an immediate.
+// Data movement.  32-token tiles (36,864 B) are staged in LDS by buffer loads
+// that write LDS directly (16 B per lane); three tile buffers give a prefetch
+// distance of two tiles.  The descriptor's size is the tile's valid bytes, so
+// rows past the end of a sequence read as zeros (their scores are masked to
+// -inf, and a zero value row keeps 0 * v finite even when the slot holds NaN).
+// LDS tile layout: 1 KB blocks of 8 rows x 8 chunks (a chunk is 16 B = 8 bf16);
+// chunk c of row t sits at (c>>3)*4096 + (t>>3)*1024 + (t&7)*128 +
+// ((c&7) ^ f(t))*16 with f(t) = (t&7 with bits 1 and 2 swapped) ^ ((t>>3)&1).
+// One load instruction fills one block from 8 whole 128-byte row segments
+// (full cache lines), and with 64 LDS banks both the K-fragment reads (32 rows
+// of one chunk) and the transposing V reads (4 rows x 32 B) are free of bank
+// conflicts.  Every LDS address is a per-lane base plus an immediate.
 //
+// Per tile k: wait for tile k, barrier, issue tile k+2, partial scores, write
+// them, barrier, add the peer's, softmax, PV.
 // Softmax.  Scores are kept in the log2 domain (scale * log2 e folded into one
 // FMA).  The running max is raised lazily: the accumulators are rescaled only
 // when a head's max grows by more than 8 (a factor 256), which keeps every
@@ -44,26 +49,79 @@ constexpr int kRowBytes = kV2Row * 2;                 // 1152
 constexpr int kTileTok = 32;
 constexpr int kTileBytes = kTileTok * kRowBytes;      // 36864
 constexpr int kNumBuf = 3;
-constexpr int kXsOffset = kNumBuf * kTileBytes;       // partial-score exchange area
-constexpr int kLdsBytes = kXsOffset + 4 * 4096;       // 126976
-constexpr int kDecThreads = 256;
-constexpr int kLoadsPerWave = 9;                      // 36 two-column loads per tile
+constexpr int kWaves = 8;
+constexpr int kDecThreads = 64 * kWaves;
+constexpr int kXsBytes = kWaves * 4096;               // partial-score exchange area
+constexpr int kQpeBytes = kV2Heads * kV2Rope * 2;     // RoPE part of the query, 16 KB
 constexpr float kRescaleSlack = 8.0f;                 // log2 units
 constexpr uint32_t kBufferFlags = 0x00020000u;        // raw buffer, 32-bit data format
 
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-// Direct-to-LDS loads of one 32-token tile.  Wavefront w issues column pairs
-// 9w .. 9w+8; `voff_lane` = ((lane&31) ^ 4*(lane>>5)) * 1152 + (lane>>5) * 16.
-__device__ __forceinline__ void issue_tile(const char* tile_ptr, int valid, char MLA_LDS* buf, int wave, int voff_lane) {
-  __amdgpu_buffer_rsrc_t rsrc =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(tile_ptr), 0, valid * kRowBytes, kBufferFlags);
-  // The column offset is a scalar offset: with or without it in the hardware
-  // range check, global row t is in range exactly when t < valid.
+// chunk-slot swizzle of row t (see the layout note above)
+__host__ __device__ constexpr int swz_f(int t) {
+  return ((t & 1) | ((t & 2) << 1) | ((t & 4) >> 1)) ^ ((t >> 3) & 1);
+}
+__host__ __device__ constexpr int tile_offset(int t, int c) {
+  return (c >> 3) * 4096 + (t >> 3) * 1024 + (t & 7) * 128 + (((c & 7) ^ swz_f(t)) * 16);
+}
+
+// Tile loads per wavefront: 36 one-block loads, 5 each for wavefronts 0-3
+// (blocks 5w..5w+4) and 4 each for wavefronts 4-7 (blocks 20+4(w-4)..).
+__device__ __forceinline__ int first_block(int wave) { return wave < 4 ? 5 * wave : 20 + 4 * (wave - 4); }
+__device__ __forceinline__ int num_blocks(int wave) { return wave < 4 ? 5 : 4; }
+
+// Direct-to-LDS loads of one 32-token tile (block i = 4*(chunk group) + row
+// block).  Lane l of a block load reads row 8*rb + (l>>3), logical chunk
+// 8*g + ((l&7) ^ f(row)), so that it lands at LDS offset i*1024 + 16*l.
+// `voff_even` / `voff_odd` hold the per-lane row/chunk byte offset for even /
+// odd row blocks; the row block's 9216 B step is added here and the chunk
+// group's 128 B step is the scalar offset.  With or without the scalar offset
+// in the hardware range check, a row is in range exactly when it is below
+// `valid`, so rows past the sequence end read as zeros.
+// The loads are inline assembly so that the compiler does not track them: they
+// have no destination registers (data goes to LDS at M0 + 16*lane) and their
+// completion is waited for explicitly (vmcnt) before the barrier that publishes
+// a tile.  The compiler's own vmcnt waits for other loads stay correct, only
+// possibly stricter, since these loads are not counted by it.
+__device__ __forceinline__ void issue_tile(const char* tile_ptr, int valid, char MLA_LDS* buf, int wave) {
+  int ln = threadIdx.x & 63;
+  asm volatile("" : "+v"(ln));  // recomputed at each use instead of held across the loop
+  const int r = ln >> 3, sl = ln & 7;
+  const int voff_even = r * kRowBytes + ((sl ^ swz_f(r)) * 16);
+  const int voff_odd = r * kRowBytes + ((sl ^ swz_f(r + 8)) * 16);
+  const uint64_t base = reinterpret_cast<uint64_t>(tile_ptr);
+  i32x4 rsrc;
+  rsrc[0] = uniform(int(uint32_t(base)));
+  rsrc[1] = uniform(int(uint32_t(base >> 32) & 0xFFFFu));  // stride 0
+  rsrc[2] = uniform(valid * kRowBytes);
+  rsrc[3] = int(kBufferFlags);
+  const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>(buf));
+  const int b0 = first_block(wave), nb = num_blocks(wave);
 #pragma unroll
-  for (int j = 0; j < kLoadsPerWave; ++j) {
-    const int q = wave * kLoadsPerWave + j;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, buf + q * 1024, 16, voff_lane, q * 32, 0, 0);
+  for (int j = 0; j < 5; ++j) {
+    if (j < nb) {
+      const int i = b0 + j;
+      const int rb = i & 3, g = i >> 2;
+      const int m0 = uniform(int(lds0 + i * 1024));
+      const int soff = uniform(g * 128);
+      const int voff = ((rb & 1) ? voff_odd : voff_even) + rb * 8 * kRowBytes;
+      asm volatile(
+          "s_mov_b32 m0, %0\n\t"
+          "s_nop 0\n\t"
+          "buffer_load_dwordx4 %1, %2, %3 offen lds"
+          :
+          : "s"(m0), "v"(voff), "s"(rsrc), "s"(soff)
+          : "memory", "m0");
+    }
   }
+}
+
+// wait until this wavefront's loads of the tile before the newest are done
+__device__ __forceinline__ void wait_tile(int wave, bool newer_in_flight) {
+  if (!newer_in_flight) __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  else if (wave < 4) __builtin_amdgcn_s_waitcnt(waitcnt_vm(5));
+  else __builtin_amdgcn_s_waitcnt(waitcnt_vm(4));
 }
 
 __device__ __forceinline__ bf16x8 lds_read_b128(const char MLA_LDS* p) {
@@ -85,99 +143,114 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& p, int base) {
   return r;
 }
 
-__global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_v2_bf16_kernel(V2DecodeArgs a) {
-  __shared__ __attribute__((aligned(1024))) char smem_raw[kLdsBytes];
-  char MLA_LDS* smem = (char MLA_LDS*)smem_raw;
-  // workgroup id -> (work item, head half); ids 16k + x and 16k + 8 + x share an XCD
-  const int bid = blockIdx.x;
-  const int item = (bid >> 4) * 8 + (bid & 7);
-  const int hh = (bid >> 3) & 1;
+  __shared__ __attribute__((aligned(1024))) char tiles_raw[kNumBuf * kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char xs_raw[kXsBytes];
+  __shared__ __attribute__((aligned(1024))) char qpe_raw[kQpeBytes];
+  char MLA_LDS* const tiles = (char MLA_LDS*)tiles_raw;
+  char MLA_LDS* const qpe_lds = (char MLA_LDS*)qpe_raw;
+  const int item = blockIdx.x;
   const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63, h = lane >> 5;
-  const int pair = wave & 1, dh = wave >> 1;
-  const int head = hh * 64 + pair * 32 + (lane & 31);
+  const int pair = wave & 3, dh = wave >> 2;   // pair members w and w^4 share a SIMD
+  const int head = pair * 32 + (lane & 31);
   if (item >= a.n_items) return;
 
-  // per-lane address parts
-  const int voff_lane = ((lane & 31) ^ (4 * h)) * kRowBytes + h * 16;
-  const int kbase = (36 * dh + h) * 512 + ((lane & 31) ^ (4 * h)) * 16;   // + kk*1024
-  int vbase;                                                                // + mt*2048 + ks*256 (+128)
-  {
-    const int g = lane >> 4, j = lane & 15, bsel = (j >> 1) & 1;
-    vbase = (32 * dh + 2 * (g & 1) + bsel) * 512 + (((4 * h + (j >> 2)) ^ (4 * bsel)) * 16) + (j & 1) * 8;
-  }
-  char MLA_LDS* xs_mine = smem + kXsOffset + wave * 4096 + lane * 16;
-  const char MLA_LDS* xs_peer = smem + kXsOffset + (wave ^ 2) * 4096 + lane * 16;
-  int cur = 0;  // buffer of the next tile to issue; advances across segments
 
   SegmentIter it;
-  it.init(a.pp, a.seq_lens, item, reinterpret_cast<int*>(smem_raw), a.meta);
+  it.init(a.pp, a.seq_lens, item, reinterpret_cast<int*>(tiles_raw), a.meta);
   Segment sg;
   while (it.next(sg)) {
     const int b = uniform(sg.b);
     const int t0 = uniform(sg.t0), t1 = uniform(sg.t1);
-    // query slice: dims 288*dh + 16*kk + 8*h .. +8 of head `head` (B operand of S^T = K Q^T)
-    bf16x8 qf[18];
-    {
-      const uint16_t* ql = a.q_lat + (int64_t(b) * kV2Heads + head) * kV2Lat;
-      const uint16_t* qp = a.q_pe + (int64_t(b) * kV2Heads + head) * kV2Rope;
-#pragma unroll
-      for (int kk = 0; kk < 18; ++kk) {
-        const int d = 288 * dh + 16 * kk + 8 * h;
-        qf[kk] = *reinterpret_cast<const bf16x8*>(d < kV2Lat ? ql + d : qp + (d - kV2Lat));
-      }
-    }
-    f32x16 acc[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = f32x16{};
-    float m_run = -INFINITY, lsum = 0.f;
-
     const int32_t* bt = a.block_table + int64_t(b) * a.max_pages;
     const char* kv = static_cast<const char*>(a.kv);
     const int ntiles = ceil_div(t1 - t0, kTileTok);
     auto tile_ptr = [&](int k) -> const char* {
       const int tok = t0 + k * kTileTok;
-      return kv + int64_t(uniform(bt[tok / kV2Page])) * (kV2Page * kRowBytes) + (tok % kV2Page) * kRowBytes;
+      return kv + int64_t(load_const(bt, tok / kV2Page)) * (kV2Page * kRowBytes) + (tok % kV2Page) * kRowBytes;
     };
-    issue_tile(tile_ptr(0), min(kTileTok, t1 - t0), smem + cur * kTileBytes, wave, voff_lane);
-    if (ntiles > 1)
-      issue_tile(tile_ptr(1), min(kTileTok, t1 - t0 - kTileTok), smem + ((cur + 1) % kNumBuf) * kTileBytes, wave,
-                 voff_lane);
+    auto tile_valid = [&](int k) { return min(kTileTok, t1 - t0 - k * kTileTok); };
+    auto tile_buf = [&](int k) { return tiles + (k % kNumBuf) * kTileBytes; };
+
+    // every wavefront is done with the previous segment's tiles, scores and query
+    raw_barrier();
+    issue_tile(tile_ptr(0), tile_valid(0), tile_buf(0), wave);
+    // latent query slice: dims 256*dh + 16*kk + 8*h .. +8 of head `head`
+    bf16x8 qf[16];
+    {
+      const uint16_t* ql = a.q_lat + (int64_t(b) * kV2Heads + head) * kV2Lat + 256 * dh + 8 * h;
+#pragma unroll
+      for (int kk = 0; kk < 16; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(ql + 16 * kk);
+      // RoPE query of all heads into LDS: thread x copies chunk (x & 7) of head x >> 3, x < 1024
+#pragma unroll
+      for (int rep = 0; rep < 2; ++rep) {
+        const int x = rep * kDecThreads + threadIdx.x;
+        const int hd = x >> 3, c = x & 7;
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(a.q_pe + (int64_t(b) * kV2Heads + hd) * kV2Rope + c * 8);
+        *reinterpret_cast<bf16x8 MLA_LDS*>(qpe_lds + hd * 128 + ((c ^ (hd & 7)) * 16)) = v;
+      }
+    }
+    // tile 0 and the query are needed first; an explicit full wait here also tells
+    // the compiler that the query registers are ready, so it puts no waits for
+    // them inside the tile loop (where they would drain the tile prefetches).
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    if (ntiles > 1) issue_tile(tile_ptr(1), tile_valid(1), tile_buf(1), wave);
+
+    f32x16 acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = f32x16{};
+    float m_run = -INFINITY, lsum = 0.f;
 
     for (int k = 0; k < ntiles; ++k) {
-      const int valid = min(kTileTok, t1 - t0 - k * kTileTok);
-      if (k + 1 < ntiles) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      if (k + 2 < ntiles)
-        issue_tile(tile_ptr(k + 2), min(kTileTok, t1 - t0 - (k + 2) * kTileTok),
-                   smem + ((cur + 2) % kNumBuf) * kTileBytes, wave, voff_lane);
-      const char MLA_LDS* tile = smem + cur * kTileBytes;
-
-      // ---- partial S^T over this wavefront's 288 row dims (18 k-steps)
-      f32x16 s = {};
-      {
-        const char MLA_LDS* kp = tile + kbase;
-        bf16x8 kf[2][2];
-        kf[0][0] = lds_read_b128(kp);
-        kf[0][1] = lds_read_b128(kp + 1024);
+      const int valid = tile_valid(k);
+      // ---- tile k (and, on the first tile, the RoPE query) visible to all
+      wait_tile(wave, k + 1 < ntiles);
+      __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
+      raw_barrier();
+      if (k + 2 < ntiles) issue_tile(tile_ptr(k + 2), tile_valid(k + 2), tile_buf(k + 2), wave);
+      const char MLA_LDS* tile = tile_buf(k);
+      // Per-lane address bases, recomputed every tile from an opaque copy of the
+      // lane id: keeping them live across the loop would cost ~12 registers,
+      // which two wavefronts per SIMD cannot spare.
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int lh = ln >> 5;
+      // K fragment of latent k-step kk = 4n+m (chunk 32dh + 2kk + h): kb[m] + n*4096;
+      // RoPE k-step j (chunk 64 + 4dh + 2j + h): kb[2dh + j] + 32768 - 16384*dh
+      int kb[4];
 #pragma unroll
-        for (int grp = 0; grp < 9; ++grp) {
-          if (grp + 1 < 9) {
-            kf[(grp + 1) & 1][0] = lds_read_b128(kp + (2 * grp + 2) * 1024);
-            kf[(grp + 1) & 1][1] = lds_read_b128(kp + (2 * grp + 3) * 1024);
-          }
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[grp & 1][0], qf[2 * grp], s, 0, 0, 0);
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[grp & 1][1], qf[2 * grp + 1], s, 0, 0, 0);
-        }
+      for (int m = 0; m < 4; ++m) kb[m] = tile_offset(ln & 31, 32 * dh + 2 * m + lh);
+      const int kq_off = 32768 - 16384 * dh;
+      // RoPE query fragment j from LDS: [head][8 chunks], chunk position c ^ (head & 7)
+      const int hd = pair * 32 + (ln & 31);
+      int qpe_off[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) qpe_off[j] = hd * 128 + (((4 * dh + 2 * j + lh) ^ (hd & 7)) * 16);
+
+      // ---- partial S^T over this wavefront's 288 row dims
+      f32x16 s = {};
+#pragma unroll
+      for (int kk = 0; kk < 16; ++kk) {
+        const bf16x8 kf = lds_read_b128(tile + kb[kk & 3] + (kk >> 2) * 4096);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s, 0, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const bf16x8 kf = lds_read_b128(tile + (dh ? kb[2 + j] : kb[j]) + kq_off);
+        const bf16x8 qv = lds_read_b128(qpe_lds + qpe_off[j]);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qv, s, 0, 0, 0);
       }
       // ---- exchange partial scores within the pair
+      char MLA_LDS* xs_mine = (char MLA_LDS*)xs_raw + wave * 4096 + ln * 16;
+      const char MLA_LDS* xs_peer = (const char MLA_LDS*)xs_raw + (wave ^ 4) * 4096 + ln * 16;
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         f32x4 v = {s[4 * q4], s[4 * q4 + 1], s[4 * q4 + 2], s[4 * q4 + 3]};
         *reinterpret_cast<f32x4 MLA_LDS*>(xs_mine + q4 * 1024) = v;
       }
-      __syncthreads();
+      __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
+      raw_barrier();
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const f32x4 v = *reinterpret_cast<const f32x4 MLA_LDS*>(xs_peer + q4 * 1024);
@@ -189,7 +262,7 @@ void decode_v2_bf16_kernel(V2DecodeArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int tok = 8 * (r >> 2) + 4 * h + (r & 3);
-        if (tok >= valid) s[r] = -INFINITY;
+        s[r] = tok < valid ? s[r] : -INFINITY;
         mx = fmaxf(mx, s[r]);
       }
       mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -208,23 +281,31 @@ void decode_v2_bf16_kernel(V2DecodeArgs a) {
       }
       const bf16x8 pk0 = pack8(s, 0), pk1 = pack8(s, 8);
       // ---- O^T += V^T . P^T over this wavefront's 256 columns
+      // V^T fragment of column tile 2n+p, token half ks, row group sec: vb[p][sec] + n*4096 + ks*2048
+      int vb[2][2];
       {
-        const char MLA_LDS* vp = tile + vbase;
-        bf16x8 vf[2][2];
-        vf[0][0] = lds_read_tr_pair(vp, vp + 128);
-        vf[0][1] = lds_read_tr_pair(vp + 256, vp + 384);
+        int l2 = lane;
+        asm volatile("" : "+v"(l2));
+        const int g = l2 >> 4, j = l2 & 15, hh2 = l2 >> 5;
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+#pragma unroll
+          for (int sec = 0; sec < 2; ++sec) {
+            const int cc = 32 * dh + 4 * p + 2 * (g & 1) + ((j >> 1) & 1);
+            const int r = 8 * sec + 4 * hh2 + (j >> 2);
+            vb[p][sec] = tile_offset(r, cc) + (j & 1) * 8;
+          }
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
-          if (mt + 1 < 8) {
-            const char MLA_LDS* q = vp + (mt + 1) * 2048;
-            vf[(mt + 1) & 1][0] = lds_read_tr_pair(q, q + 128);
-            vf[(mt + 1) & 1][1] = lds_read_tr_pair(q + 256, q + 384);
-          }
-          acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[mt & 1][0], pk0, acc[mt], 0, 0, 0);
-          acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[mt & 1][1], pk1, acc[mt], 0, 0, 0);
+          const int p = mt & 1, n = mt >> 1;
+          const bf16x8 vf = lds_read_tr_pair(tile + vb[p][0] + n * 4096 + ks * 2048,
+                                             tile + vb[p][1] + n * 4096 + ks * 2048);
+          acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, ks ? pk1 : pk0, acc[mt], 0, 0, 0);
         }
       }
-      cur = (cur + 1) % kNumBuf;
     }
 
     // ---- epilogue: normalise, write o (final or partial) and lse
@@ -274,12 +355,8 @@ void decode_v2_bf16_kernel(V2DecodeArgs a) {
   }
 }
 
-// Grid: two workgroups per work item, padded so that ids map one-to-one onto
-// (item, head half) with both halves of an item on the same XCD.
-int decode_v2_grid(int n_items) { return 2 * ((n_items + 7) / 8) * 8; }
-
 hipError_t launch_decode_v2(const V2DecodeArgs& a, hipStream_t st) {
-  decode_v2_bf16_kernel<<<decode_v2_grid(a.n_items), kDecThreads, 0, st>>>(a);
+  decode_v2_bf16_kernel<<<a.n_items, kDecThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -2,60 +2,91 @@
 // own normalised output o_s and lse_s = log sum_{j in s} exp(score_j); the whole
 // sequence has lse = log sum_s exp(lse_s) and o = sum_s exp(lse_s - lse) o_s.
 // This is the exact softmax identity used for split-K attention; it is not
-// printed on the pages.  One wavefront per (sequence, head).
+// printed on the pages.  One wavefront per (sequence, head); each lane owns
+// d_c/64 consecutive columns (8 for d_c = 512, read as two 16-byte loads).
 #include "kernels.cuh"
 
 namespace mla {
 
-
 constexpr int kMergeWaves = 4;
 
+template <int COLS>  // columns per lane when d_c == 64 * COLS (vector path); 0 = any d_c
 __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(MergeArgs a) {
   const int b = blockIdx.x;
   const int head = blockIdx.y * kMergeWaves + threadIdx.x / 64;
   const int lane = threadIdx.x % 64;
   if (head >= a.n_heads) return;
-  const int T = a.seq_lens[b];
+  const int T = load_const(a.seq_lens, b);
   const int64_t out_row = (int64_t(b) * a.n_heads + head);
   if (T <= 0) {
     for (int c = lane; c < a.d_latent; c += 64) store_any(a.o_lat, out_row * a.d_latent + c, 0.f, a.o_dt);
     if (lane == 0 && a.lse != nullptr) a.lse[out_row] = -INFINITY;
     return;
   }
-  int first, count, stride;
+  int first, count;
   if (a.pp.mode == PART_FIXED) {
     count = ceil_div(T, a.pp.split_tokens);
     first = b * a.pp.fixed_slots;
-    stride = 1;
   } else if (a.pp.mode == PART_BALANCED) {
     const int wf = a.meta[b], wl = a.meta[a.pp.batch + b];
     count = wl - wf + 1;
     first = wf + b;
-    stride = 1;
   } else {
     return;
   }
   if (count <= 1) return;
   float M = -INFINITY;
-  for (int s = 0; s < count; ++s) M = fmaxf(M, a.lse_part[int64_t(first + s * stride) * a.n_heads + head]);
+  for (int s = 0; s < count; ++s) M = fmaxf(M, a.lse_part[int64_t(first + s) * a.n_heads + head]);
   float Z = 0.f;
-  for (int s = 0; s < count; ++s) Z += expf(a.lse_part[int64_t(first + s * stride) * a.n_heads + head] - M);
-  const float invZ = 1.f / Z;
-  for (int c = lane; c < a.d_latent; c += 64) {
-    float acc = 0.f;
+  if (COLS > 0) {
+    float acc[COLS > 0 ? COLS : 1];
+#pragma unroll
+    for (int e = 0; e < COLS; ++e) acc[e] = 0.f;
     for (int s = 0; s < count; ++s) {
-      const int64_t slot = first + s * stride;
-      const float w = expf(a.lse_part[slot * a.n_heads + head] - M);
-      acc += w * a.o_part[(slot * a.n_heads + head) * a.d_latent + c];
+      const int64_t slot = first + s;
+      const float w = __expf(a.lse_part[slot * a.n_heads + head] - M);
+      Z += w;
+      const f32x4* src = reinterpret_cast<const f32x4*>(a.o_part + (slot * a.n_heads + head) * a.d_latent) +
+                         lane * (COLS / 4);
+#pragma unroll
+      for (int v = 0; v < COLS / 4; ++v) {
+        const f32x4 x = src[v];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[4 * v + e] += w * x[e];
+      }
     }
-    store_any(a.o_lat, out_row * a.d_latent + c, acc * invZ, a.o_dt);
+    const float invZ = 1.f / Z;
+    const int64_t base = out_row * a.d_latent + lane * COLS;
+    if (a.o_dt == MLA_BF16) {
+      bf16x8 o;
+#pragma unroll
+      for (int e = 0; e < COLS; ++e) o[e % 8] = (__bf16)(acc[e] * invZ);
+      if (COLS == 8) *reinterpret_cast<bf16x8*>(static_cast<uint16_t*>(a.o_lat) + base) = o;
+      else
+        for (int e = 0; e < COLS; ++e) store_any(a.o_lat, base + e, acc[e] * invZ, a.o_dt);
+    } else {
+#pragma unroll
+      for (int e = 0; e < COLS; ++e) static_cast<float*>(a.o_lat)[base + e] = acc[e] * invZ;
+    }
+  } else {
+    for (int s = 0; s < count; ++s) Z += __expf(a.lse_part[int64_t(first + s) * a.n_heads + head] - M);
+    const float invZ = 1.f / Z;
+    for (int c = lane; c < a.d_latent; c += 64) {
+      float acc = 0.f;
+      for (int s = 0; s < count; ++s) {
+        const int64_t slot = first + s;
+        acc += __expf(a.lse_part[slot * a.n_heads + head] - M) * a.o_part[(slot * a.n_heads + head) * a.d_latent + c];
+      }
+      store_any(a.o_lat, out_row * a.d_latent + c, acc * invZ, a.o_dt);
+    }
   }
-  if (lane == 0 && a.lse != nullptr) a.lse[out_row] = M + logf(Z);
+  if (lane == 0 && a.lse != nullptr) a.lse[out_row] = M + __logf(Z);
 }
 
 hipError_t launch_merge(const MergeArgs& a, int batch, hipStream_t st) {
   dim3 grid(batch, ceil_div(a.n_heads, kMergeWaves));
-  merge_kernel<<<grid, 64 * kMergeWaves, 0, st>>>(a);
+  if (a.d_latent == 512) merge_kernel<8><<<grid, 64 * kMergeWaves, 0, st>>>(a);
+  else merge_kernel<0><<<grid, 64 * kMergeWaves, 0, st>>>(a);
   return hipGetLastError();
 }
 

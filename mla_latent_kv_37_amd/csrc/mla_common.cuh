@@ -80,6 +80,30 @@ struct PartParams {
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Read-only int32 metadata (block table, lengths) through the constant address
+// space: scalar loads, counted by lgkmcnt, so waiting for them never waits for
+// in-flight vector loads of cache tiles.
+#define MLA_CONST __attribute__((address_space(4)))
+__device__ __forceinline__ int load_const(const int32_t* p, int64_t i) {
+  return ((const MLA_CONST int32_t*)(p))[i];
+}
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] |
+// vmcnt_hi[15:14]); fields not waited on are at their maximum.  Issued through
+// the builtin so the compiler's own wait insertion knows what has completed.
+constexpr int waitcnt_vm(int n) { return (n & 0xF) | (7 << 4) | (0xF << 8) | (((n >> 4) & 3) << 14); }
+constexpr int waitcnt_lgkm(int n) { return 0xF | (7 << 4) | ((n & 0xF) << 8) | (3 << 14); }
+
+// Workgroup barrier without the release/acquire fence that __syncthreads()
+// implies (which waits for every outstanding vector memory operation).  The
+// caller waits for what the other wavefronts must see (vmcnt for direct-to-LDS
+// loads, lgkmcnt for LDS writes) before calling it.
+__device__ __forceinline__ void raw_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 __host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 // First page of part w when `pages` pages are divided into `parts` parts.

@@ -58,7 +58,7 @@ struct SegmentIter {
     const int B = pp.batch, page = pp.page_size;
     const int tid = threadIdx.x, nt = blockDim.x;
     int local = 0;
-    for (int i = tid; i < B; i += nt) local += ceil_div(max(seq_lens[i], 0), page);
+    for (int i = tid; i < B; i += nt) local += ceil_div(max(load_const(seq_lens, i), 0), page);
     int P = 0;
     block_inclusive_scan(local, scratch, &P);
     const int W = min(pp.num_parts, P);
@@ -71,7 +71,7 @@ struct SegmentIter {
     int offset = 0;
     for (int base = 0; base < B; base += nt) {
       const int i = base + tid;
-      const int np = i < B ? ceil_div(max(seq_lens[i], 0), page) : 0;
+      const int np = i < B ? ceil_div(max(load_const(seq_lens, i), 0), page) : 0;
       int tot = 0;
       const int incl = block_inclusive_scan(np, scratch, &tot);
       const int excl = incl - np;
@@ -92,7 +92,7 @@ struct SegmentIter {
     if (pp.mode == PART_WHOLE) {
       done = true;
       if (item >= B) return false;
-      const int T = seq_lens[item];
+      const int T = load_const(seq_lens, item);
       if (T <= 0) return false;
       sg = Segment{item, 0, T, -1, true};
       return true;
@@ -101,14 +101,14 @@ struct SegmentIter {
       done = true;
       const int bb = item / pp.fixed_slots, sp = item % pp.fixed_slots;
       if (bb >= B) return false;
-      const int T = seq_lens[bb];
+      const int T = load_const(seq_lens, bb);
       const int n = ceil_div(T, pp.split_tokens);
       if (sp >= n) return false;
       sg = Segment{bb, sp * pp.split_tokens, min(T, (sp + 1) * pp.split_tokens), item, n == 1};
       return true;
     }
     while (b < B && S < p1) {
-      const int T = max(seq_lens[b], 0);
+      const int T = max(load_const(seq_lens, b), 0);
       const int np = ceil_div(T, page);
       const int64_t Sb = S;
       const int bb = b;
