@@ -52,7 +52,6 @@ constexpr int kNumBuf = 3;
 constexpr int kWaves = 8;
 constexpr int kDecThreads = 64 * kWaves;
 constexpr int kXsBytes = kWaves * 4096;               // partial-score exchange area
-constexpr int kQpeBytes = kV2Heads * kV2Rope * 2;     // RoPE part of the query, 16 KB
 constexpr float kRescaleSlack = 8.0f;                 // log2 units
 constexpr uint32_t kBufferFlags = 0x00020000u;        // raw buffer, 32-bit data format
 
@@ -147,9 +146,7 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(2, 
 void decode_v2_bf16_kernel(V2DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) char tiles_raw[kNumBuf * kTileBytes];
   __shared__ __attribute__((aligned(1024))) char xs_raw[kXsBytes];
-  __shared__ __attribute__((aligned(1024))) char qpe_raw[kQpeBytes];
   char MLA_LDS* const tiles = (char MLA_LDS*)tiles_raw;
-  char MLA_LDS* const qpe_lds = (char MLA_LDS*)qpe_raw;
   const int item = blockIdx.x;
   const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63, h = lane >> 5;
   const int pair = wave & 3, dh = wave >> 2;   // pair members w and w^4 share a SIMD
@@ -176,26 +173,45 @@ void decode_v2_bf16_kernel(V2DecodeArgs a) {
     // every wavefront is done with the previous segment's tiles, scores and query
     raw_barrier();
     issue_tile(tile_ptr(0), tile_valid(0), tile_buf(0), wave);
-    // latent query slice: dims 256*dh + 16*kk + 8*h .. +8 of head `head`
-    bf16x8 qf[16];
+    // query slices of head `head` (MFMA B operand: lane holds 8 consecutive dims):
+    // latent dims 256*dh + 16*kk + 8*h .. +8, RoPE dims 32*dh + 16*j + 8*h .. +8
+    bf16x8 qf[16], qr[2];
     {
       const uint16_t* ql = a.q_lat + (int64_t(b) * kV2Heads + head) * kV2Lat + 256 * dh + 8 * h;
 #pragma unroll
       for (int kk = 0; kk < 16; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(ql + 16 * kk);
-      // RoPE query of all heads into LDS: thread x copies chunk (x & 7) of head x >> 3, x < 1024
+      const uint16_t* qp = a.q_pe + (int64_t(b) * kV2Heads + head) * kV2Rope + 32 * dh + 8 * h;
 #pragma unroll
-      for (int rep = 0; rep < 2; ++rep) {
-        const int x = rep * kDecThreads + threadIdx.x;
-        const int hd = x >> 3, c = x & 7;
-        const bf16x8 v = *reinterpret_cast<const bf16x8*>(a.q_pe + (int64_t(b) * kV2Heads + hd) * kV2Rope + c * 8);
-        *reinterpret_cast<bf16x8 MLA_LDS*>(qpe_lds + hd * 128 + ((c ^ (hd & 7)) * 16)) = v;
-      }
+      for (int j = 0; j < 2; ++j) qr[j] = *reinterpret_cast<const bf16x8*>(qp + 16 * j);
     }
     // tile 0 and the query are needed first; an explicit full wait here also tells
     // the compiler that the query registers are ready, so it puts no waits for
     // them inside the tile loop (where they would drain the tile prefetches).
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     if (ntiles > 1) issue_tile(tile_ptr(1), tile_valid(1), tile_buf(1), wave);
+
+    // Per-lane LDS offsets inside a tile, without the chunk-group part (a
+    // wavefront-uniform 16384*dh for its latent half, 32768 for the RoPE group,
+    // n*4096 for later groups), which is added as a scalar or an immediate.  The
+    // chunk slot occupies address bits 4-6 and every base is a multiple of 1024,
+    // so moving to chunk c ^ x within a group is an XOR of the address with 16*x.
+    // K fragment of latent k-step 4n+m: token lane&31, chunk 32dh + 2m + h:
+    //   kb0 ^ 32m (+ n*4096).  RoPE k-step j: chunk 64 + 4dh + 2j + h:
+    //   kb0 ^ (64dh + 32j) in the RoPE group.
+    const int kb0 = tile_offset(lane & 31, h);
+    // V^T fragment (transposing reads) of column tile 2n+p, token half ks, row
+    // group sec: (vb[sec] ^ 64p) + n*4096 + ks*2048 in this wavefront's half.
+    int vb[2];
+    {
+      const int g = lane >> 4, j = lane & 15;
+#pragma unroll
+      for (int sec = 0; sec < 2; ++sec) {
+        const int cc = 2 * (g & 1) + ((j >> 1) & 1);
+        const int r = 8 * sec + 4 * h + (j >> 2);
+        vb[sec] = tile_offset(r, cc) + (j & 1) * 8;
+      }
+    }
+    const int xs_lane = lane * 16;
 
     f32x16 acc[8];
 #pragma unroll
@@ -204,68 +220,69 @@ void decode_v2_bf16_kernel(V2DecodeArgs a) {
 
     for (int k = 0; k < ntiles; ++k) {
       const int valid = tile_valid(k);
-      // ---- tile k (and, on the first tile, the RoPE query) visible to all
+      // ---- tile k visible to all
       wait_tile(wave, k + 1 < ntiles);
       __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
       raw_barrier();
       if (k + 2 < ntiles) issue_tile(tile_ptr(k + 2), tile_valid(k + 2), tile_buf(k + 2), wave);
-      const char MLA_LDS* tile = tile_buf(k);
-      // Per-lane address bases, recomputed every tile from an opaque copy of the
-      // lane id: keeping them live across the loop would cost ~12 registers,
-      // which two wavefronts per SIMD cannot spare.
-      int ln = lane;
-      asm volatile("" : "+v"(ln));
-      const int lh = ln >> 5;
-      // K fragment of latent k-step kk = 4n+m (chunk 32dh + 2kk + h): kb[m] + n*4096;
-      // RoPE k-step j (chunk 64 + 4dh + 2j + h): kb[2dh + j] + 32768 - 16384*dh
-      int kb[4];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) kb[m] = tile_offset(ln & 31, 32 * dh + 2 * m + lh);
-      const int kq_off = 32768 - 16384 * dh;
-      // RoPE query fragment j from LDS: [head][8 chunks], chunk position c ^ (head & 7)
-      const int hd = pair * 32 + (ln & 31);
-      int qpe_off[2];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) qpe_off[j] = hd * 128 + (((4 * dh + 2 * j + lh) ^ (hd & 7)) * 16);
+      // LDS byte address of this tile (scalar), kept opaque so that the
+      // constant parts of the offsets stay in the instructions' immediates
+      int tbase = uniform(int(uint32_t(reinterpret_cast<uintptr_t>(tile_buf(k)))));
+      asm volatile("" : "+s"(tbase));
+      const uint32_t kl = uint32_t(tbase + 16384 * dh) + kb0, krp = uint32_t(tbase + 32768) + kb0;
 
-      // ---- partial S^T over this wavefront's 288 row dims
+      // ---- partial S^T over this wavefront's 288 row dims; fragment reads run
+      // two k-steps ahead of the (dependent) MFMA chain
+      auto kfrag = [&](int st) -> bf16x8 {
+        const uint32_t ad = st < 16 ? (kl ^ (32 * (st & 3))) + (st >> 2) * 4096 : krp ^ (64 * dh + 32 * (st - 16));
+        return lds_read_b128((const char MLA_LDS*)(uintptr_t)ad);
+      };
       f32x16 s = {};
+      bf16x8 k0 = kfrag(0), k1 = kfrag(1);
 #pragma unroll
-      for (int kk = 0; kk < 16; ++kk) {
-        const bf16x8 kf = lds_read_b128(tile + kb[kk & 3] + (kk >> 2) * 4096);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s, 0, 0, 0);
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const bf16x8 kf = lds_read_b128(tile + (dh ? kb[2 + j] : kb[j]) + kq_off);
-        const bf16x8 qv = lds_read_b128(qpe_lds + qpe_off[j]);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qv, s, 0, 0, 0);
+      for (int st = 0; st < 18; ++st) {
+        bf16x8 k2;
+        if (st + 2 < 18) k2 = kfrag(st + 2);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, st < 16 ? qf[st] : qr[st - 16], s, 0, 0, 0);
+        k0 = k1;
+        k1 = k2;
       }
       // ---- exchange partial scores within the pair
-      char MLA_LDS* xs_mine = (char MLA_LDS*)xs_raw + wave * 4096 + ln * 16;
-      const char MLA_LDS* xs_peer = (const char MLA_LDS*)xs_raw + (wave ^ 4) * 4096 + ln * 16;
+      {
+        char MLA_LDS* xm = (char MLA_LDS*)xs_raw + wave * 4096 + xs_lane;
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        f32x4 v = {s[4 * q4], s[4 * q4 + 1], s[4 * q4 + 2], s[4 * q4 + 3]};
-        *reinterpret_cast<f32x4 MLA_LDS*>(xs_mine + q4 * 1024) = v;
+        for (int q4 = 0; q4 < 4; ++q4) {
+          f32x4 v = {s[4 * q4], s[4 * q4 + 1], s[4 * q4 + 2], s[4 * q4 + 3]};
+          *reinterpret_cast<f32x4 MLA_LDS*>(xm + q4 * 1024) = v;
+        }
       }
       __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
       raw_barrier();
+      {
+        const char MLA_LDS* xp = (const char MLA_LDS*)xs_raw + (wave ^ 4) * 4096 + xs_lane;
+        f32x4 v[4];
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4 v = *reinterpret_cast<const f32x4 MLA_LDS*>(xs_peer + q4 * 1024);
+        for (int q4 = 0; q4 < 4; ++q4) v[q4] = *reinterpret_cast<const f32x4 MLA_LDS*>(xp + q4 * 1024);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) s[4 * q4 + e] += v[e];
+        for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s[4 * q4 + e] += v[q4][e];
       }
       // ---- online softmax (lane: head `head`, 16 of the tile's tokens; lane^32 the other 16)
-      float mx = -INFINITY;
+      if (valid < kTileTok) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int tok = 8 * (r >> 2) + 4 * h + (r & 3);
-        s[r] = tok < valid ? s[r] : -INFINITY;
-        mx = fmaxf(mx, s[r]);
+        for (int r = 0; r < 16; ++r) {
+          const int tok = 8 * (r >> 2) + 4 * h + (r & 3);
+          s[r] = tok < valid ? s[r] : -INFINITY;
+        }
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      float mx = s[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+      {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      }
       const float m_new = fmaxf(m_run, mx * a.scale_log2);
       if (__any(m_new > m_run + kRescaleSlack)) {
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -275,36 +292,30 @@ void decode_v2_bf16_kernel(V2DecodeArgs a) {
         m_run = m_new;
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.scale_log2, -m_run));
-        lsum += s[r];
+      for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.scale_log2, -m_run));
+      {
+        float t0 = (s[0] + s[1]) + (s[2] + s[3]), t1 = (s[4] + s[5]) + (s[6] + s[7]);
+        float t2 = (s[8] + s[9]) + (s[10] + s[11]), t3 = (s[12] + s[13]) + (s[14] + s[15]);
+        lsum += (t0 + t1) + (t2 + t3);
       }
       const bf16x8 pk0 = pack8(s, 0), pk1 = pack8(s, 8);
-      // ---- O^T += V^T . P^T over this wavefront's 256 columns
-      // V^T fragment of column tile 2n+p, token half ks, row group sec: vb[p][sec] + n*4096 + ks*2048
-      int vb[2][2];
-      {
-        int l2 = lane;
-        asm volatile("" : "+v"(l2));
-        const int g = l2 >> 4, j = l2 & 15, hh2 = l2 >> 5;
+      // ---- O^T += V^T . P^T over this wavefront's 256 columns, fragment reads
+      // two MFMAs ahead
+      const uint32_t vl0 = uint32_t(tbase + 16384 * dh) + vb[0], vl1 = uint32_t(tbase + 16384 * dh) + vb[1];
+      auto vfrag = [&](int st) -> bf16x8 {
+        const int ks = st >> 3, mt = st & 7, p = mt & 1, n = mt >> 1;
+        const uint32_t a0 = (vl0 ^ (64 * p)) + n * 4096 + ks * 2048, a1 = (vl1 ^ (64 * p)) + n * 4096 + ks * 2048;
+        return lds_read_tr_pair((const char MLA_LDS*)(uintptr_t)a0, (const char MLA_LDS*)(uintptr_t)a1);
+      };
+      bf16x8 v0 = vfrag(0), v1 = vfrag(1);
 #pragma unroll
-        for (int p = 0; p < 2; ++p)
-#pragma unroll
-          for (int sec = 0; sec < 2; ++sec) {
-            const int cc = 32 * dh + 4 * p + 2 * (g & 1) + ((j >> 1) & 1);
-            const int r = 8 * sec + 4 * hh2 + (j >> 2);
-            vb[p][sec] = tile_offset(r, cc) + (j & 1) * 8;
-          }
-      }
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
-          const int p = mt & 1, n = mt >> 1;
-          const bf16x8 vf = lds_read_tr_pair(tile + vb[p][0] + n * 4096 + ks * 2048,
-                                             tile + vb[p][1] + n * 4096 + ks * 2048);
-          acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, ks ? pk1 : pk0, acc[mt], 0, 0, 0);
-        }
+      for (int st = 0; st < 16; ++st) {
+        bf16x8 v2;
+        if (st + 2 < 16) v2 = vfrag(st + 2);
+        const int mt = st & 7;
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, st < 8 ? pk0 : pk1, acc[mt], 0, 0, 0);
+        v0 = v1;
+        v1 = v2;
       }
     }
 
