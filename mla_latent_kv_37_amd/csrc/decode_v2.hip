@@ -9,23 +9,33 @@
 //   O^T [512 x heads]   += V^T [512 x tokens] . P^T [tokens x heads]
 //
 // Work decomposition.  A work item is a list of (sequence, token range)
-// segments (partition.cuh); one workgroup of 8 wavefronts (2 per SIMD, so one
-// wavefront's memory and LDS waits are covered by the other's matrix work)
-// serves one work item for all 128 heads.  The wavefronts form 4 pairs; pair p
-// owns heads 32p..32p+31 and its two members sit on the same SIMD.  Member d
+// segments (partition.cuh); one workgroup of 8 wavefronts serves one work item
+// for all 128 heads.  Wavefronts w and w+4 run on the same SIMD.  Pair
+// p = w >> 1 (wavefronts 2p, 2p+1) owns heads 32p..32p+31; member d = w & 1
 // multiplies half of the 576 row dims for the scores (latent dims
 // [256d, 256d+256) plus RoPE dims [32d, 32d+32)) and owns output columns
 // [256d, 256d+256).  The pair adds its two fp32 partial score blocks through
 // LDS, both members run the (identical) softmax, and each accumulates its 256
-// columns.  Per wavefront that is 64 registers of query (the RoPE part of the
-// query is read from LDS) and 128 of accumulator, which fits two wavefronts per
-// SIMD.
+// columns.  Per wavefront that is 72 registers of query and 128 of
+// accumulator, which fits two wavefronts per SIMD.
+//
+// Ping-pong schedule.  Wavefronts 0-3 (team X) and 4-7 (team Y) run the same
+// per-tile program half a tile apart, so that on every SIMD one wavefront's
+// score MFMAs overlap the other's softmax.  Time is cut into slots, each
+// opened by a workgroup barrier.  For a segment of n tiles there are 2n+1
+// slots; team X computes the partial scores of tile k in slot 2k and the
+// softmax and PV product of tile k in slot 2k+1, team Y one slot later.  The
+// barrier between the two slots of a tile also publishes the pair's partial
+// scores.
 //
 // Data movement.  32-token tiles (36,864 B) are staged in LDS by buffer loads
-// that write LDS directly (16 B per lane); three tile buffers give a prefetch
-// distance of two tiles.  The descriptor's size is the tile's valid bytes, so
-// rows past the end of a sequence read as zeros (their scores are masked to
-// -inf, and a zero value row keeps 0 * v finite even when the slot holds NaN).
+// that write LDS directly (16 B per lane); three tile buffers.  Tile t reuses
+// the buffer of tile t-3, whose last reader (team Y's PV) runs in slot 2t-4,
+// so it is issued at the start of slot 2t-3 and must be complete at the
+// barrier that opens slot 2t: three slots of latency cover.  The descriptor's
+// size is the tile's valid bytes, so rows past the end of a sequence read as
+// zeros (their scores are masked to -inf, and a zero value row keeps 0 * v
+// finite even when the slot holds NaN).
 // LDS tile layout: 1 KB blocks of 8 rows x 8 chunks (a chunk is 16 B = 8 bf16);
 // chunk c of row t sits at (c>>3)*4096 + (t>>3)*1024 + (t&7)*128 +
 // ((c&7) ^ f(t))*16 with f(t) = (t&7 with bits 1 and 2 swapped) ^ ((t>>3)&1).
@@ -34,8 +44,6 @@
 // of one chunk) and the transposing V reads (4 rows x 32 B) are free of bank
 // conflicts.  Every LDS address is a per-lane base plus an immediate.
 //
-// Per tile k: wait for tile k, barrier, issue tile k+2, partial scores, write
-// them, barrier, add the peer's, softmax, PV.
 // Softmax.  Scores are kept in the log2 domain (scale * log2 e folded into one
 // FMA).  The running max is raised lazily: the accumulators are rescaled only
 // when a head's max grows by more than 8 (a factor 256), which keeps every
@@ -46,6 +54,7 @@ namespace mla {
 
 constexpr int kV2Heads = 128, kV2Lat = 512, kV2Rope = 64, kV2Row = 576, kV2Page = 64;
 constexpr int kRowBytes = kV2Row * 2;                 // 1152
+constexpr int kPageBytes = kV2Page * kRowBytes;       // 73728
 constexpr int kTileTok = 32;
 constexpr int kTileBytes = kTileTok * kRowBytes;      // 36864
 constexpr int kNumBuf = 3;
@@ -65,17 +74,18 @@ __host__ __device__ constexpr int tile_offset(int t, int c) {
   return (c >> 3) * 4096 + (t >> 3) * 1024 + (t & 7) * 128 + (((c & 7) ^ swz_f(t)) * 16);
 }
 
-// Tile loads per wavefront: 36 one-block loads, 5 each for wavefronts 0-3
-// (blocks 5w..5w+4) and 4 each for wavefronts 4-7 (blocks 20+4(w-4)..).
-__device__ __forceinline__ int first_block(int wave) { return wave < 4 ? 5 * wave : 20 + 4 * (wave - 4); }
-__device__ __forceinline__ int num_blocks(int wave) { return wave < 4 ? 5 : 4; }
+// Tile loads: block i = 4g + rb holds rows 8rb..8rb+7 of chunk group g (chunks
+// 8g..8g+7).  Wavefront w loads row block rb = w & 3 of chunk groups 0-4
+// (w < 4) or 5-8 (w >= 4): 36 one-block loads per tile.  Lane l of a block load
+// reads row 8rb + (l>>3), logical chunk 8g + ((l&7) ^ f(row)), so that it lands
+// at LDS offset i*1024 + 16*l; its byte offset in the tile is the per-lane
+// `voff` (fixed per wavefront) plus g*128 (the scalar offset).
+__device__ __forceinline__ int dma_voff(int wave, int lane) {
+  const int row = 8 * (wave & 3) + (lane >> 3);
+  return row * kRowBytes + (((lane & 7) ^ swz_f(row)) * 16);
+}
 
-// Direct-to-LDS loads of one 32-token tile (block i = 4*(chunk group) + row
-// block).  Lane l of a block load reads row 8*rb + (l>>3), logical chunk
-// 8*g + ((l&7) ^ f(row)), so that it lands at LDS offset i*1024 + 16*l.
-// `voff_even` / `voff_odd` hold the per-lane row/chunk byte offset for even /
-// odd row blocks; the row block's 9216 B step is added here and the chunk
-// group's 128 B step is the scalar offset.  With or without the scalar offset
+// Issue this wavefront's loads of one tile.  With or without the scalar offset
 // in the hardware range check, a row is in range exactly when it is below
 // `valid`, so rows past the sequence end read as zeros.
 // The loads are inline assembly so that the compiler does not track them: they
@@ -83,28 +93,25 @@ __device__ __forceinline__ int num_blocks(int wave) { return wave < 4 ? 5 : 4; }
 // completion is waited for explicitly (vmcnt) before the barrier that publishes
 // a tile.  The compiler's own vmcnt waits for other loads stay correct, only
 // possibly stricter, since these loads are not counted by it.
-__device__ __forceinline__ void issue_tile(const char* tile_ptr, int valid, char MLA_LDS* buf, int wave) {
+__device__ __forceinline__ void issue_tile(const char* src, int valid, uint32_t buf, int wave) {
+  // per-lane offset, recomputed at each use from an opaque lane id instead of
+  // being held in a register across the tile loop
   int ln = threadIdx.x & 63;
-  asm volatile("" : "+v"(ln));  // recomputed at each use instead of held across the loop
-  const int r = ln >> 3, sl = ln & 7;
-  const int voff_even = r * kRowBytes + ((sl ^ swz_f(r)) * 16);
-  const int voff_odd = r * kRowBytes + ((sl ^ swz_f(r + 8)) * 16);
-  const uint64_t base = reinterpret_cast<uint64_t>(tile_ptr);
+  asm volatile("" : "+v"(ln));
+  const int voff = dma_voff(wave, ln);
+  const uint64_t base = reinterpret_cast<uint64_t>(src);
   i32x4 rsrc;
   rsrc[0] = uniform(int(uint32_t(base)));
   rsrc[1] = uniform(int(uint32_t(base >> 32) & 0xFFFFu));  // stride 0
   rsrc[2] = uniform(valid * kRowBytes);
   rsrc[3] = int(kBufferFlags);
-  const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>(buf));
-  const int b0 = first_block(wave), nb = num_blocks(wave);
+  const int rb = wave & 3, g0 = wave < 4 ? 0 : 5, nb = wave < 4 ? 5 : 4;
 #pragma unroll
   for (int j = 0; j < 5; ++j) {
     if (j < nb) {
-      const int i = b0 + j;
-      const int rb = i & 3, g = i >> 2;
-      const int m0 = uniform(int(lds0 + i * 1024));
+      const int g = g0 + j;
+      const int m0 = uniform(int(buf + uint32_t((4 * g + rb) * 1024)));
       const int soff = uniform(g * 128);
-      const int voff = ((rb & 1) ? voff_odd : voff_even) + rb * 8 * kRowBytes;
       asm volatile(
           "s_mov_b32 m0, %0\n\t"
           "s_nop 0\n\t"
@@ -123,13 +130,13 @@ __device__ __forceinline__ void wait_tile(int wave, bool newer_in_flight) {
   else __builtin_amdgcn_s_waitcnt(waitcnt_vm(4));
 }
 
-__device__ __forceinline__ bf16x8 lds_read_b128(const char MLA_LDS* p) {
-  return *reinterpret_cast<const bf16x8 MLA_LDS*>(p);
+__device__ __forceinline__ bf16x8 lds_read_b128(uint32_t addr) {
+  return *reinterpret_cast<const bf16x8 MLA_LDS*>((const char MLA_LDS*)(uintptr_t)addr);
 }
 
-__device__ __forceinline__ bf16x8 lds_read_tr_pair(const char MLA_LDS* p0, const char MLA_LDS* p1) {
-  s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 MLA_LDS*)(p0));
-  s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 MLA_LDS*)(p1));
+__device__ __forceinline__ bf16x8 lds_read_tr_pair(uint32_t a0, uint32_t a1) {
+  s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 MLA_LDS*)(uintptr_t)a0);
+  s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 MLA_LDS*)(uintptr_t)a1);
   typedef short s16x8 __attribute__((ext_vector_type(8)));
   s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(bf16x8, v);
@@ -144,35 +151,57 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& p, int base) {
 
 __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_v2_bf16_kernel(V2DecodeArgs a) {
-  __shared__ __attribute__((aligned(1024))) char tiles_raw[kNumBuf * kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char xs_raw[kXsBytes];
-  char MLA_LDS* const tiles = (char MLA_LDS*)tiles_raw;
+  // alignment: tile buffers at multiples of 2048 and the exchange area at a
+  // multiple of 8192 keep the XOR address tricks below exact
+  __shared__ __attribute__((aligned(2048))) char tiles_raw[kNumBuf * kTileBytes];
+  __shared__ __attribute__((aligned(8192))) char xs_raw[kXsBytes];
   const int item = blockIdx.x;
   const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63, h = lane >> 5;
-  const int pair = wave & 3, dh = wave >> 2;   // pair members w and w^4 share a SIMD
+  const int team = wave >> 2;                   // 0: wavefronts 0-3, 1: wavefronts 4-7
+  const int pair = wave >> 1, dh = wave & 1;    // pair members 2p, 2p+1 are in one team
   const int head = pair * 32 + (lane & 31);
   if (item >= a.n_items) return;
 
+  const uint32_t tiles_lds = uint32_t(reinterpret_cast<uintptr_t>(tiles_raw));
+  const uint32_t xs_lds = uint32_t(reinterpret_cast<uintptr_t>(xs_raw));
+  // Per-lane LDS offsets inside a tile, without the chunk-group part (a
+  // wavefront-uniform 16384*dh for its latent half, 32768 for the RoPE group,
+  // n*4096 for later groups), which is added as a scalar or an immediate.  The
+  // chunk slot occupies address bits 4-6 and every base is a multiple of 1024,
+  // so moving to chunk c ^ x within a group is an XOR of the address with 16*x.
+  // K fragment of latent k-step 4n+m: token lane&31, chunk 32dh + 2m + h:
+  //   kb0 ^ 32m (+ n*4096).  RoPE k-step j: chunk 64 + 4dh + 2j + h:
+  //   kb0 ^ (64dh + 32j) in the RoPE group.
+  const int kb0 = tile_offset(lane & 31, h);
+  // V^T fragment (transposing reads) of column tile 2n+p, token half ks: two
+  // 8-byte reads at rows 4h + (j>>2) and 8 + 4h + (j>>2) (j = lane & 15) of
+  // chunk 2(g&1) + ((j>>1)&1) (g = lane >> 4), byte (j&1)*8 of the chunk.  The
+  // second row's address is the first's ^ 0x410 (next row block: +1024, which
+  // flips bit 0 of the chunk swizzle: ^16); then ^ 64p + n*4096 + ks*2048.
+  const int vb0 = tile_offset(4 * h + ((lane & 15) >> 2), 2 * ((lane >> 4) & 1) + ((lane >> 1) & 1)) + (lane & 1) * 8;
+  // exchange area: wavefront w writes [w*4096, w*4096 + 4096); its partner w^1
+  // reads it (address ^ 4096)
+  const uint32_t xs_mine = xs_lds + uint32_t(wave * 4096 + lane * 16);
 
   SegmentIter it;
   it.init(a.pp, a.seq_lens, item, reinterpret_cast<int*>(tiles_raw), a.meta);
   Segment sg;
   while (it.next(sg)) {
     const int b = uniform(sg.b);
-    const int t0 = uniform(sg.t0), t1 = uniform(sg.t1);
-    const int32_t* bt = a.block_table + int64_t(b) * a.max_pages;
+    const int t0 = uniform(sg.t0), t1 = uniform(sg.t1);   // t0 is a multiple of the page size
+    const int32_t* bt = a.block_table + int64_t(b) * a.max_pages + t0 / kV2Page;
     const char* kv = static_cast<const char*>(a.kv);
     const int ntiles = ceil_div(t1 - t0, kTileTok);
-    auto tile_ptr = [&](int k) -> const char* {
-      const int tok = t0 + k * kTileTok;
-      return kv + int64_t(load_const(bt, tok / kV2Page)) * (kV2Page * kRowBytes) + (tok % kV2Page) * kRowBytes;
+    auto tile_src = [&](int k, int page_id) -> const char* {
+      return kv + int64_t(page_id) * kPageBytes + (k & 1) * kTileBytes;
     };
     auto tile_valid = [&](int k) { return min(kTileTok, t1 - t0 - k * kTileTok); };
-    auto tile_buf = [&](int k) { return tiles + (k % kNumBuf) * kTileBytes; };
+    auto tile_buf = [&](int k) { return tiles_lds + uint32_t((k % kNumBuf) * kTileBytes); };
 
-    // every wavefront is done with the previous segment's tiles, scores and query
+    // every wavefront is done with the previous segment's tiles and scores
     raw_barrier();
-    issue_tile(tile_ptr(0), tile_valid(0), tile_buf(0), wave);
+    const int page_first = load_const(bt, 0);
+    issue_tile(tile_src(0, page_first), tile_valid(0), tile_buf(0), wave);
     // query slices of head `head` (MFMA B operand: lane holds 8 consecutive dims):
     // latent dims 256*dh + 16*kk + 8*h .. +8, RoPE dims 32*dh + 16*j + 8*h .. +8
     bf16x8 qf[16], qr[2];
@@ -188,97 +217,94 @@ void decode_v2_bf16_kernel(V2DecodeArgs a) {
     // the compiler that the query registers are ready, so it puts no waits for
     // them inside the tile loop (where they would drain the tile prefetches).
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    if (ntiles > 1) issue_tile(tile_ptr(1), tile_valid(1), tile_buf(1), wave);
-
-    // Per-lane LDS offsets inside a tile, without the chunk-group part (a
-    // wavefront-uniform 16384*dh for its latent half, 32768 for the RoPE group,
-    // n*4096 for later groups), which is added as a scalar or an immediate.  The
-    // chunk slot occupies address bits 4-6 and every base is a multiple of 1024,
-    // so moving to chunk c ^ x within a group is an XOR of the address with 16*x.
-    // K fragment of latent k-step 4n+m: token lane&31, chunk 32dh + 2m + h:
-    //   kb0 ^ 32m (+ n*4096).  RoPE k-step j: chunk 64 + 4dh + 2j + h:
-    //   kb0 ^ (64dh + 32j) in the RoPE group.
-    const int kb0 = tile_offset(lane & 31, h);
-    // V^T fragment (transposing reads) of column tile 2n+p, token half ks, row
-    // group sec: (vb[sec] ^ 64p) + n*4096 + ks*2048 in this wavefront's half.
-    int vb[2];
-    {
-      const int g = lane >> 4, j = lane & 15;
-#pragma unroll
-      for (int sec = 0; sec < 2; ++sec) {
-        const int cc = 2 * (g & 1) + ((j >> 1) & 1);
-        const int r = 8 * sec + 4 * h + (j >> 2);
-        vb[sec] = tile_offset(r, cc) + (j & 1) * 8;
-      }
-    }
-    const int xs_lane = lane * 16;
+    if (ntiles > 1) issue_tile(tile_src(1, page_first), tile_valid(1), tile_buf(1), wave);
+    // page of the next tile to issue (tile 2); loaded a slot before its use
+    int page_next = ntiles > 2 ? load_const(bt, 1) : 0;
 
     f32x16 acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = f32x16{};
     float m_run = -INFINITY, lsum = 0.f;
 
-    for (int k = 0; k < ntiles; ++k) {
-      const int valid = tile_valid(k);
-      // ---- tile k visible to all
-      wait_tile(wave, k + 1 < ntiles);
+    // Opening of slot j (the same in every wavefront): wait for this
+    // wavefront's share of the tile that becomes visible, barrier, issue the
+    // loads that slot j starts, and after the slot's work prefetch the page id
+    // of the next tile to issue.
+    auto open_slot = [&](int j) {
+      if ((j & 1) == 0 && j >= 2 && j / 2 < ntiles) wait_tile(wave, j / 2 + 1 < ntiles);
       __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
       raw_barrier();
-      if (k + 2 < ntiles) issue_tile(tile_ptr(k + 2), tile_valid(k + 2), tile_buf(k + 2), wave);
-      // LDS byte address of this tile (scalar), kept opaque so that the
-      // constant parts of the offsets stay in the instructions' immediates
-      int tbase = uniform(int(uint32_t(reinterpret_cast<uintptr_t>(tile_buf(k)))));
-      asm volatile("" : "+s"(tbase));
-      const uint32_t kl = uint32_t(tbase + 16384 * dh) + kb0, krp = uint32_t(tbase + 32768) + kb0;
-
-      // ---- partial S^T over this wavefront's 288 row dims; fragment reads run
-      // two k-steps ahead of the (dependent) MFMA chain
-      auto kfrag = [&](int st) -> bf16x8 {
-        const uint32_t ad = st < 16 ? (kl ^ (32 * (st & 3))) + (st >> 2) * 4096 : krp ^ (64 * dh + 32 * (st - 16));
-        return lds_read_b128((const char MLA_LDS*)(uintptr_t)ad);
-      };
-      f32x16 s = {};
-      bf16x8 k0 = kfrag(0), k1 = kfrag(1);
-#pragma unroll
-      for (int st = 0; st < 18; ++st) {
-        bf16x8 k2;
-        if (st + 2 < 18) k2 = kfrag(st + 2);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, st < 16 ? qf[st] : qr[st - 16], s, 0, 0, 0);
-        k0 = k1;
-        k1 = k2;
+      if (j & 1) {
+        const int tn = (j + 3) >> 1;
+        if (tn < ntiles) issue_tile(tile_src(tn, page_next), tile_valid(tn), tile_buf(tn), wave);
       }
-      // ---- exchange partial scores within the pair
+    };
+    auto close_slot = [&](int j) {
+      if ((j & 1) == 0) {
+        const int tn = (j + 4) >> 1;
+        if (tn < ntiles) page_next = load_const(bt, tn >> 1);
+      }
+    };
+
+    if (team == 1) {  // slot 0 belongs to team X alone
+      open_slot(0);
+      close_slot(0);
+    }
+    for (int k = 0; k < ntiles; ++k) {
+      // ======== slot 2k + team: partial S^T of tile k over this wavefront's 288
+      // row dims; fragment reads run two k-steps ahead of the (dependent) MFMA chain
+      const int jq = 2 * k + team;
+      open_slot(jq);
+      const uint32_t tb = tile_buf(k);
+      f32x16 s = {};
       {
-        char MLA_LDS* xm = (char MLA_LDS*)xs_raw + wave * 4096 + xs_lane;
+        const uint32_t kl = tb + uint32_t(16384 * dh + kb0), krp = tb + uint32_t(32768 + kb0);
+        auto kfrag = [&](int st) -> bf16x8 {
+          return lds_read_b128(st < 16 ? (kl ^ uint32_t(32 * (st & 3))) + uint32_t((st >> 2) * 4096)
+                                       : krp ^ uint32_t(64 * dh + 32 * (st - 16)));
+        };
+        bf16x8 k0 = kfrag(0), k1 = kfrag(1);
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          f32x4 v = {s[4 * q4], s[4 * q4 + 1], s[4 * q4 + 2], s[4 * q4 + 3]};
-          *reinterpret_cast<f32x4 MLA_LDS*>(xm + q4 * 1024) = v;
+        for (int st = 0; st < 18; ++st) {
+          bf16x8 k2;
+          if (st + 2 < 18) k2 = kfrag(st + 2);
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, st < 16 ? qf[st] : qr[st - 16], s, 0, 0, 0);
+          k0 = k1;
+          k1 = k2;
         }
       }
-      __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
-      raw_barrier();
+      // publish it for the pair partner (read after the next barrier)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        f32x4 v = {s[4 * q4], s[4 * q4 + 1], s[4 * q4 + 2], s[4 * q4 + 3]};
+        *reinterpret_cast<f32x4 MLA_LDS*>((char MLA_LDS*)(uintptr_t)(xs_mine + q4 * 1024)) = v;
+      }
+      close_slot(jq);
+
+      // ======== slot 2k + team + 1: softmax and O^T += V^T . P^T of tile k
+      open_slot(jq + 1);
       {
-        const char MLA_LDS* xp = (const char MLA_LDS*)xs_raw + (wave ^ 4) * 4096 + xs_lane;
         f32x4 v[4];
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) v[q4] = *reinterpret_cast<const f32x4 MLA_LDS*>(xp + q4 * 1024);
+        for (int q4 = 0; q4 < 4; ++q4)
+          v[q4] = *reinterpret_cast<const f32x4 MLA_LDS*>((const char MLA_LDS*)(uintptr_t)((xs_mine ^ 4096u) + q4 * 1024));
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4)
 #pragma unroll
           for (int e = 0; e < 4; ++e) s[4 * q4 + e] += v[q4][e];
       }
-      // ---- online softmax (lane: head `head`, 16 of the tile's tokens; lane^32 the other 16)
+      // online softmax (lane: head `head`, 16 of the tile's tokens; lane^32 the other 16)
+      const int valid = tile_valid(k);
       if (valid < kTileTok) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int tok = 8 * (r >> 2) + 4 * h + (r & 3);
-          s[r] = tok < valid ? s[r] : -INFINITY;
+        for (int rr = 0; rr < 16; ++rr) {
+          const int tok = 8 * (rr >> 2) + 4 * h + (rr & 3);
+          s[rr] = tok < valid ? s[rr] : -INFINITY;
         }
       }
       float mx = s[0];
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+      for (int rr = 1; rr < 16; ++rr) mx = fmaxf(mx, s[rr]);
       {
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
         mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
@@ -292,31 +318,38 @@ void decode_v2_bf16_kernel(V2DecodeArgs a) {
         m_run = m_new;
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.scale_log2, -m_run));
+      for (int rr = 0; rr < 16; ++rr) s[rr] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rr], a.scale_log2, -m_run));
       {
-        float t0 = (s[0] + s[1]) + (s[2] + s[3]), t1 = (s[4] + s[5]) + (s[6] + s[7]);
-        float t2 = (s[8] + s[9]) + (s[10] + s[11]), t3 = (s[12] + s[13]) + (s[14] + s[15]);
-        lsum += (t0 + t1) + (t2 + t3);
+        float u0 = (s[0] + s[1]) + (s[2] + s[3]), u1 = (s[4] + s[5]) + (s[6] + s[7]);
+        float u2 = (s[8] + s[9]) + (s[10] + s[11]), u3 = (s[12] + s[13]) + (s[14] + s[15]);
+        lsum += (u0 + u1) + (u2 + u3);
       }
       const bf16x8 pk0 = pack8(s, 0), pk1 = pack8(s, 8);
-      // ---- O^T += V^T . P^T over this wavefront's 256 columns, fragment reads
-      // two MFMAs ahead
-      const uint32_t vl0 = uint32_t(tbase + 16384 * dh) + vb[0], vl1 = uint32_t(tbase + 16384 * dh) + vb[1];
-      auto vfrag = [&](int st) -> bf16x8 {
-        const int ks = st >> 3, mt = st & 7, p = mt & 1, n = mt >> 1;
-        const uint32_t a0 = (vl0 ^ (64 * p)) + n * 4096 + ks * 2048, a1 = (vl1 ^ (64 * p)) + n * 4096 + ks * 2048;
-        return lds_read_tr_pair((const char MLA_LDS*)(uintptr_t)a0, (const char MLA_LDS*)(uintptr_t)a1);
-      };
-      bf16x8 v0 = vfrag(0), v1 = vfrag(1);
+      // PV over this wavefront's 256 columns, fragment reads two MFMAs ahead
+      {
+        const uint32_t vh = tb + uint32_t(16384 * dh);
+        const uint32_t vl0 = vh + uint32_t(vb0), vl1 = vl0 ^ 0x410u;
+        auto vfrag = [&](int st) -> bf16x8 {
+          const int ks = st >> 3, mt = st & 7, p = mt & 1, n = mt >> 1;
+          const uint32_t off = uint32_t(n * 4096 + ks * 2048);
+          return lds_read_tr_pair((vl0 ^ uint32_t(64 * p)) + off, (vl1 ^ uint32_t(64 * p)) + off);
+        };
+        bf16x8 v0 = vfrag(0), v1 = vfrag(1);
 #pragma unroll
-      for (int st = 0; st < 16; ++st) {
-        bf16x8 v2;
-        if (st + 2 < 16) v2 = vfrag(st + 2);
-        const int mt = st & 7;
-        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, st < 8 ? pk0 : pk1, acc[mt], 0, 0, 0);
-        v0 = v1;
-        v1 = v2;
+        for (int st = 0; st < 16; ++st) {
+          bf16x8 v2;
+          if (st + 2 < 16) v2 = vfrag(st + 2);
+          const int mt = st & 7;
+          acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, st < 8 ? pk0 : pk1, acc[mt], 0, 0, 0);
+          v0 = v1;
+          v1 = v2;
+        }
       }
+      close_slot(jq + 1);
+    }
+    if (team == 0) {  // the last slot belongs to team Y alone
+      open_slot(2 * ntiles);
+      close_slot(2 * ntiles);
     }
 
     // ---- epilogue: normalise, write o (final or partial) and lse
