@@ -155,7 +155,12 @@ void decode_v2_bf16_kernel(V2DecodeArgs a) {
   // multiple of 8192 keep the XOR address tricks below exact
   __shared__ __attribute__((aligned(2048))) char tiles_raw[kNumBuf * kTileBytes];
   __shared__ __attribute__((aligned(8192))) char xs_raw[kXsBytes];
-  const int item = blockIdx.x;
+  // Work items w and w+1 usually share a sequence (and so its query).  Blocks
+  // are dealt to the 8 XCDs round robin (block x runs on XCD x % 8), so when
+  // the item count allows, XCD x gets the contiguous item range
+  // [x*n/8, (x+1)*n/8) and repeated query reads hit its L2.
+  const int n_items = a.n_items;
+  const int item = (n_items & 7) == 0 ? int(blockIdx.x & 7) * (n_items >> 3) + int(blockIdx.x >> 3) : int(blockIdx.x);
   const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63, h = lane >> 5;
   const int team = wave >> 2;                   // 0: wavefronts 0-3, 1: wavefronts 4-7
   const int pair = wave >> 1, dh = wave & 1;    // pair members 2p, 2p+1 are in one team

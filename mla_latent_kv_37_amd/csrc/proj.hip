@@ -69,51 +69,72 @@ hipError_t launch_outproj_generic(const void* o, mla_dtype_t o_dt, const void* w
 constexpr int kPH = 128, kPL = 512;
 
 // absorb, computed transposed: q_lat^T [cols x batch] = W^T [cols x k] . q^T [k x batch].
-// Workgroup (head i, 128-column block): the W^UK block [128 k x 128 cols] is
-// staged in LDS (row pitch 288 B so a 4-row transposing read hits distinct
-// banks); wavefront w owns columns 32w..32w+31 and loops over 32-row batch tiles.
-constexpr int kWPitch = 144;  // bf16 elements per staged row
+// Workgroup (head i, 128-column block, 32-row batch tile): the W^UK block
+// [128 k x 128 cols] (row pitch 288 B, so a 4-row transposing read hits
+// distinct banks) and the query tile [32 rows x 128 k] (row pitch 272 B) are
+// staged in LDS, with every global load issued before the first wait;
+// wavefront w owns columns 32w..32w+31.  Query rows past the batch are clamped
+// to the last row; their results are not stored.
+constexpr int kWPitch = 144;  // bf16 elements per staged weight row
+constexpr int kQPitch = 136;  // bf16 elements per staged query row
 
 __global__ __launch_bounds__(256) void absorb_v2_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ w,
                                                         uint16_t* __restrict__ out, int batch) {
   __shared__ __attribute__((aligned(16))) uint16_t ws[kPH * kWPitch];
-  const int i = blockIdx.x, cb = blockIdx.y * 128;
+  __shared__ __attribute__((aligned(16))) uint16_t qs[32 * kQPitch];
+  const int i = blockIdx.x, cb = blockIdx.y * 128, bt = blockIdx.z * 32;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5;
-  // stage W^UK[i*128 + k][cb .. cb+127]: 128 rows x 16 chunks of 16 B
-  for (int e = tid; e < kPH * 16; e += 256) {
-    const int k = e >> 4, ch = e & 15;
-    const uint4 v = *reinterpret_cast<const uint4*>(w + (int64_t(i) * kPH + k) * kPL + cb + ch * 8);
-    *reinterpret_cast<uint4*>(ws + k * kWPitch + ch * 8) = v;
+  // W^UK[i*128 + k][cb .. cb+127]: 128 rows x 16 chunks of 16 B, 8 per thread;
+  // q[bt + r][i][:]: 32 rows x 16 chunks, 2 per thread
+  uint4 wv[8], qv[2];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const int e = tid + 256 * r, k = e >> 4, ch = e & 15;
+    wv[r] = *reinterpret_cast<const uint4*>(w + (int64_t(i) * kPH + k) * kPL + cb + ch * 8);
+  }
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int e = tid + 256 * r, row = e >> 4, ch = e & 15;
+    const int bq = min(bt + row, batch - 1);
+    qv[r] = *reinterpret_cast<const uint4*>(q + (int64_t(bq) * kPH + i) * kPH + ch * 8);
+  }
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const int e = tid + 256 * r, k = e >> 4, ch = e & 15;
+    *reinterpret_cast<uint4*>(ws + k * kWPitch + ch * 8) = wv[r];
+  }
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int e = tid + 256 * r, row = e >> 4, ch = e & 15;
+    *reinterpret_cast<uint4*>(qs + row * kQPitch + ch * 8) = qv[r];
   }
   __syncthreads();
   // transposing read: lane (group g = lane/16, j = lane%16) -> row kbase + j/4, cols 16(g&1) + 4(j&3)
   const int g = lane >> 4, j = lane & 15;
   const uint16_t MLA_LDS* wl = (const uint16_t MLA_LDS*)ws;
+  const uint16_t MLA_LDS* ql = (const uint16_t MLA_LDS*)qs + (lane & 31) * kQPitch + 8 * h;
   const int col_l = wave * 32 + 16 * (g & 1) + 4 * (j & 3);
-  for (int bt = 0; bt < batch; bt += 32) {
-    const int bq = bt + (lane & 31);
-    f32x16 acc = {};
+  f32x16 acc = {};
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const int r0 = 16 * kk + 8 * h + (j >> 2);
-      s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 MLA_LDS*)(wl + r0 * kWPitch + col_l));
-      s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 MLA_LDS*)(wl + (r0 + 4) * kWPitch + col_l));
-      typedef short s16x8 __attribute__((ext_vector_type(8)));
-      s16x8 av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      bf16x8 bv = {};
-      if (bq < batch) bv = *reinterpret_cast<const bf16x8*>(q + (int64_t(bq) * kPH + i) * kPH + 16 * kk + 8 * h);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), bv, acc, 0, 0, 0);
-    }
-    // D[col][b]: lane has b = lane%32, cols 8(r/4) + 4h + r%4 of the wave's 32 columns
-    if (bq < batch) {
-      uint16_t* o = out + (int64_t(bq) * kPH + i) * kPL + cb + wave * 32 + 4 * h;
+  for (int kk = 0; kk < 8; ++kk) {
+    const int r0 = 16 * kk + 8 * h + (j >> 2);
+    s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 MLA_LDS*)(wl + r0 * kWPitch + col_l));
+    s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 MLA_LDS*)(wl + (r0 + 4) * kWPitch + col_l));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    s16x8 av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    const bf16x8 bv = *reinterpret_cast<const bf16x8 MLA_LDS*>(ql + 16 * kk);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), bv, acc, 0, 0, 0);
+  }
+  // D[col][b]: lane has b = lane%32, cols 8(r/4) + 4h + r%4 of the wave's 32 columns
+  const int bq = bt + (lane & 31);
+  if (bq < batch) {
+    uint16_t* o = out + (int64_t(bq) * kPH + i) * kPL + cb + wave * 32 + 4 * h;
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        bf16x4 v;
+    for (int q4 = 0; q4 < 4; ++q4) {
+      bf16x4 v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (__bf16)acc[4 * q4 + e];
-        *reinterpret_cast<bf16x4*>(o + 8 * q4) = v;
-      }
+      for (int e = 0; e < 4; ++e) v[e] = (__bf16)acc[4 * q4 + e];
+      *reinterpret_cast<bf16x4*>(o + 8 * q4) = v;
     }
   }
 }
@@ -121,6 +142,8 @@ __global__ __launch_bounds__(256) void absorb_v2_kernel(const uint16_t* __restri
 // out proj, computed transposed: o^T [k x batch] = W^UV_i [k x c] . o_lat^T [c x batch].
 // Both operands are read straight from global memory (c is contiguous in both).
 // Workgroup (head i, 32-row batch tile); wavefront w owns rows k = 32w..32w+31.
+// The 32 k-steps run in 4 groups of 8 whose operand loads are issued one group
+// ahead; batch rows past the end are clamped to the last row and not stored.
 template <bool OF32>
 __global__ __launch_bounds__(256) void outproj_v2_kernel(const void* __restrict__ o_lat, const uint16_t* __restrict__ w,
                                                          uint16_t* __restrict__ out, int batch) {
@@ -128,23 +151,36 @@ __global__ __launch_bounds__(256) void outproj_v2_kernel(const void* __restrict_
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5;
   const int krow = wave * 32 + (lane & 31);
   const int bq = bt + (lane & 31);
-  const bf16x8* wr = reinterpret_cast<const bf16x8*>(w + (int64_t(i) * kPH + krow) * kPL);
-  f32x16 acc = {};
-#pragma unroll 8
-  for (int kk = 0; kk < kPL / 16; ++kk) {
-    const bf16x8 av = wr[2 * kk + h];
-    bf16x8 bv = {};
-    if (bq < batch) {
+  const int bl = min(bq, batch - 1);
+  const bf16x8* wr = reinterpret_cast<const bf16x8*>(w + (int64_t(i) * kPH + krow) * kPL) + h;
+  const int64_t orow = (int64_t(bl) * kPH + i) * kPL + 8 * h;
+  constexpr int kG = 8;  // k-steps per group
+  struct Ops { bf16x8 a[kG], b[kG]; };
+  auto load = [&](int grp, Ops& o) {
+#pragma unroll
+    for (int t = 0; t < kG; ++t) {
+      const int kk = grp * kG + t;
+      o.a[t] = wr[2 * kk];
       if (OF32) {
-        const float* op = static_cast<const float*>(o_lat) + (int64_t(bq) * kPH + i) * kPL + 16 * kk + 8 * h;
+        const float* op = static_cast<const float*>(o_lat) + orow + 16 * kk;
         const f32x4 x0 = *reinterpret_cast<const f32x4*>(op), x1 = *reinterpret_cast<const f32x4*>(op + 4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) { bv[e] = (__bf16)x0[e]; bv[4 + e] = (__bf16)x1[e]; }
+        for (int e = 0; e < 4; ++e) { o.b[t][e] = (__bf16)x0[e]; o.b[t][4 + e] = (__bf16)x1[e]; }
       } else {
-        bv = reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(o_lat) + (int64_t(bq) * kPH + i) * kPL)[2 * kk + h];
+        o.b[t] = *reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(o_lat) + orow + 16 * kk);
       }
     }
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
+  };
+  f32x16 acc = {};
+  Ops cur, nxt;
+  load(0, cur);
+#pragma unroll
+  for (int grp = 0; grp < kPL / 16 / kG; ++grp) {
+    if (grp + 1 < kPL / 16 / kG) load(grp + 1, nxt);
+    __builtin_amdgcn_sched_barrier(0);  // the next group's loads go out before this group's MFMAs
+#pragma unroll
+    for (int t = 0; t < kG; ++t) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.a[t], cur.b[t], acc, 0, 0, 0);
+    cur = nxt;
   }
   if (bq < batch) {
     uint16_t* o = out + int64_t(bq) * kPH * kPH + int64_t(i) * kPH + wave * 32 + 4 * h;
@@ -159,7 +195,7 @@ __global__ __launch_bounds__(256) void outproj_v2_kernel(const void* __restrict_
 }
 
 hipError_t launch_absorb_v2(const void* q, const void* w, void* out, int batch, hipStream_t st) {
-  absorb_v2_kernel<<<dim3(kPH, kPL / 128), 256, 0, st>>>(static_cast<const uint16_t*>(q),
+  absorb_v2_kernel<<<dim3(kPH, kPL / 128, ceil_div(batch, 32)), 256, 0, st>>>(static_cast<const uint16_t*>(q),
                                                           static_cast<const uint16_t*>(w),
                                                           static_cast<uint16_t*>(out), batch);
   return hipGetLastError();
