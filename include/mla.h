@@ -138,10 +138,11 @@ mla_status_t mla_absorb_q(const mla_dims_t* dims, int32_t batch,
                           void* q_lat, mla_dtype_t out_dt, void* stream);
 
 /*
- * Workspace needed by mla_decode / mla_merge_splits for a partition: fp32 split
- * partials o_part [num_slots, n_h, d_c] at offset 0, then fp32 lse_part
- * [num_slots, n_h] at offset mla_lse_part_offset(...).  *bytes = 0 when the
- * partition never splits.  num_parts < 0 needs a current HIP device.
+ * Workspace needed by mla_decode / mla_merge_splits for a partition: split
+ * partials o_part [num_slots, n_h, d_c] at offset 0, stored in the o_dt of the
+ * mla_decode call (bf16 or fp32; the area is sized for fp32), then fp32
+ * lse_part [num_slots, n_h] at offset mla_lse_part_offset(...).  *bytes = 0 when
+ * the partition never splits.  num_parts < 0 needs a current HIP device.
  */
 mla_status_t mla_decode_workspace_size(const mla_dims_t* dims, int32_t batch,
                                        int32_t max_pages_per_seq, int32_t page_size,
@@ -175,7 +176,8 @@ mla_status_t mla_decode(const mla_dims_t* dims, int32_t batch,
  * work items, lse = log sum_s exp(lse_s) and o_lat = sum_s exp(lse_s - lse) o_s.
  * Sequences with no tokens get o_lat = 0 and lse = -inf.  Sequences covered by
  * one work item are left untouched.  Arguments must match the mla_decode call
- * whose partials are merged; seq_lens is the cache's device array.
+ * whose partials are merged (o_dt included: it is also the partials' dtype);
+ * seq_lens is the cache's device array.
  */
 mla_status_t mla_merge_splits(const mla_dims_t* dims, int32_t batch,
                               const int32_t* seq_lens, int32_t page_size,

@@ -77,13 +77,14 @@ class DecodeStep:
         self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
 
     def partials(self):
-        """Views (o_part [slots, n_h, d_c], lse_part [slots, n_h]) into the workspace."""
+        """Views (o_part [slots, n_h, d_c] in the output dtype, lse_part [slots, n_h] fp32) into the workspace."""
         n, h, c = self.num_slots, self.d.n_heads, self.d.d_latent
         if n == 0:
             return None, None
         off = lse_part_offset(self.d, n)
         ws = self.workspace
-        o = ws[: n * h * c * 4].view(self.torch.float32).view(n, h, c)
+        odt = self.o_lat.dtype
+        o = ws[: n * h * c * odt.itemsize].view(odt).view(n, h, c)
         l = ws[off: off + n * h * 4].view(self.torch.float32).view(n, h)
         return o, l
 

@@ -171,7 +171,7 @@ mla_status_t mla_decode(const mla_dims_t* dims, int32_t batch, const void* q_lat
   if (L.total > 0 && !aligned16(workspace)) return MLA_ERR_ALIGNMENT;
   if (batch == 0 || n_items == 0) return MLA_OK;
   char* ws = static_cast<char*>(workspace);
-  float* o_part = L.total ? reinterpret_cast<float*>(ws + L.o_part) : nullptr;
+  void* o_part = L.total ? static_cast<void*>(ws + L.o_part) : nullptr;
   float* lse_part = L.total ? reinterpret_cast<float*>(ws + L.lse_part) : nullptr;
   int32_t* meta = (L.total && pp.mode == PART_BALANCED) ? reinterpret_cast<int32_t*>(ws + L.meta) : nullptr;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -243,7 +243,7 @@ mla_status_t mla_merge_splits(const mla_dims_t* dims, int32_t batch, const int32
   a.pp = pp;
   a.n_heads = dims->n_heads;
   a.d_latent = dims->d_latent;
-  a.o_part = L.total ? reinterpret_cast<const float*>(ws + L.o_part) : nullptr;
+  a.o_part = L.total ? static_cast<const void*>(ws + L.o_part) : nullptr;
   a.lse_part = L.total ? reinterpret_cast<const float*>(ws + L.lse_part) : nullptr;
   a.meta = (L.total && pp.mode == PART_BALANCED) ? reinterpret_cast<const int32_t*>(ws + L.meta) : nullptr;
   a.o_lat = o_lat;

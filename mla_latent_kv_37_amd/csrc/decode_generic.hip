@@ -107,7 +107,7 @@ __global__ __launch_bounds__(kGenThreads) void decode_generic_kernel(GenericDeco
 #pragma unroll
       for (int k = 0; k < kGenMaxCols; ++k) {
         const int c = tid + k * kGenThreads;
-        if (c < a.d_latent) a.o_part[ob + c] = o[k] * inv;
+        if (c < a.d_latent) store_any(a.o_part, ob + c, o[k] * inv, a.o_dt);
       }
       if (tid == 0) a.lse_part[int64_t(sg.slot) * a.n_heads + head] = lse;
     }

@@ -61,6 +61,7 @@ constexpr int kNumBuf = 3;
 constexpr int kWaves = 8;
 constexpr int kDecThreads = 64 * kWaves;
 constexpr int kXsBytes = kWaves * 4096;               // partial-score exchange area
+constexpr int kQpeBytes = kV2Heads * kV2Rope * 2;     // RoPE part of the query, 16 KB
 constexpr float kRescaleSlack = 8.0f;                 // log2 units
 constexpr uint32_t kBufferFlags = 0x00020000u;        // raw buffer, 32-bit data format
 
@@ -155,6 +156,7 @@ void decode_v2_bf16_kernel(V2DecodeArgs a) {
   // multiple of 8192 keep the XOR address tricks below exact
   __shared__ __attribute__((aligned(2048))) char tiles_raw[kNumBuf * kTileBytes];
   __shared__ __attribute__((aligned(8192))) char xs_raw[kXsBytes];
+  __shared__ __attribute__((aligned(1024))) char qpe_raw[kQpeBytes];
   // Work items w and w+1 usually share a sequence (and so its query).  Blocks
   // are dealt to the 8 XCDs round robin (block x runs on XCD x % 8), so when
   // the item count allows, XCD x gets the contiguous item range
@@ -177,16 +179,24 @@ void decode_v2_bf16_kernel(V2DecodeArgs a) {
   // K fragment of latent k-step 4n+m: token lane&31, chunk 32dh + 2m + h:
   //   kb0 ^ 32m (+ n*4096).  RoPE k-step j: chunk 64 + 4dh + 2j + h:
   //   kb0 ^ (64dh + 32j) in the RoPE group.
-  const int kb0 = tile_offset(lane & 31, h);
+  auto kb0_of = [](int ln) { return tile_offset(ln & 31, ln >> 5); };
   // V^T fragment (transposing reads) of column tile 2n+p, token half ks: two
   // 8-byte reads at rows 4h + (j>>2) and 8 + 4h + (j>>2) (j = lane & 15) of
   // chunk 2(g&1) + ((j>>1)&1) (g = lane >> 4), byte (j&1)*8 of the chunk.  The
   // second row's address is the first's ^ 0x410 (next row block: +1024, which
   // flips bit 0 of the chunk swizzle: ^16); then ^ 64p + n*4096 + ks*2048.
-  const int vb0 = tile_offset(4 * h + ((lane & 15) >> 2), 2 * ((lane >> 4) & 1) + ((lane >> 1) & 1)) + (lane & 1) * 8;
+  auto vb0_of = [](int ln) {
+    return tile_offset(4 * (ln >> 5) + ((ln & 15) >> 2), 2 * ((ln >> 4) & 1) + ((ln >> 1) & 1)) + (ln & 1) * 8;
+  };
   // exchange area: wavefront w writes [w*4096, w*4096 + 4096); its partner w^1
   // reads it (address ^ 4096)
-  const uint32_t xs_mine = xs_lds + uint32_t(wave * 4096 + lane * 16);
+  auto xs_of = [&](int ln) { return xs_lds + uint32_t(wave * 4096 + ln * 16); };
+  // RoPE query of head hd, chunk c (dims 8c..8c+7) in LDS: hd*128 + ((c ^ (hd & 7)) * 16)
+  const uint32_t qpe_lds = uint32_t(reinterpret_cast<uintptr_t>(qpe_raw));
+  // The per-lane bases above are recomputed in every slot from an opaque copy
+  // of the lane id: held across the tile loop they would cost registers that
+  // two wavefronts per SIMD cannot spare.
+  auto opaque_lane = [&]() { int ln = lane; asm volatile("" : "+v"(ln)); return ln; };
 
   SegmentIter it;
   it.init(a.pp, a.seq_lens, item, reinterpret_cast<int*>(tiles_raw), a.meta);
@@ -209,14 +219,19 @@ void decode_v2_bf16_kernel(V2DecodeArgs a) {
     issue_tile(tile_src(0, page_first), tile_valid(0), tile_buf(0), wave);
     // query slices of head `head` (MFMA B operand: lane holds 8 consecutive dims):
     // latent dims 256*dh + 16*kk + 8*h .. +8, RoPE dims 32*dh + 16*j + 8*h .. +8
-    bf16x8 qf[16], qr[2];
+    bf16x8 qf[16];
     {
       const uint16_t* ql = a.q_lat + (int64_t(b) * kV2Heads + head) * kV2Lat + 256 * dh + 8 * h;
 #pragma unroll
       for (int kk = 0; kk < 16; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(ql + 16 * kk);
-      const uint16_t* qp = a.q_pe + (int64_t(b) * kV2Heads + head) * kV2Rope + 32 * dh + 8 * h;
+      // RoPE query of all heads into LDS: thread x copies chunk (x & 7) of head x >> 3
 #pragma unroll
-      for (int j = 0; j < 2; ++j) qr[j] = *reinterpret_cast<const bf16x8*>(qp + 16 * j);
+      for (int rep = 0; rep < 2; ++rep) {
+        const int x = rep * kDecThreads + threadIdx.x;
+        const int hd = x >> 3, c = x & 7;
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(a.q_pe + (int64_t(b) * kV2Heads + hd) * kV2Rope + c * 8);
+        *reinterpret_cast<bf16x8 MLA_LDS*>((char MLA_LDS*)(uintptr_t)(qpe_lds + hd * 128 + ((c ^ (hd & 7)) * 16))) = v;
+      }
     }
     // tile 0 and the query are needed first; an explicit full wait here also tells
     // the compiler that the query registers are ready, so it puts no waits for
@@ -251,7 +266,7 @@ void decode_v2_bf16_kernel(V2DecodeArgs a) {
       }
     };
 
-    if (team == 1) {  // slot 0 belongs to team X alone
+    if (team == 1) {  // slot 0 belongs to team X alone (and issues no loads)
       open_slot(0);
       close_slot(0);
     }
@@ -263,41 +278,64 @@ void decode_v2_bf16_kernel(V2DecodeArgs a) {
       const uint32_t tb = tile_buf(k);
       f32x16 s = {};
       {
+        const int ln = opaque_lane();
+        const int kb0 = kb0_of(ln);
         const uint32_t kl = tb + uint32_t(16384 * dh + kb0), krp = tb + uint32_t(32768 + kb0);
+        const int hq = pair * 32 + (ln & 31);
+        const uint32_t qpl = qpe_lds + uint32_t(hq * 128);
         auto kfrag = [&](int st) -> bf16x8 {
           return lds_read_b128(st < 16 ? (kl ^ uint32_t(32 * (st & 3))) + uint32_t((st >> 2) * 4096)
                                        : krp ^ uint32_t(64 * dh + 32 * (st - 16)));
+        };
+        // RoPE query fragment j: chunk 4dh + 2j + h of head hq
+        auto qfrag = [&](int j) -> bf16x8 {
+          return lds_read_b128(qpl + uint32_t(((4 * dh + 2 * j + (ln >> 5)) ^ (hq & 7)) * 16));
         };
         bf16x8 k0 = kfrag(0), k1 = kfrag(1);
 #pragma unroll
         for (int st = 0; st < 18; ++st) {
           bf16x8 k2;
           if (st + 2 < 18) k2 = kfrag(st + 2);
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, st < 16 ? qf[st] : qr[st - 16], s, 0, 0, 0);
+          if (st < 16) {
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[st], s, 0, 0, 0);
+          } else {
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qfrag(st - 16), s, 0, 0, 0);
+          }
           k0 = k1;
           k1 = k2;
+          __builtin_amdgcn_sched_barrier(0);  // keep the reads two steps ahead
         }
       }
       // publish it for the pair partner (read after the next barrier)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         f32x4 v = {s[4 * q4], s[4 * q4 + 1], s[4 * q4 + 2], s[4 * q4 + 3]};
-        *reinterpret_cast<f32x4 MLA_LDS*>((char MLA_LDS*)(uintptr_t)(xs_mine + q4 * 1024)) = v;
+        *reinterpret_cast<f32x4 MLA_LDS*>((char MLA_LDS*)(uintptr_t)(xs_of(opaque_lane()) + q4 * 1024)) = v;
       }
       close_slot(jq);
 
       // ======== slot 2k + team + 1: softmax and O^T += V^T . P^T of tile k
       open_slot(jq + 1);
-      {
-        f32x4 v[4];
+      // V^T fragments of this wavefront's column half (transposing reads)
+      const int lnp = opaque_lane();
+      const uint32_t vl0 = tb + uint32_t(16384 * dh + vb0_of(lnp)), vl1 = vl0 ^ 0x410u;
+      const uint32_t xs_peer = xs_of(lnp) ^ 4096u;
+      auto vfrag = [&](int st) -> bf16x8 {
+        const int ks = st >> 3, mt = st & 7, p = mt & 1, n = mt >> 1;
+        const uint32_t off = uint32_t(n * 4096 + ks * 2048);
+        return lds_read_tr_pair((vl0 ^ uint32_t(64 * p)) + off, (vl1 ^ uint32_t(64 * p)) + off);
+      };
+      // the partner's partial scores first (a wavefront's LDS reads return in
+      // order), then the first V fragments, which do not depend on the softmax
+      f32x4 pv[4];
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-          v[q4] = *reinterpret_cast<const f32x4 MLA_LDS*>((const char MLA_LDS*)(uintptr_t)((xs_mine ^ 4096u) + q4 * 1024));
+      for (int q4 = 0; q4 < 4; ++q4)
+        pv[q4] = *reinterpret_cast<const f32x4 MLA_LDS*>((const char MLA_LDS*)(uintptr_t)(xs_peer + q4 * 1024));
+      bf16x8 v0 = vfrag(0), v1 = vfrag(1);
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
+      for (int q4 = 0; q4 < 4; ++q4)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) s[4 * q4 + e] += v[q4][e];
-      }
+        for (int e = 0; e < 4; ++e) s[4 * q4 + e] += pv[q4][e];
       // online softmax (lane: head `head`, 16 of the tile's tokens; lane^32 the other 16)
       const int valid = tile_valid(k);
       if (valid < kTileTok) {
@@ -322,37 +360,32 @@ void decode_v2_bf16_kernel(V2DecodeArgs a) {
         lsum *= alpha;
         m_run = m_new;
       }
+      // Rows 0-7 of the lane (tokens 0-15 of the tile) first; the MFMAs of that
+      // token half overlap the exponentials of rows 8-15 (tokens 16-31).
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) s[rr] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rr], a.scale_log2, -m_run));
+      for (int rr = 0; rr < 8; ++rr) s[rr] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rr], a.scale_log2, -m_run));
+      const bf16x8 pk0 = pack8(s, 0);
+      bf16x8 pk1;
+#pragma unroll
+      for (int st = 0; st < 16; ++st) {
+        bf16x8 v2;
+        if (st + 2 < 16) v2 = vfrag(st + 2);
+        if (st == 8) pk1 = pack8(s, 8);
+        const int mt = st & 7;
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, st < 8 ? pk0 : pk1, acc[mt], 0, 0, 0);
+        if (st < 8) s[8 + st] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 + st], a.scale_log2, -m_run));
+        v0 = v1;
+        v1 = v2;
+        __builtin_amdgcn_sched_barrier(0);  // keep this step's order: read ahead, MFMA, exponential
+      }
       {
         float u0 = (s[0] + s[1]) + (s[2] + s[3]), u1 = (s[4] + s[5]) + (s[6] + s[7]);
         float u2 = (s[8] + s[9]) + (s[10] + s[11]), u3 = (s[12] + s[13]) + (s[14] + s[15]);
         lsum += (u0 + u1) + (u2 + u3);
       }
-      const bf16x8 pk0 = pack8(s, 0), pk1 = pack8(s, 8);
-      // PV over this wavefront's 256 columns, fragment reads two MFMAs ahead
-      {
-        const uint32_t vh = tb + uint32_t(16384 * dh);
-        const uint32_t vl0 = vh + uint32_t(vb0), vl1 = vl0 ^ 0x410u;
-        auto vfrag = [&](int st) -> bf16x8 {
-          const int ks = st >> 3, mt = st & 7, p = mt & 1, n = mt >> 1;
-          const uint32_t off = uint32_t(n * 4096 + ks * 2048);
-          return lds_read_tr_pair((vl0 ^ uint32_t(64 * p)) + off, (vl1 ^ uint32_t(64 * p)) + off);
-        };
-        bf16x8 v0 = vfrag(0), v1 = vfrag(1);
-#pragma unroll
-        for (int st = 0; st < 16; ++st) {
-          bf16x8 v2;
-          if (st + 2 < 16) v2 = vfrag(st + 2);
-          const int mt = st & 7;
-          acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, st < 8 ? pk0 : pk1, acc[mt], 0, 0, 0);
-          v0 = v1;
-          v1 = v2;
-        }
-      }
       close_slot(jq + 1);
     }
-    if (team == 0) {  // the last slot belongs to team Y alone
+    if (team == 0) {  // the last slot belongs to team Y alone (and issues no loads)
       open_slot(2 * ntiles);
       close_slot(2 * ntiles);
     }
@@ -362,34 +395,23 @@ void decode_v2_bf16_kernel(V2DecodeArgs a) {
     const float inv = 1.f / ltot;
     const float lse_nat = (m_run + __log2f(ltot)) * kLn2;
     const int colbase = 256 * dh + 4 * h;
-    if (sg.whole) {
-      const int64_t orow = (int64_t(b) * kV2Heads + head) * kV2Lat + colbase;
-      if (a.o_dt == MLA_BF16) {
-        uint16_t* o = static_cast<uint16_t*>(a.o_lat) + orow;
+    // final output of a sequence covered by this item alone, else a split
+    // partial (normalised within the split); both in the output dtype
+    void* const obase = sg.whole ? a.o_lat : a.o_part;
+    const int64_t orow = (int64_t(sg.whole ? b : sg.slot) * kV2Heads + head) * kV2Lat + colbase;
+    if (a.o_dt == MLA_BF16) {
+      uint16_t* o = static_cast<uint16_t*>(obase) + orow;
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
+      for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            bf16x4 v;
+        for (int q4 = 0; q4 < 4; ++q4) {
+          bf16x4 v;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[mt][4 * q4 + e] * inv);
-            *reinterpret_cast<bf16x4*>(o + 32 * mt + 8 * q4) = v;
-          }
-      } else {
-        float* o = static_cast<float*>(a.o_lat) + orow;
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            f32x4 v;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = acc[mt][4 * q4 + e] * inv;
-            *reinterpret_cast<f32x4*>(o + 32 * mt + 8 * q4) = v;
-          }
-      }
-      if (h == 0 && dh == 0 && a.lse != nullptr) a.lse[int64_t(b) * kV2Heads + head] = lse_nat;
+          for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[mt][4 * q4 + e] * inv);
+          *reinterpret_cast<bf16x4*>(o + 32 * mt + 8 * q4) = v;
+        }
     } else {
-      float* o = a.o_part + (int64_t(sg.slot) * kV2Heads + head) * kV2Lat + colbase;
+      float* o = static_cast<float*>(obase) + orow;
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
@@ -399,7 +421,10 @@ void decode_v2_bf16_kernel(V2DecodeArgs a) {
           for (int e = 0; e < 4; ++e) v[e] = acc[mt][4 * q4 + e] * inv;
           *reinterpret_cast<f32x4*>(o + 32 * mt + 8 * q4) = v;
         }
-      if (h == 0 && dh == 0) a.lse_part[int64_t(sg.slot) * kV2Heads + head] = lse_nat;
+    }
+    if (h == 0 && dh == 0) {
+      if (!sg.whole) a.lse_part[int64_t(sg.slot) * kV2Heads + head] = lse_nat;
+      else if (a.lse != nullptr) a.lse[int64_t(b) * kV2Heads + head] = lse_nat;
     }
   }
 }

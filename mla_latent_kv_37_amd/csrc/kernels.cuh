@@ -19,7 +19,7 @@ struct GenericDecodeArgs {
   int n_heads, d_rope, d_latent;
   float scale;
   PartParams pp;
-  float* o_part;
+  void* o_part;            // split partials, element type o_dt
   float* lse_part;
   int32_t* meta;
   void* o_lat;
@@ -37,7 +37,7 @@ struct V2DecodeArgs {
   int n_items;
   float scale_log2;        // softmax_scale * log2(e)
   PartParams pp;
-  float* o_part;
+  void* o_part;            // split partials, element type o_dt
   float* lse_part;
   int32_t* meta;
   void* o_lat;
@@ -49,7 +49,7 @@ struct MergeArgs {
   const int32_t* seq_lens;
   PartParams pp;
   int n_heads, d_latent;
-  const float* o_part;
+  const void* o_part;      // split partials, element type o_dt
   const float* lse_part;
   const int32_t* meta;
   void* o_lat;

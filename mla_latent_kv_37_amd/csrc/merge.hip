@@ -2,8 +2,9 @@
 // own normalised output o_s and lse_s = log sum_{j in s} exp(score_j); the whole
 // sequence has lse = log sum_s exp(lse_s) and o = sum_s exp(lse_s - lse) o_s.
 // This is the exact softmax identity used for split-K attention; it is not
-// printed on the pages.  One wavefront per (sequence, head); each lane owns
-// d_c/64 consecutive columns (8 for d_c = 512, read as two 16-byte loads).
+// printed on the pages.  Partials are stored in the output dtype.  One
+// wavefront per (sequence, head); each lane owns d_c/64 consecutive columns
+// (8 for d_c = 512: one 16-byte load per partial in bf16, two in fp32).
 #include "kernels.cuh"
 
 namespace mla {
@@ -46,13 +47,22 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(MergeArgs a) {
       const int64_t slot = first + s;
       const float w = __expf(a.lse_part[slot * a.n_heads + head] - M);
       Z += w;
-      const f32x4* src = reinterpret_cast<const f32x4*>(a.o_part + (slot * a.n_heads + head) * a.d_latent) +
-                         lane * (COLS / 4);
+      const int64_t src = (slot * a.n_heads + head) * a.d_latent + lane * COLS;
+      if (a.o_dt == MLA_BF16 && COLS == 8) {
+        const bf16x8 x = *reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(a.o_part) + src);
 #pragma unroll
-      for (int v = 0; v < COLS / 4; ++v) {
-        const f32x4 x = src[v];
+        for (int e = 0; e < COLS; ++e) acc[e] += w * float(x[e % 8]);
+      } else if (a.o_dt == MLA_F32) {
+        const f32x4* x4 = reinterpret_cast<const f32x4*>(static_cast<const float*>(a.o_part) + src);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[4 * v + e] += w * x[e];
+        for (int v = 0; v < COLS / 4; ++v) {
+          const f32x4 x = x4[v];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[4 * v + e] += w * x[e];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < COLS; ++e) acc[e] += w * load_any(a.o_part, src + e, a.o_dt);
       }
     }
     const float invZ = 1.f / Z;
@@ -75,7 +85,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(MergeArgs a) {
       float acc = 0.f;
       for (int s = 0; s < count; ++s) {
         const int64_t slot = first + s;
-        acc += __expf(a.lse_part[slot * a.n_heads + head] - M) * a.o_part[(slot * a.n_heads + head) * a.d_latent + c];
+        acc += __expf(a.lse_part[slot * a.n_heads + head] - M) * load_any(a.o_part, (slot * a.n_heads + head) * a.d_latent + c, a.o_dt);
       }
       store_any(a.o_lat, out_row * a.d_latent + c, acc * invZ, a.o_dt);
     }
