@@ -103,7 +103,7 @@ const char* mla_status_string(mla_status_t s) {
 }
 
 const char* mla_build_info(void) {
-  return "libmla gfx950: absorb(v2 mfma, generic), decode(v2 bf16 mfma paired-wave, generic f32/bf16/fp8), "
+  return "libmla gfx950: absorb(v2 mfma, generic), decode(v2 bf16 / fp8-dequant mfma ping-pong, generic f32/bf16/fp8), "
          "merge, out_proj(v2 mfma, generic)";
 }
 
@@ -157,6 +157,7 @@ mla_status_t mla_decode(const mla_dims_t* dims, int32_t batch, const void* q_lat
   if (cache->num_pages < 1 || cache->page_size < 1 || cache->max_pages_per_seq < 1) return MLA_ERR_INVALID_ARG;
   if (!(softmax_scale > 0.f) || softmax_scale == INFINITY) return MLA_ERR_INVALID_ARG;
   if (cache->dtype == MLA_FP8_E4M3 && !cache->scales) return MLA_ERR_INVALID_ARG;
+  if (cache->dtype == MLA_FP8_E4M3 && !aligned16(cache->scales)) return MLA_ERR_ALIGNMENT;
   // supported combinations: f32 cache with f32 queries; bf16/fp8 cache with bf16 queries
   if (cache->dtype == MLA_F32 ? q_dt != MLA_F32 : q_dt != MLA_BF16) return MLA_ERR_UNSUPPORTED;
   if (o_dt == MLA_FP8_E4M3) return MLA_ERR_UNSUPPORTED;
@@ -176,13 +177,16 @@ mla_status_t mla_decode(const mla_dims_t* dims, int32_t batch, const void* q_lat
   int32_t* meta = (L.total && pp.mode == PART_BALANCED) ? reinterpret_cast<int32_t*>(ws + L.meta) : nullptr;
   hipStream_t st = static_cast<hipStream_t>(stream);
 
-  const bool fast = is_v2(dims) && cache->page_size == 64 && q_dt == MLA_BF16 && cache->dtype == MLA_BF16;
+  const bool fast = is_v2(dims) && cache->page_size == 64 && q_dt == MLA_BF16 &&
+                    (cache->dtype == MLA_BF16 || cache->dtype == MLA_FP8_E4M3);
   hipError_t e;
   if (fast) {
     V2DecodeArgs a{};
     a.q_lat = static_cast<const uint16_t*>(q_lat);
     a.q_pe = static_cast<const uint16_t*>(q_pe);
     a.kv = cache->kv;
+    a.scales = cache->dtype == MLA_FP8_E4M3 ? cache->scales : nullptr;
+    a.kv_dt = cache->dtype;
     a.block_table = cache->block_table;
     a.seq_lens = cache->seq_lens;
     a.max_pages = cache->max_pages_per_seq;

@@ -131,6 +131,91 @@ __device__ __forceinline__ void wait_tile(int wave, bool newer_in_flight) {
   else __builtin_amdgcn_s_waitcnt(waitcnt_vm(4));
 }
 
+// ---------------------------------------------------------------------------
+// fp8 cache (OCP E4M3 codes, one fp32 scale per token per 128-channel group;
+// the stored value is code * scale).  A tile's codes (32 rows x 576 B, one
+// contiguous run inside a page) and scales (32 x 5 fp32) are copied into an LDS
+// staging buffer, then dequantised once into the bf16 tile layout above, which
+// the score and PV steps read unchanged.
+constexpr int kF8TileBytes = kTileTok * kV2Row;       // 18432
+constexpr int kF8Groups = 5;                          // scale groups per row
+constexpr int kF8StageBytes = kF8TileBytes + 1024;    // codes, then scales (640 B used)
+constexpr int kF8NumBuf = 2;                          // bf16 tile buffers (and staging buffers)
+
+// Loads of one staged tile: 18 one-KB code blocks and one scale block, 3 per
+// wavefront for wavefronts 0-2 and 2 for 3-7 (load i: codes block i for i < 18,
+// the scales for i = 18).  Rows past `valid` read as zeros (codes and scales).
+__device__ __forceinline__ int f8_first_load(int wave) { return wave < 3 ? 3 * wave : 9 + 2 * (wave - 3); }
+__device__ __forceinline__ int f8_num_loads(int wave) { return wave < 3 ? 3 : 2; }
+
+__device__ __forceinline__ void issue_tile_f8(const char* codes, const float* scales, int valid, uint32_t stage,
+                                              int wave) {
+  int ln = threadIdx.x & 63;
+  asm volatile("" : "+v"(ln));
+  const int voff = ln * 16;
+  const uint64_t cb = reinterpret_cast<uint64_t>(codes), sb = reinterpret_cast<uint64_t>(scales);
+  i32x4 rc, rs;
+  rc[0] = uniform(int(uint32_t(cb)));
+  rc[1] = uniform(int(uint32_t(cb >> 32) & 0xFFFFu));
+  rc[2] = uniform(valid * kV2Row);
+  rc[3] = int(kBufferFlags);
+  rs[0] = uniform(int(uint32_t(sb)));
+  rs[1] = uniform(int(uint32_t(sb >> 32) & 0xFFFFu));
+  rs[2] = uniform(valid * kF8Groups * 4);
+  rs[3] = int(kBufferFlags);
+  const int i0 = f8_first_load(wave), nl = f8_num_loads(wave);
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    if (j < nl) {
+      const int i = i0 + j;
+      const int m0 = uniform(int(stage + uint32_t(i * 1024)));
+      if (i < 18) {
+        const int soff = uniform(i * 1024);
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                     : : "s"(m0), "v"(voff), "s"(rc), "s"(soff) : "memory", "m0");
+      } else {
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                     : : "s"(m0), "v"(voff), "s"(rs) : "memory", "m0");
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void wait_tile_f8(int wave, bool newer_in_flight) {
+  if (!newer_in_flight) __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  else if (wave < 3) __builtin_amdgcn_s_waitcnt(waitcnt_vm(3));
+  else __builtin_amdgcn_s_waitcnt(waitcnt_vm(2));
+}
+
+// Dequantise a staged tile into a bf16 tile buffer.  Item i (0..2303) is one
+// bf16 chunk (8 values) of one row; 16 consecutive items cover 8 consecutive
+// chunks of one chunk group in 2 consecutive rows, so a 16-lane group of the
+// 16-byte LDS writes hits 16 distinct bank quads.
+__device__ __forceinline__ void convert_tile_f8(uint32_t stage, uint32_t buf) {
+#pragma unroll
+  for (int r = 0; r < 5; ++r) {
+    const int i = r * kDecThreads + int(threadIdx.x);
+    if (r < 4 || i < kTileTok * (kV2Row / 8)) {
+      const int grp = i >> 4;
+      const int t = 2 * (grp / 9) + ((i >> 3) & 1), c = 8 * (grp % 9) + (i & 7);
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      const u32x2 code = *reinterpret_cast<const u32x2 MLA_LDS*>((const char MLA_LDS*)(uintptr_t)(stage + uint32_t(t * kV2Row + c * 8)));
+      const float sc = *reinterpret_cast<const float MLA_LDS*>(
+          (const char MLA_LDS*)(uintptr_t)(stage + uint32_t(kF8TileBytes + (t * kF8Groups + (c >> 4)) * 4)));
+      const auto f0 = __builtin_amdgcn_cvt_pk_f32_fp8(int(code[0]), false);
+      const auto f1 = __builtin_amdgcn_cvt_pk_f32_fp8(int(code[0]), true);
+      const auto f2 = __builtin_amdgcn_cvt_pk_f32_fp8(int(code[1]), false);
+      const auto f3 = __builtin_amdgcn_cvt_pk_f32_fp8(int(code[1]), true);
+      bf16x8 v;
+      v[0] = (__bf16)(f0[0] * sc); v[1] = (__bf16)(f0[1] * sc);
+      v[2] = (__bf16)(f1[0] * sc); v[3] = (__bf16)(f1[1] * sc);
+      v[4] = (__bf16)(f2[0] * sc); v[5] = (__bf16)(f2[1] * sc);
+      v[6] = (__bf16)(f3[0] * sc); v[7] = (__bf16)(f3[1] * sc);
+      *reinterpret_cast<bf16x8 MLA_LDS*>((char MLA_LDS*)(uintptr_t)(buf + uint32_t(tile_offset(t, c)))) = v;
+    }
+  }
+}
+
 __device__ __forceinline__ bf16x8 lds_read_b128(uint32_t addr) {
   return *reinterpret_cast<const bf16x8 MLA_LDS*>((const char MLA_LDS*)(uintptr_t)addr);
 }
@@ -150,11 +235,16 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& p, int base) {
   return r;
 }
 
+// kF8: fp8 cache (staged and dequantised per tile); else bf16 cache.
+template <bool kF8>
 __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void decode_v2_bf16_kernel(V2DecodeArgs a) {
+void decode_v2_kernel(V2DecodeArgs a) {
+  // bf16 tile buffers (3 for a bf16 cache; 2 plus 2 staging buffers for fp8)
+  constexpr int kBufs = kF8 ? kF8NumBuf : kNumBuf;
+  constexpr int kTileArea = kBufs * kTileBytes + (kF8 ? kF8NumBuf * kF8StageBytes : 0);
   // alignment: tile buffers at multiples of 2048 and the exchange area at a
   // multiple of 8192 keep the XOR address tricks below exact
-  __shared__ __attribute__((aligned(2048))) char tiles_raw[kNumBuf * kTileBytes];
+  __shared__ __attribute__((aligned(2048))) char tiles_raw[kTileArea];
   __shared__ __attribute__((aligned(8192))) char xs_raw[kXsBytes];
   __shared__ __attribute__((aligned(1024))) char qpe_raw[kQpeBytes];
   // Work items w and w+1 usually share a sequence (and so its query).  Blocks
@@ -211,12 +301,25 @@ void decode_v2_bf16_kernel(V2DecodeArgs a) {
       return kv + int64_t(page_id) * kPageBytes + (k & 1) * kTileBytes;
     };
     auto tile_valid = [&](int k) { return min(kTileTok, t1 - t0 - k * kTileTok); };
-    auto tile_buf = [&](int k) { return tiles_lds + uint32_t((k % kNumBuf) * kTileBytes); };
+    auto tile_buf = [&](int k) { return tiles_lds + uint32_t((k % kBufs) * kTileBytes); };
+    // fp8: staging buffer of tile k, and the issue of its loads
+    auto stage_buf = [&](int k) {
+      return tiles_lds + uint32_t(kBufs * kTileBytes + (k % kF8NumBuf) * kF8StageBytes);
+    };
+    auto issue = [&](int k, int page_id) {
+      if constexpr (kF8) {
+        const char* codes = kv + (int64_t(page_id) * kV2Page + (k & 1) * kTileTok) * kV2Row;
+        const float* sc = a.scales + (int64_t(page_id) * kV2Page + (k & 1) * kTileTok) * kF8Groups;
+        issue_tile_f8(codes, sc, tile_valid(k), stage_buf(k), wave);
+      } else {
+        issue_tile(tile_src(k, page_id), tile_valid(k), tile_buf(k), wave);
+      }
+    };
 
     // every wavefront is done with the previous segment's tiles and scores
     raw_barrier();
     const int page_first = load_const(bt, 0);
-    issue_tile(tile_src(0, page_first), tile_valid(0), tile_buf(0), wave);
+    issue(0, page_first);
     // query slices of head `head` (MFMA B operand: lane holds 8 consecutive dims):
     // latent dims 256*dh + 16*kk + 8*h .. +8, RoPE dims 32*dh + 16*j + 8*h .. +8
     bf16x8 qf[16];
@@ -237,7 +340,13 @@ void decode_v2_bf16_kernel(V2DecodeArgs a) {
     // the compiler that the query registers are ready, so it puts no waits for
     // them inside the tile loop (where they would drain the tile prefetches).
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    if (ntiles > 1) issue_tile(tile_src(1, page_first), tile_valid(1), tile_buf(1), wave);
+    if constexpr (kF8) {
+      // tile 0's staged codes visible to all, dequantised before slot 0
+      __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
+      raw_barrier();
+      convert_tile_f8(stage_buf(0), tile_buf(0));
+    }
+    if (ntiles > 1) issue(1, page_first);
     // page of the next tile to issue (tile 2); loaded a slot before its use
     int page_next = ntiles > 2 ? load_const(bt, 1) : 0;
 
@@ -247,22 +356,46 @@ void decode_v2_bf16_kernel(V2DecodeArgs a) {
     float m_run = -INFINITY, lsum = 0.f;
 
     // Opening of slot j (the same in every wavefront): wait for this
-    // wavefront's share of the tile that becomes visible, barrier, issue the
-    // loads that slot j starts, and after the slot's work prefetch the page id
-    // of the next tile to issue.
+    // wavefront's loads that the slot needs, barrier, issue the loads that slot
+    // j starts, and after the slot's work prefetch the page id of the next tile
+    // to issue.
+    // bf16: tile t is issued in slot 2t-3 and read from slot 2t on.
+    // fp8:  tile t is issued in slot 2t-4, dequantised in slot 2t-1 and read
+    //       from slot 2t on (its bf16 buffer's previous tile, t-2, was last read
+    //       in slot 2t-2; its staging buffer's, in slot 2t-3).
     auto open_slot = [&](int j) {
-      if ((j & 1) == 0 && j >= 2 && j / 2 < ntiles) wait_tile(wave, j / 2 + 1 < ntiles);
-      __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
-      raw_barrier();
-      if (j & 1) {
-        const int tn = (j + 3) >> 1;
-        if (tn < ntiles) issue_tile(tile_src(tn, page_next), tile_valid(tn), tile_buf(tn), wave);
+      if constexpr (kF8) {
+        const int tc = (j + 1) >> 1;
+        if ((j & 1) && tc < ntiles) wait_tile_f8(wave, tc + 1 < ntiles);
+        __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
+        raw_barrier();
+        if ((j & 1) == 0) {
+          const int tn = (j >> 1) + 2;
+          if (tn < ntiles) issue(tn, page_next);
+        } else if (tc < ntiles) {
+          convert_tile_f8(stage_buf(tc), tile_buf(tc));
+        }
+      } else {
+        if ((j & 1) == 0 && j >= 2 && j / 2 < ntiles) wait_tile(wave, j / 2 + 1 < ntiles);
+        __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
+        raw_barrier();
+        if (j & 1) {
+          const int tn = (j + 3) >> 1;
+          if (tn < ntiles) issue(tn, page_next);
+        }
       }
     };
     auto close_slot = [&](int j) {
-      if ((j & 1) == 0) {
-        const int tn = (j + 4) >> 1;
-        if (tn < ntiles) page_next = load_const(bt, tn >> 1);
+      if constexpr (kF8) {
+        if (j & 1) {
+          const int tn = ((j + 1) >> 1) + 2;
+          if (tn < ntiles) page_next = load_const(bt, tn >> 1);
+        }
+      } else {
+        if ((j & 1) == 0) {
+          const int tn = (j + 4) >> 1;
+          if (tn < ntiles) page_next = load_const(bt, tn >> 1);
+        }
       }
     };
 
@@ -430,7 +563,8 @@ void decode_v2_bf16_kernel(V2DecodeArgs a) {
 }
 
 hipError_t launch_decode_v2(const V2DecodeArgs& a, hipStream_t st) {
-  decode_v2_bf16_kernel<<<a.n_items, kDecThreads, 0, st>>>(a);
+  if (a.kv_dt == MLA_FP8_E4M3) decode_v2_kernel<true><<<a.n_items, kDecThreads, 0, st>>>(a);
+  else decode_v2_kernel<false><<<a.n_items, kDecThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -30,7 +30,9 @@ struct GenericDecodeArgs {
 struct V2DecodeArgs {
   const uint16_t* q_lat;   // [B, 128, 512] bf16
   const uint16_t* q_pe;    // [B, 128, 64] bf16
-  const void* kv;          // [P, 64, 576] bf16
+  const void* kv;          // [P, 64, 576] bf16 or fp8 E4M3 codes
+  const float* scales;     // fp8: [P, 64, 5] fp32 group scales; else null
+  mla_dtype_t kv_dt;
   const int32_t* block_table;
   const int32_t* seq_lens;
   int max_pages;

@@ -51,6 +51,15 @@ class Case:
         return ostore.stored_rows_f64(self.cache, b)
 
     def reference(self, b: int, heads=None, chunk: Optional[int] = None):
+        """Oracle results for sequence b (memoised: a case is compared under
+        several partitions)."""
+        key = (b, None if heads is None else tuple(heads), chunk)
+        memo = self.__dict__.setdefault("_memo", {})
+        if key not in memo:
+            memo[key] = self._reference(b, heads, chunk)
+        return memo[key]
+
+    def _reference(self, b: int, heads=None, chunk: Optional[int] = None):
         rows = self.stored_rows(b)
         dc = self.dims.d_latent
         args = (self.q_nope[b], self.q_pe[b], rows[:, :dc], rows[:, dc:], self.W_UK, self.W_UV, self.scale, heads)

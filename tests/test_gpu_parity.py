@@ -183,6 +183,35 @@ def test_v2_fp8_small():
         compare_all(case, step, TOL["fp8"])
 
 
+FP8_RAGGED = [31, 32, 33, 64, 95, 129, 200, 700, 1100, 5]
+
+
+@pytest.fixture(scope="module")
+def v2_fp8_ragged():
+    case = direct_case(5, FP8_RAGGED, max_pages=20)
+    return case, to_device(case)
+
+
+@pytest.mark.parametrize("part", [(0, 0), (0, 3), (0, 16), (64, 0), (0, -1)])
+def test_v2_fp8_ragged(v2_fp8_ragged, part):
+    # tile tails around the 32-token tile edge, several tiles per item,
+    # segments that start mid-item
+    case, dev = v2_fp8_ragged
+    print(f"case: V2 fp8 lens={FP8_RAGGED} part={part}", flush=True)
+    step = run_step(case, dev, *part)
+    compare_all(case, step, TOL["fp8"])
+
+
+def test_v2_fp8_sharp():
+    # queries x34: logits spread wide enough that the running max is raised
+    # mid-sequence (the rescale path) on the fp8 tiles too
+    lens = [700, 1500]
+    print(f"case: V2 fp8 sharp lens={lens}", flush=True)
+    case = direct_case(5, lens, query_gain=34.0, max_pages=24)
+    step = run_step(case, to_device(case), 0, 8)
+    compare_all(case, step, TOL["fp8"])
+
+
 # ---------------------------------------------------------------------------
 # full sizes, in the launch configuration the benchmark times
 # ---------------------------------------------------------------------------
@@ -224,3 +253,11 @@ def test_fullsize_long_b4_split4096():
     dev = to_device(case)
     step = run_step(case, dev, 4096, 0)
     _sampled(case, step, TOL["bf16"], seqs=[0, 3])
+
+
+def test_fullsize_fp8_b32():
+    print("case: full-size fp8 B=32 T=16384 balanced over CUs", flush=True)
+    case = direct_case(5, [16384] * 32, max_pages=256)
+    dev = to_device(case)
+    step = run_step(case, dev, 0, -1)
+    _sampled(case, step, TOL["fp8"], seqs=[0, 31])
