@@ -246,7 +246,8 @@ def run(args):
                 traffic = tj.get("decode_bytes_per_launch")
         res["roofline"] = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": ach / HBM_PEAK_GBS, "traffic": traffic,
-                           "kernel": "decode_v2_bf16_kernel", "algorithmic_bytes_per_launch": alg["decode_bytes"],
+                           "kernel": "decode_v2_kernel<true> (fp8 cache)" if cid == 5 else "decode_v2_kernel<false> (bf16 cache)",
+                           "algorithmic_bytes_per_launch": alg["decode_bytes"],
                            "mean_launch_ms": per_kernel["decode"],
                            "mfma_frac": alg["decode_flops"] / dec_s / (MFMA_BF16_PEAK_TFLOPS * 1e12)}
     res["wall_s_timed"] = wall
@@ -335,7 +336,7 @@ def summarize_pmc(fetch_dir, write_dir, copy_bytes, out_json, out_md, cmd=""):
              f"- calibration: the runtime's device copy of {copy_bytes} B; FETCH_SIZE reads "
              f"{f_copy:.4f} KiB per KiB copied and WRITE_SIZE {w_copy:.4f}; all figures below are divided by "
              "these factors",
-             f"- decode kernel (decode_v2_bf16_kernel, source sha256[:16] {res['decode_source_sha']}): "
+             f"- decode kernel (decode_v2_kernel<false>, bf16 cache; source sha256[:16] {res['decode_source_sha']}): "
              f"fetched {f_dec / 1e6:.2f} MB, written {w_dec / 1e6:.2f} MB, total {(f_dec + w_dec) / 1e6:.2f} MB "
              "per launch"]
     for k, v in others.items():

@@ -11,7 +11,9 @@ namespace mla {
 
 constexpr int kMergeWaves = 4;
 
-template <int COLS>  // columns per lane when d_c == 64 * COLS (vector path); 0 = any d_c
+// COLS: columns per lane when d_c == 64 * COLS (vector path), 0 = any d_c;
+// BF16: partials (and output) in bf16, else fp32 (vector path only)
+template <int COLS, bool BF16>
 __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(MergeArgs a) {
   const int b = blockIdx.x;
   const int head = blockIdx.y * kMergeWaves + threadIdx.x / 64;
@@ -36,38 +38,65 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(MergeArgs a) {
     return;
   }
   if (count <= 1) return;
+  // the partials' loads are independent: unrolled so that several are in flight
   float M = -INFINITY;
+#pragma unroll 8
   for (int s = 0; s < count; ++s) M = fmaxf(M, a.lse_part[int64_t(first + s) * a.n_heads + head]);
   float Z = 0.f;
   if (COLS > 0) {
     float acc[COLS > 0 ? COLS : 1];
 #pragma unroll
     for (int e = 0; e < COLS; ++e) acc[e] = 0.f;
-    for (int s = 0; s < count; ++s) {
-      const int64_t slot = first + s;
-      const float w = __expf(a.lse_part[slot * a.n_heads + head] - M);
-      Z += w;
-      const int64_t src = (slot * a.n_heads + head) * a.d_latent + lane * COLS;
-      if (a.o_dt == MLA_BF16 && COLS == 8) {
-        const bf16x8 x = *reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(a.o_part) + src);
+    // partial s's columns of this lane, as floats
+    const int64_t stride = int64_t(a.n_heads) * a.d_latent;
+    const int64_t src0 = (int64_t(first) * a.n_heads + head) * a.d_latent + lane * COLS;
+    auto load_cols = [&](int s, float* x) {
+      const int64_t src = src0 + s * stride;
+      if (BF16 && COLS == 8) {
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(a.o_part) + src);
 #pragma unroll
-        for (int e = 0; e < COLS; ++e) acc[e] += w * float(x[e % 8]);
-      } else if (a.o_dt == MLA_F32) {
+        for (int e = 0; e < COLS; ++e) x[e] = float(v[e % 8]);
+      } else if (!BF16) {
         const f32x4* x4 = reinterpret_cast<const f32x4*>(static_cast<const float*>(a.o_part) + src);
 #pragma unroll
         for (int v = 0; v < COLS / 4; ++v) {
-          const f32x4 x = x4[v];
+          const f32x4 y = x4[v];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc[4 * v + e] += w * x[e];
+          for (int e = 0; e < 4; ++e) x[4 * v + e] = y[e];
         }
       } else {
 #pragma unroll
-        for (int e = 0; e < COLS; ++e) acc[e] += w * load_any(a.o_part, src + e, a.o_dt);
+        for (int e = 0; e < COLS; ++e) x[e] = load_any(a.o_part, src + e, a.o_dt);
       }
+    };
+    // four partials per step: their loads are issued together
+    int s = 0;
+    for (; s + 4 <= count; s += 4) {
+      float l[4], x[4][COLS > 0 ? COLS : 1];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        l[j] = a.lse_part[int64_t(first + s + j) * a.n_heads + head];
+        load_cols(s + j, x[j]);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float w = __expf(l[j] - M);
+        Z += w;
+#pragma unroll
+        for (int e = 0; e < COLS; ++e) acc[e] += w * x[j][e];
+      }
+    }
+    for (; s < count; ++s) {
+      float x[COLS > 0 ? COLS : 1];
+      const float w = __expf(a.lse_part[int64_t(first + s) * a.n_heads + head] - M);
+      load_cols(s, x);
+      Z += w;
+#pragma unroll
+      for (int e = 0; e < COLS; ++e) acc[e] += w * x[e];
     }
     const float invZ = 1.f / Z;
     const int64_t base = out_row * a.d_latent + lane * COLS;
-    if (a.o_dt == MLA_BF16) {
+    if (BF16) {
       bf16x8 o;
 #pragma unroll
       for (int e = 0; e < COLS; ++e) o[e % 8] = (__bf16)(acc[e] * invZ);
@@ -95,8 +124,9 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(MergeArgs a) {
 
 hipError_t launch_merge(const MergeArgs& a, int batch, hipStream_t st) {
   dim3 grid(batch, ceil_div(a.n_heads, kMergeWaves));
-  if (a.d_latent == 512) merge_kernel<8><<<grid, 64 * kMergeWaves, 0, st>>>(a);
-  else merge_kernel<0><<<grid, 64 * kMergeWaves, 0, st>>>(a);
+  if (a.d_latent == 512 && a.o_dt == MLA_BF16) merge_kernel<8, true><<<grid, 64 * kMergeWaves, 0, st>>>(a);
+  else if (a.d_latent == 512 && a.o_dt == MLA_F32) merge_kernel<8, false><<<grid, 64 * kMergeWaves, 0, st>>>(a);
+  else merge_kernel<0, false><<<grid, 64 * kMergeWaves, 0, st>>>(a);
   return hipGetLastError();
 }
 
