@@ -22,4 +22,4 @@ from . import mla, storage  # noqa: F401
 from .mla import (attend, attend_head, chunk_partials, forward_from_h, merge_partials,  # noqa: F401
                   out_project, project_cache, project_query, rope, softmax_scale)
 from .storage import (bf16_bits_to_f64, dequantize_rows, e4m3fn_to_f64,  # noqa: F401
-                      gather_sequence, stored_rows_f64)
+                      f32_to_bf16_bits, f64_to_e4m3fn, gather_sequence, quantize_e4m3_groups, stored_rows_f64)

@@ -12,6 +12,12 @@ Test infrastructure only (see oracle/__init__.py).
 * A paged cache stores token t of sequence b in page block_table[b][t // page]
   at slot t % page (the paged KV memory idea the DeepSeek-V2 explainer,
   一文通透DeepSeek-V2 §2.1.1, names as a KV-cache optimisation).
+* Encoding (for the cache-store step): bf16 is binary32 rounded to nearest,
+  ties to even, at bit 16; E4M3FN takes the nearest representable value, ties to
+  the even mantissa.  A group's scale is amax / 448 computed in binary32 (an
+  all-zero group gets 1, so that its codes are 0), and each value is divided by
+  it in binary32 before rounding: the quotient stays within +-448 up to a
+  binary32 rounding error, which rounds back to 448.
 """
 from __future__ import annotations
 
@@ -71,3 +77,73 @@ def stored_rows_f64(cache, b: int) -> np.ndarray:
         sc = gather_sequence(cache.scales, cache.block_table[b], t, cache.page_size)
         return dequantize_rows(words, sc)
     raise ValueError(cache.dtype)
+
+
+# ---------------------------------------------------------------------------
+# encoders (the store side of the formats above)
+# ---------------------------------------------------------------------------
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """binary32 values -> bf16 bit patterns, round to nearest, ties to even.
+
+    Adding 0x7FFF plus the lowest kept bit and truncating is that rounding on the
+    bit pattern; NaN stays a (quiet) NaN.
+    """
+    u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    keep = (u >> np.uint64(16)) & np.uint64(1)
+    r = ((u + np.uint64(0x7FFF) + keep) >> np.uint64(16)).astype(np.uint16)
+    nan = (u & np.uint64(0x7FFFFFFF)) > np.uint64(0x7F800000)
+    return np.where(nan, ((u >> np.uint64(16)) | np.uint64(0x40)).astype(np.uint16), r)
+
+
+E4M3_MAX = 448.0
+
+
+def f64_to_e4m3fn(x: np.ndarray) -> np.ndarray:
+    """Values -> OCP E4M3FN codes: the nearest representable value, ties to the
+    even mantissa (the 3-bit field), sign kept (also for zero).
+
+    Magnitudes are multiples of the quantum 2**(e-3) of their binade e (e >= -6;
+    below 2**-6 the subnormal quantum 2**-9 holds).  A magnitude at or past the
+    midpoint 464 between 448 and the next binade step has no finite nearest
+    value and becomes NaN (0x7F), as the format has no infinity.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    v = np.abs(x)
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(v > 0, v, 1.0)))
+    e = np.clip(e, -6, 8)
+    quantum = np.exp2(e - 3)
+    q = np.round(v / quantum) * quantum          # numpy rounds halves to even
+    # encode q (its binade may be one higher than v's after rounding up)
+    with np.errstate(divide="ignore"):
+        eq = np.floor(np.log2(np.where(q > 0, q, 1.0)))
+    sub = q < 2.0 ** -6
+    exp_field = np.where(sub, 0, eq + 7).astype(np.int64)
+    mant = np.where(sub, q / 2.0 ** -9, q / np.exp2(eq - 3) - 8.0)
+    mant = np.rint(mant).astype(np.int64)
+    code = (exp_field << 3) | mant
+    code = np.where(q == 0, 0, code)
+    code = np.where(np.signbit(x), code | 0x80, code)
+    bad = (v >= 464.0) | np.isnan(x)
+    return np.where(bad, 0x7F | np.where(np.signbit(x), 0x80, 0), code).astype(np.uint8)
+
+
+def quantize_e4m3_groups(rows: np.ndarray, group: int = 128):
+    """binary32 rows [N, W] -> (codes uint8 [N, W], scales float32 [N, ceil(W/group)]).
+
+    Per row and group of `group` columns: scale = amax / 448 in binary32 (1 when
+    the group is all zero), code = E4M3FN(binary32(x / scale)).
+    """
+    x = np.asarray(rows, dtype=np.float32)
+    n, w = x.shape
+    ng = (w + group - 1) // group
+    codes = np.zeros((n, w), dtype=np.uint8)
+    scales = np.ones((n, ng), dtype=np.float32)
+    for g in range(ng):
+        sl = slice(g * group, min((g + 1) * group, w))
+        amax = np.max(np.abs(x[:, sl]), axis=1)
+        sc = np.where(amax > 0, (amax / np.float32(E4M3_MAX)).astype(np.float32), np.float32(1.0)).astype(np.float32)
+        scales[:, g] = sc
+        codes[:, sl] = f64_to_e4m3fn((x[:, sl] / sc[:, None]).astype(np.float32).astype(np.float64))
+    return codes, scales

@@ -281,3 +281,69 @@ def test_from_h_chain_against_explicit_matrix_products():
         heads.append(p @ (h @ WV[hs].T))
     np.testing.assert_allclose(r["o_heads"], np.array(heads), rtol=1e-11, atol=1e-14)
     np.testing.assert_allclose(r["u"], W["W_O"] @ np.concatenate(heads), rtol=1e-10, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# encoders of the cache-store step
+# ---------------------------------------------------------------------------
+
+def test_e4m3_encoder_roundtrip_ties_and_torch():
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    vals = ostore.e4m3fn_to_f64(codes)
+    fin = ~np.isnan(vals)
+    # every finite code is its own value's encoding (both zeros included)
+    assert np.array_equal(ostore.f64_to_e4m3fn(vals[fin]), codes[fin])
+    # midpoints between neighbouring positive values go to the even mantissa
+    pos = np.sort(np.unique(vals[fin & (vals > 0)]))
+    mids = (pos[:-1] + pos[1:]) / 2
+    got = ostore.f64_to_e4m3fn(mids)
+    lo, hi = ostore.f64_to_e4m3fn(pos[:-1]), ostore.f64_to_e4m3fn(pos[1:])
+    want = np.where((lo & 1) == 0, lo, hi)
+    assert np.array_equal(got, want)
+    # past the last midpoint (464) there is no finite nearest value: NaN
+    assert ostore.f64_to_e4m3fn(np.array([464.0, -500.0])).tolist() == [0x7F, 0xFF]
+    assert ostore.f64_to_e4m3fn(np.array([463.99]))[0] == 0x7E
+    # an independent implementation: torch's float8_e4m3fn cast of binary32 values
+    rng = np.random.default_rng(11)
+    x = np.concatenate([rng.uniform(-460, 460, 20000), rng.normal(size=20000) * 1e-2,
+                        rng.normal(size=5000) * 2.0 ** -8]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(ostore.f64_to_e4m3fn(x.astype(np.float64)), ref)
+
+
+def test_bf16_encoder_against_torch():
+    import torch
+    rng = np.random.default_rng(12)
+    x = (rng.normal(size=50000) * np.exp2(rng.integers(-30, 30, 50000))).astype(np.float32)
+    # exact ties (lower half 0x8000) with both parities of the kept bit
+    u = rng.integers(0, 2 ** 31, 4000, dtype=np.uint64).astype(np.uint32)
+    ties = ((u & np.uint32(0x7F7F0000)) | np.uint32(0x8000)).view(np.float32)
+    x = np.concatenate([x, ties, np.array([0.0, -0.0, 3.4e38, -1e-40], dtype=np.float32)])
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ostore.f32_to_bf16_bits(x), ref)
+
+
+def test_group_quantizer_properties():
+    rng = np.random.default_rng(13)
+    rows = (rng.normal(size=(64, 576)) * np.exp2(rng.integers(-6, 6, (64, 1)))).astype(np.float32)
+    rows[3, 128:256] = 0.0                     # an all-zero group
+    rows[5, 512:] *= 1e-3                      # a small RoPE group
+    codes, scales = ostore.quantize_e4m3_groups(rows)
+    assert codes.shape == (64, 576) and scales.shape == (64, 5) and scales.dtype == np.float32
+    assert scales[3, 1] == 1.0 and np.all(codes[3, 128:256] == 0)
+    deq = ostore.dequantize_rows(codes, scales)
+    for g in range(5):
+        sl = slice(128 * g, min(128 * (g + 1), 576))
+        x = rows[:, sl].astype(np.float64)
+        # binary32 amax / 448 is the scale, so the largest magnitude maps to 448
+        amax = np.abs(x).max(axis=1)
+        nz = amax > 0
+        assert np.allclose(scales[nz, g], amax[nz] / 448.0, rtol=2 ** -23)
+        assert np.all(np.abs(ostore.e4m3fn_to_f64(codes[nz][:, sl.start:sl.stop][np.arange(nz.sum()),
+                      np.argmax(np.abs(x[nz]), axis=1)])) == 448.0)
+        # error bound: half a quantum of 3 mantissa bits, or half the subnormal
+        # quantum 2**-9 for magnitudes below 2**-6 (in units of the scale)
+        err = np.abs(deq[:, sl] - x)
+        bound = np.maximum(np.abs(x) * 2.0 ** -4, scales[:, g:g + 1].astype(np.float64) * 2.0 ** -10) * (1 + 1e-6)
+        assert np.all(err <= bound)
