@@ -197,6 +197,44 @@ mla_status_t mla_out_proj(const mla_dims_t* dims, int32_t batch,
                           void* o_heads, mla_dtype_t out_dt, void* stream);
 
 /*
+ * Store one new token row per sequence into the paged cache, the step that
+ * precedes decoding it: the cache keeps per token [c^KV | k^R] with k^R after
+ * its rotation [DeepSeek-V2 explainer §2.2.2].
+ *   rows: [batch, d_c + d_rope] (rows_dt MLA_F32 or MLA_BF16): the new rows.
+ *   positions: [batch] int32 DEVICE array: token index t of each row; it is
+ *       written to page block_table[b * max_pages_per_seq + t / page_size], slot
+ *       t % page_size.  Sequences with t < 0, t >= max_pages_per_seq * page_size
+ *       or a page id outside [0, num_pages) are skipped.
+ *   rope_base: > 0 rotates the last d_rope columns first: pair (2k, 2k+1) by the
+ *       angle t * rope_base^(-2k/d_rope) (evaluated in fp64); 0 stores the rows
+ *       as given (k^R already rotated).
+ *   cache: kv (and, for fp8, scales) are WRITTEN at those slots only (the const
+ *       in mla_paged_cache_t is cast away); seq_lens is neither read nor updated.
+ *       Rounding: bf16 to nearest even; fp8 per token and 128-column group:
+ *       scale = amax / 448 in fp32 (1 for an all-zero group), code = E4M3 nearest
+ *       even of x / scale (the 1x128 format of the V3 interview notes, section
+ *       F8量化策略).
+ * d_c and d_rope must be even, d_c + d_rope <= 1280.
+ */
+mla_status_t mla_cache_store(const mla_dims_t* dims, int32_t batch, const void* rows, mla_dtype_t rows_dt,
+                             const int32_t* positions, float rope_base, const mla_paged_cache_t* cache,
+                             void* stream);
+
+/*
+ * Project and store: rows = [W^DKV h ; W^KR h] per sequence (the cache-side
+ * projections of [DeepSeek-V2 explainer §2.2.1 and §2.2.2]), fp32 accumulation,
+ * written to `rows`; then mla_cache_store(rows, positions, rope_base, cache).
+ *   h: [batch, d_model] (h_dt f32 or bf16) hidden state of the new token.
+ *   w_dkv: [d_c, d_model], w_kr: [d_rope, d_model] (w_dt f32 or bf16).
+ *   rows: [batch, d_c + d_rope] fp32 device scratch filled by the call (the rows
+ *       before rotation and rounding).
+ */
+mla_status_t mla_cache_append(const mla_dims_t* dims, int32_t d_model, int32_t batch, const void* h,
+                              mla_dtype_t h_dt, const void* w_dkv, const void* w_kr, mla_dtype_t w_dt, float* rows,
+                              const int32_t* positions, float rope_base, const mla_paged_cache_t* cache,
+                              void* stream);
+
+/*
  * Host helper (no device access): for host copies of seq_lens, the workspace
  * slots that hold sequence b's partials: slots part_first[b] .. part_first[b] +
  * part_count[b] - 1.  part_count[b] == 1 means mla_decode writes the final

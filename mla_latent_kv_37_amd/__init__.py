@@ -4,14 +4,15 @@ The product is libmla.so (include/mla.h), built from csrc/ by
 ``python -m mla_latent_kv_37_amd.build``.  This package is a thin binding:
 ``_lib`` marshals torch tensors into the C ABI, ``DecodeStep`` chains the four
 calls of one decode step (absorb -> decode -> merge -> out proj) with buffers
-allocated once.  Every arithmetic step runs in the library's HIP kernels.
+allocated once; ``cache_store`` / ``cache_append`` write new tokens into the
+cache.  Every arithmetic step runs in the library's HIP kernels.
 """
 from __future__ import annotations
 
 from . import _lib
-from ._lib import (MLA_BF16, MLA_F32, MLA_FP8_E4M3, MlaError, absorb_q, build_info, decode, dims,  # noqa: F401
-                   lse_part_offset, make_cache, merge_splits, out_proj, partition, partition_host, status_string,
-                   workspace_size)
+from ._lib import (MLA_BF16, MLA_F32, MLA_FP8_E4M3, MlaError, absorb_q, build_info, cache_append,  # noqa: F401
+                   cache_store, decode, dims, lse_part_offset, make_cache, merge_splits, out_proj, partition,
+                   partition_host, status_string, workspace_size)
 
 __all__ = ["DecodeStep", "DeviceCache", "upload_cache"]
 

@@ -18,7 +18,8 @@ MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_ALIGNMENT, MLA_ERR_WOR
 MLA_F32, MLA_BF16, MLA_FP8_E4M3 = 0, 1, 2
 
 EXPORTS = ("mla_status_string", "mla_build_info", "mla_absorb_q", "mla_decode_workspace_size",
-           "mla_lse_part_offset", "mla_decode", "mla_merge_splits", "mla_out_proj", "mla_partition_host")
+           "mla_lse_part_offset", "mla_decode", "mla_merge_splits", "mla_out_proj", "mla_cache_store",
+           "mla_cache_append", "mla_partition_host")
 
 
 class MlaError(RuntimeError):
@@ -67,6 +68,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                       P, P]),
         "mla_merge_splits": (ctypes.c_int, [PD, I32, P, I32, I32, PP, P, SZ, P, ctypes.c_int, P, P]),
         "mla_out_proj": (ctypes.c_int, [PD, I32, P, ctypes.c_int, P, ctypes.c_int, P, ctypes.c_int, P]),
+        "mla_cache_store": (ctypes.c_int, [PD, I32, P, ctypes.c_int, P, ctypes.c_float, PC, P]),
+        "mla_cache_append": (ctypes.c_int, [PD, I32, I32, P, ctypes.c_int, P, P, ctypes.c_int, P, P, ctypes.c_float,
+                                            PC, P]),
         "mla_partition_host": (ctypes.c_int, [ctypes.POINTER(I32), I32, I32, I32, PP, ctypes.POINTER(I32),
                                               ctypes.POINTER(I32)]),
     }
@@ -181,6 +185,19 @@ def out_proj(d: Dims, o_lat, w_uv, o_heads, stream=None):
     _check(load().mla_out_proj(ctypes.byref(d), o_lat.shape[0], _ptr(o_lat), dtype_code(o_lat), _ptr(w_uv),
                                dtype_code(w_uv), _ptr(o_heads), dtype_code(o_heads), _stream(stream)), "mla_out_proj")
     return o_heads
+
+
+def cache_store(d: Dims, rows, positions, cache: PagedCache, rope_base: float = 0.0, stream=None):
+    """Write rows [B, d_c+d_rope] (f32/bf16) at token positions [B] (int32, device) into the cache."""
+    _check(load().mla_cache_store(ctypes.byref(d), rows.shape[0], _ptr(rows), dtype_code(rows), _ptr(positions),
+                                  ctypes.c_float(rope_base), ctypes.byref(cache), _stream(stream)), "mla_cache_store")
+
+
+def cache_append(d: Dims, h, w_dkv, w_kr, rows, positions, cache: PagedCache, rope_base: float, stream=None):
+    """rows = [W^DKV h ; W^KR h] (fp32 scratch [B, d_c+d_rope]), then cache_store(rows, positions, rope_base)."""
+    _check(load().mla_cache_append(ctypes.byref(d), h.shape[1], h.shape[0], _ptr(h), dtype_code(h), _ptr(w_dkv),
+                                   _ptr(w_kr), dtype_code(w_dkv), _ptr(rows), _ptr(positions),
+                                   ctypes.c_float(rope_base), ctypes.byref(cache), _stream(stream)), "mla_cache_append")
 
 
 def partition_host(seq_lens, page_size: int, max_pages: int, part: Partition):

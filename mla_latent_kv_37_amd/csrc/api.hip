@@ -86,6 +86,39 @@ WsLayout ws_layout(const mla_dims_t* d, int n_slots, int batch, bool balanced) {
   return L;
 }
 
+// checks shared by the cache-store entry points; fills the store arguments
+mla_status_t store_args(const mla_dims_t* dims, int32_t batch, const void* rows, mla_dtype_t rows_dt,
+                        const int32_t* positions, float rope_base, const mla_paged_cache_t* cache,
+                        CacheStoreArgs* a) {
+  if (mla_status_t s = check_dims(dims)) return s;
+  if (batch < 0 || cache == nullptr) return MLA_ERR_INVALID_ARG;
+  if (!(rope_base >= 0.f)) return MLA_ERR_INVALID_ARG;
+  if (rows_dt != MLA_F32 && rows_dt != MLA_BF16) return valid_dtype(rows_dt) ? MLA_ERR_UNSUPPORTED : MLA_ERR_INVALID_ARG;
+  if (!valid_dtype(cache->dtype)) return MLA_ERR_INVALID_ARG;
+  const int W = dims->d_latent + dims->d_rope;
+  if ((dims->d_latent & 1) || (dims->d_rope & 1)) return MLA_ERR_UNSUPPORTED;   // columns go in pairs
+  if (W > kGenMaxRow) return MLA_ERR_UNSUPPORTED;
+  if (cache->page_size < 1 || cache->max_pages_per_seq < 1 || cache->num_pages < 1) return MLA_ERR_INVALID_ARG;
+  if (batch == 0) return MLA_OK;
+  if (!rows || !positions || !cache->kv || !cache->block_table) return MLA_ERR_INVALID_ARG;
+  if (cache->dtype == MLA_FP8_E4M3 && !cache->scales) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(rows) || !aligned16(cache->kv)) return MLA_ERR_ALIGNMENT;
+  a->rows = rows;
+  a->rows_dt = rows_dt;
+  a->positions = positions;
+  a->rope_base = rope_base;
+  a->kv = const_cast<void*>(cache->kv);
+  a->scales = const_cast<float*>(cache->scales);
+  a->kv_dt = cache->dtype;
+  a->block_table = cache->block_table;
+  a->max_pages = cache->max_pages_per_seq;
+  a->page_size = cache->page_size;
+  a->num_pages = cache->num_pages;
+  a->d_latent = dims->d_latent;
+  a->d_rope = dims->d_rope;
+  return MLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -104,6 +137,7 @@ const char* mla_status_string(mla_status_t s) {
 
 const char* mla_build_info(void) {
   return "libmla gfx950: absorb(v2 mfma, generic), decode(v2 bf16 / fp8-dequant mfma ping-pong, generic f32/bf16/fp8), "
+         "cache store (f32/bf16/fp8 1x128), cache append (mfma / generic projection), "
          "merge, out_proj(v2 mfma, generic)";
 }
 
@@ -274,6 +308,45 @@ mla_status_t mla_out_proj(const mla_dims_t* dims, int32_t batch, const void* o_l
     e = launch_outproj_generic(o_lat, o_dt, w_uv, w_dt, o_heads, out_dt, batch, dims->n_heads, dims->d_head,
                                dims->d_latent, st);
   }
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status_t mla_cache_store(const mla_dims_t* dims, int32_t batch, const void* rows, mla_dtype_t rows_dt,
+                             const int32_t* positions, float rope_base, const mla_paged_cache_t* cache,
+                             void* stream) {
+  CacheStoreArgs a{};
+  if (mla_status_t s = store_args(dims, batch, rows, rows_dt, positions, rope_base, cache, &a)) return s;
+  if (batch == 0) return MLA_OK;
+  const hipError_t e = launch_cache_store(a, batch, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status_t mla_cache_append(const mla_dims_t* dims, int32_t d_model, int32_t batch, const void* h,
+                              mla_dtype_t h_dt, const void* w_dkv, const void* w_kr, mla_dtype_t w_dt, float* rows,
+                              const int32_t* positions, float rope_base, const mla_paged_cache_t* cache,
+                              void* stream) {
+  CacheStoreArgs a{};
+  if (mla_status_t s = store_args(dims, batch, rows, MLA_F32, positions, rope_base, cache, &a)) return s;
+  if (d_model < 1) return MLA_ERR_INVALID_ARG;
+  if ((h_dt != MLA_F32 && h_dt != MLA_BF16) || (w_dt != MLA_F32 && w_dt != MLA_BF16))
+    return valid_dtype(h_dt) && valid_dtype(w_dt) ? MLA_ERR_UNSUPPORTED : MLA_ERR_INVALID_ARG;
+  if (batch == 0) return MLA_OK;
+  if (!h || !w_dkv || (dims->d_rope > 0 && !w_kr)) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(h) || !aligned16(w_dkv) || (w_kr && !aligned16(w_kr))) return MLA_ERR_ALIGNMENT;
+  ProjectArgs p{};
+  p.h = h;
+  p.h_dt = h_dt;
+  p.w_dkv = w_dkv;
+  p.w_kr = w_kr;
+  p.w_dt = w_dt;
+  p.rows = rows;
+  p.batch = batch;
+  p.d_model = d_model;
+  p.d_latent = dims->d_latent;
+  p.d_rope = dims->d_rope;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_project(p, st);
+  if (e == hipSuccess) e = launch_cache_store(a, batch, st);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

@@ -60,7 +60,32 @@ struct MergeArgs {
 };
 
 hipError_t launch_decode_generic(const GenericDecodeArgs& a, int n_items, hipStream_t st);
+struct CacheStoreArgs {
+  const void* rows;        // [B, d_c + d_rope]
+  mla_dtype_t rows_dt;
+  const int32_t* positions;
+  float rope_base;
+  void* kv;
+  float* scales;
+  mla_dtype_t kv_dt;
+  const int32_t* block_table;
+  int max_pages, page_size, num_pages;
+  int d_latent, d_rope;
+};
+
+struct ProjectArgs {
+  const void* h;           // [B, d_model]
+  mla_dtype_t h_dt;
+  const void* w_dkv;       // [d_c, d_model]
+  const void* w_kr;        // [d_rope, d_model]
+  mla_dtype_t w_dt;
+  float* rows;             // [B, d_c + d_rope]
+  int batch, d_model, d_latent, d_rope;
+};
+
 hipError_t launch_decode_v2(const V2DecodeArgs& a, hipStream_t st);
+hipError_t launch_cache_store(const CacheStoreArgs& a, int batch, hipStream_t st);
+hipError_t launch_project(const ProjectArgs& a, hipStream_t st);
 hipError_t launch_merge(const MergeArgs& a, int batch, hipStream_t st);
 hipError_t launch_absorb_generic(const void* q, mla_dtype_t q_dt, const void* w, mla_dtype_t w_dt, void* out,
                                  mla_dtype_t o_dt, int batch, int n_heads, int d_head, int d_latent, hipStream_t st);

@@ -108,6 +108,24 @@ def test_validation_errors_before_any_device_access(lib):
     assert L.mla_out_proj(ctypes.byref(d), 1, fake, 1, None, 1, fake, 1, None) == lib.MLA_ERR_INVALID_ARG
     # batch 0 is a no-op that touches nothing
     assert L.mla_absorb_q(ctypes.byref(d), 0, fake, 1, fake, 1, fake, 1, None) == lib.MLA_OK
+    # cache store / append: fp8 rows unsupported, missing positions, negative RoPE base,
+    # odd column counts, misaligned rows, fp8 cache without scales
+    cs = L.mla_cache_store
+    assert cs(ctypes.byref(d), 1, fake, lib.MLA_FP8_E4M3, fake, 0.0, ctypes.byref(cache), None) == lib.MLA_ERR_UNSUPPORTED
+    assert cs(ctypes.byref(d), 1, fake, lib.MLA_F32, None, 0.0, ctypes.byref(cache), None) == lib.MLA_ERR_INVALID_ARG
+    assert cs(ctypes.byref(d), 1, fake, lib.MLA_F32, fake, -1.0, ctypes.byref(cache), None) == lib.MLA_ERR_INVALID_ARG
+    d_odd = lib.dims(128, 128, 63, 512)
+    assert cs(ctypes.byref(d_odd), 1, fake, lib.MLA_F32, fake, 0.0, ctypes.byref(cache), None) == lib.MLA_ERR_UNSUPPORTED
+    assert cs(ctypes.byref(d), 1, odd, lib.MLA_F32, fake, 0.0, ctypes.byref(cache), None) == lib.MLA_ERR_ALIGNMENT
+    assert cs(ctypes.byref(d), 1, fake, lib.MLA_F32, fake, 0.0, ctypes.byref(c3), None) == lib.MLA_ERR_INVALID_ARG
+    assert cs(ctypes.byref(d), 0, fake, lib.MLA_F32, fake, 0.0, ctypes.byref(cache), None) == lib.MLA_OK
+    ca = L.mla_cache_append
+    assert ca(ctypes.byref(d), 5120, 1, None, 1, fake, fake, 1, fake, fake, 1e4, ctypes.byref(cache),
+              None) == lib.MLA_ERR_INVALID_ARG
+    assert ca(ctypes.byref(d), 0, 1, fake, 1, fake, fake, 1, fake, fake, 1e4, ctypes.byref(cache),
+              None) == lib.MLA_ERR_INVALID_ARG
+    assert ca(ctypes.byref(d), 5120, 1, fake, lib.MLA_FP8_E4M3, fake, fake, 1, fake, fake, 1e4, ctypes.byref(cache),
+              None) == lib.MLA_ERR_UNSUPPORTED
 
 
 def _brute_parts(lens, page, W):
