@@ -226,8 +226,9 @@ mla_status_t mla_cache_store(const mla_dims_t* dims, int32_t batch, const void* 
  * written to `rows`; then mla_cache_store(rows, positions, rope_base, cache).
  *   h: [batch, d_model] (h_dt f32 or bf16) hidden state of the new token.
  *   w_dkv: [d_c, d_model], w_kr: [d_rope, d_model] (w_dt f32 or bf16).
- *   rows: [batch, d_c + d_rope] fp32 device scratch filled by the call (the rows
- *       before rotation and rounding).
+ *   rows: fp32 device scratch of 8 * batch * (d_c + d_rope) floats; on return
+ *       its first batch * (d_c + d_rope) floats hold the rows before rotation
+ *       and rounding (the rest holds partial sums of the projection).
  */
 mla_status_t mla_cache_append(const mla_dims_t* dims, int32_t d_model, int32_t batch, const void* h,
                               mla_dtype_t h_dt, const void* w_dkv, const void* w_kr, mla_dtype_t w_dt, float* rows,

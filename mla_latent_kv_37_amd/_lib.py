@@ -194,7 +194,9 @@ def cache_store(d: Dims, rows, positions, cache: PagedCache, rope_base: float = 
 
 
 def cache_append(d: Dims, h, w_dkv, w_kr, rows, positions, cache: PagedCache, rope_base: float, stream=None):
-    """rows = [W^DKV h ; W^KR h] (fp32 scratch [B, d_c+d_rope]), then cache_store(rows, positions, rope_base)."""
+    """rows = [W^DKV h ; W^KR h], then cache_store(rows, positions, rope_base).
+
+    rows: fp32 scratch [8, B, d_c+d_rope]; rows[0] holds the projected rows afterwards."""
     _check(load().mla_cache_append(ctypes.byref(d), h.shape[1], h.shape[0], _ptr(h), dtype_code(h), _ptr(w_dkv),
                                    _ptr(w_kr), dtype_code(w_dkv), _ptr(rows), _ptr(positions),
                                    ctypes.c_float(rope_base), ctypes.byref(cache), _stream(stream)), "mla_cache_append")

@@ -317,6 +317,8 @@ mla_status_t mla_cache_store(const mla_dims_t* dims, int32_t batch, const void* 
   CacheStoreArgs a{};
   if (mla_status_t s = store_args(dims, batch, rows, rows_dt, positions, rope_base, cache, &a)) return s;
   if (batch == 0) return MLA_OK;
+  a.batch = batch;
+  a.n_partials = 1;
   const hipError_t e = launch_cache_store(a, batch, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
@@ -344,6 +346,9 @@ mla_status_t mla_cache_append(const mla_dims_t* dims, int32_t d_model, int32_t b
   p.d_model = d_model;
   p.d_latent = dims->d_latent;
   p.d_rope = dims->d_rope;
+  p.ksplit = project_ksplit(h_dt, w_dt, dims->d_latent + dims->d_rope, d_model);
+  a.batch = batch;
+  a.n_partials = p.ksplit;
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = launch_project(p, st);
   if (e == hipSuccess) e = launch_cache_store(a, batch, st);

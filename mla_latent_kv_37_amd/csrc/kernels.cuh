@@ -71,6 +71,8 @@ struct CacheStoreArgs {
   const int32_t* block_table;
   int max_pages, page_size, num_pages;
   int d_latent, d_rope;
+  int batch;
+  int n_partials;          // > 1: rows holds that many fp32 k-slices of the projection
 };
 
 struct ProjectArgs {
@@ -79,13 +81,16 @@ struct ProjectArgs {
   const void* w_dkv;       // [d_c, d_model]
   const void* w_kr;        // [d_rope, d_model]
   mla_dtype_t w_dt;
-  float* rows;             // [B, d_c + d_rope]
+  float* rows;             // [ksplit, B, d_c + d_rope]
   int batch, d_model, d_latent, d_rope;
+  int ksplit;              // k slices (1: the generic kernel writes the rows directly)
 };
 
 hipError_t launch_decode_v2(const V2DecodeArgs& a, hipStream_t st);
 hipError_t launch_cache_store(const CacheStoreArgs& a, int batch, hipStream_t st);
 hipError_t launch_project(const ProjectArgs& a, hipStream_t st);
+// k slices the projection of mla_cache_append uses for these operands
+int project_ksplit(mla_dtype_t h_dt, mla_dtype_t w_dt, int width, int d_model);
 hipError_t launch_merge(const MergeArgs& a, int batch, hipStream_t st);
 hipError_t launch_absorb_generic(const void* q, mla_dtype_t q_dt, const void* w, mla_dtype_t w_dt, void* out,
                                  mla_dtype_t o_dt, int batch, int n_heads, int d_head, int d_latent, hipStream_t st);

@@ -217,10 +217,10 @@ def test_cache_append_v2(kind):
     perm = _targets(rng, pos, max_pages, num_pages)
     kv, scales, bt, cache = _device_cache(kind, num_pages, width, perm)
     t = lambda x: torch.from_numpy(x.astype(np.float32)).cuda().to(torch.bfloat16)  # noqa: E731
-    rows = torch.empty((batch, width), dtype=torch.float32, device="cuda")
+    rows = torch.empty((8, batch, width), dtype=torch.float32, device="cuda")
     mk.cache_append(d, t(h), t(w_dkv), t(w_kr), rows, torch.from_numpy(pos).cuda(), cache, 10000.0)
     torch.cuda.synchronize()
-    rows_gpu = rows.cpu().numpy()
+    rows_gpu = rows[0].cpu().numpy()
     ref_c, ref_r = h @ w_dkv.T, h @ w_kr.T          # the projections, float64
     ref = np.concatenate([ref_c, ref_r], axis=1)
     err = np.abs(rows_gpu - ref).max() / np.abs(ref).max()
@@ -253,14 +253,14 @@ def test_cache_append_tiny_f32():
     pos = rng.integers(0, max_pages * PAGE, batch).astype(np.int32)
     kv, scales, bt, cache = _device_cache("f32", num_pages, width, perm)
     f = lambda x: torch.from_numpy(np.asarray(x, dtype=np.float32)).cuda()  # noqa: E731
-    rows = torch.empty((batch, width), dtype=torch.float32, device="cuda")
+    rows = torch.empty((8, batch, width), dtype=torch.float32, device="cuda")
     mk.cache_append(d, f(h), f(W["W_DKV"]), f(W["W_KR"]), rows, torch.from_numpy(pos).cuda(), cache, 10000.0)
     torch.cuda.synchronize()
     hd = h.astype(np.float64)
     wdkv, wkr = W["W_DKV"].astype(np.float32).astype(np.float64), W["W_KR"].astype(np.float32).astype(np.float64)
     c_kv, k_r = oracle.project_cache(hd, {"W_DKV": wdkv, "W_KR": wkr}, pos)
     ref = np.concatenate([hd @ wdkv.T, hd @ wkr.T], axis=1)
-    assert np.abs(rows.cpu().numpy() - ref).max() <= 1e-4 * np.abs(ref).max()
+    assert np.abs(rows[0].cpu().numpy() - ref).max() <= 1e-4 * np.abs(ref).max()
     got = _stored_values("f32", kv, scales, perm, pos, num_pages, width)
     for b in range(batch):
         full = np.concatenate([c_kv[b], k_r[b]])
