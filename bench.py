@@ -364,7 +364,72 @@ def copy_calibration(nbytes: int, reps: int = 3):
 # ---------------------------------------------------------------------------
 
 APPEND_WORKLOADS = {"append_bf16": "bf16", "append_fp8": "fp8"}
+QUERY_WORKLOADS = {"query_prep": "bf16"}
 D_MODEL = 5120
+D_QLATENT = 1536
+
+
+def _cold_weight_steps(fn, args):
+    """Per-step durations (ms, sorted) of fn on the current stream, HIP events around
+    each call; 512 MB copied between steps pushes the weights out of the 256 MB
+    Infinity Cache, so every step streams them from HBM."""
+    import torch
+    flush_src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+    flush_dst = torch.empty_like(flush_src)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        fn()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        flush_dst.copy_(flush_src)
+        evs[i][0].record(stream)
+        fn()
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    return sorted(e[0].elapsed_time(e[1]) for e in evs)
+
+
+def run_query(args):
+    """Query-side projections of one decode step for the 64-sequence batch:
+    c^Q = W^DQ h, q^C = W^UQ c^Q, q^R = RoPE(W^QR c^Q), bf16 weights (91 MB) read
+    cold each step."""
+    import numpy as np
+    import torch
+    import synth
+    import mla_latent_kv_37_amd as mk
+    torch.cuda.set_device(0)
+    mk._lib.load()
+    w = synth.workload(3)
+    lens = np.asarray(w.lens, dtype=np.int32)
+    B = len(lens)
+    W = synth.weights(synth.V2, 0.006, synth.rng_for(3, synth.S_WEIGHTS), with_wo=False)
+    bf = lambda x: torch.from_numpy(np.asarray(x, dtype=np.float32)).cuda().to(torch.bfloat16)  # noqa: E731
+    w_dq, w_uq, w_qr = bf(W["W_DQ"]), bf(W["W_UQ"]), bf(W["W_QR"])
+    h = bf(synth.hidden_states(B, D_MODEL, synth.rng_for(3, synth.S_H)))
+    pos = torch.from_numpy(lens).cuda()
+    d = mk.dims(N_H, D_H, D_R, D_C)
+    scratch = torch.empty(mk.query_prep_scratch_size(d, D_QLATENT, B), dtype=torch.uint8, device="cuda")
+    q_nope = torch.empty((B, N_H, D_H), dtype=torch.bfloat16, device="cuda")
+    q_pe = torch.empty((B, N_H, D_R), dtype=torch.bfloat16, device="cuda")
+    times = _cold_weight_steps(lambda: mk.query_prep(d, h, w_dq, w_uq, w_qr, pos, q_nope, q_pe, scratch, 10000.0),
+                               args)
+    ms = times[len(times) // 2]
+    w_bytes = 2 * (D_QLATENT * D_MODEL + N_H * (D_H + D_R) * D_QLATENT)
+    alg_bytes = w_bytes + B * D_MODEL * 2 + B * N_H * (D_H + D_R) * 2 + B * 4
+    ach = alg_bytes / (ms * 1e-3) / 1e9
+    return {
+        "metric": "MLA query projections, sequences/s (c^Q = W^DQ h, q^C = W^UQ c^Q, q^R = RoPE(W^QR c^Q))",
+        "value": B / (ms * 1e-3), "unit": "sequences/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"v2_query_prep_b{B}", "batch": B, "d_model": D_MODEL, "d_qlatent": D_QLATENT,
+                   "weights": "cold (512 MB copied between steps)", "timing": "median of per-step HIP events"},
+        "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": ach / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "gemm_ws_mfma_kernel x2 + reduce_cast_kernel + query_finish_kernel",
+                     "algorithmic_bytes_per_launch": alg_bytes, "mean_launch_ms": sum(times) / len(times)},
+    }
 
 
 def run_append(args):
@@ -395,21 +460,7 @@ def run_append(args):
     pos = torch.from_numpy(lens).cuda()
     rows = torch.empty((8, B, width), dtype=torch.float32, device="cuda")
     d = mk.dims(N_H, D_H, D_R, D_C)
-    # 512 MB copied between steps pushes the weights out of the 256 MB Infinity Cache
-    flush_src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
-    flush_dst = torch.empty_like(flush_src)
-    stream = torch.cuda.current_stream()
-    for _ in range(args.warmup):
-        mk.cache_append(d, h, w_dkv, w_kr, rows, pos, cache, 10000.0)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        flush_dst.copy_(flush_src)
-        evs[i][0].record(stream)
-        mk.cache_append(d, h, w_dkv, w_kr, rows, pos, cache, 10000.0)
-        evs[i][1].record(stream)
-    torch.cuda.synchronize()
-    times = sorted(e[0].elapsed_time(e[1]) for e in evs)
+    times = _cold_weight_steps(lambda: mk.cache_append(d, h, w_dkv, w_kr, rows, pos, cache, 10000.0), args)
     ms = times[len(times) // 2]
     elem = 2 if kind == "bf16" else 1
     alg_bytes = (width * D_MODEL * 2 + B * D_MODEL * 2 + B * width * elem + (B * 5 * 4 if kind == "fp8" else 0)
@@ -423,7 +474,7 @@ def run_append(args):
         "config": {"workload": f"v2_cache_append_b{B}_{kind}", "batch": B, "d_model": D_MODEL, "cache_dtype": kind,
                    "weights": "cold (512 MB copied between steps)", "timing": "median of per-step HIP events"},
         "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": ach / HBM_PEAK_GBS, "traffic": None, "kernel": "project_mfma_kernel + cache_store_kernel",
+                     "frac": ach / HBM_PEAK_GBS, "traffic": None, "kernel": "gemm_ws_mfma_kernel + cache_store_kernel",
                      "algorithmic_bytes_per_launch": alg_bytes, "mean_launch_ms": sum(times) / len(times)},
     }
 
@@ -433,7 +484,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="ragged", choices=sorted(WORKLOADS) + sorted(APPEND_WORKLOADS))
+    ap.add_argument("--workload", default="ragged", choices=sorted(WORKLOADS) + sorted(APPEND_WORKLOADS) + sorted(QUERY_WORKLOADS))
     ap.add_argument("--copies", type=int, default=2)
     ap.add_argument("--no-kernel-events", dest="kernel_events", action="store_false")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -453,7 +504,12 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
-    res = run_append(args) if args.workload in APPEND_WORKLOADS else run(args)
+    if args.workload in APPEND_WORKLOADS:
+        res = run_append(args)
+    elif args.workload in QUERY_WORKLOADS:
+        res = run_query(args)
+    else:
+        res = run(args)
     print(json.dumps(res), flush=True)
 
 

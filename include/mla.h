@@ -236,6 +236,28 @@ mla_status_t mla_cache_append(const mla_dims_t* dims, int32_t d_model, int32_t b
                               void* stream);
 
 /*
+ * Query side of a decode step, before absorption [DeepSeek-V2 explainer §2.2.1
+ * (query compression) and §2.2.2 (decoupled RoPE); deepseek(2) 關鍵技術 §1]:
+ *   c^Q = W^DQ h,   q^C = W^UQ c^Q,   q^R = RoPE(W^QR c^Q) per head,
+ * with fp32 accumulation; c^Q is rounded to w_dt between the two products.
+ *   h: [batch, d_model] (h_dt f32 or bf16); w_dq: [d_qlatent, d_model];
+ *   w_uq: [n_h * d_h, d_qlatent]; w_qr: [n_h * d_rope, d_qlatent] (w_dt).
+ *   positions: [batch] int32 DEVICE array: the query token's position; head
+ *       i's q^R pair (2k, 2k+1) is rotated by position * rope_base^(-2k/d_rope)
+ *       (angle in fp64); rope_base = 0 leaves q^R unrotated.
+ *   q_nope: [batch, n_h, d_h], q_pe: [batch, n_h, d_rope] (out_dt f32 or bf16),
+ *       the inputs of mla_absorb_q and mla_decode.
+ *   scratch: device memory of mla_query_prep_scratch_size(...) bytes, 16-B
+ *       aligned (k-slice partial sums and c^Q).
+ * d_h and d_rope must be even.
+ */
+size_t mla_query_prep_scratch_size(const mla_dims_t* dims, int32_t d_qlatent, int32_t batch);
+mla_status_t mla_query_prep(const mla_dims_t* dims, int32_t d_model, int32_t d_qlatent, int32_t batch,
+                            const void* h, mla_dtype_t h_dt, const void* w_dq, const void* w_uq, const void* w_qr,
+                            mla_dtype_t w_dt, const int32_t* positions, float rope_base, void* q_nope, void* q_pe,
+                            mla_dtype_t out_dt, void* scratch, size_t scratch_bytes, void* stream);
+
+/*
  * Host helper (no device access): for host copies of seq_lens, the workspace
  * slots that hold sequence b's partials: slots part_first[b] .. part_first[b] +
  * part_count[b] - 1.  part_count[b] == 1 means mla_decode writes the final

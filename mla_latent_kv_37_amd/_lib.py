@@ -19,7 +19,7 @@ MLA_F32, MLA_BF16, MLA_FP8_E4M3 = 0, 1, 2
 
 EXPORTS = ("mla_status_string", "mla_build_info", "mla_absorb_q", "mla_decode_workspace_size",
            "mla_lse_part_offset", "mla_decode", "mla_merge_splits", "mla_out_proj", "mla_cache_store",
-           "mla_cache_append", "mla_partition_host")
+           "mla_cache_append", "mla_query_prep_scratch_size", "mla_query_prep", "mla_partition_host")
 
 
 class MlaError(RuntimeError):
@@ -71,6 +71,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "mla_cache_store": (ctypes.c_int, [PD, I32, P, ctypes.c_int, P, ctypes.c_float, PC, P]),
         "mla_cache_append": (ctypes.c_int, [PD, I32, I32, P, ctypes.c_int, P, P, ctypes.c_int, P, P, ctypes.c_float,
                                             PC, P]),
+        "mla_query_prep_scratch_size": (SZ, [PD, I32, I32]),
+        "mla_query_prep": (ctypes.c_int, [PD, I32, I32, I32, P, ctypes.c_int, P, P, P, ctypes.c_int, P,
+                                          ctypes.c_float, P, P, ctypes.c_int, P, SZ, P]),
         "mla_partition_host": (ctypes.c_int, [ctypes.POINTER(I32), I32, I32, I32, PP, ctypes.POINTER(I32),
                                               ctypes.POINTER(I32)]),
     }
@@ -200,6 +203,22 @@ def cache_append(d: Dims, h, w_dkv, w_kr, rows, positions, cache: PagedCache, ro
     _check(load().mla_cache_append(ctypes.byref(d), h.shape[1], h.shape[0], _ptr(h), dtype_code(h), _ptr(w_dkv),
                                    _ptr(w_kr), dtype_code(w_dkv), _ptr(rows), _ptr(positions),
                                    ctypes.c_float(rope_base), ctypes.byref(cache), _stream(stream)), "mla_cache_append")
+
+
+def query_prep_scratch_size(d: Dims, d_qlatent: int, batch: int) -> int:
+    return load().mla_query_prep_scratch_size(ctypes.byref(d), d_qlatent, batch)
+
+
+def query_prep(d: Dims, h, w_dq, w_uq, w_qr, positions, q_nope, q_pe, scratch, rope_base: float = 10000.0,
+               stream=None):
+    """c^Q = W^DQ h, q_nope = W^UQ c^Q, q_pe = RoPE(W^QR c^Q) per head; shapes [B, d], [d_q, d],
+    [n_h d_h, d_q], [n_h d_r, d_q], positions [B] int32, outputs [B, n_h, d_h], [B, n_h, d_r]."""
+    nbytes = scratch.numel() * scratch.element_size()
+    _check(load().mla_query_prep(ctypes.byref(d), h.shape[1], w_dq.shape[0], h.shape[0], _ptr(h), dtype_code(h),
+                                 _ptr(w_dq), _ptr(w_uq), _ptr(w_qr), dtype_code(w_dq), _ptr(positions),
+                                 ctypes.c_float(rope_base), _ptr(q_nope), _ptr(q_pe), dtype_code(q_nope),
+                                 _ptr(scratch), nbytes, _stream(stream)), "mla_query_prep")
+    return q_nope, q_pe
 
 
 def partition_host(seq_lens, page_size: int, max_pages: int, part: Partition):

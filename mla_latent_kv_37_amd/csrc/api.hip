@@ -119,6 +119,21 @@ mla_status_t store_args(const mla_dims_t* dims, int32_t batch, const void* rows,
   return MLA_OK;
 }
 
+// mla_query_prep scratch: stage-1 slices, c^Q (in the weights' dtype; its area
+// is sized for fp32 whatever the dtype, so one size serves every call), stage-2
+// slices
+struct QueryScratch { size_t s1, cq, s2, total; };
+QueryScratch query_scratch(const mla_dims_t* d, int32_t d_qlatent, int32_t batch) {
+  QueryScratch q{};
+  const size_t B = size_t(batch > 0 ? batch : 0);
+  const size_t n2 = size_t(d->n_heads) * (d->d_head + d->d_rope);
+  q.s1 = 0;
+  q.cq = align256(kGemmMaxSlices * B * d_qlatent * sizeof(float));
+  q.s2 = q.cq + align256(B * d_qlatent * sizeof(float));
+  q.total = q.s2 + align256(kGemmMaxSlices * B * n2 * sizeof(float));
+  return q;
+}
+
 }  // namespace
 
 extern "C" {
@@ -137,7 +152,8 @@ const char* mla_status_string(mla_status_t s) {
 
 const char* mla_build_info(void) {
   return "libmla gfx950: absorb(v2 mfma, generic), decode(v2 bf16 / fp8-dequant mfma ping-pong, generic f32/bf16/fp8), "
-         "cache store (f32/bf16/fp8 1x128), cache append (mfma / generic projection), "
+         "cache store (f32/bf16/fp8 1x128), cache append and query prep (weight-streaming mfma / generic "
+         "products), "
          "merge, out_proj(v2 mfma, generic)";
 }
 
@@ -335,23 +351,91 @@ mla_status_t mla_cache_append(const mla_dims_t* dims, int32_t d_model, int32_t b
   if (batch == 0) return MLA_OK;
   if (!h || !w_dkv || (dims->d_rope > 0 && !w_kr)) return MLA_ERR_INVALID_ARG;
   if (!aligned16(h) || !aligned16(w_dkv) || (w_kr && !aligned16(w_kr))) return MLA_ERR_ALIGNMENT;
-  ProjectArgs p{};
-  p.h = h;
-  p.h_dt = h_dt;
-  p.w_dkv = w_dkv;
-  p.w_kr = w_kr;
-  p.w_dt = w_dt;
-  p.rows = rows;
-  p.batch = batch;
-  p.d_model = d_model;
-  p.d_latent = dims->d_latent;
-  p.d_rope = dims->d_rope;
-  p.ksplit = project_ksplit(h_dt, w_dt, dims->d_latent + dims->d_rope, d_model);
+  GemmArgs g{};
+  g.x = h;
+  g.x_dt = h_dt;
+  g.w0 = w_dkv;
+  g.w1 = w_kr;
+  g.w_dt = w_dt;
+  g.out = rows;
+  g.batch = batch;
+  g.K = d_model;
+  g.N = dims->d_latent + dims->d_rope;
+  g.n0 = dims->d_latent;
+  gemm_ws_plan(g);
   a.batch = batch;
-  a.n_partials = p.ksplit;
+  a.n_partials = g.slices;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = launch_project(p, st);
+  hipError_t e = launch_gemm_ws(g, st);
   if (e == hipSuccess) e = launch_cache_store(a, batch, st);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+size_t mla_query_prep_scratch_size(const mla_dims_t* dims, int32_t d_qlatent, int32_t batch) {
+  if (check_dims(dims) != MLA_OK || d_qlatent < 1 || batch < 0) return 0;
+  return query_scratch(dims, d_qlatent, batch).total;
+}
+
+mla_status_t mla_query_prep(const mla_dims_t* dims, int32_t d_model, int32_t d_qlatent, int32_t batch,
+                            const void* h, mla_dtype_t h_dt, const void* w_dq, const void* w_uq, const void* w_qr,
+                            mla_dtype_t w_dt, const int32_t* positions, float rope_base, void* q_nope, void* q_pe,
+                            mla_dtype_t out_dt, void* scratch, size_t scratch_bytes, void* stream) {
+  if (mla_status_t s = check_dims(dims)) return s;
+  if (batch < 0 || d_model < 1 || d_qlatent < 1 || !(rope_base >= 0.f)) return MLA_ERR_INVALID_ARG;
+  for (mla_dtype_t t : {h_dt, w_dt, out_dt})
+    if (t != MLA_F32 && t != MLA_BF16) return valid_dtype(t) ? MLA_ERR_UNSUPPORTED : MLA_ERR_INVALID_ARG;
+  if ((dims->d_head & 1) || (dims->d_rope & 1)) return MLA_ERR_UNSUPPORTED;
+  const QueryScratch L = query_scratch(dims, d_qlatent, batch);
+  if (batch == 0) return MLA_OK;
+  if (!h || !w_dq || !w_uq || !q_nope || (dims->d_rope > 0 && (!w_qr || !q_pe || !positions)))
+    return MLA_ERR_INVALID_ARG;
+  if (!scratch || scratch_bytes < L.total) return MLA_ERR_WORKSPACE;
+  if (!aligned16(h) || !aligned16(w_dq) || !aligned16(w_uq) || (w_qr && !aligned16(w_qr)) || !aligned16(scratch))
+    return MLA_ERR_ALIGNMENT;
+  char* ws = static_cast<char*>(scratch);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // stage 1: c^Q = W^DQ h
+  GemmArgs g1{};
+  g1.x = h;
+  g1.x_dt = h_dt;
+  g1.w0 = w_dq;
+  g1.w1 = nullptr;
+  g1.w_dt = w_dt;
+  g1.out = reinterpret_cast<float*>(ws + L.s1);
+  g1.batch = batch;
+  g1.K = d_model;
+  g1.N = d_qlatent;
+  g1.n0 = d_qlatent;
+  gemm_ws_plan(g1);
+  hipError_t e = launch_gemm_ws(g1, st);
+  if (e == hipSuccess) e = launch_reduce_cast(g1.out, g1.slices, int64_t(batch) * d_qlatent, ws + L.cq, w_dt, st);
+  // stage 2: [q^C ; q^R before rotation] = [W^UQ ; W^QR] c^Q, then rotate and write
+  GemmArgs g2{};
+  g2.x = ws + L.cq;
+  g2.x_dt = w_dt;
+  g2.w0 = w_uq;
+  g2.w1 = w_qr;
+  g2.w_dt = w_dt;
+  g2.out = reinterpret_cast<float*>(ws + L.s2);
+  g2.batch = batch;
+  g2.K = d_qlatent;
+  g2.N = dims->n_heads * (dims->d_head + dims->d_rope);
+  g2.n0 = dims->n_heads * dims->d_head;
+  gemm_ws_plan(g2);
+  if (e == hipSuccess) e = launch_gemm_ws(g2, st);
+  QueryFinishArgs f{};
+  f.slices = g2.out;
+  f.n_slices = g2.slices;
+  f.batch = batch;
+  f.n_heads = dims->n_heads;
+  f.d_head = dims->d_head;
+  f.d_rope = dims->d_rope;
+  f.positions = positions;
+  f.rope_base = rope_base;
+  f.q_nope = q_nope;
+  f.q_pe = q_pe;
+  f.out_dt = out_dt;
+  if (e == hipSuccess) e = launch_query_finish(f, st);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

@@ -18,9 +18,8 @@
 // pos * base^(-2k/d_h^R); the angle and its sine and cosine are evaluated in
 // fp64, since positions reach 1e5 and a binary32 angle would be off by 1e-2.
 //
-// project kernels: rows[b] = [W^DKV h_b ; W^KR h_b] in fp32, a weight-streaming
-// GEMM (v_mfma_f32_32x32x16_bf16 for bf16 operands and 32-aligned widths, in k
-// slices that the store kernel adds up; else a VALU dot product).
+// The projection rows[b] = [W^DKV h_b ; W^KR h_b] of mla_cache_append is the
+// weight-streaming product of gemm.hip, in k slices that this kernel adds up.
 #include "kernels.cuh"
 
 namespace mla {
@@ -93,112 +92,10 @@ __global__ __launch_bounds__(640) void cache_store_kernel(CacheStoreArgs a) {
   }
 }
 
-// rows[b][n] = sum_k h[b][k] * Wn[k], Wn = row n of [W^DKV ; W^KR] (any shapes)
-__global__ __launch_bounds__(256) void project_generic_kernel(ProjectArgs a) {
-  const int b = blockIdx.x, n = blockIdx.y * 256 + threadIdx.x;
-  const int W = a.d_latent + a.d_rope;
-  if (n >= W) return;
-  const void* w = n < a.d_latent ? a.w_dkv : a.w_kr;
-  const int64_t wr = int64_t(n < a.d_latent ? n : n - a.d_latent) * a.d_model;
-  float acc = 0.f;
-  for (int k = 0; k < a.d_model; ++k)
-    acc = __builtin_fmaf(load_any(a.h, int64_t(b) * a.d_model + k, a.h_dt), load_any(w, wr + k, a.w_dt), acc);
-  a.rows[int64_t(b) * W + n] = acc;
-}
-
-// MFMA version for bf16 h and weights, (d_c + d_rope) % 32 == 0, d_model % 512 == 0:
-// rows^T [n x b] = Wcat [n x k] . h^T [k x b].  Workgroup (32-row tile of n, one
-// of kProjSplit slices of k): every weight is read once, and each weight
-// fragment feeds two MFMAs (two 32-row batch tiles, 64 batch rows per pass).
-// The 4 wavefronts split the slice again, with all their operand loads issued
-// before the first MFMA (operands straight from global memory, contiguous
-// along k), and add their partial tiles in LDS.  Slice s writes its partial
-// rows to rows + s * batch * W; the store kernel sums the slices in order.
-constexpr int kProjWaves = 4;
-constexpr int kProjSteps = 10;   // k-steps of 16 per wavefront for d_model = 5120
-
-__global__ __launch_bounds__(64 * kProjWaves) void project_mfma_kernel(ProjectArgs a) {
-  __shared__ float red[kProjWaves - 1][2][16][64];
-  const int nt = blockIdx.x * 32, slice = blockIdx.y;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, h = lane >> 5;
-  const int n = nt + (lane & 31);
-  const uint16_t* w = static_cast<const uint16_t*>(n < a.d_latent ? a.w_dkv : a.w_kr) +
-                      int64_t(n < a.d_latent ? n : n - a.d_latent) * a.d_model;
-  const int kw = a.d_model / (a.ksplit * kProjWaves);   // k per wavefront, a multiple of 16
-  const int k0 = (slice * kProjWaves + wave) * kw;
-  const int nsteps = kw / 16;
-  const int W = a.d_latent + a.d_rope;
-  float* out = a.rows + int64_t(slice) * a.batch * W;
-  for (int bc = 0; bc < a.batch; bc += 64) {
-    const uint16_t* h0 = static_cast<const uint16_t*>(a.h) + int64_t(min(bc + (lane & 31), a.batch - 1)) * a.d_model;
-    const uint16_t* h1 = static_cast<const uint16_t*>(a.h) + int64_t(min(bc + 32 + (lane & 31), a.batch - 1)) * a.d_model;
-    f32x16 acc0 = {}, acc1 = {};
-    for (int s0 = 0; s0 < nsteps; s0 += kProjSteps) {
-      bf16x8 wf[kProjSteps], x0[kProjSteps], x1[kProjSteps];
-#pragma unroll
-      for (int t = 0; t < kProjSteps; ++t) {
-        const int k = k0 + (s0 + min(t, nsteps - 1 - s0)) * 16 + 8 * h;
-        wf[t] = *reinterpret_cast<const bf16x8*>(w + k);
-        x0[t] = *reinterpret_cast<const bf16x8*>(h0 + k);
-        x1[t] = *reinterpret_cast<const bf16x8*>(h1 + k);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int t = 0; t < kProjSteps; ++t) {
-        if (s0 + t < nsteps) {
-          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[t], x0[t], acc0, 0, 0, 0);
-          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[t], x1[t], acc1, 0, 0, 0);
-        }
-      }
-    }
-    if (wave > 0) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        red[wave - 1][0][r][lane] = acc0[r];
-        red[wave - 1][1][r][lane] = acc1[r];
-      }
-    }
-    __syncthreads();
-    if (wave == 0) {
-      // D[n][b]: lane holds b = lane % 32, n = 8(r/4) + 4(lane/32) + r%4
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float v0 = acc0[r], v1 = acc1[r];
-#pragma unroll
-        for (int q = 0; q < kProjWaves - 1; ++q) {
-          v0 += red[q][0][r][lane];
-          v1 += red[q][1][r][lane];
-        }
-        const int nn = nt + 8 * (r >> 2) + 4 * h + (r & 3);
-        const int b0 = bc + (lane & 31), b1 = b0 + 32;
-        if (b0 < a.batch) out[int64_t(b0) * W + nn] = v0;
-        if (b1 < a.batch) out[int64_t(b1) * W + nn] = v1;
-      }
-    }
-    __syncthreads();
-  }
-}
-
-int project_ksplit(mla_dtype_t h_dt, mla_dtype_t w_dt, int width, int d_model) {
-  constexpr int kSplit = 8;
-  if (h_dt == MLA_BF16 && w_dt == MLA_BF16 && width % 32 == 0 && d_model % (kSplit * kProjWaves * 16) == 0)
-    return kSplit;
-  return 1;
-}
-
 hipError_t launch_cache_store(const CacheStoreArgs& a, int batch, hipStream_t st) {
   const int W = a.d_latent + a.d_rope;
   const int ng = (W + kGroup - 1) / kGroup;
   cache_store_kernel<<<batch, 64 * ng, 0, st>>>(a);
-  return hipGetLastError();
-}
-
-hipError_t launch_project(const ProjectArgs& a, hipStream_t st) {
-  const int W = a.d_latent + a.d_rope;
-  if (a.ksplit > 1)
-    project_mfma_kernel<<<dim3(W / 32, a.ksplit), 64 * kProjWaves, 0, st>>>(a);
-  else
-    project_generic_kernel<<<dim3(a.batch, ceil_div(W, 256)), 256, 0, st>>>(a);
   return hipGetLastError();
 }
 

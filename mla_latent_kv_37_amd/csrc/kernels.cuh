@@ -75,22 +75,37 @@ struct CacheStoreArgs {
   int n_partials;          // > 1: rows holds that many fp32 k-slices of the projection
 };
 
-struct ProjectArgs {
-  const void* h;           // [B, d_model]
-  mla_dtype_t h_dt;
-  const void* w_dkv;       // [d_c, d_model]
-  const void* w_kr;        // [d_rope, d_model]
+// out[s][b][n] = sum_{k in slice s} x[b][k] * W[n][k]; W = w0 rows [0, n0) over w1 rows [n0, N)
+struct GemmArgs {
+  const void* x;           // [batch, K]
+  mla_dtype_t x_dt;
+  const void* w0;          // [n0, K]
+  const void* w1;          // [N - n0, K]
   mla_dtype_t w_dt;
-  float* rows;             // [ksplit, B, d_c + d_rope]
-  int batch, d_model, d_latent, d_rope;
-  int ksplit;              // k slices (1: the generic kernel writes the rows directly)
+  float* out;              // [slices, batch, N] fp32
+  int batch, K, N, n0;
+  int slices;              // set by gemm_ws_plan
+  bool use_mfma;           // set by gemm_ws_plan
 };
 
 hipError_t launch_decode_v2(const V2DecodeArgs& a, hipStream_t st);
 hipError_t launch_cache_store(const CacheStoreArgs& a, int batch, hipStream_t st);
-hipError_t launch_project(const ProjectArgs& a, hipStream_t st);
-// k slices the projection of mla_cache_append uses for these operands
-int project_ksplit(mla_dtype_t h_dt, mla_dtype_t w_dt, int width, int d_model);
+struct QueryFinishArgs {
+  const float* slices;     // [n_slices, batch, n_h * (d_h + d_rope)] fp32
+  int n_slices, batch, n_heads, d_head, d_rope;
+  const int32_t* positions;
+  float rope_base;
+  void* q_nope;            // [batch, n_h, d_h]
+  void* q_pe;              // [batch, n_h, d_rope]
+  mla_dtype_t out_dt;
+};
+
+constexpr int kGemmMaxSlices = 8;
+void gemm_ws_plan(GemmArgs& a);          // chooses slices (<= kGemmMaxSlices) and the kernel
+hipError_t launch_gemm_ws(const GemmArgs& a, hipStream_t st);
+hipError_t launch_reduce_cast(const float* slices, int n_slices, int64_t count, void* out, mla_dtype_t out_dt,
+                              hipStream_t st);
+hipError_t launch_query_finish(const QueryFinishArgs& a, hipStream_t st);
 hipError_t launch_merge(const MergeArgs& a, int batch, hipStream_t st);
 hipError_t launch_absorb_generic(const void* q, mla_dtype_t q_dt, const void* w, mla_dtype_t w_dt, void* out,
                                  mla_dtype_t o_dt, int batch, int n_heads, int d_head, int d_latent, hipStream_t st);

@@ -126,6 +126,16 @@ def test_validation_errors_before_any_device_access(lib):
               None) == lib.MLA_ERR_INVALID_ARG
     assert ca(ctypes.byref(d), 5120, 1, fake, lib.MLA_FP8_E4M3, fake, fake, 1, fake, fake, 1e4, ctypes.byref(cache),
               None) == lib.MLA_ERR_UNSUPPORTED
+    # query prep: too-small scratch, fp8 weights, null weight
+    qp = L.mla_query_prep
+    need = L.mla_query_prep_scratch_size(ctypes.byref(d), 1536, 4)
+    assert need >= 4 * 128 * 192 * 4
+    assert qp(ctypes.byref(d), 5120, 1536, 4, fake, 1, fake, fake, fake, 1, fake, 1e4, fake, fake, 1, fake, need - 1,
+              None) == lib.MLA_ERR_WORKSPACE
+    assert qp(ctypes.byref(d), 5120, 1536, 4, fake, 1, fake, fake, fake, lib.MLA_FP8_E4M3, fake, 1e4, fake, fake, 1,
+              fake, need, None) == lib.MLA_ERR_UNSUPPORTED
+    assert qp(ctypes.byref(d), 5120, 1536, 4, fake, 1, None, fake, fake, 1, fake, 1e4, fake, fake, 1, fake, need,
+              None) == lib.MLA_ERR_INVALID_ARG
 
 
 def _brute_parts(lens, page, W):

@@ -1,0 +1,109 @@
+"""GPU tests of the query-side projection entry point against the oracle.
+
+mla_query_prep computes c^Q = W^DQ h, q^C = W^UQ c^Q and q^R = RoPE(W^QR c^Q)
+per head; the oracle's project_query is the float64 reference, on the same
+inputs (bf16 inputs are rounded to bf16 values before the oracle sees them).
+Between the two products the device rounds c^Q to the weights' dtype, so the
+bf16 cases are held to the bf16 tolerance of the decode path (1e-2 of the
+largest reference magnitude), the fp32 ones to 1e-4.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import storage as ostore
+from oracle.mla import ROPE_BASE
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 1e-2}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mla_latent_kv_37_amd as mk
+    print(mk.build_info(), flush=True)
+
+
+def _round(x, kind):
+    x = np.asarray(x, dtype=np.float64)
+    if kind == "f32":
+        return x.astype(np.float32).astype(np.float64)
+    return ostore.bf16_bits_to_f64(ostore.f32_to_bf16_bits(x.astype(np.float32)))
+
+
+def _run(dims, batch, h_kind, w_kind, out_kind, seed, rope_base=10000.0, max_pos=None, sigma=None):
+    import torch
+    import synth
+    import mla_latent_kv_37_amd as mk
+    assert rope_base in (0.0, ROPE_BASE), "the oracle's RoPE base is fixed"
+    rng = np.random.default_rng(seed)
+    sigma = synth.V2_SIGMA_W if sigma is None else sigma
+    W = synth.weights(dims, sigma, rng, with_wo=False)
+    W = {k: _round(W[k], w_kind) for k in ("W_DQ", "W_UQ", "W_QR")}
+    h = _round(rng.normal(size=(batch, dims.d_model)), h_kind)
+    pos = rng.integers(0, max_pos or 32768, batch).astype(np.int32)
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16}
+    dev = lambda x, k: torch.from_numpy(x.astype(np.float32)).cuda().to(tdt[k]).contiguous()  # noqa: E731
+    d = mk.dims(dims.n_heads, dims.d_head, dims.d_rope, dims.d_latent)
+    nbytes = mk.query_prep_scratch_size(d, dims.d_qlatent, batch)
+    scratch = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    q_nope = torch.empty((batch, dims.n_heads, dims.d_head), dtype=tdt[out_kind], device="cuda")
+    q_pe = torch.empty((batch, dims.n_heads, dims.d_rope), dtype=tdt[out_kind], device="cuda")
+    print(f"case: query prep B={batch} d={dims.d_model} h {h_kind} w {w_kind} out {out_kind} "
+          f"base {rope_base} scratch {nbytes}", flush=True)
+    mk.query_prep(d, dev(h, h_kind), dev(W["W_DQ"], w_kind), dev(W["W_UQ"], w_kind), dev(W["W_QR"], w_kind),
+                  torch.from_numpy(pos).cuda(), q_nope, q_pe, scratch, rope_base)
+    torch.cuda.synchronize()
+    got_c = q_nope.float().cpu().numpy().astype(np.float64)
+    got_r = q_pe.float().cpu().numpy().astype(np.float64)
+    ref_c = np.empty_like(got_c)
+    ref_r = np.empty_like(got_r)
+    for b in range(batch):
+        qc, qr = oracle.project_query(h[b], W, int(pos[b]), dims.n_heads)
+        ref_c[b] = qc
+        # rope_base 0 means the device leaves q^R unrotated: position 0 in the oracle
+        ref_r[b] = qr if rope_base > 0 else oracle.project_query(h[b], W, 0, dims.n_heads)[1]
+    return got_c, got_r, ref_c, ref_r
+
+
+def _rel(got, ref):
+    return np.abs(got - ref).max() / np.abs(ref).max()
+
+
+@pytest.mark.parametrize("batch", [64, 37, 100])
+def test_query_prep_v2_bf16(batch):
+    import synth
+    got_c, got_r, ref_c, ref_r = _run(synth.V2, batch, "bf16", "bf16", "bf16", seed=100 + batch)
+    ec, er = _rel(got_c, ref_c), _rel(got_r, ref_r)
+    print(f"q^C rel err {ec:.3e}  q^R rel err {er:.3e}", flush=True)
+    assert ec <= TOL["bf16"] and er <= TOL["bf16"]
+
+
+def test_query_prep_v2_mixed_f32_out():
+    """fp32 h and fp32 outputs around bf16 weights: the first product takes the
+    generic path, the second the MFMA one (c^Q is rounded to bf16)."""
+    import synth
+    got_c, got_r, ref_c, ref_r = _run(synth.V2, 16, "f32", "bf16", "f32", seed=7)
+    ec, er = _rel(got_c, ref_c), _rel(got_r, ref_r)
+    print(f"q^C rel err {ec:.3e}  q^R rel err {er:.3e}", flush=True)
+    assert ec <= TOL["bf16"] and er <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("batch", [1, 9])
+def test_query_prep_tiny_f32(batch):
+    import synth
+    got_c, got_r, ref_c, ref_r = _run(synth.TINY, batch, "f32", "f32", "f32", seed=200 + batch, sigma=0.05,
+                                      max_pos=100000)
+    assert _rel(got_c, ref_c) <= TOL["f32"]
+    assert _rel(got_r, ref_r) <= TOL["f32"]
+
+
+def test_query_prep_unrotated():
+    import synth
+    got_c, got_r, ref_c, ref_r = _run(synth.TINY, 5, "f32", "f32", "f32", seed=3, rope_base=0.0, sigma=0.05)
+    assert _rel(got_c, ref_c) <= TOL["f32"]
+    assert _rel(got_r, ref_r) <= TOL["f32"]
