@@ -364,7 +364,7 @@ def copy_calibration(nbytes: int, reps: int = 3):
 # ---------------------------------------------------------------------------
 
 APPEND_WORKLOADS = {"append_bf16": "bf16", "append_fp8": "fp8"}
-QUERY_WORKLOADS = {"query_prep": "bf16"}
+QUERY_WORKLOADS = ("query_prep", "query_lat", "query_lat_fused")
 D_MODEL = 5120
 D_QLATENT = 1536
 
@@ -391,13 +391,16 @@ def _cold_weight_steps(fn, args):
 
 
 def run_query(args):
-    """Query-side projections of one decode step for the 64-sequence batch:
-    c^Q = W^DQ h, q^C = W^UQ c^Q, q^R = RoPE(W^QR c^Q), bf16 weights (91 MB) read
-    cold each step."""
+    """Query side of one decode step for the 64-sequence batch, bf16 weights read
+    cold each step:
+      query_prep      - c^Q = W^DQ h, q^C = W^UQ c^Q, q^R = RoPE(W^QR c^Q) (91 MB of weights);
+      query_lat       - the same, then q_lat_i = W^UK_i^T q^C_i (mla_absorb_q; +16.8 MB);
+      query_lat_fused - one product on the offline-fused W^UK_i^T W^UQ_i (201 MB) writes q_lat."""
     import numpy as np
     import torch
     import synth
     import mla_latent_kv_37_amd as mk
+    variant = args.workload
     torch.cuda.set_device(0)
     mk._lib.load()
     w = synth.workload(3)
@@ -405,76 +408,57 @@ def run_query(args):
     B = len(lens)
     W = synth.weights(synth.V2, 0.006, synth.rng_for(3, synth.S_WEIGHTS), with_wo=False)
     bf = lambda x: torch.from_numpy(np.asarray(x, dtype=np.float32)).cuda().to(torch.bfloat16)  # noqa: E731
-    w_dq, w_uq, w_qr = bf(W["W_DQ"]), bf(W["W_UQ"]), bf(W["W_QR"])
     h = bf(synth.hidden_states(B, D_MODEL, synth.rng_for(3, synth.S_H)))
     pos = torch.from_numpy(lens).cuda()
-    d = mk.dims(N_H, D_H, D_R, D_C)
-    scratch = torch.empty(mk.query_prep_scratch_size(d, D_QLATENT, B), dtype=torch.uint8, device="cuda")
-    q_nope = torch.empty((B, N_H, D_H), dtype=torch.bfloat16, device="cuda")
+    w_dq, w_qr = bf(W["W_DQ"]), bf(W["W_QR"])
     q_pe = torch.empty((B, N_H, D_R), dtype=torch.bfloat16, device="cuda")
-    times = _cold_weight_steps(lambda: mk.query_prep(d, h, w_dq, w_uq, w_qr, pos, q_nope, q_pe, scratch, 10000.0),
-                               args)
+    d = mk.dims(N_H, D_H, D_R, D_C)
+    if variant == "query_lat_fused":
+        # offline weight preparation (host, float32): head i's block is W^UK_i^T W^UQ_i
+        wuk = W["W_UK"].astype(np.float32).reshape(N_H, D_H, D_C)
+        wuq = W["W_UQ"].astype(np.float32).reshape(N_H, D_H, D_QLATENT)
+        w_uq = bf(np.matmul(wuk.transpose(0, 2, 1), wuq).reshape(N_H * D_C, D_QLATENT))
+        dq = mk.dims(N_H, D_C, D_R, D_C)
+        q_out = torch.empty((B, N_H, D_C), dtype=torch.bfloat16, device="cuda")
+        w_bytes = 2 * (D_QLATENT * D_MODEL + N_H * (D_C + D_R) * D_QLATENT)
+        out_bytes = B * N_H * (D_C + D_R) * 2
+    else:
+        w_uq = bf(W["W_UQ"])
+        dq = d
+        q_out = torch.empty((B, N_H, D_H), dtype=torch.bfloat16, device="cuda")
+        w_bytes = 2 * (D_QLATENT * D_MODEL + N_H * (D_H + D_R) * D_QLATENT)
+        out_bytes = B * N_H * (D_H + D_R) * 2
+    scratch = torch.empty(mk.query_prep_scratch_size(dq, D_QLATENT, B), dtype=torch.uint8, device="cuda")
+    if variant == "query_lat":
+        w_uk = bf(W["W_UK"])
+        q_lat = torch.empty((B, N_H, D_C), dtype=torch.bfloat16, device="cuda")
+        w_bytes += 2 * N_H * D_H * D_C
+        out_bytes = B * N_H * (D_C + D_R) * 2
+
+        def fn():
+            mk.query_prep(d, h, w_dq, w_uq, w_qr, pos, q_out, q_pe, scratch, 10000.0)
+            mk.absorb_q(d, q_out, w_uk, q_lat)
+    else:
+        def fn():
+            mk.query_prep(dq, h, w_dq, w_uq, w_qr, pos, q_out, q_pe, scratch, 10000.0)
+    times = _cold_weight_steps(fn, args)
     ms = times[len(times) // 2]
-    w_bytes = 2 * (D_QLATENT * D_MODEL + N_H * (D_H + D_R) * D_QLATENT)
-    alg_bytes = w_bytes + B * D_MODEL * 2 + B * N_H * (D_H + D_R) * 2 + B * 4
+    alg_bytes = w_bytes + B * D_MODEL * 2 + out_bytes + B * 4
     ach = alg_bytes / (ms * 1e-3) / 1e9
+    kernels = "gemm_ws_mfma_kernel x2 + reduce_cast_kernel + query_finish_kernel"
+    if variant == "query_lat":
+        kernels += " + absorb_v2_kernel"
+    outputs = "q^C, q^R" if variant == "query_prep" else "q_lat, q^R"
     return {
-        "metric": "MLA query projections, sequences/s (c^Q = W^DQ h, q^C = W^UQ c^Q, q^R = RoPE(W^QR c^Q))",
+        "metric": f"MLA query-side projections, sequences/s (h -> {outputs})",
         "value": B / (ms * 1e-3), "unit": "sequences/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"v2_query_prep_b{B}", "batch": B, "d_model": D_MODEL, "d_qlatent": D_QLATENT,
-                   "weights": "cold (512 MB copied between steps)", "timing": "median of per-step HIP events"},
+        "config": {"workload": f"v2_{variant}_b{B}", "batch": B, "d_model": D_MODEL, "d_qlatent": D_QLATENT,
+                   "weight_bytes": w_bytes, "weights": "cold (512 MB copied between steps)",
+                   "timing": "median of per-step HIP events"},
         "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": ach / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "gemm_ws_mfma_kernel x2 + reduce_cast_kernel + query_finish_kernel",
-                     "algorithmic_bytes_per_launch": alg_bytes, "mean_launch_ms": sum(times) / len(times)},
-    }
-
-
-def run_append(args):
-    import numpy as np
-    import torch
-    import synth
-    import mla_latent_kv_37_amd as mk
-    kind = APPEND_WORKLOADS[args.workload]
-    torch.cuda.set_device(0)
-    mk._lib.load()
-    w = synth.workload(3)
-    lens = np.asarray(w.lens, dtype=np.int32)
-    B = len(lens)
-    rng = synth.rng_for(3, synth.S_WEIGHTS)
-    W = synth.weights(synth.V2, 0.006, rng, with_wo=False)
-    bf = lambda x: torch.from_numpy(np.asarray(x, dtype=np.float32)).cuda().to(torch.bfloat16)  # noqa: E731
-    w_dkv, w_kr = bf(W["W_DKV"]), bf(W["W_KR"])
-    h = bf(synth.hidden_states(B, D_MODEL, synth.rng_for(3, synth.S_H)))
-    # one page of its own per sequence for the new token's slot
-    max_pages = int((lens.max() + 64) // 64) + 1
-    bt = np.zeros((B, max_pages), dtype=np.int32)
-    bt[np.arange(B), lens // 64] = np.arange(B)
-    width = D_C + D_R
-    tdt = torch.bfloat16 if kind == "bf16" else torch.uint8
-    kv = torch.zeros((B, 64, width), dtype=tdt, device="cuda")
-    scales = torch.zeros((B, 64, 5), dtype=torch.float32, device="cuda") if kind == "fp8" else None
-    cache = mk.make_cache(kv, torch.from_numpy(bt).cuda(), torch.from_numpy(lens).cuda(), 64, scales)
-    pos = torch.from_numpy(lens).cuda()
-    rows = torch.empty((8, B, width), dtype=torch.float32, device="cuda")
-    d = mk.dims(N_H, D_H, D_R, D_C)
-    times = _cold_weight_steps(lambda: mk.cache_append(d, h, w_dkv, w_kr, rows, pos, cache, 10000.0), args)
-    ms = times[len(times) // 2]
-    elem = 2 if kind == "bf16" else 1
-    alg_bytes = (width * D_MODEL * 2 + B * D_MODEL * 2 + B * width * elem + (B * 5 * 4 if kind == "fp8" else 0)
-                 + B * 4 * 2)
-    ach = alg_bytes / (ms * 1e-3) / 1e9
-    return {
-        "metric": "MLA cache append new tokens/s (project [W^DKV; W^KR] h, RoPE, round, scatter)",
-        "value": B / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": f"v2_cache_append_b{B}_{kind}", "batch": B, "d_model": D_MODEL, "cache_dtype": kind,
-                   "weights": "cold (512 MB copied between steps)", "timing": "median of per-step HIP events"},
-        "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": ach / HBM_PEAK_GBS, "traffic": None, "kernel": "gemm_ws_mfma_kernel + cache_store_kernel",
+                     "frac": ach / HBM_PEAK_GBS, "traffic": None, "kernel": kernels,
                      "algorithmic_bytes_per_launch": alg_bytes, "mean_launch_ms": sum(times) / len(times)},
     }
 

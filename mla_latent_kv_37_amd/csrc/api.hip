@@ -119,18 +119,20 @@ mla_status_t store_args(const mla_dims_t* dims, int32_t batch, const void* rows,
   return MLA_OK;
 }
 
-// mla_query_prep scratch: stage-1 slices, c^Q (in the weights' dtype; its area
-// is sized for fp32 whatever the dtype, so one size serves every call), stage-2
-// slices
+// mla_query_prep scratch: stage-1 k slices (at most kGemmMaxSlices: d_model is
+// not an argument of the size query), c^Q (in the weights' dtype; its area is
+// sized for fp32), stage-2 k slices (as many as the bf16 plan for
+// [n_h (d_h + d_rope)] x d_qlatent uses; every other plan uses one).  One size
+// serves every dtype.
 struct QueryScratch { size_t s1, cq, s2, total; };
 QueryScratch query_scratch(const mla_dims_t* d, int32_t d_qlatent, int32_t batch) {
   QueryScratch q{};
   const size_t B = size_t(batch > 0 ? batch : 0);
-  const size_t n2 = size_t(d->n_heads) * (d->d_head + d->d_rope);
+  const int n2 = d->n_heads * (d->d_head + d->d_rope);
   q.s1 = 0;
   q.cq = align256(kGemmMaxSlices * B * d_qlatent * sizeof(float));
   q.s2 = q.cq + align256(B * d_qlatent * sizeof(float));
-  q.total = q.s2 + align256(kGemmMaxSlices * B * n2 * sizeof(float));
+  q.total = q.s2 + align256(size_t(gemm_ws_slices(n2, d_qlatent)) * B * n2 * sizeof(float));
   return q;
 }
 

@@ -92,17 +92,18 @@ __global__ __launch_bounds__(256) void gemm_ws_generic_kernel(GemmArgs a) {
   a.out[int64_t(b) * a.N + n] = acc;
 }
 
+int gemm_ws_slices(int N, int K) {
+  if (N % 32 != 0 || K % (16 * kGemmWaves) != 0) return 1;
+  // k slices until the tiles x slices cover the chip about four times
+  const int tiles = N / 32;
+  for (int sl : {8, 4, 2})
+    if (K % (16 * kGemmWaves * sl) == 0 && tiles * sl <= 1024) return sl;
+  return 1;
+}
+
 void gemm_ws_plan(GemmArgs& a) {
   a.use_mfma = a.x_dt == MLA_BF16 && a.w_dt == MLA_BF16 && a.N % 32 == 0 && a.K % (16 * kGemmWaves) == 0;
-  a.slices = 1;
-  if (!a.use_mfma) return;
-  // k slices until the tiles x slices cover the chip about four times
-  const int tiles = a.N / 32;
-  for (int sl : {8, 4, 2})
-    if (a.K % (16 * kGemmWaves * sl) == 0 && tiles * sl <= 1024) {
-      a.slices = sl;
-      return;
-    }
+  a.slices = a.use_mfma ? gemm_ws_slices(a.N, a.K) : 1;
 }
 
 hipError_t launch_gemm_ws(const GemmArgs& a, hipStream_t st) {

@@ -101,6 +101,8 @@ struct QueryFinishArgs {
 };
 
 constexpr int kGemmMaxSlices = 8;
+// k slices of the MFMA plan for an N x K bf16 product (1 for every other plan)
+int gemm_ws_slices(int N, int K);
 void gemm_ws_plan(GemmArgs& a);          // chooses slices (<= kGemmMaxSlices) and the kernel
 hipError_t launch_gemm_ws(const GemmArgs& a, hipStream_t st);
 hipError_t launch_reduce_cast(const float* slices, int n_slices, int64_t count, void* out, mla_dtype_t out_dt,

@@ -107,3 +107,59 @@ def test_query_prep_unrotated():
     got_c, got_r, ref_c, ref_r = _run(synth.TINY, 5, "f32", "f32", "f32", seed=3, rope_base=0.0, sigma=0.05)
     assert _rel(got_c, ref_c) <= TOL["f32"]
     assert _rel(got_r, ref_r) <= TOL["f32"]
+
+
+def _fused_weights(W, n_heads, d_head):
+    """The offline-fused query weight of the pages' absorption remark: head i's
+    block is W^UK_i^T W^UQ_i, so W^UQK c^Q gives every head's q_lat directly."""
+    return np.concatenate([oracle.mla.head_rows(W["W_UK"], i, d_head).T @ oracle.mla.head_rows(W["W_UQ"], i, d_head)
+                           for i in range(n_heads)], axis=0)
+
+
+@pytest.mark.parametrize("batch", [64, 37])
+def test_query_prep_fused_absorb_v2(batch):
+    """q_lat two ways, each against q_lat_i = W^UK_i^T q^C_i from the oracle's q^C:
+    (1) query prep then mla_absorb_q; (2) query prep on the fused weight
+    [W^UK_i^T W^UQ_i] (d_h replaced by d_c), which writes q_lat itself."""
+    import torch
+    import synth
+    import mla_latent_kv_37_amd as mk
+    dims = synth.V2
+    nh, dh, dr, dc, dq = dims.n_heads, dims.d_head, dims.d_rope, dims.d_latent, dims.d_qlatent
+    rng = np.random.default_rng(500 + batch)
+    W = synth.weights(dims, synth.V2_SIGMA_W, rng, with_wo=False)
+    W = {k: _round(W[k], "bf16") for k in ("W_DQ", "W_UQ", "W_QR", "W_UK")}
+    fused = _round(_fused_weights(W, nh, dh), "bf16")
+    h = _round(rng.normal(size=(batch, dims.d_model)), "bf16")
+    pos = rng.integers(0, 32768, batch).astype(np.int32)
+    bf = lambda x: torch.from_numpy(np.asarray(x, dtype=np.float32)).cuda().to(torch.bfloat16).contiguous()  # noqa: E731
+    pos_d = torch.from_numpy(pos).cuda()
+    print(f"case: q_lat via absorb and via fused weights, B={batch}", flush=True)
+    # (1) unfused
+    d = mk.dims(nh, dh, dr, dc)
+    scratch = torch.empty(mk.query_prep_scratch_size(d, dq, batch), dtype=torch.uint8, device="cuda")
+    q_nope = torch.empty((batch, nh, dh), dtype=torch.bfloat16, device="cuda")
+    q_pe = torch.empty((batch, nh, dr), dtype=torch.bfloat16, device="cuda")
+    mk.query_prep(d, bf(h), bf(W["W_DQ"]), bf(W["W_UQ"]), bf(W["W_QR"]), pos_d, q_nope, q_pe, scratch, ROPE_BASE)
+    q_lat1 = torch.empty((batch, nh, dc), dtype=torch.bfloat16, device="cuda")
+    mk.absorb_q(d, q_nope, bf(W["W_UK"]), q_lat1)
+    # (2) fused: the same entry point with d_h := d_c and W^UQK in place of W^UQ
+    dfu = mk.dims(nh, dc, dr, dc)
+    scratch2 = torch.empty(mk.query_prep_scratch_size(dfu, dq, batch), dtype=torch.uint8, device="cuda")
+    q_lat2 = torch.empty((batch, nh, dc), dtype=torch.bfloat16, device="cuda")
+    q_pe2 = torch.empty((batch, nh, dr), dtype=torch.bfloat16, device="cuda")
+    mk.query_prep(dfu, bf(h), bf(W["W_DQ"]), bf(fused), bf(W["W_QR"]), pos_d, q_lat2, q_pe2, scratch2, ROPE_BASE)
+    torch.cuda.synchronize()
+    ref_lat = np.empty((batch, nh, dc))
+    ref_r = np.empty((batch, nh, dr))
+    for b in range(batch):
+        qc, qr = oracle.project_query(h[b], W, int(pos[b]), nh)
+        for i in range(nh):
+            ref_lat[b, i] = oracle.mla.head_rows(W["W_UK"], i, dh).T @ qc[i]
+        ref_r[b] = qr
+    got1 = q_lat1.float().cpu().numpy()
+    got2 = q_lat2.float().cpu().numpy()
+    e1, e2 = _rel(got1, ref_lat), _rel(got2, ref_lat)
+    er1, er2 = _rel(q_pe.float().cpu().numpy(), ref_r), _rel(q_pe2.float().cpu().numpy(), ref_r)
+    print(f"q_lat rel err: absorb {e1:.3e}, fused {e2:.3e}; q^R {er1:.3e} / {er2:.3e}", flush=True)
+    assert max(e1, e2, er1, er2) <= TOL["bf16"]
