@@ -148,6 +148,35 @@ def attend(q_c: np.ndarray, q_r: np.ndarray, c_kv: np.ndarray, k_r: np.ndarray,
     return out
 
 
+def attend_new_tokens(q_c: np.ndarray, q_r: np.ndarray, c_kv: np.ndarray, k_r: np.ndarray,
+                      W_UK: np.ndarray, W_UV: np.ndarray, scale: Optional[float] = None,
+                      heads: Optional[Sequence[int]] = None) -> List[Dict[str, np.ndarray]]:
+    """Attention of a sequence's q_len newest tokens, each at its own position.
+
+    q_c [q_len, n_h, d_h], q_r [q_len, n_h, d_r]; c_kv [T, d_c], k_r [T, d_r] hold
+    all T cached tokens, the q_len new ones last.  New token t sits at position
+    T - q_len + t, and the single-token formula's sum over the tokens up to and
+    including the query's own position ([Key-tech] §1, the attention-output
+    formula) applies at that position: token t attends to cache rows
+    0 .. T - q_len + t.  Several new tokens per step arise when the multi-token
+    prediction modules are kept for decoding ([Key-tech] §2.2, MTP at inference).
+    Returns one attend() dict per new token (a token with no visible row, when
+    T < q_len, gets lse = -inf and zero outputs).
+    """
+    q_len = q_c.shape[0]
+    T = c_kv.shape[0]
+    out = []
+    for t in range(q_len):
+        n = T - q_len + t + 1
+        if n <= 0:
+            n_h, d_h = q_c.shape[1:]
+            out.append({"o_heads": np.zeros((n_h, d_h)), "lse": np.full(n_h, -np.inf),
+                        "o_lat": np.zeros((n_h, c_kv.shape[1]))})
+            continue
+        out.append(attend(q_c[t], q_r[t], c_kv[:n], k_r[:n], W_UK, W_UV, scale, heads))
+    return out
+
+
 def chunk_partials(q_c, q_r, c_kv, k_r, W_UK, W_UV, chunk: int, scale=None, heads=None):
     """Attention restricted to each chunk [s*chunk, min((s+1)*chunk, T)) of the cache.
 

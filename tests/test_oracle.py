@@ -92,6 +92,59 @@ def test_attend_matches_torch_sdpa_float64():
         np.testing.assert_allclose(r["o_heads"][i], o, rtol=1e-12, atol=1e-14)
 
 
+def test_new_tokens_single_token_is_attend():
+    """q_len = 1: the one new token is the query of the single-token formula."""
+    pr = _tiny_problem(11, T=13)
+    r1 = oracle.attend_new_tokens(pr["q_c"][None], pr["q_r"][None], pr["c_kv"], pr["k_r"], pr["W_UK"], pr["W_UV"])
+    r0 = oracle.attend(pr["q_c"], pr["q_r"], pr["c_kv"], pr["k_r"], pr["W_UK"], pr["W_UV"])
+    assert len(r1) == 1
+    np.testing.assert_array_equal(r1[0]["o_heads"], r0["o_heads"])
+    np.testing.assert_array_equal(r1[0]["lse"], r0["lse"])
+
+
+@pytest.mark.parametrize("q_len,T", [(2, 9), (4, 21), (3, 3)])
+def test_new_tokens_match_torch_sdpa_causal_mask(q_len, T):
+    """The q_len new tokens against torch's scaled_dot_product_attention in float64
+    with an explicit boolean mask: new token t sees cache row j iff j <= T - q_len + t
+    (the causal mask aligned to the end of the cache)."""
+    torch = pytest.importorskip("torch")
+    import torch.nn.functional as F
+    rng = np.random.default_rng(100 + q_len)
+    n_h, d_h, d_r, d_c = 3, 4, 2, 6
+    q_c = rng.normal(size=(q_len, n_h, d_h)) * 2.0
+    q_r = rng.normal(size=(q_len, n_h, d_r)) * 2.0
+    c_kv, k_r = rng.normal(size=(T, d_c)), rng.normal(size=(T, d_r))
+    W_UK, W_UV = rng.normal(size=(n_h * d_h, d_c)) * 0.5, rng.normal(size=(n_h * d_h, d_c)) * 0.5
+    scale = 1.0 / math.sqrt(d_h + d_r)
+    res = oracle.attend_new_tokens(q_c, q_r, c_kv, k_r, W_UK, W_UV)
+    mask = torch.from_numpy(np.arange(T)[None, :] <= (T - q_len + np.arange(q_len))[:, None])
+    c = torch.from_numpy(c_kv)
+    for i in range(n_h):
+        k = torch.cat([c @ torch.from_numpy(W_UK[i * d_h:(i + 1) * d_h]).T, torch.from_numpy(k_r)], dim=1)
+        v = c @ torch.from_numpy(W_UV[i * d_h:(i + 1) * d_h]).T
+        q = torch.cat([torch.from_numpy(q_c[:, i]), torch.from_numpy(q_r[:, i])], dim=1)
+        o = F.scaled_dot_product_attention(q[None, None], k[None, None], v[None, None], attn_mask=mask,
+                                           scale=scale)[0, 0].numpy()
+        for t in range(q_len):
+            np.testing.assert_allclose(res[t]["o_heads"][i], o[t], rtol=1e-12, atol=1e-14)
+
+
+def test_new_tokens_shorter_cache_than_q_len():
+    """T < q_len: the first q_len - T new tokens see no row (lse -inf, zero output);
+    the others see rows 0 .. T - q_len + t."""
+    pr = _tiny_problem(12, T=2)
+    q_c = np.stack([pr["q_c"]] * 4)
+    q_r = np.stack([pr["q_r"]] * 4)
+    res = oracle.attend_new_tokens(q_c, q_r, pr["c_kv"], pr["k_r"], pr["W_UK"], pr["W_UV"])
+    for t in (0, 1):
+        assert np.all(np.isneginf(res[t]["lse"])) and np.all(res[t]["o_heads"] == 0)
+    one = oracle.attend(pr["q_c"], pr["q_r"], pr["c_kv"][:1], pr["k_r"][:1], pr["W_UK"], pr["W_UV"])
+    # one visible row: the output is that row's value projection (softmax weight 1)
+    np.testing.assert_allclose(res[2]["o_heads"], one["o_heads"], rtol=1e-15)
+    v0 = np.stack([pr["W_UV"][i * 4:(i + 1) * 4] @ pr["c_kv"][0] for i in range(3)])
+    np.testing.assert_allclose(res[2]["o_heads"], v0, rtol=1e-12)
+
+
 def test_absorbed_identity():
     """q_{t,i}.k_{j,i} = (W^UK_i^T q^C_i).c^KV_j + q^R_i.k^R_j and o_i = W^UV_i o_lat_i."""
     pr = _tiny_problem(7, T=20, n_h=4, d_h=6, d_r=4, d_c=10)
