@@ -47,7 +47,10 @@ WORKLOADS = {
     "long": (4, "v2_bf16_long_b4_t131072_split4096", (4096, 0)),
     "fp8": (5, "v2_fp8_b32_t16384", (0, -1)),
     "v2b1": (2, "v2_bf16_b1_t4096", (0, -1)),
+    # the ragged batch with two new query tokens per sequence (causal within them)
+    "mtp2": (3, "v2_bf16_ragged_b64_t1024-8192_qlen2", (0, -1)),
 }
+Q_LEN = {"mtp2": 2}
 
 
 def decode_source_hash() -> str:
@@ -58,7 +61,7 @@ def decode_source_hash() -> str:
 # algorithmic bytes / flops (what the method must move / compute)
 # ---------------------------------------------------------------------------
 
-def algorithmic(lens, cache_dtype: str):
+def algorithmic(lens, cache_dtype: str, q_len: int = 1):
     """Bytes and flops of one decode step and of the decode kernel alone.
 
     Per cached token: the row [c^KV | k^R] (1152 B bf16; 576 B + 5 fp32 scales
@@ -73,18 +76,22 @@ def algorithmic(lens, cache_dtype: str):
     row = ROW_BYTES_BF16 if cache_dtype == "bf16" else (D_C + D_R) + 4 * 5
     cache = T * row
     meta = pages * 4 + B * 4
-    q_in = B * N_H * (D_H + D_R) * 2
+    Q = B * q_len                      # query tokens: each reads its inputs, writes its outputs
+    q_in = Q * N_H * (D_H + D_R) * 2
     weights = 2 * N_H * D_H * D_C * 2
-    out = B * N_H * D_H * 2
+    out = Q * N_H * D_H * 2
     flops_tok = 2 * N_H * (D_C + D_R) + 2 * N_H * D_C
-    step_flops = T * flops_tok + 2 * 2 * B * N_H * D_H * D_C
-    decode_bytes = cache + meta + B * N_H * (D_C + D_R) * 2 + B * N_H * (D_C * 2 + 4)
+    # new token t of a sequence of T_b tokens attends to T_b - q_len + t + 1 of them
+    attended = sum(max(t - q_len + k + 1, 0) for t in lens for k in range(q_len))
+    step_flops = attended * flops_tok + 2 * 2 * Q * N_H * D_H * D_C
+    decode_bytes = cache + meta + Q * N_H * (D_C + D_R) * 2 + Q * N_H * (D_C * 2 + 4)
     return {
         "step_bytes": cache + meta + q_in + weights + out,
         "step_flops": step_flops,
         "decode_bytes": decode_bytes,
-        "decode_flops": T * flops_tok,
+        "decode_flops": attended * flops_tok,
         "cache_bytes": cache,
+        "attended_tokens": attended,
     }
 
 
@@ -92,7 +99,7 @@ def algorithmic(lens, cache_dtype: str):
 # inputs
 # ---------------------------------------------------------------------------
 
-def make_inputs(config_id: int, copies: int, device="cuda"):
+def make_inputs(config_id: int, copies: int, device="cuda", q_len: int = 1):
     import numpy as np
     import torch
     import synth
@@ -107,6 +114,15 @@ def make_inputs(config_id: int, copies: int, device="cuda"):
         scales.append(sc)
     del inp["rows"]
     maxp = max((t + 63) // 64 for t in lens)
+    if q_len > 1:
+        # q_len queries per sequence ([B, q_len, ...] flattened), the first one the workload's own
+        rq = synth.rng_for(config_id, synth.S_QUERY + 50)
+        B = len(lens)
+        extra = lambda x: rq.normal(0.0, synth.V2_SD_QUERY, size=(B, q_len - 1) + x.shape[1:])  # noqa: E731
+        inp["q_nope"] = np.concatenate([inp["q_nope"][:, None], extra(inp["q_nope"])], axis=1).reshape(
+            (B * q_len,) + inp["q_nope"].shape[1:])
+        inp["q_pe"] = np.concatenate([inp["q_pe"][:, None], extra(inp["q_pe"])], axis=1).reshape(
+            (B * q_len,) + inp["q_pe"].shape[1:])
     sets = []
     for c in range(copies):
         cache = synth.build_paged(words, w.cache_dtype, synth.rng_for(config_id, synth.S_PERM + 10 * c),
@@ -169,13 +185,21 @@ def run(args):
     import torch
     import mla_latent_kv_37_amd as mk
     cid, wname, (split, parts) = WORKLOADS[args.workload]
+    q_len = Q_LEN.get(args.workload, 1)
     torch.cuda.set_device(0)
     mk._lib.load()
-    w, lens, sets = make_inputs(cid, args.copies)
+    w, lens, sets = make_inputs(cid, args.copies, q_len=q_len)
     maxp = sets[0]["cache"].max_pages
-    step = mk.DecodeStep(N_H, D_H, D_R, D_C, len(lens), maxp, 64, split, parts)
+    B = len(lens)
+    step = mk.DecodeStep(N_H, D_H, D_R, D_C, B * q_len, maxp, 64, split, parts)
     scale = 1.0 / math.sqrt(D_H + D_R)
     stream = torch.cuda.current_stream()
+    if q_len > 1:
+        nbytes, _ = mk.multi_workspace_size(step.d, B, q_len, maxp, 64, step.part)
+        multi_ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        q_lat_m = step.q_lat.view(B, q_len, N_H, D_C)
+        o_lat_m = step.o_lat.view(B, q_len, N_H, D_C)
+        lse_m = step.lse.view(B, q_len, N_H)
 
     def one(i, ev=None):
         s = sets[i % len(sets)]
@@ -184,11 +208,18 @@ def run(args):
         step.absorb(s["q_nope"], s["W_UK"])
         if ev is not None:
             ev[1].record(stream)
-        mk.decode(step.d, step.q_lat, s["q_pe"], s["cache"].desc, scale, step.part, step.workspace, step.o_lat,
-                  step.lse)
-        if ev is not None:
-            ev[2].record(stream)
-        mk.merge_splits(step.d, s["cache"].seq_lens, 64, maxp, step.part, step.workspace, step.o_lat, step.lse)
+        if q_len > 1:
+            # expand + decode + merge in one call
+            mk.decode_multi(step.d, q_lat_m, s["q_pe"].view(B, q_len, N_H, D_R), s["cache"].desc, scale, step.part,
+                            multi_ws, o_lat_m, lse_m)
+            if ev is not None:
+                ev[2].record(stream)
+        else:
+            mk.decode(step.d, step.q_lat, s["q_pe"], s["cache"].desc, scale, step.part, step.workspace, step.o_lat,
+                      step.lse)
+            if ev is not None:
+                ev[2].record(stream)
+            mk.merge_splits(step.d, s["cache"].seq_lens, 64, maxp, step.part, step.workspace, step.o_lat, step.lse)
         if ev is not None:
             ev[3].record(stream)
         step.project(s["W_UV"])
@@ -215,20 +246,28 @@ def run(args):
     if args.kernel_events:
         names = ["absorb", "decode", "merge", "out_proj"]
         per_kernel = {n: sum(e[k].elapsed_time(e[k + 1]) for e in evs) / args.steps for k, n in enumerate(names)}
-    alg = algorithmic(lens, w.cache_dtype)
+    alg = algorithmic(lens, w.cache_dtype, q_len)
     T = sum(lens)
     value = T * args.steps / (total_ms * 1e-3)
+    metric, unit = METRIC, "KV-tokens/s"
+    if q_len > 1:
+        metric = f"MLA multi-token decode query-tokens/s ({q_len} new tokens per sequence, causal)"
+        unit = "query-tokens/s"
+        value = B * q_len * args.steps / (total_ms * 1e-3)
     res = {
-        "metric": METRIC, "value": value, "unit": "KV-tokens/s", "n_gpus": 1, "steps": args.steps,
+        "metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wname, "batch": len(lens), "sum_cache_tokens": T, "cache_dtype": w.cache_dtype,
                    "heads": N_H, "d_latent": D_C, "d_rope": D_R, "page_size": 64,
                    "partition": {"split_tokens": split, "num_parts": parts}, "input_copies": args.copies,
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU", "q_len": q_len},
     }
     step_s = ms_per_step * 1e-3
-    res["query_tokens_per_s"] = len(lens) / step_s
+    res["query_tokens_per_s"] = B * q_len / step_s
+    res["cache_tokens_per_s"] = T / step_s
+    if q_len > 1:
+        res["attended_kv_tokens_per_s"] = alg["attended_tokens"] / step_s
     res["step_TBps"] = alg["step_bytes"] / step_s / 1e12
     res["step_roofline"] = {
         "hbm_us": alg["step_bytes"] / (HBM_PEAK_GBS * 1e9) * 1e6,
@@ -247,12 +286,14 @@ def run(args):
                 traffic = tj.get("decode_bytes_per_launch")
         res["roofline"] = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": ach / HBM_PEAK_GBS, "traffic": traffic,
-                           "kernel": "decode_v2_kernel<true> (fp8 cache)" if cid == 5 else "decode_v2_kernel<false> (bf16 cache)",
+                           "kernel": ("decode_v2_kernel<true> (fp8 cache)" if cid == 5 else
+                                      "decode_v2_kernel<false> (bf16 cache)") +
+                                     (" + expand_kernel + merge_kernel (mla_decode_multi)" if q_len > 1 else ""),
                            "algorithmic_bytes_per_launch": alg["decode_bytes"],
                            "mean_launch_ms": per_kernel["decode"],
                            "mfma_frac": alg["decode_flops"] / dec_s / (MFMA_BF16_PEAK_TFLOPS * 1e12)}
     res["wall_s_timed"] = wall
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and q_len == 1:
         res["cpu_baseline"] = cpu_baseline(cid, args.cpu_budget)
     return res
 

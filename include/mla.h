@@ -186,6 +186,32 @@ mla_status_t mla_merge_splits(const mla_dims_t* dims, int32_t batch,
                               void* o_lat, mla_dtype_t o_dt, float* lse, void* stream);
 
 /*
+ * Several new query tokens per sequence, causal within them ([deepseek(2)
+ * 關鍵技術] §1: each query attends to the tokens up to its own position; §2.2:
+ * the multi-token prediction modules may be kept for decoding).  The q_len
+ * new tokens of sequence b are the last q_len of its seq_lens[b] cached tokens:
+ * new token t sits at position seq_lens[b] - q_len + t and attends to cache
+ * tokens [0, seq_lens[b] - q_len + t + 1) (none if that is empty: o_lat = 0,
+ * lse = -inf).
+ *   q_lat: [batch, q_len, n_h, d_c], q_pe: [batch, q_len, n_h, d_rope] (q_dt);
+ *   o_lat: [batch, q_len, n_h, d_c] (o_dt), lse: [batch, q_len, n_h] or NULL.
+ * One call runs the whole attention, merge included: each (sequence, new
+ * token) pair is a virtual sequence of mla_decode's batch * q_len, with the
+ * partition `part` applied to the virtual batch; the virtual lengths and block
+ * table live in the workspace.  Same cache and dtype rules as mla_decode.
+ *   workspace: mla_decode_multi_workspace_size(...) bytes, 16-B aligned (never 0).
+ */
+mla_status_t mla_decode_multi_workspace_size(const mla_dims_t* dims, int32_t batch, int32_t q_len,
+                                             int32_t max_pages_per_seq, int32_t page_size,
+                                             const mla_partition_t* part, size_t* bytes,
+                                             int32_t* num_slots);
+mla_status_t mla_decode_multi(const mla_dims_t* dims, int32_t batch, int32_t q_len,
+                              const void* q_lat, const void* q_pe, mla_dtype_t q_dt,
+                              const mla_paged_cache_t* cache, float softmax_scale,
+                              const mla_partition_t* part, void* workspace, size_t workspace_bytes,
+                              void* o_lat, mla_dtype_t o_dt, float* lse, void* stream);
+
+/*
  * o_heads[b, i*d_h + k] = sum_c W^UV[i*d_h + k, c] o_lat[b, i, c]  (W^UV applied
  * after attention, [DeepSeek-V2 explainer §2.2.2]).
  *   o_lat: [batch, n_h, d_c] (o_dt);  w_uv: [n_h * d_h, d_c] (w_dt);

@@ -19,7 +19,8 @@ MLA_F32, MLA_BF16, MLA_FP8_E4M3 = 0, 1, 2
 
 EXPORTS = ("mla_status_string", "mla_build_info", "mla_absorb_q", "mla_decode_workspace_size",
            "mla_lse_part_offset", "mla_decode", "mla_merge_splits", "mla_out_proj", "mla_cache_store",
-           "mla_cache_append", "mla_query_prep_scratch_size", "mla_query_prep", "mla_partition_host")
+           "mla_cache_append", "mla_query_prep_scratch_size", "mla_query_prep", "mla_partition_host",
+           "mla_decode_multi_workspace_size", "mla_decode_multi")
 
 
 class MlaError(RuntimeError):
@@ -76,6 +77,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                           ctypes.c_float, P, P, ctypes.c_int, P, SZ, P]),
         "mla_partition_host": (ctypes.c_int, [ctypes.POINTER(I32), I32, I32, I32, PP, ctypes.POINTER(I32),
                                               ctypes.POINTER(I32)]),
+        "mla_decode_multi_workspace_size": (ctypes.c_int, [PD, I32, I32, I32, I32, PP, ctypes.POINTER(SZ),
+                                                           ctypes.POINTER(I32)]),
+        "mla_decode_multi": (ctypes.c_int, [PD, I32, I32, P, P, ctypes.c_int, PC, ctypes.c_float, PP, P, SZ, P,
+                                            ctypes.c_int, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -180,6 +185,28 @@ def merge_splits(d: Dims, seq_lens, page_size: int, max_pages: int, part: Partit
     _check(load().mla_merge_splits(ctypes.byref(d), seq_lens.shape[0], _ptr(seq_lens), page_size, max_pages,
                                    ctypes.byref(part), _ptr(workspace), ws_bytes, _ptr(o_lat), dtype_code(o_lat),
                                    _ptr(lse), _stream(stream)), "mla_merge_splits")
+    return o_lat
+
+
+def multi_workspace_size(d: Dims, batch: int, q_len: int, max_pages: int, page_size: int,
+                         part: Partition) -> Tuple[int, int]:
+    nbytes = ctypes.c_size_t(0)
+    slots = ctypes.c_int32(0)
+    _check(load().mla_decode_multi_workspace_size(ctypes.byref(d), batch, q_len, max_pages, page_size,
+                                                  ctypes.byref(part), ctypes.byref(nbytes), ctypes.byref(slots)),
+           "mla_decode_multi_workspace_size")
+    return nbytes.value, slots.value
+
+
+def decode_multi(d: Dims, q_lat, q_pe, cache: PagedCache, softmax_scale: float, part: Partition, workspace, o_lat,
+                 lse=None, stream=None):
+    """q_len new tokens per sequence, causal within them: q_lat [B, q_len, n_h, d_c], q_pe [B, q_len, n_h, d_r],
+    o_lat [B, q_len, n_h, d_c], lse [B, q_len, n_h] (merge included)."""
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load().mla_decode_multi(ctypes.byref(d), q_lat.shape[0], q_lat.shape[1], _ptr(q_lat), _ptr(q_pe),
+                                   dtype_code(q_lat), ctypes.byref(cache), ctypes.c_float(softmax_scale),
+                                   ctypes.byref(part), _ptr(workspace), ws_bytes, _ptr(o_lat), dtype_code(o_lat),
+                                   _ptr(lse), _stream(stream)), "mla_decode_multi")
     return o_lat
 
 

@@ -198,10 +198,15 @@ size_t mla_lse_part_offset(const mla_dims_t* dims, int32_t num_slots) {
   return align256(size_t(num_slots) * dims->n_heads * dims->d_latent * sizeof(float));
 }
 
-mla_status_t mla_decode(const mla_dims_t* dims, int32_t batch, const void* q_lat, const void* q_pe,
-                        mla_dtype_t q_dt, const mla_paged_cache_t* cache, float softmax_scale,
-                        const mla_partition_t* part, void* workspace, size_t workspace_bytes, void* o_lat,
-                        mla_dtype_t o_dt, float* lse, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// mla_decode's checks and launch; with dry = true only the checks.
+mla_status_t decode_impl(const mla_dims_t* dims, int32_t batch, const void* q_lat, const void* q_pe,
+                         mla_dtype_t q_dt, const mla_paged_cache_t* cache, float softmax_scale,
+                         const mla_partition_t* part, void* workspace, size_t workspace_bytes, void* o_lat,
+                         mla_dtype_t o_dt, float* lse, void* stream, bool dry) {
   if (mla_status_t s = check_dims(dims)) return s;
   if (!cache || !q_lat || !o_lat || (dims->d_rope > 0 && !q_pe)) return MLA_ERR_INVALID_ARG;
   if (!cache->kv || !cache->block_table || !cache->seq_lens) return MLA_ERR_INVALID_ARG;
@@ -222,15 +227,16 @@ mla_status_t mla_decode(const mla_dims_t* dims, int32_t batch, const void* q_lat
   const WsLayout L = ws_layout(dims, n_slots, batch, pp.mode == PART_BALANCED);
   if (L.total > 0 && (workspace == nullptr || workspace_bytes < L.total)) return MLA_ERR_WORKSPACE;
   if (L.total > 0 && !aligned16(workspace)) return MLA_ERR_ALIGNMENT;
-  if (batch == 0 || n_items == 0) return MLA_OK;
+  const bool fast = is_v2(dims) && cache->page_size == 64 && q_dt == MLA_BF16 &&
+                    (cache->dtype == MLA_BF16 || cache->dtype == MLA_FP8_E4M3);
+  if (!fast && (dims->d_latent > kGenMaxLatent || dims->d_latent + dims->d_rope > kGenMaxRow))
+    return MLA_ERR_UNSUPPORTED;
+  if (dry || batch == 0 || n_items == 0) return MLA_OK;
   char* ws = static_cast<char*>(workspace);
   void* o_part = L.total ? static_cast<void*>(ws + L.o_part) : nullptr;
   float* lse_part = L.total ? reinterpret_cast<float*>(ws + L.lse_part) : nullptr;
   int32_t* meta = (L.total && pp.mode == PART_BALANCED) ? reinterpret_cast<int32_t*>(ws + L.meta) : nullptr;
   hipStream_t st = static_cast<hipStream_t>(stream);
-
-  const bool fast = is_v2(dims) && cache->page_size == 64 && q_dt == MLA_BF16 &&
-                    (cache->dtype == MLA_BF16 || cache->dtype == MLA_FP8_E4M3);
   hipError_t e;
   if (fast) {
     V2DecodeArgs a{};
@@ -253,7 +259,6 @@ mla_status_t mla_decode(const mla_dims_t* dims, int32_t batch, const void* q_lat
     a.lse = lse;
     e = launch_decode_v2(a, st);
   } else {
-    if (dims->d_latent > kGenMaxLatent || dims->d_latent + dims->d_rope > kGenMaxRow) return MLA_ERR_UNSUPPORTED;
     GenericDecodeArgs a{};
     a.q_lat = q_lat;
     a.q_pe = q_pe;
@@ -278,6 +283,43 @@ mla_status_t mla_decode(const mla_dims_t* dims, int32_t batch, const void* q_lat
     e = launch_decode_generic(a, n_items, st);
   }
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+// mla_decode_multi workspace: virtual lengths, virtual block table, then the
+// workspace of the decode over batch * q_len virtual sequences.
+struct MultiLayout {
+  size_t lens, bt, dec, dec_bytes, total;
+};
+
+mla_status_t multi_layout(const mla_dims_t* dims, int32_t batch, int32_t q_len, int32_t max_pages,
+                          int32_t page_size, const mla_partition_t* part, MultiLayout* M, int* n_slots) {
+  if (mla_status_t s = check_dims(dims)) return s;
+  if (batch < 0 || q_len < 1 || max_pages < 1) return MLA_ERR_INVALID_ARG;
+  const int64_t vb = int64_t(batch) * q_len;
+  if (vb > (int64_t(1) << 30) / max_pages) return MLA_ERR_INVALID_ARG;
+  PartParams pp;
+  int n_items = 0;
+  if (mla_status_t s = resolve(dims, int(vb), max_pages, page_size, part, &pp, &n_items, n_slots)) return s;
+  MultiLayout m{};
+  m.lens = 0;
+  m.bt = align256(size_t(vb) * sizeof(int32_t));
+  m.dec = m.bt + align256(size_t(vb) * max_pages * sizeof(int32_t));
+  m.dec_bytes = ws_layout(dims, *n_slots, int(vb), pp.mode == PART_BALANCED).total;
+  m.total = m.dec + m.dec_bytes;
+  *M = m;
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status_t mla_decode(const mla_dims_t* dims, int32_t batch, const void* q_lat, const void* q_pe,
+                        mla_dtype_t q_dt, const mla_paged_cache_t* cache, float softmax_scale,
+                        const mla_partition_t* part, void* workspace, size_t workspace_bytes, void* o_lat,
+                        mla_dtype_t o_dt, float* lse, void* stream) {
+  return decode_impl(dims, batch, q_lat, q_pe, q_dt, cache, softmax_scale, part, workspace, workspace_bytes, o_lat,
+                     o_dt, lse, stream, false);
 }
 
 mla_status_t mla_merge_splits(const mla_dims_t* dims, int32_t batch, const int32_t* seq_lens, int32_t page_size,
@@ -307,6 +349,52 @@ mla_status_t mla_merge_splits(const mla_dims_t* dims, int32_t batch, const int32
   a.lse = lse;
   const hipError_t e = launch_merge(a, batch, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status_t mla_decode_multi_workspace_size(const mla_dims_t* dims, int32_t batch, int32_t q_len,
+                                             int32_t max_pages_per_seq, int32_t page_size,
+                                             const mla_partition_t* part, size_t* bytes, int32_t* num_slots) {
+  if (!bytes) return MLA_ERR_INVALID_ARG;
+  MultiLayout M;
+  int n_slots = 0;
+  if (mla_status_t s = multi_layout(dims, batch, q_len, max_pages_per_seq, page_size, part, &M, &n_slots)) return s;
+  *bytes = M.total;
+  if (num_slots) *num_slots = n_slots;
+  return MLA_OK;
+}
+
+mla_status_t mla_decode_multi(const mla_dims_t* dims, int32_t batch, int32_t q_len, const void* q_lat,
+                              const void* q_pe, mla_dtype_t q_dt, const mla_paged_cache_t* cache,
+                              float softmax_scale, const mla_partition_t* part, void* workspace,
+                              size_t workspace_bytes, void* o_lat, mla_dtype_t o_dt, float* lse, void* stream) {
+  if (!cache) return MLA_ERR_INVALID_ARG;
+  MultiLayout M;
+  int n_slots = 0;
+  if (mla_status_t s = multi_layout(dims, batch, q_len, cache->max_pages_per_seq, cache->page_size, part, &M, &n_slots))
+    return s;
+  if (!cache->block_table || !cache->seq_lens) return MLA_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < M.total) return MLA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return MLA_ERR_ALIGNMENT;
+  if (o_dt != MLA_F32 && o_dt != MLA_BF16) return valid_dtype(o_dt) ? MLA_ERR_UNSUPPORTED : MLA_ERR_INVALID_ARG;
+  char* ws = static_cast<char*>(workspace);
+  const int vb = batch * q_len;
+  mla_paged_cache_t vc = *cache;
+  vc.seq_lens = reinterpret_cast<const int32_t*>(ws + M.lens);
+  vc.block_table = reinterpret_cast<const int32_t*>(ws + M.bt);
+  void* dec_ws = M.dec_bytes ? static_cast<void*>(ws + M.dec) : nullptr;
+  if (mla_status_t s = decode_impl(dims, vb, q_lat, q_pe, q_dt, &vc, softmax_scale, part, dec_ws, M.dec_bytes, o_lat,
+                                   o_dt, lse, stream, true))
+    return s;
+  if (batch == 0) return MLA_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (launch_expand(cache->seq_lens, cache->block_table, batch, q_len, cache->max_pages_per_seq,
+                    reinterpret_cast<int32_t*>(ws + M.lens), reinterpret_cast<int32_t*>(ws + M.bt), st) != hipSuccess)
+    return MLA_ERR_HIP;
+  if (mla_status_t s = decode_impl(dims, vb, q_lat, q_pe, q_dt, &vc, softmax_scale, part, dec_ws, M.dec_bytes, o_lat,
+                                   o_dt, lse, stream, false))
+    return s;
+  return mla_merge_splits(dims, vb, vc.seq_lens, cache->page_size, cache->max_pages_per_seq, part, dec_ws,
+                          M.dec_bytes, o_lat, o_dt, lse, stream);
 }
 
 mla_status_t mla_out_proj(const mla_dims_t* dims, int32_t batch, const void* o_lat, mla_dtype_t o_dt, const void* w_uv,

@@ -138,6 +138,42 @@ def test_validation_errors_before_any_device_access(lib):
               None) == lib.MLA_ERR_INVALID_ARG
 
 
+def test_multi_decode_workspace_and_validation(lib):
+    """mla_decode_multi: the workspace holds the virtual lengths and block table
+    (B * q_len rows) before the decode workspace of the virtual batch; checks fail
+    before any device access."""
+    L = _raw(lib)
+    d = _v2(lib)
+    fake = ctypes.c_void_p(0x10000)
+    B, q, mp = 8, 3, 10
+    nbytes, slots = lib.multi_workspace_size(d, B, q, mp, 64, lib.partition(0, 0))
+    align = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    assert slots == 0 and nbytes == align(B * q * 4) + align(B * q * mp * 4)
+    dec, dslots = lib.workspace_size(d, B * q, mp, 64, lib.partition(0, 40))
+    nbytes, slots = lib.multi_workspace_size(d, B, q, mp, 64, lib.partition(0, 40))
+    assert slots == dslots and nbytes == align(B * q * 4) + align(B * q * mp * 4) + dec
+    sz = ctypes.c_size_t(0)
+    part = lib.partition(0, 0)
+    assert L.mla_decode_multi_workspace_size(ctypes.byref(d), B, 0, mp, 64, ctypes.byref(part), ctypes.byref(sz),
+                                             None) == lib.MLA_ERR_INVALID_ARG
+    cache = lib.PagedCache(0x10000, None, lib.MLA_BF16, 64, 100, 0x20000, mp, 0x30000)
+    need, _ = lib.multi_workspace_size(d, B, q, mp, 64, part)
+    dm = L.mla_decode_multi
+    # q_len 0, too-small workspace, f32 queries on a bf16 cache, fp8 output, null output
+    assert dm(ctypes.byref(d), B, 0, fake, fake, 1, ctypes.byref(cache), 0.07, ctypes.byref(part), fake, need, fake,
+              1, None, None) == lib.MLA_ERR_INVALID_ARG
+    assert dm(ctypes.byref(d), B, q, fake, fake, 1, ctypes.byref(cache), 0.07, ctypes.byref(part), fake, need - 1,
+              fake, 1, None, None) == lib.MLA_ERR_WORKSPACE
+    assert dm(ctypes.byref(d), B, q, fake, fake, lib.MLA_F32, ctypes.byref(cache), 0.07, ctypes.byref(part), fake,
+              need, fake, 1, None, None) == lib.MLA_ERR_UNSUPPORTED
+    assert dm(ctypes.byref(d), B, q, fake, fake, 1, ctypes.byref(cache), 0.07, ctypes.byref(part), fake, need, fake,
+              lib.MLA_FP8_E4M3, None, None) == lib.MLA_ERR_UNSUPPORTED
+    assert dm(ctypes.byref(d), B, q, fake, fake, 1, ctypes.byref(cache), 0.07, ctypes.byref(part), fake, need, None,
+              1, None, None) == lib.MLA_ERR_INVALID_ARG
+    assert dm(ctypes.byref(d), 0, q, fake, fake, 1, ctypes.byref(cache), 0.07, ctypes.byref(part), fake, need, fake,
+              1, None, None) == lib.MLA_OK
+
+
 def _brute_parts(lens, page, W):
     """Pages in sequence order cut into W' = min(W, P) parts of floor(w P / W') .. -> (first slot, count)."""
     npg = [(t + page - 1) // page for t in lens]
