@@ -49,6 +49,8 @@ WORKLOADS = {
     "v2b1": (2, "v2_bf16_b1_t4096", (0, -1)),
     # the ragged batch with two new query tokens per sequence (causal within them)
     "mtp2": (3, "v2_bf16_ragged_b64_t1024-8192_qlen2", (0, -1)),
+    # the ragged batch at DeepSeek-V2-Lite's 16 heads (same cache row)
+    "lite": (6, "v2lite_bf16_ragged_b64_t1024-8192", (0, -1)),
 }
 Q_LEN = {"mtp2": 2}
 
@@ -61,7 +63,7 @@ def decode_source_hash() -> str:
 # algorithmic bytes / flops (what the method must move / compute)
 # ---------------------------------------------------------------------------
 
-def algorithmic(lens, cache_dtype: str, q_len: int = 1):
+def algorithmic(lens, cache_dtype: str, q_len: int = 1, n_h: int = N_H):
     """Bytes and flops of one decode step and of the decode kernel alone.
 
     Per cached token: the row [c^KV | k^R] (1152 B bf16; 576 B + 5 fp32 scales
@@ -77,14 +79,14 @@ def algorithmic(lens, cache_dtype: str, q_len: int = 1):
     cache = T * row
     meta = pages * 4 + B * 4
     Q = B * q_len                      # query tokens: each reads its inputs, writes its outputs
-    q_in = Q * N_H * (D_H + D_R) * 2
-    weights = 2 * N_H * D_H * D_C * 2
-    out = Q * N_H * D_H * 2
-    flops_tok = 2 * N_H * (D_C + D_R) + 2 * N_H * D_C
+    q_in = Q * n_h * (D_H + D_R) * 2
+    weights = 2 * n_h * D_H * D_C * 2
+    out = Q * n_h * D_H * 2
+    flops_tok = 2 * n_h * (D_C + D_R) + 2 * n_h * D_C
     # new token t of a sequence of T_b tokens attends to T_b - q_len + t + 1 of them
     attended = sum(max(t - q_len + k + 1, 0) for t in lens for k in range(q_len))
-    step_flops = attended * flops_tok + 2 * 2 * Q * N_H * D_H * D_C
-    decode_bytes = cache + meta + Q * N_H * (D_C + D_R) * 2 + Q * N_H * (D_C * 2 + 4)
+    step_flops = attended * flops_tok + 2 * 2 * Q * n_h * D_H * D_C
+    decode_bytes = cache + meta + Q * n_h * (D_C + D_R) * 2 + Q * n_h * (D_C * 2 + 4)
     return {
         "step_bytes": cache + meta + q_in + weights + out,
         "step_flops": step_flops,
@@ -173,7 +175,7 @@ def cpu_baseline(config_id: int, budget_s: float = 15.0):
         if elapsed >= budget_s:
             break
     return {"value": tokens / elapsed, "unit": "KV-tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"oracle.attend (float64, non-absorbed, all {N_H} heads) on the first {nseq} sequences "
+            "sample": f"oracle.attend (float64, non-absorbed, all {w.dims.n_heads} heads) on the first {nseq} sequences "
                       f"({tokens} cached tokens) of the same workload; {elapsed:.1f} s"}
 
 
@@ -191,7 +193,8 @@ def run(args):
     w, lens, sets = make_inputs(cid, args.copies, q_len=q_len)
     maxp = sets[0]["cache"].max_pages
     B = len(lens)
-    step = mk.DecodeStep(N_H, D_H, D_R, D_C, B * q_len, maxp, 64, split, parts)
+    n_h = w.dims.n_heads
+    step = mk.DecodeStep(n_h, D_H, D_R, D_C, B * q_len, maxp, 64, split, parts)
     scale = 1.0 / math.sqrt(D_H + D_R)
     stream = torch.cuda.current_stream()
     if q_len > 1:
@@ -246,7 +249,7 @@ def run(args):
     if args.kernel_events:
         names = ["absorb", "decode", "merge", "out_proj"]
         per_kernel = {n: sum(e[k].elapsed_time(e[k + 1]) for e in evs) / args.steps for k, n in enumerate(names)}
-    alg = algorithmic(lens, w.cache_dtype, q_len)
+    alg = algorithmic(lens, w.cache_dtype, q_len, n_h)
     T = sum(lens)
     value = T * args.steps / (total_ms * 1e-3)
     metric, unit = METRIC, "KV-tokens/s"
@@ -259,7 +262,7 @@ def run(args):
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wname, "batch": len(lens), "sum_cache_tokens": T, "cache_dtype": w.cache_dtype,
-                   "heads": N_H, "d_latent": D_C, "d_rope": D_R, "page_size": 64,
+                   "heads": n_h, "d_latent": D_C, "d_rope": D_R, "page_size": 64,
                    "partition": {"split_tokens": split, "num_parts": parts}, "input_copies": args.copies,
                    "parallelism": "single GPU", "q_len": q_len},
     }
@@ -287,6 +290,7 @@ def run(args):
         res["roofline"] = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": ach / HBM_PEAK_GBS, "traffic": traffic,
                            "kernel": ("decode_v2_kernel<true> (fp8 cache)" if cid == 5 else
+                                      "decode_lite_kernel (16 heads, bf16 cache)" if n_h == 16 else
                                       "decode_v2_kernel<false> (bf16 cache)") +
                                      (" + expand_kernel + merge_kernel (mla_decode_multi)" if q_len > 1 else ""),
                            "algorithmic_bytes_per_launch": alg["decode_bytes"],

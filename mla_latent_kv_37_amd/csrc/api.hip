@@ -153,7 +153,8 @@ const char* mla_status_string(mla_status_t s) {
 }
 
 const char* mla_build_info(void) {
-  return "libmla gfx950: absorb(v2 mfma, generic), decode(v2 bf16 / fp8-dequant mfma ping-pong, generic f32/bf16/fp8), "
+  return "libmla gfx950: absorb(v2 mfma, generic), decode(v2 bf16 / fp8-dequant mfma ping-pong, 16-head bf16 mfma, "
+         "generic f32/bf16/fp8), "
          "cache store (f32/bf16/fp8 1x128), cache append and query prep (weight-streaming mfma / generic "
          "products), "
          "merge, out_proj(v2 mfma, generic)";
@@ -170,8 +171,8 @@ mla_status_t mla_absorb_q(const mla_dims_t* dims, int32_t batch, const void* q_n
   if (batch == 0) return MLA_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
-  if (is_v2(dims) && dims->d_head == 128 && q_dt == MLA_BF16 && w_dt == MLA_BF16 && out_dt == MLA_BF16) {
-    e = launch_absorb_v2(q_nope, w_uk, q_lat, batch, st);
+  if (dims->d_head == 128 && dims->d_latent == 512 && q_dt == MLA_BF16 && w_dt == MLA_BF16 && out_dt == MLA_BF16) {
+    e = launch_absorb_v2(q_nope, w_uk, q_lat, batch, dims->n_heads, st);
   } else {
     if (dims->d_head > kGenMaxHead) return MLA_ERR_UNSUPPORTED;
     e = launch_absorb_generic(q_nope, q_dt, w_uk, w_dt, q_lat, out_dt, batch, dims->n_heads, dims->d_head,
@@ -229,7 +230,9 @@ mla_status_t decode_impl(const mla_dims_t* dims, int32_t batch, const void* q_la
   if (L.total > 0 && !aligned16(workspace)) return MLA_ERR_ALIGNMENT;
   const bool fast = is_v2(dims) && cache->page_size == 64 && q_dt == MLA_BF16 &&
                     (cache->dtype == MLA_BF16 || cache->dtype == MLA_FP8_E4M3);
-  if (!fast && (dims->d_latent > kGenMaxLatent || dims->d_latent + dims->d_rope > kGenMaxRow))
+  const bool lite = dims->n_heads == 16 && dims->d_latent == 512 && dims->d_rope == 64 && cache->page_size == 64 &&
+                    q_dt == MLA_BF16 && cache->dtype == MLA_BF16;
+  if (!fast && !lite && (dims->d_latent > kGenMaxLatent || dims->d_latent + dims->d_rope > kGenMaxRow))
     return MLA_ERR_UNSUPPORTED;
   if (dry || batch == 0 || n_items == 0) return MLA_OK;
   char* ws = static_cast<char*>(workspace);
@@ -238,7 +241,7 @@ mla_status_t decode_impl(const mla_dims_t* dims, int32_t batch, const void* q_la
   int32_t* meta = (L.total && pp.mode == PART_BALANCED) ? reinterpret_cast<int32_t*>(ws + L.meta) : nullptr;
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
-  if (fast) {
+  if (fast || lite) {
     V2DecodeArgs a{};
     a.q_lat = static_cast<const uint16_t*>(q_lat);
     a.q_pe = static_cast<const uint16_t*>(q_pe);
@@ -257,7 +260,7 @@ mla_status_t decode_impl(const mla_dims_t* dims, int32_t batch, const void* q_la
     a.o_lat = o_lat;
     a.o_dt = o_dt;
     a.lse = lse;
-    e = launch_decode_v2(a, st);
+    e = fast ? launch_decode_v2(a, st) : launch_decode_lite(a, st);
   } else {
     GenericDecodeArgs a{};
     a.q_lat = q_lat;
@@ -407,8 +410,8 @@ mla_status_t mla_out_proj(const mla_dims_t* dims, int32_t batch, const void* o_l
   if (batch == 0) return MLA_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
-  if (is_v2(dims) && dims->d_head == 128 && w_dt == MLA_BF16 && out_dt == MLA_BF16) {
-    e = launch_outproj_v2(o_lat, o_dt == MLA_F32, w_uv, o_heads, batch, st);
+  if (dims->d_head == 128 && dims->d_latent == 512 && w_dt == MLA_BF16 && out_dt == MLA_BF16) {
+    e = launch_outproj_v2(o_lat, o_dt == MLA_F32, w_uv, o_heads, batch, dims->n_heads, st);
   } else {
     if (dims->d_latent > kGenMaxLatent) return MLA_ERR_UNSUPPORTED;
     e = launch_outproj_generic(o_lat, o_dt, w_uv, w_dt, o_heads, out_dt, batch, dims->n_heads, dims->d_head,

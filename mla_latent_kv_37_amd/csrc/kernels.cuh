@@ -89,6 +89,8 @@ struct GemmArgs {
 };
 
 hipError_t launch_decode_v2(const V2DecodeArgs& a, hipStream_t st);
+// 16 heads, d_c = 512, d_rope = 64, page 64, bf16 cache and queries (same arguments)
+hipError_t launch_decode_lite(const V2DecodeArgs& a, hipStream_t st);
 hipError_t launch_cache_store(const CacheStoreArgs& a, int batch, hipStream_t st);
 struct QueryFinishArgs {
   const float* slices;     // [n_slices, batch, n_h * (d_h + d_rope)] fp32
@@ -116,7 +118,8 @@ hipError_t launch_absorb_generic(const void* q, mla_dtype_t q_dt, const void* w,
 hipError_t launch_outproj_generic(const void* o, mla_dtype_t o_dt, const void* w, mla_dtype_t w_dt, void* out,
                                   mla_dtype_t out_dt, int batch, int n_heads, int d_head, int d_latent,
                                   hipStream_t st);
-hipError_t launch_absorb_v2(const void* q, const void* w, void* out, int batch, hipStream_t st);
-hipError_t launch_outproj_v2(const void* o_lat, bool o_f32, const void* w, void* out, int batch, hipStream_t st);
+hipError_t launch_absorb_v2(const void* q, const void* w, void* out, int batch, int n_heads, hipStream_t st);
+hipError_t launch_outproj_v2(const void* o_lat, bool o_f32, const void* w, void* out, int batch, int n_heads,
+                             hipStream_t st);
 
 }  // namespace mla

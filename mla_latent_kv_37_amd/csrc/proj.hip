@@ -64,9 +64,9 @@ hipError_t launch_outproj_generic(const void* o, mla_dtype_t o_dt, const void* w
 }
 
 // ---------------------------------------------------------------------------
-// V2 shapes (d_h = 128, d_c = 512), bf16, v_mfma_f32_32x32x16_bf16
+// d_h = 128, d_c = 512 (V2 and V2-Lite), any head count, bf16, v_mfma_f32_32x32x16_bf16
 // ---------------------------------------------------------------------------
-constexpr int kPH = 128, kPL = 512;
+constexpr int kPH = 128, kPL = 512;   // d_h, d_c
 
 // absorb, computed transposed: q_lat^T [cols x batch] = W^T [cols x k] . q^T [k x batch].
 // Workgroup (head i, 128-column block, 32-row batch tile): the W^UK block
@@ -79,7 +79,7 @@ constexpr int kWPitch = 144;  // bf16 elements per staged weight row
 constexpr int kQPitch = 136;  // bf16 elements per staged query row
 
 __global__ __launch_bounds__(256) void absorb_v2_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ w,
-                                                        uint16_t* __restrict__ out, int batch) {
+                                                        uint16_t* __restrict__ out, int batch, int n_heads) {
   __shared__ __attribute__((aligned(16))) uint16_t ws[kPH * kWPitch];
   __shared__ __attribute__((aligned(16))) uint16_t qs[32 * kQPitch];
   const int i = blockIdx.x, cb = blockIdx.y * 128, bt = blockIdx.z * 32;
@@ -96,7 +96,7 @@ __global__ __launch_bounds__(256) void absorb_v2_kernel(const uint16_t* __restri
   for (int r = 0; r < 2; ++r) {
     const int e = tid + 256 * r, row = e >> 4, ch = e & 15;
     const int bq = min(bt + row, batch - 1);
-    qv[r] = *reinterpret_cast<const uint4*>(q + (int64_t(bq) * kPH + i) * kPH + ch * 8);
+    qv[r] = *reinterpret_cast<const uint4*>(q + (int64_t(bq) * n_heads + i) * kPH + ch * 8);
   }
 #pragma unroll
   for (int r = 0; r < 8; ++r) {
@@ -128,7 +128,7 @@ __global__ __launch_bounds__(256) void absorb_v2_kernel(const uint16_t* __restri
   // D[col][b]: lane has b = lane%32, cols 8(r/4) + 4h + r%4 of the wave's 32 columns
   const int bq = bt + (lane & 31);
   if (bq < batch) {
-    uint16_t* o = out + (int64_t(bq) * kPH + i) * kPL + cb + wave * 32 + 4 * h;
+    uint16_t* o = out + (int64_t(bq) * n_heads + i) * kPL + cb + wave * 32 + 4 * h;
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       bf16x4 v;
@@ -146,14 +146,14 @@ __global__ __launch_bounds__(256) void absorb_v2_kernel(const uint16_t* __restri
 // ahead; batch rows past the end are clamped to the last row and not stored.
 template <bool OF32>
 __global__ __launch_bounds__(256) void outproj_v2_kernel(const void* __restrict__ o_lat, const uint16_t* __restrict__ w,
-                                                         uint16_t* __restrict__ out, int batch) {
+                                                         uint16_t* __restrict__ out, int batch, int n_heads) {
   const int i = blockIdx.x, bt = blockIdx.y * 32;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5;
   const int krow = wave * 32 + (lane & 31);
   const int bq = bt + (lane & 31);
   const int bl = min(bq, batch - 1);
   const bf16x8* wr = reinterpret_cast<const bf16x8*>(w + (int64_t(i) * kPH + krow) * kPL) + h;
-  const int64_t orow = (int64_t(bl) * kPH + i) * kPL + 8 * h;
+  const int64_t orow = (int64_t(bl) * n_heads + i) * kPL + 8 * h;
   constexpr int kG = 8;  // k-steps per group
   struct Ops { bf16x8 a[kG], b[kG]; };
   auto load = [&](int grp, Ops& o) {
@@ -183,7 +183,7 @@ __global__ __launch_bounds__(256) void outproj_v2_kernel(const void* __restrict_
     cur = nxt;
   }
   if (bq < batch) {
-    uint16_t* o = out + int64_t(bq) * kPH * kPH + int64_t(i) * kPH + wave * 32 + 4 * h;
+    uint16_t* o = out + (int64_t(bq) * n_heads + i) * kPH + wave * 32 + 4 * h;
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       bf16x4 v;
@@ -194,19 +194,22 @@ __global__ __launch_bounds__(256) void outproj_v2_kernel(const void* __restrict_
   }
 }
 
-hipError_t launch_absorb_v2(const void* q, const void* w, void* out, int batch, hipStream_t st) {
-  absorb_v2_kernel<<<dim3(kPH, kPL / 128, ceil_div(batch, 32)), 256, 0, st>>>(static_cast<const uint16_t*>(q),
-                                                          static_cast<const uint16_t*>(w),
-                                                          static_cast<uint16_t*>(out), batch);
+hipError_t launch_absorb_v2(const void* q, const void* w, void* out, int batch, int n_heads, hipStream_t st) {
+  absorb_v2_kernel<<<dim3(n_heads, kPL / 128, ceil_div(batch, 32)), 256, 0, st>>>(static_cast<const uint16_t*>(q),
+                                                              static_cast<const uint16_t*>(w),
+                                                              static_cast<uint16_t*>(out), batch, n_heads);
   return hipGetLastError();
 }
 
-hipError_t launch_outproj_v2(const void* o_lat, bool o_f32, const void* w, void* out, int batch, hipStream_t st) {
-  dim3 grid(kPH, ceil_div(batch, 32));
+hipError_t launch_outproj_v2(const void* o_lat, bool o_f32, const void* w, void* out, int batch, int n_heads,
+                             hipStream_t st) {
+  dim3 grid(n_heads, ceil_div(batch, 32));
   if (o_f32)
-    outproj_v2_kernel<true><<<grid, 256, 0, st>>>(o_lat, static_cast<const uint16_t*>(w), static_cast<uint16_t*>(out), batch);
+    outproj_v2_kernel<true><<<grid, 256, 0, st>>>(o_lat, static_cast<const uint16_t*>(w), static_cast<uint16_t*>(out),
+                                                  batch, n_heads);
   else
-    outproj_v2_kernel<false><<<grid, 256, 0, st>>>(o_lat, static_cast<const uint16_t*>(w), static_cast<uint16_t*>(out), batch);
+    outproj_v2_kernel<false><<<grid, 256, 0, st>>>(o_lat, static_cast<const uint16_t*>(w), static_cast<uint16_t*>(out),
+                                                   batch, n_heads);
   return hipGetLastError();
 }
 

@@ -12,7 +12,8 @@ softmax, no absorption.  Storage conversions are delegated to torch's CPU casts
 Workloads follow the DeepSeek-V2 shapes given in the DeepSeek-V2 explainer
 (一文通透DeepSeek-V2, §3.1.1 model hyper-parameters): 128 heads of width 128,
 latent width 512, query latent 1536, decoupled RoPE width 64, hidden 5120, and
-weights drawn with standard deviation 0.006.
+weights drawn with standard deviation 0.006; one workload uses the V2-Lite
+shapes of the same page (16 heads, hidden 2048, no query compression).
 """
 from __future__ import annotations
 
@@ -53,6 +54,12 @@ class Dims:
 
 TINY = Dims(n_heads=4, d_head=16, d_rope=8, d_latent=32, d_qlatent=48, d_model=128)
 V2 = Dims(n_heads=128, d_head=128, d_rope=64, d_latent=512, d_qlatent=1536, d_model=5120)
+# DeepSeek-V2-Lite (V2 explainer, the V2-Lite paragraph): 16 heads of width 128,
+# latent 512, RoPE width 64, hidden 2048; the query is not compressed (d_c' = 0).
+V2LITE = Dims(n_heads=16, d_head=128, d_rope=64, d_latent=512, d_qlatent=0, d_model=2048)
+# With weights ~ N(0, 0.006) and h ~ N(0, 1) at V2-Lite shapes, c^KV = W^DKV h and
+# the uncompressed q^C = W^Q h both have standard deviation 0.006 * sqrt(2048).
+V2LITE_SD = V2_SIGMA_W * math.sqrt(2048.0)
 
 
 def rng_for(config_id: int, stream: int, seed: Optional[int] = None) -> np.random.Generator:
@@ -258,13 +265,15 @@ WORKLOADS = {
     3: Workload("v2_bf16_ragged_b64_t1024-8192", V2, [], "bf16", 0, False),
     4: Workload("v2_bf16_long_b4_t131072_split4096", V2, [131072] * 4, "bf16", 4096, False),
     5: Workload("v2_fp8_b32_t16384", V2, [16384] * 32, "fp8", 0, False),
+    # the ragged batch of workload 3 at V2-Lite's 16 heads
+    6: Workload("v2lite_bf16_ragged_b64_t1024-8192", V2LITE, [], "bf16", 0, False),
 }
 
 
 def workload(config_id: int, seed: Optional[int] = None) -> Workload:
     w = WORKLOADS[config_id]
-    if config_id == 3:
-        lens = ragged_lengths(64, 1024, 8192, rng_for(3, S_LENS, seed)).tolist()
+    if config_id in (3, 6):
+        lens = ragged_lengths(64, 1024, 8192, rng_for(config_id, S_LENS, seed)).tolist()
         w = dataclasses.replace(w, lens=lens)
     return w
 
@@ -274,13 +283,16 @@ def direct_inputs_for(config_id: int, seed: Optional[int] = None, lens=None,
     """Direct-draw hot-path inputs for the V2 workloads 3, 4, 5 (or a resized copy)."""
     w = workload(config_id, seed)
     lens = w.lens if lens is None else lens
+    sd_q = V2_SD_QUERY
     if config_id == 4:
         sd_lat, frac, mult = 1.0, 0.01, 8.0
+    elif config_id == 6:
+        sd_lat, sd_q, frac, mult = V2LITE_SD, V2LITE_SD, 0.0, 1.0
     else:
         sd_lat, frac, mult = V2_SD_LATENT, 0.0, 1.0
     out = direct_decode_inputs(
         w.dims, lens, rng_for(config_id, S_CACHE, seed), rng_for(config_id, S_QUERY, seed),
-        sd_latent=sd_lat, sd_query=V2_SD_QUERY * query_gain, outlier_frac=frac,
+        sd_latent=sd_lat, sd_query=sd_q * query_gain, outlier_frac=frac,
         outlier_mult=mult, rng_outlier=rng_for(config_id, S_OUTLIER, seed),
         rng_weights=rng_for(config_id, S_WEIGHTS, seed))
     out["workload"] = w
