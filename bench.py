@@ -253,6 +253,8 @@ def run(args):
     T = sum(lens)
     value = T * args.steps / (total_ms * 1e-3)
     metric, unit = METRIC, "KV-tokens/s"
+    if n_h != N_H:
+        metric = f"MLA decode KV-tokens/s + achieved TB/s & % roofline, {n_h} heads (V2-Lite), d_c=512"
     if q_len > 1:
         metric = f"MLA multi-token decode query-tokens/s ({q_len} new tokens per sequence, causal)"
         unit = "query-tokens/s"
