@@ -510,6 +510,53 @@ def run_query(args):
     }
 
 
+def run_append(args):
+    import numpy as np
+    import torch
+    import synth
+    import mla_latent_kv_37_amd as mk
+    kind = APPEND_WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    mk._lib.load()
+    w = synth.workload(3)
+    lens = np.asarray(w.lens, dtype=np.int32)
+    B = len(lens)
+    rng = synth.rng_for(3, synth.S_WEIGHTS)
+    W = synth.weights(synth.V2, 0.006, rng, with_wo=False)
+    bf = lambda x: torch.from_numpy(np.asarray(x, dtype=np.float32)).cuda().to(torch.bfloat16)  # noqa: E731
+    w_dkv, w_kr = bf(W["W_DKV"]), bf(W["W_KR"])
+    h = bf(synth.hidden_states(B, D_MODEL, synth.rng_for(3, synth.S_H)))
+    # one page of its own per sequence for the new token's slot
+    max_pages = int((lens.max() + 64) // 64) + 1
+    bt = np.zeros((B, max_pages), dtype=np.int32)
+    bt[np.arange(B), lens // 64] = np.arange(B)
+    width = D_C + D_R
+    tdt = torch.bfloat16 if kind == "bf16" else torch.uint8
+    kv = torch.zeros((B, 64, width), dtype=tdt, device="cuda")
+    scales = torch.zeros((B, 64, 5), dtype=torch.float32, device="cuda") if kind == "fp8" else None
+    cache = mk.make_cache(kv, torch.from_numpy(bt).cuda(), torch.from_numpy(lens).cuda(), 64, scales)
+    pos = torch.from_numpy(lens).cuda()
+    rows = torch.empty((8, B, width), dtype=torch.float32, device="cuda")
+    d = mk.dims(N_H, D_H, D_R, D_C)
+    times = _cold_weight_steps(lambda: mk.cache_append(d, h, w_dkv, w_kr, rows, pos, cache, 10000.0), args)
+    ms = times[len(times) // 2]
+    elem = 2 if kind == "bf16" else 1
+    alg_bytes = (width * D_MODEL * 2 + B * D_MODEL * 2 + B * width * elem + (B * 5 * 4 if kind == "fp8" else 0)
+                 + B * 4 * 2)
+    ach = alg_bytes / (ms * 1e-3) / 1e9
+    return {
+        "metric": "MLA cache append new tokens/s (project [W^DKV; W^KR] h, RoPE, round, scatter)",
+        "value": B / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"v2_cache_append_b{B}_{kind}", "batch": B, "d_model": D_MODEL, "cache_dtype": kind,
+                   "weights": "cold (512 MB copied between steps)", "timing": "median of per-step HIP events"},
+        "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": ach / HBM_PEAK_GBS, "traffic": None, "kernel": "gemm_ws_mfma_kernel + cache_store_kernel",
+                     "algorithmic_bytes_per_launch": alg_bytes, "mean_launch_ms": sum(times) / len(times)},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)

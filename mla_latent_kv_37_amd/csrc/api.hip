@@ -119,7 +119,7 @@ mla_status_t store_args(const mla_dims_t* dims, int32_t batch, const void* rows,
   return MLA_OK;
 }
 
-// mla_query_prep scratch: stage-1 k slices (at most kGemmMaxSlices: d_model is
+// mla_query_prep scratch: stage-1 k slices (at most kQueryMaxSlices: d_model is
 // not an argument of the size query), c^Q (in the weights' dtype; its area is
 // sized for fp32), stage-2 k slices (as many as the bf16 plan for
 // [n_h (d_h + d_rope)] x d_qlatent uses; every other plan uses one).  One size
@@ -130,9 +130,9 @@ QueryScratch query_scratch(const mla_dims_t* d, int32_t d_qlatent, int32_t batch
   const size_t B = size_t(batch > 0 ? batch : 0);
   const int n2 = d->n_heads * (d->d_head + d->d_rope);
   q.s1 = 0;
-  q.cq = align256(kGemmMaxSlices * B * d_qlatent * sizeof(float));
+  q.cq = align256(kQueryMaxSlices * B * d_qlatent * sizeof(float));
   q.s2 = q.cq + align256(B * d_qlatent * sizeof(float));
-  q.total = q.s2 + align256(size_t(gemm_ws_slices(n2, d_qlatent)) * B * n2 * sizeof(float));
+  q.total = q.s2 + align256(size_t(gemm_ws_slices(n2, d_qlatent, int(B), kQueryMaxSlices)) * B * n2 * sizeof(float));
   return q;
 }
 
@@ -455,7 +455,7 @@ mla_status_t mla_cache_append(const mla_dims_t* dims, int32_t d_model, int32_t b
   g.K = d_model;
   g.N = dims->d_latent + dims->d_rope;
   g.n0 = dims->d_latent;
-  gemm_ws_plan(g);
+  gemm_ws_plan(g, kGemmMaxSlices);
   a.batch = batch;
   a.n_partials = g.slices;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -499,7 +499,7 @@ mla_status_t mla_query_prep(const mla_dims_t* dims, int32_t d_model, int32_t d_q
   g1.K = d_model;
   g1.N = d_qlatent;
   g1.n0 = d_qlatent;
-  gemm_ws_plan(g1);
+  gemm_ws_plan(g1, kQueryMaxSlices);
   hipError_t e = launch_gemm_ws(g1, st);
   if (e == hipSuccess) e = launch_reduce_cast(g1.out, g1.slices, int64_t(batch) * d_qlatent, ws + L.cq, w_dt, st);
   // stage 2: [q^C ; q^R before rotation] = [W^UQ ; W^QR] c^Q, then rotate and write
@@ -514,7 +514,7 @@ mla_status_t mla_query_prep(const mla_dims_t* dims, int32_t d_model, int32_t d_q
   g2.K = d_qlatent;
   g2.N = dims->n_heads * (dims->d_head + dims->d_rope);
   g2.n0 = dims->n_heads * dims->d_head;
-  gemm_ws_plan(g2);
+  gemm_ws_plan(g2, kQueryMaxSlices);
   if (e == hipSuccess) e = launch_gemm_ws(g2, st);
   QueryFinishArgs f{};
   f.slices = g2.out;

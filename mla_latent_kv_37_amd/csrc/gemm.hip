@@ -3,80 +3,106 @@
 // W = rows [0, n0) of w0 stacked on rows [n0, N) of w1 (both row-major, K
 // columns), x [batch, K], out fp32 [slices, batch, N].  With small batches every
 // weight is read once and the product is bound by the weight stream, so the
-// work is cut along n (32-row tiles) and along k (slices) to spread it over the
+// work is cut along n (64-row tiles) and along k (slices) to spread it over the
 // whole chip; the consumer adds the slices in slice order (deterministic).
 //
-// gemm_ws_mfma_kernel (bf16 x and W, N % 32 == 0, K % (16 * 4 * slices) == 0):
-// rows^T [n x b] = W [n x k] . x^T [k x b] on v_mfma_f32_32x32x16_bf16.  A
-// workgroup owns one 32-row tile of n and one k slice; each weight fragment
-// feeds two MFMAs (two 32-row batch tiles, 64 batch rows per pass); its 4
-// wavefronts split the slice again and read their operands straight from global
-// memory (contiguous along k), 10 k-steps of loads in flight before the first
-// MFMA of a group, and add their partial tiles in LDS.
+// gemm_ws_mfma_kernel (bf16 x and W, N % 64 == 0, K % (64 * slices) == 0):
+// out^T [n x b] = W [n x k] . x^T [k x b] on v_mfma_f32_32x32x16_bf16.  A
+// workgroup owns a tile of 64 weight rows by 64 batch rows (one 32 x 32 MFMA
+// tile per wavefront) and one k slice, which it walks in chunks of 64.
+// Operands reach LDS by plain loads in which 8 consecutive lanes read one
+// row's 128-byte chunk (whole cache lines per instruction), kGemmDepth chunks
+// ahead of use in registers; the chunk is written to one of two LDS buffers
+// (row r's 16-byte piece p at r*128 + ((p ^ (r&7) ^ ((r>>3)&1)) * 16), so the
+// MFMA fragment reads, 16 rows of one piece per 16 lanes, hit 64 distinct
+// banks), then one barrier (no memory fence, so the loads in flight stay in
+// flight) publishes it.  Batch rows past the end are clamped to the last row
+// and not stored; batches above 64 take more workgroups along z, which read
+// the weights again (from the caches when they run together).
 #include "kernels.cuh"
 
 namespace mla {
 
-constexpr int kGemmWaves = 4;
-constexpr int kGemmSteps = 10;
+constexpr int kGemmTile = 64;    // weight rows and batch rows per workgroup
+constexpr int kGemmChunk = 64;   // k per chunk
+constexpr int kGemmDepth = 8;    // chunks in flight per thread (registers)
 
-__global__ __launch_bounds__(64 * kGemmWaves) void gemm_ws_mfma_kernel(GemmArgs a) {
-  __shared__ float red[kGemmWaves - 1][2][16][64];
-  const int nt = blockIdx.x * 32, slice = blockIdx.y;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, h = lane >> 5;
-  const int n = nt + (lane & 31);
-  const uint16_t* w = static_cast<const uint16_t*>(n < a.n0 ? a.w0 : a.w1) + int64_t(n < a.n0 ? n : n - a.n0) * a.K;
-  const int kw = a.K / (a.slices * kGemmWaves);   // k per wavefront, a multiple of 16
-  const int k0 = (slice * kGemmWaves + wave) * kw;
-  const int nsteps = kw / 16;
-  float* out = a.out + int64_t(slice) * a.batch * a.N;
-  for (int bc = 0; bc < a.batch; bc += 64) {
-    const uint16_t* x0 = static_cast<const uint16_t*>(a.x) + int64_t(min(bc + (lane & 31), a.batch - 1)) * a.K;
-    const uint16_t* x1 = static_cast<const uint16_t*>(a.x) + int64_t(min(bc + 32 + (lane & 31), a.batch - 1)) * a.K;
-    f32x16 acc0 = {}, acc1 = {};
-    for (int s0 = 0; s0 < nsteps; s0 += kGemmSteps) {
-      bf16x8 wf[kGemmSteps], xa[kGemmSteps], xb[kGemmSteps];
+__global__ __launch_bounds__(256) void gemm_ws_mfma_kernel(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t lw[2][kGemmTile * kGemmChunk];
+  __shared__ __attribute__((aligned(16))) uint16_t lx[2][kGemmTile * kGemmChunk];
+  const int nt0 = blockIdx.x * kGemmTile, slice = blockIdx.y, bb = blockIdx.z * kGemmTile;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5;
+  const int kslice = a.K / a.slices;
+  const int k0 = slice * kslice;
+  const int nch = kslice / kGemmChunk;
+  // loader: rows lr and 32 + lr of the tile, 16-byte piece lp of the chunk
+  const int lr = tid >> 3, lp = tid & 7;
+  auto wrow = [&](int r) {
+    const int n = nt0 + r;
+    return static_cast<const uint16_t*>(n < a.n0 ? a.w0 : a.w1) + int64_t(n < a.n0 ? n : n - a.n0) * a.K;
+  };
+  auto xrow = [&](int r) { return static_cast<const uint16_t*>(a.x) + int64_t(min(bb + r, a.batch - 1)) * a.K; };
+  const uint16_t* wp0 = wrow(lr) + k0 + lp * 8;
+  const uint16_t* wp1 = wrow(32 + lr) + k0 + lp * 8;
+  const uint16_t* xp0 = xrow(lr) + k0 + lp * 8;
+  const uint16_t* xp1 = xrow(32 + lr) + k0 + lp * 8;
+  auto sw = [](int r, int p) { return r * kGemmChunk + ((p ^ (r & 7) ^ ((r >> 3) & 1)) * 8); };
+  const int so0 = sw(lr, lp), so1 = sw(32 + lr, lp);
+  // fragments: wavefront (n tile wave&1, batch tile wave>>1); lane row l&31, piece 2*kstep + h
+  const int fr_w = 32 * (wave & 1) + (lane & 31), fr_x = 32 * (wave >> 1) + (lane & 31);
+
+  bf16x8 rw0[kGemmDepth], rw1[kGemmDepth], rx0[kGemmDepth], rx1[kGemmDepth];
+  auto load = [&](int d, int c) {
+    const int off = min(c, nch - 1) * kGemmChunk;
+    rw0[d] = *reinterpret_cast<const bf16x8*>(wp0 + off);
+    rw1[d] = *reinterpret_cast<const bf16x8*>(wp1 + off);
+    rx0[d] = *reinterpret_cast<const bf16x8*>(xp0 + off);
+    rx1[d] = *reinterpret_cast<const bf16x8*>(xp1 + off);
+  };
+  // prologue loads in the loop's order (chunk by chunk), so that the pending
+  // loads at the loop head are in the same order on entry and on every trip
 #pragma unroll
-      for (int t = 0; t < kGemmSteps; ++t) {
-        const int k = k0 + (s0 + min(t, nsteps - 1 - s0)) * 16 + 8 * h;
-        wf[t] = *reinterpret_cast<const bf16x8*>(w + k);
-        xa[t] = *reinterpret_cast<const bf16x8*>(x0 + k);
-        xb[t] = *reinterpret_cast<const bf16x8*>(x1 + k);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+  for (int d = 0; d < kGemmDepth; ++d) {
+    load(d, d);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  f32x16 acc = {};
+  // Every step of a group stores, reloads and synchronises unconditionally (steps
+  // past the last chunk store and reload copies of it), so the load queue looks
+  // the same on every trip and the compiler can wait for one chunk's loads at a
+  // time instead of draining all of them at the top of the loop.
+  for (int c0 = 0; c0 < nch; c0 += kGemmDepth) {
 #pragma unroll
-      for (int t = 0; t < kGemmSteps; ++t) {
-        if (s0 + t < nsteps) {
-          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[t], xa[t], acc0, 0, 0, 0);
-          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[t], xb[t], acc1, 0, 0, 0);
+    for (int d = 0; d < kGemmDepth; ++d) {
+      const int c = c0 + d;
+      uint16_t MLA_LDS* bw = (uint16_t MLA_LDS*)lw[d & 1];
+      uint16_t MLA_LDS* bx = (uint16_t MLA_LDS*)lx[d & 1];
+      *reinterpret_cast<bf16x8 MLA_LDS*>(bw + so0) = rw0[d];
+      *reinterpret_cast<bf16x8 MLA_LDS*>(bw + so1) = rw1[d];
+      *reinterpret_cast<bf16x8 MLA_LDS*>(bx + so0) = rx0[d];
+      *reinterpret_cast<bf16x8 MLA_LDS*>(bx + so1) = rx1[d];
+      load(d, c + kGemmDepth);
+      __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
+      raw_barrier();
+      if (c < nch) {
+#pragma unroll
+        for (int ks = 0; ks < kGemmChunk / 16; ++ks) {
+          const bf16x8 fw = *reinterpret_cast<const bf16x8 MLA_LDS*>(bw + sw(fr_w, 2 * ks + h));
+          const bf16x8 fx = *reinterpret_cast<const bf16x8 MLA_LDS*>(bx + sw(fr_x, 2 * ks + h));
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw, fx, acc, 0, 0, 0);
         }
       }
     }
-    if (wave > 0) {
+  }
+  // D[n][b]: lane holds b = l&31, n = 8(r/4) + 4h + r%4 of the wavefront's tile
+  const int b = bb + 32 * (wave >> 1) + (lane & 31);
+  if (b < a.batch) {
+    float* o = a.out + (int64_t(slice) * a.batch + b) * a.N + nt0 + 32 * (wave & 1) + 4 * h;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        red[wave - 1][0][r][lane] = acc0[r];
-        red[wave - 1][1][r][lane] = acc1[r];
-      }
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 v = {acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+      *reinterpret_cast<f32x4*>(o + 8 * q) = v;
     }
-    __syncthreads();
-    if (wave == 0) {
-      // D[n][b]: lane holds b = lane % 32, n = 8(r/4) + 4(lane/32) + r%4
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float v0 = acc0[r], v1 = acc1[r];
-#pragma unroll
-        for (int q = 0; q < kGemmWaves - 1; ++q) {
-          v0 += red[q][0][r][lane];
-          v1 += red[q][1][r][lane];
-        }
-        const int nn = nt + 8 * (r >> 2) + 4 * h + (r & 3);
-        const int b0 = bc + (lane & 31), b1 = b0 + 32;
-        if (b0 < a.batch) out[int64_t(b0) * a.N + nn] = v0;
-        if (b1 < a.batch) out[int64_t(b1) * a.N + nn] = v1;
-      }
-    }
-    __syncthreads();
   }
 }
 
@@ -92,23 +118,23 @@ __global__ __launch_bounds__(256) void gemm_ws_generic_kernel(GemmArgs a) {
   a.out[int64_t(b) * a.N + n] = acc;
 }
 
-int gemm_ws_slices(int N, int K) {
-  if (N % 32 != 0 || K % (16 * kGemmWaves) != 0) return 1;
-  // k slices until the tiles x slices cover the chip about four times
-  const int tiles = N / 32;
-  for (int sl : {8, 4, 2})
-    if (K % (16 * kGemmWaves * sl) == 0 && tiles * sl <= 1024) return sl;
+int gemm_ws_slices(int N, int K, int batch, int max_slices) {
+  if (N % kGemmTile != 0 || K % kGemmChunk != 0) return 1;
+  // k slices until tiles x slices fill the chip about twice (two workgroups per CU)
+  const int tiles = (N / kGemmTile) * ceil_div(max(batch, 1), kGemmTile);
+  for (int sl : {16, 8, 4, 2})
+    if (sl <= max_slices && K % (kGemmChunk * sl) == 0 && tiles * sl <= 512) return sl;
   return 1;
 }
 
-void gemm_ws_plan(GemmArgs& a) {
-  a.use_mfma = a.x_dt == MLA_BF16 && a.w_dt == MLA_BF16 && a.N % 32 == 0 && a.K % (16 * kGemmWaves) == 0;
-  a.slices = a.use_mfma ? gemm_ws_slices(a.N, a.K) : 1;
+void gemm_ws_plan(GemmArgs& a, int max_slices) {
+  a.use_mfma = a.x_dt == MLA_BF16 && a.w_dt == MLA_BF16 && a.N % kGemmTile == 0 && a.K % kGemmChunk == 0;
+  a.slices = a.use_mfma ? gemm_ws_slices(a.N, a.K, a.batch, max_slices) : 1;
 }
 
 hipError_t launch_gemm_ws(const GemmArgs& a, hipStream_t st) {
   if (a.use_mfma)
-    gemm_ws_mfma_kernel<<<dim3(a.N / 32, a.slices), 64 * kGemmWaves, 0, st>>>(a);
+    gemm_ws_mfma_kernel<<<dim3(a.N / kGemmTile, a.slices, ceil_div(a.batch, kGemmTile)), 256, 0, st>>>(a);
   else
     gemm_ws_generic_kernel<<<dim3(a.batch, ceil_div(a.N, 256)), 256, 0, st>>>(a);
   return hipGetLastError();

@@ -102,10 +102,11 @@ struct QueryFinishArgs {
   mla_dtype_t out_dt;
 };
 
-constexpr int kGemmMaxSlices = 8;
-// k slices of the MFMA plan for an N x K bf16 product (1 for every other plan)
-int gemm_ws_slices(int N, int K);
-void gemm_ws_plan(GemmArgs& a);          // chooses slices (<= kGemmMaxSlices) and the kernel
+constexpr int kGemmMaxSlices = 8;      // k slices of mla_cache_append's projection (its scratch holds 8)
+constexpr int kQueryMaxSlices = 16;    // k slices of mla_query_prep's products
+// k slices of the MFMA plan for an N x K bf16 product over `batch` rows (1 for every other plan)
+int gemm_ws_slices(int N, int K, int batch, int max_slices);
+void gemm_ws_plan(GemmArgs& a, int max_slices);   // chooses slices (<= max_slices) and the kernel
 hipError_t launch_gemm_ws(const GemmArgs& a, hipStream_t st);
 hipError_t launch_reduce_cast(const float* slices, int n_slices, int64_t count, void* out, mla_dtype_t out_dt,
                               hipStream_t st);
