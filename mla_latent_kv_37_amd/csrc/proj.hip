@@ -69,31 +69,33 @@ hipError_t launch_outproj_generic(const void* o, mla_dtype_t o_dt, const void* w
 constexpr int kPH = 128, kPL = 512;   // d_h, d_c
 
 // absorb, computed transposed: q_lat^T [cols x batch] = W^T [cols x k] . q^T [k x batch].
-// Workgroup (head i, 128-column block, 32-row batch tile): the W^UK block
+// Workgroup (head i, 128-column block, 64-row batch tile): the W^UK block
 // [128 k x 128 cols] (row pitch 288 B, so a 4-row transposing read hits
-// distinct banks) and the query tile [32 rows x 128 k] (row pitch 272 B) are
+// distinct banks) and the query tile [64 rows x 128 k] (row pitch 272 B) are
 // staged in LDS, with every global load issued before the first wait;
-// wavefront w owns columns 32w..32w+31.  Query rows past the batch are clamped
-// to the last row; their results are not stored.
+// wavefront w owns columns 32w..32w+31 and both 32-row halves of the batch
+// tile, so each weight fragment feeds two MFMAs and every weight byte is read
+// once for up to 64 sequences.  Query rows past the batch are clamped to the
+// last row; their results are not stored.
 constexpr int kWPitch = 144;  // bf16 elements per staged weight row
 constexpr int kQPitch = 136;  // bf16 elements per staged query row
 
 __global__ __launch_bounds__(256) void absorb_v2_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ w,
                                                         uint16_t* __restrict__ out, int batch, int n_heads) {
   __shared__ __attribute__((aligned(16))) uint16_t ws[kPH * kWPitch];
-  __shared__ __attribute__((aligned(16))) uint16_t qs[32 * kQPitch];
-  const int i = blockIdx.x, cb = blockIdx.y * 128, bt = blockIdx.z * 32;
+  __shared__ __attribute__((aligned(16))) uint16_t qs[64 * kQPitch];
+  const int i = blockIdx.x, cb = blockIdx.y * 128, bt = blockIdx.z * 64;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5;
   // W^UK[i*128 + k][cb .. cb+127]: 128 rows x 16 chunks of 16 B, 8 per thread;
-  // q[bt + r][i][:]: 32 rows x 16 chunks, 2 per thread
-  uint4 wv[8], qv[2];
+  // q[bt + r][i][:]: 64 rows x 16 chunks, 4 per thread
+  uint4 wv[8], qv[4];
 #pragma unroll
   for (int r = 0; r < 8; ++r) {
     const int e = tid + 256 * r, k = e >> 4, ch = e & 15;
     wv[r] = *reinterpret_cast<const uint4*>(w + (int64_t(i) * kPH + k) * kPL + cb + ch * 8);
   }
 #pragma unroll
-  for (int r = 0; r < 2; ++r) {
+  for (int r = 0; r < 4; ++r) {
     const int e = tid + 256 * r, row = e >> 4, ch = e & 15;
     const int bq = min(bt + row, batch - 1);
     qv[r] = *reinterpret_cast<const uint4*>(q + (int64_t(bq) * n_heads + i) * kPH + ch * 8);
@@ -104,7 +106,7 @@ __global__ __launch_bounds__(256) void absorb_v2_kernel(const uint16_t* __restri
     *reinterpret_cast<uint4*>(ws + k * kWPitch + ch * 8) = wv[r];
   }
 #pragma unroll
-  for (int r = 0; r < 2; ++r) {
+  for (int r = 0; r < 4; ++r) {
     const int e = tid + 256 * r, row = e >> 4, ch = e & 15;
     *reinterpret_cast<uint4*>(qs + row * kQPitch + ch * 8) = qv[r];
   }
@@ -114,7 +116,7 @@ __global__ __launch_bounds__(256) void absorb_v2_kernel(const uint16_t* __restri
   const uint16_t MLA_LDS* wl = (const uint16_t MLA_LDS*)ws;
   const uint16_t MLA_LDS* ql = (const uint16_t MLA_LDS*)qs + (lane & 31) * kQPitch + 8 * h;
   const int col_l = wave * 32 + 16 * (g & 1) + 4 * (j & 3);
-  f32x16 acc = {};
+  f32x16 acc0 = {}, acc1 = {};
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) {
     const int r0 = 16 * kk + 8 * h + (j >> 2);
@@ -122,19 +124,25 @@ __global__ __launch_bounds__(256) void absorb_v2_kernel(const uint16_t* __restri
     s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 MLA_LDS*)(wl + (r0 + 4) * kWPitch + col_l));
     typedef short s16x8 __attribute__((ext_vector_type(8)));
     s16x8 av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    const bf16x8 bv = *reinterpret_cast<const bf16x8 MLA_LDS*>(ql + 16 * kk);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), bv, acc, 0, 0, 0);
+    const bf16x8 b0 = *reinterpret_cast<const bf16x8 MLA_LDS*>(ql + 16 * kk);
+    const bf16x8 b1 = *reinterpret_cast<const bf16x8 MLA_LDS*>(ql + 32 * kQPitch + 16 * kk);
+    acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), b0, acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), b1, acc1, 0, 0, 0);
   }
-  // D[col][b]: lane has b = lane%32, cols 8(r/4) + 4h + r%4 of the wave's 32 columns
-  const int bq = bt + (lane & 31);
-  if (bq < batch) {
-    uint16_t* o = out + (int64_t(bq) * n_heads + i) * kPL + cb + wave * 32 + 4 * h;
+  // D[col][b]: lane has b = lane%32 (+32 for acc1), cols 8(r/4) + 4h + r%4 of the wave's 32 columns
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      bf16x4 v;
+  for (int half = 0; half < 2; ++half) {
+    const int bq = bt + 32 * half + (lane & 31);
+    if (bq < batch) {
+      const f32x16& acc = half ? acc1 : acc0;
+      uint16_t* o = out + (int64_t(bq) * n_heads + i) * kPL + cb + wave * 32 + 4 * h;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = (__bf16)acc[4 * q4 + e];
-      *reinterpret_cast<bf16x4*>(o + 8 * q4) = v;
+      for (int q4 = 0; q4 < 4; ++q4) {
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (__bf16)acc[4 * q4 + e];
+        *reinterpret_cast<bf16x4*>(o + 8 * q4) = v;
+      }
     }
   }
 }
@@ -195,7 +203,7 @@ __global__ __launch_bounds__(256) void outproj_v2_kernel(const void* __restrict_
 }
 
 hipError_t launch_absorb_v2(const void* q, const void* w, void* out, int batch, int n_heads, hipStream_t st) {
-  absorb_v2_kernel<<<dim3(n_heads, kPL / 128, ceil_div(batch, 32)), 256, 0, st>>>(static_cast<const uint16_t*>(q),
+  absorb_v2_kernel<<<dim3(n_heads, kPL / 128, ceil_div(batch, 64)), 256, 0, st>>>(static_cast<const uint16_t*>(q),
                                                               static_cast<const uint16_t*>(w),
                                                               static_cast<uint16_t*>(out), batch, n_heads);
   return hipGetLastError();
