@@ -27,7 +27,6 @@ __global__ __launch_bounds__(kGenThreads) void decode_generic_kernel(GenericDeco
   __shared__ float ps[kGenThreads];
   __shared__ int64_t rows[kGenThreads];
   __shared__ float red[kGenThreads / 64];
-  __shared__ int scratch[kGenThreads + 4];
 
   const int tid = threadIdx.x;
   const int head = blockIdx.y;
@@ -49,7 +48,7 @@ __global__ __launch_bounds__(kGenThreads) void decode_generic_kernel(GenericDeco
   };
 
   SegmentIter it;
-  it.init(a.pp, a.seq_lens, blockIdx.x, scratch, a.meta);
+  it.init(a.pp, a.seq_lens, blockIdx.x, a.meta);
   Segment sg;
   while (it.next(sg)) {
     const int b = sg.b;

@@ -134,7 +134,7 @@ __global__ __launch_bounds__(kLThreads) void decode_lite_kernel(V2DecodeArgs a) 
   const uint32_t vb = uint32_t(lite_offset(4 * g + (hd >> 2), (hd >> 1) & 1) + (hd & 1) * 8);
 
   SegmentIter it;
-  it.init(a.pp, a.seq_lens, item, reinterpret_cast<int*>(area_raw), a.meta);
+  it.init(a.pp, a.seq_lens, item, a.meta);
   Segment sg;
   while (it.next(sg)) {
     const int b = uniform(sg.b);

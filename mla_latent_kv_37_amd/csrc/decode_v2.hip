@@ -289,7 +289,7 @@ void decode_v2_kernel(V2DecodeArgs a) {
   auto opaque_lane = [&]() { int ln = lane; asm volatile("" : "+v"(ln)); return ln; };
 
   SegmentIter it;
-  it.init(a.pp, a.seq_lens, item, reinterpret_cast<int*>(tiles_raw), a.meta);
+  it.init(a.pp, a.seq_lens, item, a.meta);
   Segment sg;
   while (it.next(sg)) {
     const int b = uniform(sg.b);
@@ -320,6 +320,8 @@ void decode_v2_kernel(V2DecodeArgs a) {
     raw_barrier();
     const int page_first = load_const(bt, 0);
     issue(0, page_first);
+    // bf16: tile 1 goes out with tile 0, so both arrive during the query wait
+    if (!kF8 && ntiles > 1) issue(1, page_first);
     // query slices of head `head` (MFMA B operand: lane holds 8 consecutive dims):
     // latent dims 256*dh + 16*kk + 8*h .. +8, RoPE dims 32*dh + 16*j + 8*h .. +8
     bf16x8 qf[16];
@@ -346,7 +348,7 @@ void decode_v2_kernel(V2DecodeArgs a) {
       raw_barrier();
       convert_tile_f8(stage_buf(0), tile_buf(0));
     }
-    if (ntiles > 1) issue(1, page_first);
+    if (kF8 && ntiles > 1) issue(1, page_first);
     // page of the next tile to issue (tile 2); loaded a slot before its use
     int page_next = ntiles > 2 ? load_const(bt, 1) : 0;
 
@@ -533,16 +535,47 @@ void decode_v2_kernel(V2DecodeArgs a) {
     void* const obase = sg.whole ? a.o_lat : a.o_part;
     const int64_t orow = (int64_t(sg.whole ? b : sg.slot) * kV2Heads + head) * kV2Lat + colbase;
     if (a.o_dt == MLA_BF16) {
-      uint16_t* o = static_cast<uint16_t*>(obase) + orow;
+      // Through LDS, so that the global stores are whole 256-byte row pieces:
+      // a lane's direct stores would put 16 bytes into each of 32 rows per
+      // instruction.  Two rounds, one 128-column quarter of each wavefront's
+      // 256 columns per round: head hd's quarter of column half d sits at
+      // d*32768 + hd*256, its 16-byte chunk c at slot c ^ (hd & 15).
+      uint16_t* const orows = static_cast<uint16_t*>(obase) + int64_t(sg.whole ? b : sg.slot) * kV2Heads * kV2Lat;
+      __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
+      raw_barrier();   // every wavefront is done with the tile buffers
+      // per-thread addresses from an opaque thread id, so that they are computed
+      // here and not hoisted out of the segment loop (where they would hold
+      // registers through the tile loop)
+      int tx = int(threadIdx.x);
+      asm volatile("" : "+v"(tx));
+      const int hw = 32 * (tx >> 7) + (tx & 31), hh = (tx >> 5) & 1;   // head and half of this lane
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt)
+      for (int r = 0; r < 2; ++r) {
+        const uint32_t wbase = tiles_lds + uint32_t(dh * 32768 + hw * 256 + 8 * hh);
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          bf16x4 v;
+        for (int m = 0; m < 4; ++m)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[mt][4 * q4 + e] * inv);
-          *reinterpret_cast<bf16x4*>(o + 32 * mt + 8 * q4) = v;
+          for (int q4 = 0; q4 < 4; ++q4) {
+            bf16x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[4 * r + m][4 * q4 + e] * inv);
+            const uint32_t ad = wbase + uint32_t((((4 * m + q4) ^ (hw & 15)) * 16));
+            *reinterpret_cast<bf16x4 MLA_LDS*>((char MLA_LDS*)(uintptr_t)ad) = v;
+          }
+        __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
+        raw_barrier();
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int pc = tx + kDecThreads * j;
+          const int dhp = pc >> 11, hd = (pc >> 4) & 127, c = pc & 15;
+          const bf16x8 v = lds_read_b128(tiles_lds + uint32_t(dhp * 32768 + hd * 256 + ((c ^ (hd & 15)) * 16)));
+          *reinterpret_cast<bf16x8*>(orows + int64_t(hd) * kV2Lat + dhp * 256 + 128 * r + c * 8) = v;
         }
+        if (r == 0) {
+          __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
+          raw_barrier();
+        }
+      }
     } else {
       float* o = static_cast<float*>(obase) + orow;
 #pragma unroll

@@ -16,30 +16,28 @@
 
 namespace mla {
 
-// Inclusive scan of `v` over the block; `scratch` holds blockDim.x ints.  Also
-// returns the block total.  All threads must call it.
-__device__ __forceinline__ int block_inclusive_scan(int v, int* scratch, int* total) {
-  const int tid = threadIdx.x, n = blockDim.x;
-  scratch[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < n; off <<= 1) {
-    int add = tid >= off ? scratch[tid - off] : 0;
-    __syncthreads();
-    scratch[tid] += add;
-    __syncthreads();
+// Sums and scans over one wavefront (64 lanes), without LDS or barriers.
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(v, off, 64);
+    if (lane >= off) v += t;
   }
-  int incl = scratch[tid];
-  *total = scratch[n - 1];
-  __syncthreads();
-  return incl;
+  return v;
 }
 
 // Iterates over the segments of one work item, in order:
-//   SegmentIter it; it.init(pp, seq_lens, item, scratch, meta);
+//   SegmentIter it; it.init(pp, seq_lens, item, meta);
 //   Segment sg; while (it.next(sg)) { ... }
-// `scratch` must hold blockDim.x + 4 ints of LDS and is free again once init()
-// returns.  All threads of the block must call init() and next() together; the
-// results are uniform across the block.
+// Every wavefront computes the (uniform) results on its own with wavefront
+// scans over the sequences, 64 at a time; all threads of the block must call
+// init() and next() together.
 struct SegmentIter {
   PartParams pp;
   const int32_t* seq_lens;
@@ -51,38 +49,38 @@ struct SegmentIter {
   bool done;
 
   __device__ __forceinline__ void init(const PartParams& pp_, const int32_t* __restrict__ seq_lens_, int item_,
-                                       int* scratch, int32_t* meta_) {
+                                       int32_t* meta_) {
     pp = pp_; seq_lens = seq_lens_; meta = meta_; item = item_;
     done = false; b = 0; S = 0; p0 = p1 = 0;
     if (pp.mode != PART_BALANCED) return;
     const int B = pp.batch, page = pp.page_size;
-    const int tid = threadIdx.x, nt = blockDim.x;
-    int local = 0;
-    for (int i = tid; i < B; i += nt) local += ceil_div(max(load_const(seq_lens, i), 0), page);
+    const int lane = threadIdx.x & 63;
+    auto pages_of = [&](int i) { return i < B ? ceil_div(max(seq_lens[i], 0), page) : 0; };
+    // total pages P of the batch
     int P = 0;
-    block_inclusive_scan(local, scratch, &P);
+    for (int base = 0; base < B; base += 64) P += wave_sum(pages_of(base + lane));
+    P = __builtin_amdgcn_readfirstlane(P);
     const int W = min(pp.num_parts, P);
     if (P == 0 || item >= W) { done = true; return; }
     p0 = part_start(item, P, W);
     p1 = part_start(item + 1, P, W);
-    int* found = scratch + nt;  // [b_lo, S_lo]
-    if (tid == 0) { found[0] = -1; found[1] = 0; }
-    __syncthreads();
-    int offset = 0;
-    for (int base = 0; base < B; base += nt) {
-      const int i = base + tid;
-      const int np = i < B ? ceil_div(max(load_const(seq_lens, i), 0), page) : 0;
-      int tot = 0;
-      const int incl = block_inclusive_scan(np, scratch, &tot);
-      const int excl = incl - np;
-      if (i < B && np > 0 && offset + excl <= p0 && p0 < offset + incl) { found[0] = i; found[1] = offset + excl; }
-      offset += tot;
-      __syncthreads();
-      if (found[0] >= 0) break;
+    // the sequence holding page p0 (the first with pages [S_b, S_b + n_b) around it)
+    int fb = -1, fS = 0, offset = 0;
+    for (int base = 0; base < B; base += 64) {
+      const int np = pages_of(base + lane);
+      const int incl = wave_inclusive_scan(np), excl = incl - np;
+      const bool hit = np > 0 && offset + excl <= p0 && p0 < offset + incl;
+      const unsigned long long m = __ballot(hit);
+      if (m != 0ull) {
+        const int l = __ffsll(m) - 1;
+        fb = base + l;
+        fS = offset + __shfl(excl, l, 64);
+        break;
+      }
+      offset += __shfl(incl, 63, 64);
     }
-    b = __builtin_amdgcn_readfirstlane(found[0]);
-    S = __builtin_amdgcn_readfirstlane(found[1]);
-    __syncthreads();
+    b = __builtin_amdgcn_readfirstlane(fb);
+    S = __builtin_amdgcn_readfirstlane(fS);
     if (b < 0) done = true;
   }
 
