@@ -17,7 +17,7 @@ launch stream) and `cpu_baseline` (the float64 oracle on a bounded sample).
 
 Helper modes for the rocprofv3 summaries kept in profiles/:
     python bench.py --summarize-stats DIR OUT.md      (kernel-trace --stats)
-    python bench.py --summarize-pmc FETCH_DIR WRITE_DIR COPY_BYTES OUT.json OUT.md
+    python bench.py --summarize-pmc FETCH_DIR WRITE_DIR COPY_BYTES OUT.json OUT.md [--workload W]
 """
 from __future__ import annotations
 
@@ -38,8 +38,15 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix
 N_H, D_H, D_R, D_C = 128, 128, 64, 512
 ROW_BYTES_BF16 = (D_C + D_R) * 2
-DECODE_SRC = os.path.join(ROOT, "mla_latent_kv_37_amd", "csrc", "decode_v2.hip")
-TRAFFIC_JSON = os.path.join(ROOT, "profiles", "decode_traffic.json")
+CSRC = os.path.join(ROOT, "mla_latent_kv_37_amd", "csrc")
+# the decode kernel of each workload: (source file, name fragment in rocprofv3 output)
+DECODE_KERNEL = {"lite": ("decode_lite.hip", "decode_lite")}
+DEFAULT_DECODE_KERNEL = ("decode_v2.hip", "decode_v2")
+
+
+def traffic_json(workload: str) -> str:
+    """Measured HBM traffic of a workload's decode kernel (written by --summarize-pmc)."""
+    return os.path.join(ROOT, "profiles", f"decode_traffic_{workload}.json")
 
 WORKLOADS = {
     # name: (synth config id, description, partition (split_tokens, num_parts))
@@ -55,8 +62,9 @@ WORKLOADS = {
 Q_LEN = {"mtp2": 2}
 
 
-def decode_source_hash() -> str:
-    return hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()[:16]
+def decode_source_hash(workload: str = "ragged") -> str:
+    src = DECODE_KERNEL.get(workload, DEFAULT_DECODE_KERNEL)[0]
+    return hashlib.sha256(open(os.path.join(CSRC, src), "rb").read()).hexdigest()[:16]
 
 
 # ---------------------------------------------------------------------------
@@ -285,9 +293,9 @@ def run(args):
         dec_s = per_kernel["decode"] * 1e-3
         ach = alg["decode_bytes"] / dec_s / 1e9
         traffic = None
-        if os.path.exists(TRAFFIC_JSON):
-            tj = json.load(open(TRAFFIC_JSON))
-            if tj.get("decode_source_sha") == decode_source_hash() and tj.get("workload") == wname:
+        if os.path.exists(traffic_json(args.workload)):
+            tj = json.load(open(traffic_json(args.workload)))
+            if tj.get("decode_source_sha") == decode_source_hash(args.workload) and tj.get("workload") == wname:
                 traffic = tj.get("decode_bytes_per_launch")
         res["roofline"] = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": ach / HBM_PEAK_GBS, "traffic": traffic,
@@ -350,9 +358,9 @@ def _pmc_per_kernel(d, counter):
     return vals
 
 
-def summarize_pmc(fetch_dir, write_dir, copy_bytes, out_json, out_md, cmd=""):
-    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the decode kernel, scaled by
-    what the same counters read for a plain device copy of known size."""
+def summarize_pmc(fetch_dir, write_dir, copy_bytes, out_json, out_md, cmd="", workload="ragged"):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of a workload's decode kernel,
+    scaled by what the same counters read for a plain device copy of known size."""
     import statistics
     copy_bytes = int(copy_bytes)
     fetch = _pmc_per_kernel(fetch_dir, "FETCH_SIZE")
@@ -366,15 +374,16 @@ def summarize_pmc(fetch_dir, write_dir, copy_bytes, out_json, out_md, cmd=""):
     # the calibration copy is the largest dispatch of the runtime copy kernel
     f_copy = max(fetch[pick(fetch, "copyBuffer")]) * 1024 / copy_bytes
     w_copy = max(write[pick(write, "copyBuffer")]) * 1024 / copy_bytes
-    f_dec = statistics.median(fetch[pick(fetch, "decode_v2")]) * 1024 / f_copy
-    w_dec = statistics.median(write[pick(write, "decode_v2")]) * 1024 / w_copy
+    src, key = DECODE_KERNEL.get(workload, DEFAULT_DECODE_KERNEL)
+    f_dec = statistics.median(fetch[pick(fetch, key)]) * 1024 / f_copy
+    w_dec = statistics.median(write[pick(write, key)]) * 1024 / w_copy
     others = {}
     for k in ("merge_kernel", "absorb_v2", "outproj_v2"):
         kf, kw = pick(fetch, k), pick(write, k)
         if kf and kw:
             others[k] = {"fetch_bytes": statistics.median(fetch[kf]) * 1024 / f_copy,
                          "write_bytes": statistics.median(write[kw]) * 1024 / w_copy}
-    res = {"workload": WORKLOADS["ragged"][1], "decode_source_sha": decode_source_hash(),
+    res = {"workload": WORKLOADS[workload][1], "decode_source_sha": decode_source_hash(workload),
            "copy_bytes": copy_bytes, "fetch_factor": f_copy, "write_factor": w_copy,
            "decode_fetch_bytes": f_dec, "decode_write_bytes": w_dec, "decode_bytes_per_launch": f_dec + w_dec,
            "other_kernels": others, "command": cmd}
@@ -384,7 +393,7 @@ def summarize_pmc(fetch_dir, write_dir, copy_bytes, out_json, out_md, cmd=""):
              f"- calibration: the runtime's device copy of {copy_bytes} B; FETCH_SIZE reads "
              f"{f_copy:.4f} KiB per KiB copied and WRITE_SIZE {w_copy:.4f}; all figures below are divided by "
              "these factors",
-             f"- decode kernel (decode_v2_kernel<false>, bf16 cache; source sha256[:16] {res['decode_source_sha']}): "
+             f"- decode kernel ({pick(fetch, key)}, {src}; source sha256[:16] {res['decode_source_sha']}): "
              f"fetched {f_dec / 1e6:.2f} MB, written {w_dec / 1e6:.2f} MB, total {(f_dec + w_dec) / 1e6:.2f} MB "
              "per launch"]
     for k, v in others.items():
@@ -575,7 +584,7 @@ def main():
     if args.summarize_stats:
         return summarize_stats(*args.summarize_stats, cmd=args.cmd)
     if args.summarize_pmc:
-        return summarize_pmc(*args.summarize_pmc, cmd=args.cmd)
+        return summarize_pmc(*args.summarize_pmc, cmd=args.cmd, workload=args.workload)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the MLA decode path here is single-GPU (no sharding, no "
               "collectives); use --gpus 1.", file=sys.stderr)
