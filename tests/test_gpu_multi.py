@@ -158,3 +158,15 @@ def test_multi_q1_equals_single_token_decode(v2_ragged):
     torch.cuda.synchronize()
     assert np.array_equal(host(o_lat), o_lat_m[:, 0])
     assert np.array_equal(host(lse), lse_m[:, 0])
+
+
+@pytest.mark.parametrize("part", [(0, 0), (0, 6), (128, 0)])
+def test_multi_v2lite_bf16(part):
+    """Two new tokens per sequence at V2-Lite's 16 heads (the 16-head decode
+    kernel under the virtual batch), all heads."""
+    lens = [2, 70, 900, 129]
+    case = direct_case(6, lens, max_pages=16, seed=74)
+    dev = to_device(case)
+    print(f"case: multi-token V2-Lite bf16, lens {lens}, q_len 2, partition {part}", flush=True)
+    q_c, q_r = _queries(case, 2, seed=10, gain=20.0)
+    _compare(case, q_c, q_r, _run_multi(case, dev, q_c, q_r, part), TOL["bf16"])
