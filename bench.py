@@ -420,7 +420,7 @@ def copy_calibration(nbytes: int, reps: int = 3):
 # ---------------------------------------------------------------------------
 
 APPEND_WORKLOADS = {"append_bf16": "bf16", "append_fp8": "fp8"}
-QUERY_WORKLOADS = ("query_prep", "query_lat", "query_lat_fused")
+QUERY_WORKLOADS = ("query_prep", "query_lat", "query_lat_fused", "query_lite")
 D_MODEL = 5120
 D_QLATENT = 1536
 
@@ -459,6 +459,8 @@ def run_query(args):
     variant = args.workload
     torch.cuda.set_device(0)
     mk._lib.load()
+    if variant == "query_lite":
+        return run_query_lite(args)
     w = synth.workload(3)
     lens = np.asarray(w.lens, dtype=np.int32)
     B = len(lens)
@@ -515,6 +517,47 @@ def run_query(args):
                    "timing": "median of per-step HIP events"},
         "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": ach / HBM_PEAK_GBS, "traffic": None, "kernel": kernels,
+                     "algorithmic_bytes_per_launch": alg_bytes, "mean_launch_ms": sum(times) / len(times)},
+    }
+
+
+def run_query_lite(args):
+    """V2-Lite query side for the 64-sequence batch: no query compression, so one
+    product [W^Q ; W^QR] h (16 heads, d_model 2048; 12.6 MB of bf16 weights read
+    cold each step), then the per-head RoPE."""
+    import numpy as np
+    import torch
+    import synth
+    import mla_latent_kv_37_amd as mk
+    dims = synth.V2LITE
+    nh, dh, dr, dm = dims.n_heads, dims.d_head, dims.d_rope, dims.d_model
+    w = synth.workload(6)
+    lens = np.asarray(w.lens, dtype=np.int32)
+    B = len(lens)
+    rng = synth.rng_for(6, synth.S_WEIGHTS)
+    bf = lambda x: torch.from_numpy(np.asarray(x, dtype=np.float32)).cuda().to(torch.bfloat16)  # noqa: E731
+    w_q, w_qr = bf(rng.normal(0.0, synth.V2_SIGMA_W, (nh * dh, dm))), bf(rng.normal(0.0, synth.V2_SIGMA_W, (nh * dr, dm)))
+    h = bf(synth.hidden_states(B, dm, synth.rng_for(6, synth.S_H)))
+    pos = torch.from_numpy(lens).cuda()
+    d = mk.dims(nh, dh, dr, dims.d_latent)
+    scratch = torch.empty(mk.query_prep_scratch_size(d, 0, B), dtype=torch.uint8, device="cuda")
+    q_nope = torch.empty((B, nh, dh), dtype=torch.bfloat16, device="cuda")
+    q_pe = torch.empty((B, nh, dr), dtype=torch.bfloat16, device="cuda")
+    times = _cold_weight_steps(lambda: mk.query_prep(d, h, None, w_q, w_qr, pos, q_nope, q_pe, scratch, 10000.0), args)
+    ms = times[len(times) // 2]
+    w_bytes = 2 * nh * (dh + dr) * dm
+    alg_bytes = w_bytes + B * dm * 2 + B * nh * (dh + dr) * 2 + B * 4
+    ach = alg_bytes / (ms * 1e-3) / 1e9
+    return {
+        "metric": "MLA query-side projection, V2-Lite (no query compression), sequences/s (h -> q^C, q^R)",
+        "value": B / (ms * 1e-3), "unit": "sequences/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"v2lite_query_prep_b{B}", "batch": B, "d_model": dm, "heads": nh,
+                   "weight_bytes": w_bytes, "weights": "cold (512 MB copied between steps)",
+                   "timing": "median of per-step HIP events"},
+        "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": ach / HBM_PEAK_GBS, "traffic": None, "kernel": "gemm_ws_mfma_kernel + query_finish_kernel",
                      "algorithmic_bytes_per_launch": alg_bytes, "mean_launch_ms": sum(times) / len(times)},
     }
 

@@ -275,6 +275,10 @@ mla_status_t mla_cache_append(const mla_dims_t* dims, int32_t d_model, int32_t b
  *       the inputs of mla_absorb_q and mla_decode.
  *   scratch: device memory of mla_query_prep_scratch_size(...) bytes, 16-B
  *       aligned (k-slice partial sums and c^Q).
+ * d_qlatent = 0: the query is not compressed (DeepSeek-V2-Lite, [DeepSeek-V2
+ *   explainer] V2-Lite paragraph): q^C = W^UQ h, q^R = RoPE(W^QR h) in one
+ *   product; w_dq is unused (may be NULL), w_uq is [n_h * d_h, d_model] and
+ *   w_qr [n_h * d_rope, d_model].
  * d_h and d_rope must be even.
  */
 size_t mla_query_prep_scratch_size(const mla_dims_t* dims, int32_t d_qlatent, int32_t batch);

@@ -241,8 +241,9 @@ def query_prep(d: Dims, h, w_dq, w_uq, w_qr, positions, q_nope, q_pe, scratch, r
     """c^Q = W^DQ h, q_nope = W^UQ c^Q, q_pe = RoPE(W^QR c^Q) per head; shapes [B, d], [d_q, d],
     [n_h d_h, d_q], [n_h d_r, d_q], positions [B] int32, outputs [B, n_h, d_h], [B, n_h, d_r]."""
     nbytes = scratch.numel() * scratch.element_size()
-    _check(load().mla_query_prep(ctypes.byref(d), h.shape[1], w_dq.shape[0], h.shape[0], _ptr(h), dtype_code(h),
-                                 _ptr(w_dq), _ptr(w_uq), _ptr(w_qr), dtype_code(w_dq), _ptr(positions),
+    d_qlatent = 0 if w_dq is None else w_dq.shape[0]   # 0: query not compressed (w_uq, w_qr act on h)
+    _check(load().mla_query_prep(ctypes.byref(d), h.shape[1], d_qlatent, h.shape[0], _ptr(h), dtype_code(h),
+                                 _ptr(w_dq), _ptr(w_uq), _ptr(w_qr), dtype_code(w_uq), _ptr(positions),
                                  ctypes.c_float(rope_base), _ptr(q_nope), _ptr(q_pe), dtype_code(q_nope),
                                  _ptr(scratch), nbytes, _stream(stream)), "mla_query_prep")
     return q_nope, q_pe

@@ -125,6 +125,8 @@ mla_status_t store_args(const mla_dims_t* dims, int32_t batch, const void* rows,
 // [n_h (d_h + d_rope)] x d_qlatent uses; every other plan uses one).  One size
 // serves every dtype.
 struct QueryScratch { size_t s1, cq, s2, total; };
+// d_qlatent = 0 (no query compression): no stage 1, and the single product's
+// k slices are sized for the largest plan (d_model is not an argument either).
 QueryScratch query_scratch(const mla_dims_t* d, int32_t d_qlatent, int32_t batch) {
   QueryScratch q{};
   const size_t B = size_t(batch > 0 ? batch : 0);
@@ -132,7 +134,8 @@ QueryScratch query_scratch(const mla_dims_t* d, int32_t d_qlatent, int32_t batch
   q.s1 = 0;
   q.cq = align256(kQueryMaxSlices * B * d_qlatent * sizeof(float));
   q.s2 = q.cq + align256(B * d_qlatent * sizeof(float));
-  q.total = q.s2 + align256(size_t(gemm_ws_slices(n2, d_qlatent, int(B), kQueryMaxSlices)) * B * n2 * sizeof(float));
+  const size_t slices2 = d_qlatent > 0 ? size_t(gemm_ws_slices(n2, d_qlatent, int(B), kQueryMaxSlices)) : kQueryMaxSlices;
+  q.total = q.s2 + align256(slices2 * B * n2 * sizeof(float));
   return q;
 }
 
@@ -465,7 +468,7 @@ mla_status_t mla_cache_append(const mla_dims_t* dims, int32_t d_model, int32_t b
 }
 
 size_t mla_query_prep_scratch_size(const mla_dims_t* dims, int32_t d_qlatent, int32_t batch) {
-  if (check_dims(dims) != MLA_OK || d_qlatent < 1 || batch < 0) return 0;
+  if (check_dims(dims) != MLA_OK || d_qlatent < 0 || batch < 0) return 0;
   return query_scratch(dims, d_qlatent, batch).total;
 }
 
@@ -474,19 +477,23 @@ mla_status_t mla_query_prep(const mla_dims_t* dims, int32_t d_model, int32_t d_q
                             mla_dtype_t w_dt, const int32_t* positions, float rope_base, void* q_nope, void* q_pe,
                             mla_dtype_t out_dt, void* scratch, size_t scratch_bytes, void* stream) {
   if (mla_status_t s = check_dims(dims)) return s;
-  if (batch < 0 || d_model < 1 || d_qlatent < 1 || !(rope_base >= 0.f)) return MLA_ERR_INVALID_ARG;
+  if (batch < 0 || d_model < 1 || d_qlatent < 0 || !(rope_base >= 0.f)) return MLA_ERR_INVALID_ARG;
+  const bool compressed = d_qlatent > 0;
   for (mla_dtype_t t : {h_dt, w_dt, out_dt})
     if (t != MLA_F32 && t != MLA_BF16) return valid_dtype(t) ? MLA_ERR_UNSUPPORTED : MLA_ERR_INVALID_ARG;
   if ((dims->d_head & 1) || (dims->d_rope & 1)) return MLA_ERR_UNSUPPORTED;
   const QueryScratch L = query_scratch(dims, d_qlatent, batch);
   if (batch == 0) return MLA_OK;
-  if (!h || !w_dq || !w_uq || !q_nope || (dims->d_rope > 0 && (!w_qr || !q_pe || !positions)))
+  if (!h || (compressed && !w_dq) || !w_uq || !q_nope || (dims->d_rope > 0 && (!w_qr || !q_pe || !positions)))
     return MLA_ERR_INVALID_ARG;
   if (!scratch || scratch_bytes < L.total) return MLA_ERR_WORKSPACE;
-  if (!aligned16(h) || !aligned16(w_dq) || !aligned16(w_uq) || (w_qr && !aligned16(w_qr)) || !aligned16(scratch))
+  if (!aligned16(h) || (compressed && !aligned16(w_dq)) || !aligned16(w_uq) || (w_qr && !aligned16(w_qr)) ||
+      !aligned16(scratch))
     return MLA_ERR_ALIGNMENT;
   char* ws = static_cast<char*>(scratch);
   hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (compressed) {
   // stage 1: c^Q = W^DQ h
   GemmArgs g1{};
   g1.x = h;
@@ -500,18 +507,20 @@ mla_status_t mla_query_prep(const mla_dims_t* dims, int32_t d_model, int32_t d_q
   g1.N = d_qlatent;
   g1.n0 = d_qlatent;
   gemm_ws_plan(g1, kQueryMaxSlices);
-  hipError_t e = launch_gemm_ws(g1, st);
+  e = launch_gemm_ws(g1, st);
   if (e == hipSuccess) e = launch_reduce_cast(g1.out, g1.slices, int64_t(batch) * d_qlatent, ws + L.cq, w_dt, st);
-  // stage 2: [q^C ; q^R before rotation] = [W^UQ ; W^QR] c^Q, then rotate and write
+  }
+  // stage 2: [q^C ; q^R before rotation] = [W^UQ ; W^QR] c^Q (or h when the
+  // query is not compressed), then rotate and write
   GemmArgs g2{};
-  g2.x = ws + L.cq;
-  g2.x_dt = w_dt;
+  g2.x = compressed ? static_cast<const void*>(ws + L.cq) : h;
+  g2.x_dt = compressed ? w_dt : h_dt;
   g2.w0 = w_uq;
   g2.w1 = w_qr;
   g2.w_dt = w_dt;
   g2.out = reinterpret_cast<float*>(ws + L.s2);
   g2.batch = batch;
-  g2.K = d_qlatent;
+  g2.K = compressed ? d_qlatent : d_model;
   g2.N = dims->n_heads * (dims->d_head + dims->d_rope);
   g2.n0 = dims->n_heads * dims->d_head;
   gemm_ws_plan(g2, kQueryMaxSlices);

@@ -136,6 +136,13 @@ def test_validation_errors_before_any_device_access(lib):
               fake, need, None) == lib.MLA_ERR_UNSUPPORTED
     assert qp(ctypes.byref(d), 5120, 1536, 4, fake, 1, None, fake, fake, 1, fake, 1e4, fake, fake, 1, fake, need,
               None) == lib.MLA_ERR_INVALID_ARG
+    # d_qlatent = 0 (query not compressed): no W^DQ needed, single product sized for the largest k-slice plan
+    need0 = L.mla_query_prep_scratch_size(ctypes.byref(d), 0, 4)
+    assert need0 >= 16 * 4 * 128 * 192 * 4
+    assert qp(ctypes.byref(d), 2048, 0, 4, fake, 1, None, fake, fake, 1, fake, 1e4, fake, fake, 1, fake, need0 - 1,
+              None) == lib.MLA_ERR_WORKSPACE
+    assert qp(ctypes.byref(d), 2048, -1, 4, fake, 1, None, fake, fake, 1, fake, 1e4, fake, fake, 1, fake, need0,
+              None) == lib.MLA_ERR_INVALID_ARG
 
 
 def test_multi_decode_workspace_and_validation(lib):

@@ -198,18 +198,19 @@ def test_cache_store_rope(kind):
         _check_rope_part(kind, got[b], ref, dc)
 
 
-@pytest.mark.parametrize("kind", ["bf16", "fp8"])
-def test_cache_append_v2(kind):
+@pytest.mark.parametrize("model,kind", [("V2", "bf16"), ("V2", "fp8"), ("V2LITE", "bf16")])
+def test_cache_append_v2(model, kind):
+    """Projection from h (d_model 5120 for V2, 2048 for V2-Lite), RoPE, rounding and scatter."""
     import torch
     import synth
     import mla_latent_kv_37_amd as mk
-    dims = synth.V2
+    dims = getattr(synth, model)
     d = mk.dims(dims.n_heads, dims.d_head, dims.d_rope, dims.d_latent)
     dc, width = dims.d_latent, dims.d_latent + dims.d_rope
     rng = np.random.default_rng(31)
     batch, max_pages = 64, 16
     num_pages = batch + 4
-    print(f"case: cache append V2 (d_model {dims.d_model}) -> {kind}, B={batch}", flush=True)
+    print(f"case: cache append {model} (d_model {dims.d_model}) -> {kind}, B={batch}", flush=True)
     W = synth.weights(dims, 0.006, rng, with_wo=False)
     to_bf16 = lambda x: ostore.bf16_bits_to_f64(ostore.f32_to_bf16_bits(x.astype(np.float32)))  # noqa: E731
     h, w_dkv, w_kr = to_bf16(rng.normal(size=(batch, dims.d_model))), to_bf16(W["W_DKV"]), to_bf16(W["W_KR"])

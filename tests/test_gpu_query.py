@@ -163,3 +163,45 @@ def test_query_prep_fused_absorb_v2(batch):
     er1, er2 = _rel(q_pe.float().cpu().numpy(), ref_r), _rel(q_pe2.float().cpu().numpy(), ref_r)
     print(f"q_lat rel err: absorb {e1:.3e}, fused {e2:.3e}; q^R {er1:.3e} / {er2:.3e}", flush=True)
     assert max(e1, e2, er1, er2) <= TOL["bf16"]
+
+
+def _run_uncompressed(dims, batch, kind, seed, sigma):
+    """V2-Lite form (no query compression): q^C = W^UQ h, q^R = RoPE(W^QR h), with
+    W^UQ [n_h d_h, d_model], W^QR [n_h d_r, d_model].  The oracle's project_query
+    with W^DQ = I computes exactly that."""
+    import torch
+    import mla_latent_kv_37_amd as mk
+    rng = np.random.default_rng(seed)
+    nh, dh, dr, dm = dims.n_heads, dims.d_head, dims.d_rope, dims.d_model
+    W = {"W_DQ": np.eye(dm), "W_UQ": _round(rng.normal(0.0, sigma, (nh * dh, dm)), kind),
+         "W_QR": _round(rng.normal(0.0, sigma, (nh * dr, dm)), kind)}
+    h = _round(rng.normal(size=(batch, dm)), kind)
+    pos = rng.integers(0, 32768, batch).astype(np.int32)
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16}[kind]
+    dev = lambda x: torch.from_numpy(x.astype(np.float32)).cuda().to(tdt).contiguous()  # noqa: E731
+    d = mk.dims(nh, dh, dr, dims.d_latent)
+    scratch = torch.empty(mk.query_prep_scratch_size(d, 0, batch), dtype=torch.uint8, device="cuda")
+    q_nope = torch.empty((batch, nh, dh), dtype=tdt, device="cuda")
+    q_pe = torch.empty((batch, nh, dr), dtype=tdt, device="cuda")
+    print(f"case: uncompressed query prep B={batch} d={dm} {kind}", flush=True)
+    mk.query_prep(d, dev(h), None, dev(W["W_UQ"]), dev(W["W_QR"]), torch.from_numpy(pos).cuda(), q_nope, q_pe,
+                  scratch, ROPE_BASE)
+    torch.cuda.synchronize()
+    ref_c = np.stack([oracle.project_query(h[b], W, int(pos[b]), nh)[0] for b in range(batch)])
+    ref_r = np.stack([oracle.project_query(h[b], W, int(pos[b]), nh)[1] for b in range(batch)])
+    return q_nope.float().cpu().numpy(), q_pe.float().cpu().numpy(), ref_c, ref_r
+
+
+@pytest.mark.parametrize("batch", [64, 37])
+def test_query_prep_v2lite_uncompressed(batch):
+    import synth
+    got_c, got_r, ref_c, ref_r = _run_uncompressed(synth.V2LITE, batch, "bf16", 300 + batch, synth.V2_SIGMA_W)
+    ec, er = _rel(got_c, ref_c), _rel(got_r, ref_r)
+    print(f"q^C rel err {ec:.3e}  q^R rel err {er:.3e}", flush=True)
+    assert ec <= TOL["bf16"] and er <= TOL["bf16"]
+
+
+def test_query_prep_tiny_uncompressed_f32():
+    import synth
+    got_c, got_r, ref_c, ref_r = _run_uncompressed(synth.TINY, 7, "f32", 11, 0.05)
+    assert _rel(got_c, ref_c) <= TOL["f32"] and _rel(got_r, ref_r) <= TOL["f32"]
