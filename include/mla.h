@@ -105,11 +105,15 @@ typedef struct {
  *       multiple of page_size.  Chunk s of sequence b uses workspace slot
  *       b * S + s, S = ceil(max_pages_per_seq * page_size / split_tokens).
  *   split_tokens == 0, num_parts == 0: one work item per sequence, no workspace.
- *   split_tokens == 0, num_parts > 0: the pages of all sequences, taken in
- *       sequence order, are divided into min(num_parts, total pages) contiguous,
- *       equal (+-1 page) parts; part w's share of sequence b uses workspace slot
- *       w + b.  num_parts < 0 means "chosen by the library to fill the
- *       current device once": its compute-unit count.
+ *   split_tokens == 0, num_parts > 0: a cost stream made of the pages of all
+ *       non-empty sequences in sequence order, with 2 extra units between
+ *       consecutive sequences (the fixed cost of a further sequence in one work
+ *       item: its query loads and output write), C units in all, is divided
+ *       into W = min(num_parts, total pages) contiguous parts; part w takes the
+ *       pages among units [floor(w*C/W), floor((w+1)*C/W)).  A single
+ *       sequence is thus cut into equal (+-1 page) parts.  Part w's share of
+ *       sequence b uses workspace slot w + b.  num_parts < 0 means "chosen by
+ *       the library to fill the current device once": its compute-unit count.
  * A sequence covered by a single work item receives its final o_lat / lse
  * directly from mla_decode; the others (and empty sequences) receive them from
  * mla_merge_splits.

@@ -550,14 +550,16 @@ mla_status_t mla_partition_host(const int32_t* seq_lens_host, int32_t batch, int
   PartParams pp;
   int n_items = 0, n_slots = 0;
   if (mla_status_t s = resolve(&d, batch, max_pages_per_seq, page_size, part, &pp, &n_items, &n_slots)) return s;
-  int64_t P = 0;
+  int64_t P = 0, m = 0;
   for (int b = 0; b < batch; ++b) {
     if (seq_lens_host[b] < 0 || int64_t(seq_lens_host[b]) > int64_t(max_pages_per_seq) * page_size)
       return MLA_ERR_INVALID_ARG;
     P += ceil_div(seq_lens_host[b], page_size);
+    m += seq_lens_host[b] > 0 ? 1 : 0;
   }
   const int64_t W = pp.mode == PART_BALANCED ? (pp.num_parts < P ? pp.num_parts : P) : 0;
-  int64_t S = 0;
+  const int64_t C = cost_units(P, m);
+  int64_t S = 0;   // first cost unit of sequence b (balanced)
   for (int b = 0; b < batch; ++b) {
     const int T = seq_lens_host[b];
     const int np = ceil_div(T, page_size);
@@ -571,11 +573,11 @@ mla_status_t mla_partition_host(const int32_t* seq_lens_host, int32_t batch, int
       part_first[b] = b * pp.fixed_slots;
       part_count[b] = ceil_div(T, pp.split_tokens);
     } else {
-      const int wf = part_of_page(S, P, W), wl = part_of_page(S + np - 1, P, W);
+      const int wf = part_of_unit(S, C, W), wl = part_of_unit(S + np - 1, C, W);
       part_first[b] = wf + b;
       part_count[b] = wl - wf + 1;
     }
-    S += np;
+    if (np > 0) S += np + kSegCost;
   }
   return MLA_OK;
 }

@@ -326,13 +326,18 @@ void decode_v2_kernel(V2DecodeArgs a) {
     // latent dims 256*dh + 16*kk + 8*h .. +8, RoPE dims 32*dh + 16*j + 8*h .. +8
     bf16x8 qf[16];
     {
-      const uint16_t* ql = a.q_lat + (int64_t(b) * kV2Heads + head) * kV2Lat + 256 * dh + 8 * h;
+      // per-lane offsets from an opaque lane id (computed here, not held
+      // through the tile loop)
+      const int lq = opaque_lane();
+      const int hq = pair * 32 + (lq & 31);
+      const uint16_t* ql = a.q_lat + (int64_t(b) * kV2Heads + hq) * kV2Lat + 256 * dh + 8 * (lq >> 5);
 #pragma unroll
       for (int kk = 0; kk < 16; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(ql + 16 * kk);
       // RoPE query of all heads into LDS: thread x copies chunk (x & 7) of head x >> 3
+      const int tq = wave * 64 + lq;
 #pragma unroll
       for (int rep = 0; rep < 2; ++rep) {
-        const int x = rep * kDecThreads + threadIdx.x;
+        const int x = rep * kDecThreads + tq;
         const int hd = x >> 3, c = x & 7;
         const bf16x8 v = *reinterpret_cast<const bf16x8*>(a.q_pe + (int64_t(b) * kV2Heads + hd) * kV2Rope + c * 8);
         *reinterpret_cast<bf16x8 MLA_LDS*>((char MLA_LDS*)(uintptr_t)(qpe_lds + hd * 128 + ((c ^ (hd & 7)) * 16))) = v;
@@ -529,11 +534,15 @@ void decode_v2_kernel(V2DecodeArgs a) {
     const float ltot = lsum + __shfl_xor(lsum, 32);
     const float inv = 1.f / ltot;
     const float lse_nat = (m_run + __log2f(ltot)) * kLn2;
+    // the lane's head from an opaque lane id: output addresses built from
+    // `head` itself are hoisted out of the segment loop, and the register pair
+    // they hold through the tile loop is one more than the loop can spare
+    const int head_e = pair * 32 + (opaque_lane() & 31);
     const int colbase = 256 * dh + 4 * h;
     // final output of a sequence covered by this item alone, else a split
     // partial (normalised within the split); both in the output dtype
     void* const obase = sg.whole ? a.o_lat : a.o_part;
-    const int64_t orow = (int64_t(sg.whole ? b : sg.slot) * kV2Heads + head) * kV2Lat + colbase;
+    const int64_t orow = (int64_t(sg.whole ? b : sg.slot) * kV2Heads + head_e) * kV2Lat + colbase;
     if (a.o_dt == MLA_BF16) {
       // Through LDS, so that the global stores are whole 256-byte row pieces:
       // a lane's direct stores would put 16 bytes into each of 32 rows per
@@ -589,8 +598,8 @@ void decode_v2_kernel(V2DecodeArgs a) {
         }
     }
     if (h == 0 && dh == 0) {
-      if (!sg.whole) a.lse_part[int64_t(sg.slot) * kV2Heads + head] = lse_nat;
-      else if (a.lse != nullptr) a.lse[int64_t(b) * kV2Heads + head] = lse_nat;
+      if (!sg.whole) a.lse_part[int64_t(sg.slot) * kV2Heads + head_e] = lse_nat;
+      else if (a.lse != nullptr) a.lse[int64_t(b) * kV2Heads + head_e] = lse_nat;
     }
   }
 }

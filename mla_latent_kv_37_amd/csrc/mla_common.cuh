@@ -106,14 +106,30 @@ __device__ __forceinline__ void raw_barrier() {
 
 __host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-// First page of part w when `pages` pages are divided into `parts` parts.
-__host__ __device__ __forceinline__ int64_t part_start(int64_t w, int64_t pages, int64_t parts) {
-  return (w * pages) / parts;
+// Balanced partition cost stream.  The pages of the non-empty sequences, in
+// sequence order, with kSegCost extra units after each one: sequence b's pages
+// are units [u_b, u_b + n_b) and u_{b+1} = u_b + n_b + kSegCost.  The stream is
+// C = P + kSegCost * (m - 1) units long (P pages, m non-empty sequences) and
+// is cut into W equal (+-1 unit) parts.  The extra units stand for the fixed
+// cost a work item pays for every further sequence it touches (that
+// sequence's query loads and its output write), which per-phase timers put at
+// about two pages of streaming for the 128-head kernel; without them the items
+// holding two sequences finished last.  A single sequence is cut exactly as
+// plain pages are.
+constexpr int kSegCost = 2;
+
+__host__ __device__ __forceinline__ int64_t cost_units(int64_t pages, int64_t nonempty) {
+  return nonempty > 0 ? pages + int64_t(kSegCost) * (nonempty - 1) : 0;
 }
 
-// The part holding global page p: the largest w with part_start(w) <= p.
-__host__ __device__ __forceinline__ int part_of_page(int64_t p, int64_t pages, int64_t parts) {
-  int64_t w = ((p + 1) * parts + pages - 1) / pages - 1;
+// First unit of part w when `units` units are divided into `parts` parts.
+__host__ __device__ __forceinline__ int64_t part_start(int64_t w, int64_t units, int64_t parts) {
+  return (w * units) / parts;
+}
+
+// The part holding unit u: the largest w with part_start(w) <= u.
+__host__ __device__ __forceinline__ int part_of_unit(int64_t u, int64_t units, int64_t parts) {
+  int64_t w = ((u + 1) * parts + units - 1) / units - 1;
   if (w < 0) w = 0;
   if (w > parts - 1) w = parts - 1;
   return int(w);

@@ -3,13 +3,17 @@
 // Three partitions (mla_partition_t):
 //   whole:    item b = sequence b.
 //   fixed:    item b*S + s = tokens [s*L, min((s+1)*L, T_b)) of sequence b.
-//   balanced: the pages of all sequences, in sequence order, are cut into
-//             W = min(num_parts, total pages) contiguous parts; item w takes
-//             pages [floor(w*P/W), floor((w+1)*P/W)) and may span sequences.
-//             Item w's share of sequence b uses slot w + b (unique because both
-//             w and b grow along the page stream).  The item holding a
+//   balanced: the cost stream of mla_common.cuh (the pages of all sequences in
+//             sequence order, kSegCost units between consecutive non-empty
+//             sequences; C units) is cut into W = min(num_parts, total pages)
+//             contiguous parts; item w takes units [floor(w*C/W),
+//             floor((w+1)*C/W)), i.e. the pages inside that range, and may span
+//             sequences.  Item w's share of sequence b uses slot w + b (unique
+//             because both w and b grow along the stream).  The item holding a
 //             sequence's first page records w in meta[b]; the one holding its
-//             last page records w in meta[B + b], so the merge knows the slots.
+//             last page records w in meta[B + b], so the merge knows the slots;
+//             every item in between holds at least one page of that sequence
+//             (parts are at least one unit long).
 #pragma once
 
 #include "mla_common.cuh"
@@ -44,8 +48,8 @@ struct SegmentIter {
   int32_t* meta;
   int item;
   int b;          // next sequence to look at
-  int64_t S;      // its first global page (balanced)
-  int64_t p0, p1; // the item's page range (balanced)
+  int64_t S;      // its first unit in the cost stream (balanced)
+  int64_t p0, p1; // the item's unit range (balanced)
   bool done;
 
   __device__ __forceinline__ void init(const PartParams& pp_, const int32_t* __restrict__ seq_lens_, int item_,
@@ -56,19 +60,27 @@ struct SegmentIter {
     const int B = pp.batch, page = pp.page_size;
     const int lane = threadIdx.x & 63;
     auto pages_of = [&](int i) { return i < B ? ceil_div(max(seq_lens[i], 0), page) : 0; };
-    // total pages P of the batch
-    int P = 0;
-    for (int base = 0; base < B; base += 64) P += wave_sum(pages_of(base + lane));
+    // total pages P and non-empty sequences m of the batch
+    int P = 0, m = 0;
+    for (int base = 0; base < B; base += 64) {
+      const int np = pages_of(base + lane);
+      P += wave_sum(np);
+      m += wave_sum(np > 0 ? 1 : 0);
+    }
     P = __builtin_amdgcn_readfirstlane(P);
+    m = __builtin_amdgcn_readfirstlane(m);
     const int W = min(pp.num_parts, P);
     if (P == 0 || item >= W) { done = true; return; }
-    p0 = part_start(item, P, W);
-    p1 = part_start(item + 1, P, W);
-    // the sequence holding page p0 (the first with pages [S_b, S_b + n_b) around it)
+    const int64_t C = cost_units(P, m);
+    p0 = part_start(item, C, W);
+    p1 = part_start(item + 1, C, W);
+    // the sequence whose pages and following extra units [u_b, u_b + n_b +
+    // kSegCost) hold unit p0
     int fb = -1, fS = 0, offset = 0;
     for (int base = 0; base < B; base += 64) {
       const int np = pages_of(base + lane);
-      const int incl = wave_inclusive_scan(np), excl = incl - np;
+      const int cu = np > 0 ? np + kSegCost : 0;
+      const int incl = wave_inclusive_scan(cu), excl = incl - cu;
       const bool hit = np > 0 && offset + excl <= p0 && p0 < offset + incl;
       const unsigned long long m = __ballot(hit);
       if (m != 0ull) {
@@ -110,18 +122,23 @@ struct SegmentIter {
       const int np = ceil_div(T, page);
       const int64_t Sb = S;
       const int bb = b;
-      S += np;
       ++b;
       if (np == 0) continue;
+      S += np + kSegCost;
       const int64_t lo = Sb > p0 ? Sb : p0, hi = Sb + np < p1 ? Sb + np : p1;
+      if (hi <= lo) continue;   // p0 lies in the extra units after this sequence
       sg.b = bb;
       sg.t0 = int(lo - Sb) * page;
       sg.t1 = min(T, int(hi - Sb) * page);
       sg.slot = item + bb;
       sg.whole = (Sb >= p0) && (Sb + np <= p1);
       if (meta != nullptr && threadIdx.x == 0) {
-        if (Sb >= p0) meta[bb] = item;
-        if (Sb + np <= p1) meta[B + bb] = item;
+        // the stored value is moved to a vector register here, not before the
+        // caller's loop (where that register would be held, or spilled, throughout)
+        int w = item;
+        asm volatile("" : "+s"(w));
+        if (Sb >= p0) meta[bb] = w;
+        if (Sb + np <= p1) meta[B + bb] = w;
       }
       return true;
     }

@@ -181,23 +181,31 @@ def test_multi_decode_workspace_and_validation(lib):
               1, None, None) == lib.MLA_OK
 
 
+SEG_COST = 2   # extra cost units between consecutive non-empty sequences
+
+
 def _brute_parts(lens, page, W):
-    """Pages in sequence order cut into W' = min(W, P) parts of floor(w P / W') .. -> (first slot, count)."""
+    """The cost stream unit by unit: the pages of the non-empty sequences in order,
+    SEG_COST units between consecutive ones; C units cut into W' = min(W, P) parts
+    [floor(w C / W'), floor((w + 1) C / W')).  -> (first slot, count) per sequence."""
     npg = [(t + page - 1) // page for t in lens]
     P = sum(npg)
+    m = sum(1 for n in npg if n > 0)
+    C = P + SEG_COST * (m - 1) if m else 0
     Wp = min(W, P)
     owner = []
     for w in range(Wp):
-        owner += [w] * ((w + 1) * P // Wp - w * P // Wp)
-    out, s = [], 0
+        owner += [w] * ((w + 1) * C // Wp - w * C // Wp)
+    assert len(owner) == C
+    out, u = [], 0
     for b, n in enumerate(npg):
         if lens[b] == 0:
             out.append((-1, 0))
-        else:
-            ws = sorted(set(owner[s:s + n]))
-            assert ws == list(range(ws[0], ws[-1] + 1))
-            out.append((ws[0] + b, len(ws)))
-        s += n
+            continue
+        ws = sorted(set(owner[u:u + n]))
+        assert ws == list(range(ws[0], ws[-1] + 1))
+        out.append((ws[0] + b, len(ws)))
+        u += n + SEG_COST
     return out
 
 
@@ -212,6 +220,21 @@ def test_partition_host_balanced_matches_brute_force(lib, seed):
     for W in (1, 3, 16, 256, 5000):
         first, count = lib.partition_host(lens, page, maxp, lib.partition(0, W))
         assert list(zip(first.tolist(), count.tolist())) == _brute_parts(lens.tolist(), page, W)
+
+
+def test_partition_host_balanced_cost_model(lib):
+    """One sequence is cut exactly into equal page ranges; between sequences the
+    extra units move the cut: two 10-page sequences over 2 parts -> 22 units, 11
+    each, so part 0 takes all of sequence 0 (pages 0-9 and one extra unit) and
+    part 1 the second sequence (one extra unit and its 10 pages)."""
+    first, count = lib.partition_host(np.array([640], dtype=np.int32), 64, 10, lib.partition(0, 10))
+    assert (first.tolist(), count.tolist()) == ([0], [10])
+    first, count = lib.partition_host(np.array([640, 640], dtype=np.int32), 64, 10, lib.partition(0, 2))
+    assert (first.tolist(), count.tolist()) == ([0, 2], [1, 1])
+    # 3 parts: the 22 units cut at 7 and 14; sequence 0 (units 0-9) spans parts
+    # 0-1, sequence 1 (units 12-21) parts 1-2
+    first, count = lib.partition_host(np.array([640, 640], dtype=np.int32), 64, 10, lib.partition(0, 3))
+    assert (first.tolist(), count.tolist()) == ([0, 2], [2, 2])
 
 
 def test_partition_host_fixed_and_whole(lib):
