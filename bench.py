@@ -225,29 +225,36 @@ def run(args):
                             multi_ws, o_lat_m, lse_m)
             if ev is not None:
                 ev[2].record(stream)
+            if ev is not None:
+                ev[3].record(stream)
+            step.project(s["W_UV"])
         else:
             mk.decode(step.d, step.q_lat, s["q_pe"], s["cache"].desc, scale, step.part, step.workspace, step.o_lat,
                       step.lse)
             if ev is not None:
                 ev[2].record(stream)
-            mk.merge_splits(step.d, s["cache"].seq_lens, 64, maxp, step.part, step.workspace, step.o_lat, step.lse)
-        if ev is not None:
-            ev[3].record(stream)
-        step.project(s["W_UV"])
+            if args.unfused:
+                mk.merge_splits(step.d, s["cache"].seq_lens, 64, maxp, step.part, step.workspace, step.o_lat, step.lse)
+                step.project(s["W_UV"])
+            else:
+                # split merge + W^UV projection, one launch
+                mk.merge_out_proj(step.d, s["cache"].seq_lens, 64, maxp, step.part, step.workspace, step.o_lat,
+                                  s["W_UV"], step.o_heads, step.lse)
+            if ev is not None:
+                ev[3].record(stream)
         if ev is not None:
             ev[4].record(stream)
 
     for i in range(args.warmup):
         one(i)
     torch.cuda.synchronize()
-    # timed region: exactly K steps; per-kernel events on the launch stream
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    # timed region: exactly K steps, nothing else on the stream between them
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record(stream)
     for i in range(args.steps):
-        one(args.warmup + i, evs[i] if args.kernel_events else None)
+        one(args.warmup + i)
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -255,8 +262,20 @@ def run(args):
     ms_per_step = total_ms / args.steps
     per_kernel = None
     if args.kernel_events:
-        names = ["absorb", "decode", "merge", "out_proj"]
-        per_kernel = {n: sum(e[k].elapsed_time(e[k + 1]) for e in evs) / args.steps for k, n in enumerate(names)}
+        # second timed region, same K steps with an event between every two
+        # kernels on the launch stream: per-kernel times for the roofline.  The
+        # event packets lengthen the step (so this region does not give the
+        # headline), and each kernel's time includes its dispatch gap.
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            one(args.warmup + args.steps + i, evs[i])
+        torch.cuda.synchronize()
+        names = (["absorb", "decode_multi", "out_proj", "-"] if q_len > 1 else
+                 ["absorb", "decode", "merge + out_proj" if args.unfused else "merge_out_proj", "-"])
+        per_kernel = {n: sum(e[k].elapsed_time(e[k + 1]) for e in evs) / args.steps for k, n in enumerate(names)
+                      if n != "-"}
+        per_kernel_step_ms = sum(e[0].elapsed_time(e[4]) for e in evs) / args.steps
     alg = algorithmic(lens, w.cache_dtype, q_len, n_h)
     T = sum(lens)
     value = T * args.steps / (total_ms * 1e-3)
@@ -290,7 +309,9 @@ def run(args):
     res["step_roofline"]["frac_of_min_roof"] = roof_us / (ms_per_step * 1e3)
     if per_kernel:
         res["kernel_ms"] = per_kernel
-        dec_s = per_kernel["decode"] * 1e-3
+        res["kernel_events_step_ms"] = per_kernel_step_ms
+        dec_name = "decode_multi" if q_len > 1 else "decode"
+        dec_s = per_kernel[dec_name] * 1e-3
         ach = alg["decode_bytes"] / dec_s / 1e9
         traffic = None
         if os.path.exists(traffic_json(args.workload)):
@@ -304,7 +325,7 @@ def run(args):
                                       "decode_v2_kernel<false> (bf16 cache)") +
                                      (" + expand_kernel + merge_kernel (mla_decode_multi)" if q_len > 1 else ""),
                            "algorithmic_bytes_per_launch": alg["decode_bytes"],
-                           "mean_launch_ms": per_kernel["decode"],
+                           "mean_launch_ms": per_kernel[dec_name],
                            "mfma_frac": alg["decode_flops"] / dec_s / (MFMA_BF16_PEAK_TFLOPS * 1e12)}
     res["wall_s_timed"] = wall
     if not args.no_cpu_baseline and q_len == 1:
@@ -612,11 +633,15 @@ def run_append(args):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # the GPU's clocks ramp up over the first few hundred steps (~130 us each):
+    # 1000 warmup steps reach the steady state that a serving loop runs at
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--workload", default="ragged", choices=sorted(WORKLOADS) + sorted(APPEND_WORKLOADS) + sorted(QUERY_WORKLOADS))
     ap.add_argument("--copies", type=int, default=2)
     ap.add_argument("--no-kernel-events", dest="kernel_events", action="store_false")
+    ap.add_argument("--unfused", action="store_true",
+                    help="run mla_merge_splits + mla_out_proj instead of mla_merge_out_proj (comparison)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")

@@ -227,6 +227,24 @@ mla_status_t mla_out_proj(const mla_dims_t* dims, int32_t batch,
                           void* o_heads, mla_dtype_t out_dt, void* stream);
 
 /*
+ * mla_merge_splits followed by mla_out_proj, in one launch where it can:
+ * the split partials of each sequence are merged (o_lat and lse written
+ * exactly as mla_merge_splits writes them) and o_heads = W^UV_i o_lat_i is
+ * computed from the merged rows without reading o_lat back.  Arguments are
+ * those of the two calls; o_dt is both the partials' and o_lat's dtype.
+ *   Single launch for d_h = 128, d_c = 512, o_dt = w_dt = out_dt = MLA_BF16
+ *   (any n_h, any partition); otherwise the two calls run in sequence.
+ *   o_heads then equals mla_out_proj's result up to the order of fp32
+ *   additions (the contraction is split into four quarters).
+ */
+mla_status_t mla_merge_out_proj(const mla_dims_t* dims, int32_t batch, const int32_t* seq_lens,
+                                int32_t page_size, int32_t max_pages_per_seq,
+                                const mla_partition_t* part, const void* workspace,
+                                size_t workspace_bytes, void* o_lat, mla_dtype_t o_dt, float* lse,
+                                const void* w_uv, mla_dtype_t w_dt, void* o_heads,
+                                mla_dtype_t out_dt, void* stream);
+
+/*
  * Store one new token row per sequence into the paged cache, the step that
  * precedes decoding it: the cache keeps per token [c^KV | k^R] with k^R after
  * its rotation [DeepSeek-V2 explainer §2.2.2].

@@ -3,7 +3,7 @@
 The product is libmla.so (include/mla.h), built from csrc/ by
 ``python -m mla_latent_kv_37_amd.build``.  This package is a thin binding:
 ``_lib`` marshals torch tensors into the C ABI, ``DecodeStep`` chains the four
-calls of one decode step (absorb -> decode -> merge -> out proj) with buffers
+calls of one decode step (absorb -> decode -> merge + out proj) with buffers
 allocated once; ``cache_store`` / ``cache_append`` write new tokens into the
 cache.  Every arithmetic step runs in the library's HIP kernels.
 """
@@ -11,8 +11,8 @@ from __future__ import annotations
 
 from . import _lib
 from ._lib import (MLA_BF16, MLA_F32, MLA_FP8_E4M3, MlaError, absorb_q, build_info, cache_append,  # noqa: F401
-                   cache_store, decode, decode_multi, dims, lse_part_offset, make_cache, merge_splits,
-                   multi_workspace_size, out_proj, partition, partition_host, query_prep, query_prep_scratch_size,
+                   cache_store, decode, decode_multi, dims, lse_part_offset, make_cache, merge_out_proj,
+                   merge_splits, multi_workspace_size, out_proj, partition, partition_host, query_prep, query_prep_scratch_size,
                    status_string, workspace_size)
 
 __all__ = ["DecodeStep", "DeviceCache", "upload_cache"]
@@ -102,7 +102,12 @@ class DecodeStep:
     def project(self, w_uv, stream=None):
         return out_proj(self.d, self.o_lat, w_uv, self.o_heads, stream)
 
+    def attend_project(self, q_lat, q_pe, w_uv, cache: DeviceCache, scale, stream=None):
+        """decode, then the split merge and W^UV projection in one call (mla_merge_out_proj)."""
+        decode(self.d, q_lat, q_pe, cache.desc, scale, self.part, self.workspace, self.o_lat, self.lse, stream)
+        return merge_out_proj(self.d, cache.seq_lens, cache.page_size, cache.max_pages, self.part, self.workspace,
+                              self.o_lat, w_uv, self.o_heads, self.lse, stream)
+
     def __call__(self, q_nope, q_pe, w_uk, w_uv, cache: DeviceCache, scale, stream=None):
         self.absorb(q_nope, w_uk, stream)
-        self.attend(self.q_lat, q_pe, cache, scale, stream)
-        return self.project(w_uv, stream)
+        return self.attend_project(self.q_lat, q_pe, w_uv, cache, scale, stream)

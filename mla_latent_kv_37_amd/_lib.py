@@ -20,7 +20,7 @@ MLA_F32, MLA_BF16, MLA_FP8_E4M3 = 0, 1, 2
 EXPORTS = ("mla_status_string", "mla_build_info", "mla_absorb_q", "mla_decode_workspace_size",
            "mla_lse_part_offset", "mla_decode", "mla_merge_splits", "mla_out_proj", "mla_cache_store",
            "mla_cache_append", "mla_query_prep_scratch_size", "mla_query_prep", "mla_partition_host",
-           "mla_decode_multi_workspace_size", "mla_decode_multi")
+           "mla_decode_multi_workspace_size", "mla_decode_multi", "mla_merge_out_proj")
 
 
 class MlaError(RuntimeError):
@@ -69,6 +69,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                       P, P]),
         "mla_merge_splits": (ctypes.c_int, [PD, I32, P, I32, I32, PP, P, SZ, P, ctypes.c_int, P, P]),
         "mla_out_proj": (ctypes.c_int, [PD, I32, P, ctypes.c_int, P, ctypes.c_int, P, ctypes.c_int, P]),
+        "mla_merge_out_proj": (ctypes.c_int, [PD, I32, P, I32, I32, PP, P, SZ, P, ctypes.c_int, P, P, ctypes.c_int, P,
+                                              ctypes.c_int, P]),
         "mla_cache_store": (ctypes.c_int, [PD, I32, P, ctypes.c_int, P, ctypes.c_float, PC, P]),
         "mla_cache_append": (ctypes.c_int, [PD, I32, I32, P, ctypes.c_int, P, P, ctypes.c_int, P, P, ctypes.c_float,
                                             PC, P]),
@@ -214,6 +216,17 @@ def out_proj(d: Dims, o_lat, w_uv, o_heads, stream=None):
     """o_heads[b, i*d_h:(i+1)*d_h] = W^UV_i o_lat[b,i,:]; shapes [B,n_h,d_c], [n_h*d_h, d_c], [B, n_h*d_h]."""
     _check(load().mla_out_proj(ctypes.byref(d), o_lat.shape[0], _ptr(o_lat), dtype_code(o_lat), _ptr(w_uv),
                                dtype_code(w_uv), _ptr(o_heads), dtype_code(o_heads), _stream(stream)), "mla_out_proj")
+    return o_heads
+
+
+def merge_out_proj(d: Dims, seq_lens, page_size: int, max_pages: int, part: Partition, workspace, o_lat, w_uv,
+                   o_heads, lse=None, stream=None):
+    """merge_splits(...) then out_proj(o_lat, w_uv, o_heads), one launch on the bf16 fast path."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().mla_merge_out_proj(ctypes.byref(d), seq_lens.shape[0], _ptr(seq_lens), page_size, max_pages,
+                                     ctypes.byref(part), _ptr(workspace), ws_bytes, _ptr(o_lat), dtype_code(o_lat),
+                                     _ptr(lse), _ptr(w_uv), dtype_code(w_uv), _ptr(o_heads), dtype_code(o_heads),
+                                     _stream(stream)), "mla_merge_out_proj")
     return o_heads
 
 

@@ -423,6 +423,49 @@ mla_status_t mla_out_proj(const mla_dims_t* dims, int32_t batch, const void* o_l
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
+mla_status_t mla_merge_out_proj(const mla_dims_t* dims, int32_t batch, const int32_t* seq_lens, int32_t page_size,
+                                int32_t max_pages_per_seq, const mla_partition_t* part, const void* workspace,
+                                size_t workspace_bytes, void* o_lat, mla_dtype_t o_dt, float* lse, const void* w_uv,
+                                mla_dtype_t w_dt, void* o_heads, mla_dtype_t out_dt, void* stream) {
+  // validation of both calls before anything is enqueued
+  if (mla_status_t s = check_dims(dims)) return s;
+  if (batch < 0 || !seq_lens || !o_lat || !w_uv || !o_heads) return MLA_ERR_INVALID_ARG;
+  for (mla_dtype_t t : {o_dt, w_dt, out_dt})
+    if (t != MLA_F32 && t != MLA_BF16) return valid_dtype(t) ? MLA_ERR_UNSUPPORTED : MLA_ERR_INVALID_ARG;
+  if (!aligned16(o_lat) || !aligned16(w_uv) || !aligned16(o_heads)) return MLA_ERR_ALIGNMENT;
+  PartParams pp;
+  int n_items = 0, n_slots = 0;
+  if (mla_status_t s = resolve(dims, batch, max_pages_per_seq, page_size, part, &pp, &n_items, &n_slots)) return s;
+  const WsLayout L = ws_layout(dims, n_slots, batch, pp.mode == PART_BALANCED);
+  if (L.total > 0 && (workspace == nullptr || workspace_bytes < L.total)) return MLA_ERR_WORKSPACE;
+  const bool fused = dims->d_head == 128 && dims->d_latent == 512 && o_dt == MLA_BF16 && w_dt == MLA_BF16 &&
+                     out_dt == MLA_BF16;
+  if (!fused && dims->d_latent > kGenMaxLatent &&
+      !(dims->d_head == 128 && dims->d_latent == 512 && w_dt == MLA_BF16 && out_dt == MLA_BF16))
+    return MLA_ERR_UNSUPPORTED;
+  if (batch == 0) return MLA_OK;
+  if (!fused) {
+    if (mla_status_t s = mla_merge_splits(dims, batch, seq_lens, page_size, max_pages_per_seq, part, workspace,
+                                          workspace_bytes, o_lat, o_dt, lse, stream))
+      return s;
+    return mla_out_proj(dims, batch, o_lat, o_dt, w_uv, w_dt, o_heads, out_dt, stream);
+  }
+  const char* ws = static_cast<const char*>(workspace);
+  MergeArgs a{};
+  a.seq_lens = seq_lens;
+  a.pp = pp;
+  a.n_heads = dims->n_heads;
+  a.d_latent = dims->d_latent;
+  a.o_part = L.total ? static_cast<const void*>(ws + L.o_part) : nullptr;
+  a.lse_part = L.total ? reinterpret_cast<const float*>(ws + L.lse_part) : nullptr;
+  a.meta = (L.total && pp.mode == PART_BALANCED) ? reinterpret_cast<const int32_t*>(ws + L.meta) : nullptr;
+  a.o_lat = o_lat;
+  a.o_dt = o_dt;
+  a.lse = lse;
+  const hipError_t e = launch_merge_proj(a, w_uv, o_heads, batch, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
 mla_status_t mla_cache_store(const mla_dims_t* dims, int32_t batch, const void* rows, mla_dtype_t rows_dt,
                              const int32_t* positions, float rope_base, const mla_paged_cache_t* cache,
                              void* stream) {

@@ -112,6 +112,8 @@ hipError_t launch_reduce_cast(const float* slices, int n_slices, int64_t count, 
                               hipStream_t st);
 hipError_t launch_query_finish(const QueryFinishArgs& a, hipStream_t st);
 hipError_t launch_merge(const MergeArgs& a, int batch, hipStream_t st);
+// merge of split partials + W^UV projection (d_h 128, d_c 512, bf16)
+hipError_t launch_merge_proj(const MergeArgs& a, const void* w_uv, void* o_heads, int batch, hipStream_t st);
 hipError_t launch_expand(const int32_t* seq_lens, const int32_t* block_table, int batch, int q_len, int max_pages,
                          int32_t* lens_out, int32_t* bt_out, hipStream_t st);
 hipError_t launch_absorb_generic(const void* q, mla_dtype_t q_dt, const void* w, mla_dtype_t w_dt, void* out,

@@ -1,0 +1,170 @@
+// Split merge fused with the output projection: for head i and a tile of 32
+// sequences, merge each sequence's split partials into its latent output
+// o_lat[b, i, :] and multiply by W^UV_i in the same workgroup, so the merged
+// rows go from registers to LDS to the matrix cores without a round trip
+// through memory and without a second launch.
+//
+// Merge: the log-sum-exp identity of split-K attention (not printed on the
+// pages): lse = log sum_s exp(lse_s), o = sum_s exp(lse_s - lse) o_s, computed
+// with exactly the operations and order of merge_kernel<8, true>, so o_lat and
+// lse (written for split sequences, as mla_merge_splits does) are the same bits.
+// Projection: o[b, i*d_h + k] = sum_c W^UV[i*d_h + k, c] o_lat[b, i, c]
+// ([DeepSeek-V2 explainer] §2.2.2: W^UV applied after attention), as
+// o^T [k x b] = W^UV_i [k x c] . o_lat^T [c x b] on v_mfma_f32_32x32x16_bf16.
+//
+// Workgroup of 16 wavefronts.  Wavefront w = 4q + kb owns output rows
+// k = 32kb..32kb+31 and the contraction quarter c = 128q..128q+127, whose W^UV
+// fragments (8 KB) it loads first, so they arrive while the merge runs.
+// Phase 1: wavefront w merges tile rows 2w and 2w+1 (lane = 8 columns) into an
+// LDS copy of the 32 rows (bf16, 16-byte chunk j of row r at slot j ^ (r & 15):
+// conflict-free for both the row writes and the MFMA operand reads).
+// Phase 2: 8 MFMAs per wavefront; quarters 1-3 pass their fp32 partial products
+// through LDS and quarter 0 adds them in order and stores bf16.
+#include "kernels.cuh"
+
+namespace mla {
+
+constexpr int kMPH = 128, kMPL = 512;   // d_h, d_c
+constexpr int kMPRows = 32;             // sequences per workgroup
+constexpr int kMPWaves = 16;
+
+__device__ __forceinline__ uint32_t mp_row_off(int r, int chunk) {
+  return uint32_t(r * 1024 + ((chunk ^ (r & 15)) * 16));
+}
+
+// Merged (or single-split) row b of head `head`, 8 columns per lane; writes
+// o_lat / lse for sequences that were split or are empty, like merge_kernel.
+__device__ __forceinline__ bf16x8 mp_merge_row(const MergeArgs& a, int b, int head, int lane) {
+  const int T = load_const(a.seq_lens, b);
+  const int64_t out_row = int64_t(b) * a.n_heads + head;
+  uint16_t* const orow = static_cast<uint16_t*>(a.o_lat) + out_row * kMPL + lane * 8;
+  bf16x8 o = {};
+  if (T <= 0) {
+    *reinterpret_cast<bf16x8*>(orow) = o;
+    if (lane == 0 && a.lse != nullptr) a.lse[out_row] = -INFINITY;
+    return o;
+  }
+  int first = 0, count = 1;
+  if (a.pp.mode == PART_FIXED) {
+    count = ceil_div(T, a.pp.split_tokens);
+    first = b * a.pp.fixed_slots;
+  } else if (a.pp.mode == PART_BALANCED) {
+    const int wf = load_const(a.meta, b), wl = load_const(a.meta, int64_t(a.pp.batch) + b);
+    count = wl - wf + 1;
+    first = wf + b;
+  }
+  // one work item covered the sequence: mla_decode wrote the final row
+  if (count <= 1) return *reinterpret_cast<const bf16x8*>(orow);
+  float M = -INFINITY;
+#pragma unroll 8
+  for (int s = 0; s < count; ++s) M = fmaxf(M, a.lse_part[int64_t(first + s) * a.n_heads + head]);
+  float Z = 0.f, acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  const int64_t stride = int64_t(a.n_heads) * kMPL;
+  const uint16_t* const src0 = static_cast<const uint16_t*>(a.o_part) + (int64_t(first) * a.n_heads + head) * kMPL + lane * 8;
+  int s = 0;
+  for (; s + 4 <= count; s += 4) {
+    float l[4];
+    bf16x8 x[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      l[j] = a.lse_part[int64_t(first + s + j) * a.n_heads + head];
+      x[j] = *reinterpret_cast<const bf16x8*>(src0 + (s + j) * stride);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float w = __expf(l[j] - M);
+      Z += w;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += w * float(x[j][e]);
+    }
+  }
+  for (; s < count; ++s) {
+    const float w = __expf(a.lse_part[int64_t(first + s) * a.n_heads + head] - M);
+    const bf16x8 x = *reinterpret_cast<const bf16x8*>(src0 + s * stride);
+    Z += w;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += w * float(x[e]);
+  }
+  const float invZ = 1.f / Z;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = (__bf16)(acc[e] * invZ);
+  *reinterpret_cast<bf16x8*>(orow) = o;
+  if (lane == 0 && a.lse != nullptr) a.lse[out_row] = M + __logf(Z);
+  return o;
+}
+
+__global__ __launch_bounds__(64 * kMPWaves) void merge_proj_kernel(MergeArgs a, const uint16_t* __restrict__ w,
+                                                                   uint16_t* __restrict__ out, int batch) {
+  __shared__ __attribute__((aligned(1024))) char rows[kMPRows * 1024];
+  __shared__ __attribute__((aligned(1024))) float red[12 * 1024];
+  const int i = blockIdx.x, bt = blockIdx.y * kMPRows;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, h = lane >> 5;
+  const int kb = wave & 3, cq = wave >> 2;
+  // W^UV fragments of this wavefront: row 32kb + (lane & 31), columns 128cq + 16kk + 8h
+  bf16x8 wa[8];
+  {
+    const bf16x8* wr = reinterpret_cast<const bf16x8*>(w + (int64_t(i) * kMPH + 32 * kb + (lane & 31)) * kMPL +
+                                                       128 * cq + 8 * h);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) wa[kk] = wr[2 * kk];
+  }
+  const uint32_t rows_lds = uint32_t(reinterpret_cast<uintptr_t>(rows));
+#pragma unroll
+  for (int rr = 0; rr < 2; ++rr) {
+    const int r = 2 * wave + rr, b = bt + r;
+    const bf16x8 o = b < batch ? mp_merge_row(a, b, i, lane) : bf16x8{};
+    *reinterpret_cast<bf16x8 MLA_LDS*>((char MLA_LDS*)(uintptr_t)(rows_lds + mp_row_off(r, lane))) = o;
+  }
+  __syncthreads();
+  // o_lat^T fragment of k-step kk: row lane & 31, columns 128cq + 16kk + 8h (chunk 16cq + 2kk + h)
+  f32x16 acc = {};
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    const bf16x8 bo = *reinterpret_cast<const bf16x8 MLA_LDS*>(
+        (const char MLA_LDS*)(uintptr_t)(rows_lds + mp_row_off(lane & 31, 16 * cq + 2 * kk + h)));
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[kk], bo, acc, 0, 0, 0);
+  }
+  // red: quarter q (1..3) of row block kb at (4(q-1) + kb) * 1024 floats, [q4][lane] f32x4
+  if (cq > 0) {
+    float MLA_LDS* dst = (float MLA_LDS*)red + (4 * (cq - 1) + kb) * 1024 + lane * 4;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4)
+      *reinterpret_cast<f32x4 MLA_LDS*>(dst + q4 * 256) =
+          f32x4{acc[4 * q4], acc[4 * q4 + 1], acc[4 * q4 + 2], acc[4 * q4 + 3]};
+  }
+  __syncthreads();
+  if (cq == 0) {
+#pragma unroll
+    for (int q = 1; q < 4; ++q) {
+      const float MLA_LDS* src = (const float MLA_LDS*)red + (4 * (q - 1) + kb) * 1024 + lane * 4;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 v = *reinterpret_cast<const f32x4 MLA_LDS*>(src + q4 * 256);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[4 * q4 + e] += v[e];
+      }
+    }
+    // D[k][b]: lane holds b = lane & 31, k = 8(e/4) + 4h + e%4 of the row block
+    const int bq = bt + (lane & 31);
+    if (bq < batch) {
+      uint16_t* o = out + (int64_t(bq) * a.n_heads + i) * kMPH + 32 * kb + 4 * h;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (__bf16)acc[4 * q4 + e];
+        *reinterpret_cast<bf16x4*>(o + 8 * q4) = v;
+      }
+    }
+  }
+}
+
+hipError_t launch_merge_proj(const MergeArgs& a, const void* w_uv, void* o_heads, int batch, hipStream_t st) {
+  merge_proj_kernel<<<dim3(a.n_heads, ceil_div(batch, kMPRows)), 64 * kMPWaves, 0, st>>>(
+      a, static_cast<const uint16_t*>(w_uv), static_cast<uint16_t*>(o_heads), batch);
+  return hipGetLastError();
+}
+
+}  // namespace mla
