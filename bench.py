@@ -63,8 +63,13 @@ Q_LEN = {"mtp2": 2}
 
 
 def decode_source_hash(workload: str = "ragged") -> str:
+    """Hash of the decode kernel's source and the headers it includes (a measured
+    traffic record is only reported for the code it was measured on)."""
     src = DECODE_KERNEL.get(workload, DEFAULT_DECODE_KERNEL)[0]
-    return hashlib.sha256(open(os.path.join(CSRC, src), "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in (src, "kernels.cuh", "mla_common.cuh", "partition.cuh"):
+        h.update(open(os.path.join(CSRC, f), "rb").read())
+    return h.hexdigest()[:16]
 
 
 # ---------------------------------------------------------------------------
@@ -225,9 +230,9 @@ def run(args):
                             multi_ws, o_lat_m, lse_m)
             if ev is not None:
                 ev[2].record(stream)
+            step.project(s["W_UV"])
             if ev is not None:
                 ev[3].record(stream)
-            step.project(s["W_UV"])
         else:
             mk.decode(step.d, step.q_lat, s["q_pe"], s["cache"].desc, scale, step.part, step.workspace, step.o_lat,
                       step.lse)
@@ -366,6 +371,27 @@ def summarize_stats(d, out_md, cmd=""):
         lo, hi = mins.get(name, (0, 0))
         lines.append(f"| {_short(name)} | {calls} | {tot:.1f} | {avg:.2f} | {lo / 1e3:.2f} | {hi / 1e3:.2f} | "
                      f"{pct:.1f} |")
+    # steady state: the last half of each kernel's calls (the GPU's clocks ramp up
+    # over the first few hundred steps), and the idle time before each dispatch
+    disp = list(con.execute("select name, start, end, duration from kernels order by start"))
+    per, gaps = {}, {}
+    prev_end = None
+    for name, st, en, dur in disp:
+        per.setdefault(name, []).append(dur)
+        if prev_end is not None:
+            gaps.setdefault(name, []).append(st - prev_end)
+        prev_end = en
+    lines += ["", "Steady state (last half of each kernel's calls; gap = idle time between the previous "
+              "dispatch's end and this one's start):", "",
+              "| kernel | calls used | mean us | median us | median gap before us |", "|---|---|---|---|---|"]
+    for name, _, _, _, _ in rows:
+        d = per.get(name, [])
+        if not d:
+            continue
+        tail = sorted(d[len(d) // 2:])
+        g = sorted(gaps.get(name, [0])[len(gaps.get(name, [0])) // 2:])
+        lines.append(f"| {_short(name)} | {len(tail)} | {sum(tail) / len(tail) / 1e3:.2f} | "
+                     f"{tail[len(tail) // 2] / 1e3:.2f} | {g[len(g) // 2] / 1e3:.2f} |")
     open(out_md, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -399,7 +425,7 @@ def summarize_pmc(fetch_dir, write_dir, copy_bytes, out_json, out_md, cmd="", wo
     f_dec = statistics.median(fetch[pick(fetch, key)]) * 1024 / f_copy
     w_dec = statistics.median(write[pick(write, key)]) * 1024 / w_copy
     others = {}
-    for k in ("merge_kernel", "absorb_v2", "outproj_v2"):
+    for k in ("merge_kernel", "merge_proj", "absorb_v2", "outproj_v2"):
         kf, kw = pick(fetch, k), pick(write, k)
         if kf and kw:
             others[k] = {"fetch_bytes": statistics.median(fetch[kf]) * 1024 / f_copy,

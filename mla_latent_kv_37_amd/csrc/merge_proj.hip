@@ -1,4 +1,4 @@
-// Split merge fused with the output projection: for head i and a tile of 32
+// Split merge fused with the output projection: for head i and a tile of 16
 // sequences, merge each sequence's split partials into its latent output
 // o_lat[b, i, :] and multiply by W^UV_i in the same workgroup, so the merged
 // rows go from registers to LDS to the matrix cores without a round trip
@@ -12,20 +12,24 @@
 // ([DeepSeek-V2 explainer] §2.2.2: W^UV applied after attention), as
 // o^T [k x b] = W^UV_i [k x c] . o_lat^T [c x b] on v_mfma_f32_32x32x16_bf16.
 //
-// Workgroup of 16 wavefronts.  Wavefront w = 4q + kb owns output rows
-// k = 32kb..32kb+31 and the contraction quarter c = 128q..128q+127, whose W^UV
-// fragments (8 KB) it loads first, so they arrive while the merge runs.
-// Phase 1: wavefront w merges tile rows 2w and 2w+1 (lane = 8 columns) into an
-// LDS copy of the 32 rows (bf16, 16-byte chunk j of row r at slot j ^ (r & 15):
-// conflict-free for both the row writes and the MFMA operand reads).
-// Phase 2: 8 MFMAs per wavefront; quarters 1-3 pass their fp32 partial products
-// through LDS and quarter 0 adds them in order and stores bf16.
+// Workgroup of 16 wavefronts for R = 16 or 32 sequences (32 when that still
+// gives at least one workgroup per compute unit: the fewer workgroups read each
+// head's W^UV, the less traffic).  Wavefront w = 4q + kb owns
+// output rows k = 32kb..32kb+31 and the contraction quarter c = 128q..128q+127,
+// whose W^UV fragments (8 KB) it loads first, so they arrive while the merge
+// runs.  Phase 1: wavefront w merges tile rows w, w + 16 (lane = 8 columns): a row's
+// split lse values are loaded lane-parallel together with its first 8 partials
+// (two memory round trips for up to 8 splits), into an LDS copy of the R rows
+// (bf16, 16-byte chunk j of row r at slot j ^ (r & 15): conflict-free for the
+// row writes and the MFMA operand reads).  Phase 2: 8 MFMAs per wavefront (for
+// R = 16 the 32-wide batch operand repeats the 16 rows and only the first 16
+// columns are stored); quarters 1-3 pass their fp32 partial products through
+// LDS and quarter 0 adds them in order and stores bf16.
 #include "kernels.cuh"
 
 namespace mla {
 
 constexpr int kMPH = 128, kMPL = 512;   // d_h, d_c
-constexpr int kMPRows = 32;             // sequences per workgroup
 constexpr int kMPWaves = 16;
 
 __device__ __forceinline__ uint32_t mp_row_off(int r, int chunk) {
@@ -55,37 +59,50 @@ __device__ __forceinline__ bf16x8 mp_merge_row(const MergeArgs& a, int b, int he
   }
   // one work item covered the sequence: mla_decode wrote the final row
   if (count <= 1) return *reinterpret_cast<const bf16x8*>(orow);
-  float M = -INFINITY;
-#pragma unroll 8
-  for (int s = 0; s < count; ++s) M = fmaxf(M, a.lse_part[int64_t(first + s) * a.n_heads + head]);
+  // lse_s of split s sits in lane s (splits beyond 64 are read per split below);
+  // the maximum is exact in any order, so M is merge_kernel's M
+  const float* const lsp = a.lse_part + int64_t(first) * a.n_heads + head;
+  const float lv = lane < count ? lsp[int64_t(lane) * a.n_heads] : -INFINITY;
+  const int64_t stride = int64_t(a.n_heads) * kMPL;
+  const uint16_t* const src0 = static_cast<const uint16_t*>(a.o_part) + (int64_t(first) * a.n_heads + head) * kMPL + lane * 8;
+  // the first 8 partials go out with the lse loads
+  bf16x8 x8[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (j < count) x8[j] = *reinterpret_cast<const bf16x8*>(src0 + j * stride);
+  float M = lv;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+  for (int s = 64; s < count; ++s) M = fmaxf(M, lsp[int64_t(s) * a.n_heads]);
+  auto lse_of = [&](int s) {
+    return s < 64 ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lv), s)) : lsp[int64_t(s) * a.n_heads];
+  };
+  // accumulate in split order with merge_kernel's expressions
   float Z = 0.f, acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-  const int64_t stride = int64_t(a.n_heads) * kMPL;
-  const uint16_t* const src0 = static_cast<const uint16_t*>(a.o_part) + (int64_t(first) * a.n_heads + head) * kMPL + lane * 8;
-  int s = 0;
-  for (; s + 4 <= count; s += 4) {
-    float l[4];
-    bf16x8 x[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      l[j] = a.lse_part[int64_t(first + s + j) * a.n_heads + head];
-      x[j] = *reinterpret_cast<const bf16x8*>(src0 + (s + j) * stride);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float w = __expf(l[j] - M);
+  for (int j = 0; j < 8; ++j) {
+    if (j < count) {
+      const float w = __expf(lse_of(j) - M);
       Z += w;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += w * float(x[j][e]);
+      for (int e = 0; e < 8; ++e) acc[e] += w * float(x8[j][e]);
     }
   }
-  for (; s < count; ++s) {
-    const float w = __expf(a.lse_part[int64_t(first + s) * a.n_heads + head] - M);
-    const bf16x8 x = *reinterpret_cast<const bf16x8*>(src0 + s * stride);
-    Z += w;
+  for (int s0 = 8; s0 < count; s0 += 8) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] += w * float(x[e]);
+    for (int j = 0; j < 8; ++j)
+      if (s0 + j < count) x8[j] = *reinterpret_cast<const bf16x8*>(src0 + (s0 + j) * stride);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (s0 + j < count) {
+        const float w = __expf(lse_of(s0 + j) - M);
+        Z += w;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += w * float(x8[j][e]);
+      }
+    }
   }
   const float invZ = 1.f / Z;
 #pragma unroll
@@ -95,35 +112,40 @@ __device__ __forceinline__ bf16x8 mp_merge_row(const MergeArgs& a, int b, int he
   return o;
 }
 
+template <int R>
 __global__ __launch_bounds__(64 * kMPWaves) void merge_proj_kernel(MergeArgs a, const uint16_t* __restrict__ w,
                                                                    uint16_t* __restrict__ out, int batch) {
-  __shared__ __attribute__((aligned(1024))) char rows[kMPRows * 1024];
+  __shared__ __attribute__((aligned(1024))) char rows[R * 1024];
   __shared__ __attribute__((aligned(1024))) float red[12 * 1024];
-  const int i = blockIdx.x, bt = blockIdx.y * kMPRows;
+  const int i = blockIdx.x, bt = blockIdx.y * R;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, h = lane >> 5;
   const int kb = wave & 3, cq = wave >> 2;
-  // W^UV fragments of this wavefront: row 32kb + (lane & 31), columns 128cq + 16kk + 8h
+  // W^UV fragments of this wavefront: row 32kb + (lane & 31), columns 128cq + 16kk + 8h;
+  // loaded before the merge (R = 16) or after it (R = 32: two rows' merge state
+  // and the fragments do not fit the register budget together)
   bf16x8 wa[8];
-  {
+  auto load_w = [&]() {
     const bf16x8* wr = reinterpret_cast<const bf16x8*>(w + (int64_t(i) * kMPH + 32 * kb + (lane & 31)) * kMPL +
                                                        128 * cq + 8 * h);
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) wa[kk] = wr[2 * kk];
-  }
+  };
+  if (R == 16) load_w();
   const uint32_t rows_lds = uint32_t(reinterpret_cast<uintptr_t>(rows));
 #pragma unroll
-  for (int rr = 0; rr < 2; ++rr) {
-    const int r = 2 * wave + rr, b = bt + r;
+  for (int r = wave; r < R; r += kMPWaves) {
+    const int b = bt + r;
     const bf16x8 o = b < batch ? mp_merge_row(a, b, i, lane) : bf16x8{};
     *reinterpret_cast<bf16x8 MLA_LDS*>((char MLA_LDS*)(uintptr_t)(rows_lds + mp_row_off(r, lane))) = o;
   }
+  if (R == 32) load_w();
   __syncthreads();
-  // o_lat^T fragment of k-step kk: row lane & 31, columns 128cq + 16kk + 8h (chunk 16cq + 2kk + h)
+  // o_lat^T fragment of k-step kk: row lane % R, columns 128cq + 16kk + 8h (chunk 16cq + 2kk + h)
   f32x16 acc = {};
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) {
     const bf16x8 bo = *reinterpret_cast<const bf16x8 MLA_LDS*>(
-        (const char MLA_LDS*)(uintptr_t)(rows_lds + mp_row_off(lane & 31, 16 * cq + 2 * kk + h)));
+        (const char MLA_LDS*)(uintptr_t)(rows_lds + mp_row_off(lane & (R - 1), 16 * cq + 2 * kk + h)));
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[kk], bo, acc, 0, 0, 0);
   }
   // red: quarter q (1..3) of row block kb at (4(q-1) + kb) * 1024 floats, [q4][lane] f32x4
@@ -146,9 +168,10 @@ __global__ __launch_bounds__(64 * kMPWaves) void merge_proj_kernel(MergeArgs a, 
         for (int e = 0; e < 4; ++e) acc[4 * q4 + e] += v[e];
       }
     }
-    // D[k][b]: lane holds b = lane & 31, k = 8(e/4) + 4h + e%4 of the row block
+    // D[k][b]: lane holds b = lane & 31 (for R = 16 columns 16-31 repeat 0-15),
+    // k = 8(e/4) + 4h + e%4 of the row block
     const int bq = bt + (lane & 31);
-    if (bq < batch) {
+    if ((lane & 31) < R && bq < batch) {
       uint16_t* o = out + (int64_t(bq) * a.n_heads + i) * kMPH + 32 * kb + 4 * h;
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
@@ -162,8 +185,15 @@ __global__ __launch_bounds__(64 * kMPWaves) void merge_proj_kernel(MergeArgs a, 
 }
 
 hipError_t launch_merge_proj(const MergeArgs& a, const void* w_uv, void* o_heads, int batch, hipStream_t st) {
-  merge_proj_kernel<<<dim3(a.n_heads, ceil_div(batch, kMPRows)), 64 * kMPWaves, 0, st>>>(
-      a, static_cast<const uint16_t*>(w_uv), static_cast<uint16_t*>(o_heads), batch);
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return hipErrorInvalidDevice;
+  const uint16_t* w = static_cast<const uint16_t*>(w_uv);
+  uint16_t* out = static_cast<uint16_t*>(o_heads);
+  if (int64_t(a.n_heads) * ceil_div(batch, 32) >= cus)
+    merge_proj_kernel<32><<<dim3(a.n_heads, ceil_div(batch, 32)), 64 * kMPWaves, 0, st>>>(a, w, out, batch);
+  else
+    merge_proj_kernel<16><<<dim3(a.n_heads, ceil_div(batch, 16)), 64 * kMPWaves, 0, st>>>(a, w, out, batch);
   return hipGetLastError();
 }
 
