@@ -131,6 +131,57 @@ __device__ __forceinline__ void wait_tile(int wave, bool newer_in_flight) {
   else __builtin_amdgcn_s_waitcnt(waitcnt_vm(4));
 }
 
+// Query staging.  A wavefront's latent query (32 heads x 256 dims, 16 KB) is
+// copied into LDS in two passes of 128 dims (8 KB: 32 rows of 256 B) by
+// direct-to-LDS loads that each read four whole row pieces (full cache lines),
+// then read back in the MFMA operand layout.  Register loads in that layout
+// would touch every 128-byte line four times.  In the staging area chunk c
+// (16 B) of row r sits at r*256 + ((c ^ (r & 15)) * 16): the operand reads (16
+// rows of one chunk per 16 lanes) hit 16 distinct bank groups.  The loads are
+// not tracked by the compiler (inline assembly), so their completion is waited
+// for explicitly, which also lets the first tile be waited for without the
+// second.
+__device__ __forceinline__ void issue_query_pass(const uint16_t* src, uint32_t stage) {
+  int ln = threadIdx.x & 63;
+  asm volatile("" : "+v"(ln));
+  const uint64_t base = reinterpret_cast<uint64_t>(src);
+  i32x4 rsrc;
+  rsrc[0] = uniform(int(uint32_t(base)));
+  rsrc[1] = uniform(int(uint32_t(base >> 32) & 0xFFFFu));
+  rsrc[2] = 31 * kV2Lat * 2 + 256;   // rows 0..31 at a 1024-byte stride, 256 B each
+  rsrc[3] = int(kBufferFlags);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = 4 * i + (ln >> 4), c = (ln & 15) ^ (r & 15);
+    const int voff = r * (kV2Lat * 2) + c * 16;
+    const int m0 = uniform(int(stage + uint32_t(i * 1024)));
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 : : "s"(m0), "v"(voff), "s"(rsrc) : "memory", "m0");
+  }
+}
+
+// The RoPE query of all 128 heads (16 KB) into its LDS area (head hd, chunk c at
+// hd*128 + ((c ^ (hd & 7)) * 16)): one-KB blocks 2w and 2w+1 by wavefront w.
+__device__ __forceinline__ void issue_query_pe(const uint16_t* src, uint32_t qpe, int wave) {
+  int ln = threadIdx.x & 63;
+  asm volatile("" : "+v"(ln));
+  const uint64_t base = reinterpret_cast<uint64_t>(src);
+  i32x4 rsrc;
+  rsrc[0] = uniform(int(uint32_t(base)));
+  rsrc[1] = uniform(int(uint32_t(base >> 32) & 0xFFFFu));
+  rsrc[2] = kQpeBytes;
+  rsrc[3] = int(kBufferFlags);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int i = 2 * wave + j;
+    const int hd = 8 * i + (ln >> 3), c = (ln & 7) ^ (hd & 7);
+    const int voff = hd * (kV2Rope * 2) + c * 16;
+    const int m0 = uniform(int(qpe + uint32_t(i * 1024)));
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 : : "s"(m0), "v"(voff), "s"(rsrc) : "memory", "m0");
+  }
+}
+
 // ---------------------------------------------------------------------------
 // fp8 cache (OCP E4M3 codes, one fp32 scale per token per 128-channel group;
 // the stored value is code * scale).  A tile's codes (32 rows x 576 B, one
@@ -319,37 +370,46 @@ void decode_v2_kernel(V2DecodeArgs a) {
     // every wavefront is done with the previous segment's tiles and scores
     raw_barrier();
     const int page_first = load_const(bt, 0);
-    issue(0, page_first);
-    // bf16: tile 1 goes out with tile 0, so both arrive during the query wait
-    if (!kF8 && ntiles > 1) issue(1, page_first);
+    // query staging area of this wavefront (free until the loop's first
+    // barrier): the tile buffer that no tile uses before slot 1 for wavefronts
+    // 0-3, the exchange area for 4-7
+    const uint32_t qstage = (wave < 4 ? tiles_lds + uint32_t((kF8 ? 1 : 2) * kTileBytes) : xs_lds) +
+                            uint32_t((wave & 3) * 8192);
+    const uint16_t* const qsrc = a.q_lat + (int64_t(b) * kV2Heads + pair * 32) * kV2Lat + 256 * dh;
     // query slices of head `head` (MFMA B operand: lane holds 8 consecutive dims):
-    // latent dims 256*dh + 16*kk + 8*h .. +8, RoPE dims 32*dh + 16*j + 8*h .. +8
+    // latent dims 256*dh + 16*kk + 8*h .. +8, RoPE dims in LDS
     bf16x8 qf[16];
-    {
-      // per-lane offsets from an opaque lane id (computed here, not held
-      // through the tile loop)
-      const int lq = opaque_lane();
-      const int hq = pair * 32 + (lq & 31);
-      const uint16_t* ql = a.q_lat + (int64_t(b) * kV2Heads + hq) * kV2Lat + 256 * dh + 8 * (lq >> 5);
+    auto read_query_pass = [&](int pass) {
+      const int ln = opaque_lane();
+      const int r = ln & 31;
 #pragma unroll
-      for (int kk = 0; kk < 16; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(ql + 16 * kk);
-      // RoPE query of all heads into LDS: thread x copies chunk (x & 7) of head x >> 3
-      const int tq = wave * 64 + lq;
-#pragma unroll
-      for (int rep = 0; rep < 2; ++rep) {
-        const int x = rep * kDecThreads + tq;
-        const int hd = x >> 3, c = x & 7;
-        const bf16x8 v = *reinterpret_cast<const bf16x8*>(a.q_pe + (int64_t(b) * kV2Heads + hd) * kV2Rope + c * 8);
-        *reinterpret_cast<bf16x8 MLA_LDS*>((char MLA_LDS*)(uintptr_t)(qpe_lds + hd * 128 + ((c ^ (hd & 7)) * 16))) = v;
+      for (int t = 0; t < 8; ++t) {
+        const int c = 2 * t + (ln >> 5);
+        qf[8 * pass + t] = lds_read_b128(qstage + uint32_t(r * 256 + ((c ^ (r & 15)) * 16)));
       }
+    };
+    // pass 0 and the RoPE query, then tile 0; wait for the first two only
+    issue_query_pass(qsrc, qstage);
+    issue_query_pe(a.q_pe + int64_t(b) * kV2Heads * kV2Rope, qpe_lds, wave);
+    issue(0, page_first);
+    if constexpr (kF8) wait_tile_f8(wave, true);
+    else wait_tile(wave, true);
+    read_query_pass(0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));   // read before the area is refilled
+    issue_query_pass(qsrc + 128, qstage);
+    // bf16: tile 1 goes out before the wait, so only pass 1 and tile 0 are waited for
+    if (!kF8 && ntiles > 1) {
+      issue(1, page_first);
+      wait_tile(wave, true);
+    } else {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     }
-    // tile 0 and the query are needed first; an explicit full wait here also tells
-    // the compiler that the query registers are ready, so it puts no waits for
-    // them inside the tile loop (where they would drain the tile prefetches).
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    read_query_pass(1);
+    // an explicit wait here tells the compiler that the query registers are
+    // ready, so it puts no waits for them inside the tile loop
+    __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
     if constexpr (kF8) {
       // tile 0's staged codes visible to all, dequantised before slot 0
-      __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
       raw_barrier();
       convert_tile_f8(stage_buf(0), tile_buf(0));
     }
@@ -531,14 +591,20 @@ void decode_v2_kernel(V2DecodeArgs a) {
     }
 
     // ---- epilogue: normalise, write o (final or partial) and lse
-    const float ltot = lsum + __shfl_xor(lsum, 32);
+    // lane pair sum across the two row halves (a lane swap: no lane-id register)
+    float ltot;
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum), false, false);
+      ltot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
     const float inv = 1.f / ltot;
     const float lse_nat = (m_run + __log2f(ltot)) * kLn2;
     // the lane's head from an opaque lane id: output addresses built from
     // `head` itself are hoisted out of the segment loop, and the register pair
     // they hold through the tile loop is one more than the loop can spare
-    const int head_e = pair * 32 + (opaque_lane() & 31);
-    const int colbase = 256 * dh + 4 * h;
+    const int lane_e = opaque_lane();
+    const int head_e = pair * 32 + (lane_e & 31);
+    const int colbase = 256 * dh + 4 * (lane_e >> 5);
     // final output of a sequence covered by this item alone, else a split
     // partial (normalised within the split); both in the output dtype
     void* const obase = sg.whole ? a.o_lat : a.o_part;
