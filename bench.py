@@ -18,6 +18,7 @@ launch stream) and `cpu_baseline` (the float64 oracle on a bounded sample).
 Helper modes for the rocprofv3 summaries kept in profiles/:
     python bench.py --summarize-stats DIR OUT.md      (kernel-trace --stats)
     python bench.py --summarize-pmc FETCH_DIR WRITE_DIR COPY_BYTES OUT.json OUT.md [--workload W]
+    python bench.py --summarize-counters DIR OUT.md                (--pmc MfmaUtil ... OccupancyPercent)
 """
 from __future__ import annotations
 
@@ -276,11 +277,23 @@ def run(args):
         for i in range(args.steps):
             one(args.warmup + args.steps + i, evs[i])
         torch.cuda.synchronize()
+        step_evs = sorted(e[0].elapsed_time(e[4]) for e in evs)
         names = (["absorb", "decode_multi", "out_proj", "-"] if q_len > 1 else
                  ["absorb", "decode", "merge + out_proj" if args.unfused else "merge_out_proj", "-"])
         per_kernel = {n: sum(e[k].elapsed_time(e[k + 1]) for e in evs) / args.steps for k, n in enumerate(names)
                       if n != "-"}
         per_kernel_step_ms = sum(e[0].elapsed_time(e[4]) for e in evs) / args.steps
+    # warm: the same input copy every step (its cache partly stays in the 256 MB
+    # Infinity Cache between steps), K steps, timed like the headline region
+    torch.cuda.synchronize()
+    w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0.record(stream)
+    for i in range(args.steps):
+        one(0)
+    w1.record(stream)
+    torch.cuda.synchronize()
+    warm_ms = w0.elapsed_time(w1) / args.steps
+    copy_tbps = measured_copy_tbps()
     alg = algorithmic(lens, w.cache_dtype, q_len, n_h)
     T = sum(lens)
     value = T * args.steps / (total_ms * 1e-3)
@@ -312,9 +325,13 @@ def run(args):
     }
     roof_us = max(res["step_roofline"].values())
     res["step_roofline"]["frac_of_min_roof"] = roof_us / (ms_per_step * 1e3)
+    res["warm_ms_per_step"] = warm_ms
+    res["measured_copy_TBps"] = copy_tbps
     if per_kernel:
         res["kernel_ms"] = per_kernel
         res["kernel_events_step_ms"] = per_kernel_step_ms
+        n = len(step_evs)
+        res["kernel_events_step_ms_p10_p50_p90"] = [step_evs[n // 10], step_evs[n // 2], step_evs[(9 * n) // 10]]
         dec_name = "decode_multi" if q_len > 1 else "decode"
         dec_s = per_kernel[dec_name] * 1e-3
         ach = alg["decode_bytes"] / dec_s / 1e9
@@ -323,6 +340,7 @@ def run(args):
             tj = json.load(open(traffic_json(args.workload)))
             if tj.get("decode_source_sha") == decode_source_hash(args.workload) and tj.get("workload") == wname:
                 traffic = tj.get("decode_bytes_per_launch")
+        res["decode_frac_of_measured_copy"] = ach / (copy_tbps * 1e3)
         res["roofline"] = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": ach / HBM_PEAK_GBS, "traffic": traffic,
                            "kernel": ("decode_v2_kernel<true> (fp8 cache)" if cid == 5 else
@@ -405,6 +423,39 @@ def _pmc_per_kernel(d, counter):
     return vals
 
 
+COUNTER_METRICS = ("MfmaUtil", "MfmaFlopsBF16", "VALUBusy", "LdsUtil", "LDSBankConflict", "OccupancyPercent")
+
+
+def summarize_counters(d, out_md, cmd="", workload="ragged"):
+    """Median per dispatch of rocprofv3's derived metrics for each kernel of one
+    `rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 VALUBusy LdsUtil LDSBankConflict
+    OccupancyPercent` run: MFMA busy %, bf16 MFMA flops, VALU busy %, LDS busy %,
+    LDS bank-conflict stall % and occupancy % (each over the GPU-active cycles)."""
+    import statistics
+    con = _db(d)
+    vals = {}
+    for name, cnt, v in con.execute("select kernel_name, counter_name, value from counters_collection"):
+        vals.setdefault(_short(name), {}).setdefault(cnt, []).append(float(v))
+    lines = ["# Per-kernel counters (rocprofv3 derived metrics, median per dispatch)", "", f"Command: `{cmd}`", "",
+             "MfmaUtil = MFMA busy cycles / (SIMDs x GPU-active cycles); LdsUtil = LDS indexed-op cycles / "
+             "(CUs x active cycles); LDSBankConflict = bank-conflict stall cycles / (CUs x active cycles); "
+             "OccupancyPercent = resident waves / maximum; VALUBusy = VALU instruction cycles / (CUs x active "
+             "cycles); MfmaFlopsBF16 = bf16 MFMA flops per dispatch.", "",
+             "| kernel | dispatches | " + " | ".join(COUNTER_METRICS) + " |",
+             "|---|---|" + "---|" * len(COUNTER_METRICS)]
+    for k in sorted(vals, key=lambda k: -len(vals[k].get(COUNTER_METRICS[0], []))):
+        row = vals[k]
+        n = max(len(v) for v in row.values())
+        cells = []
+        for m in COUNTER_METRICS:
+            x = row.get(m)
+            cells.append("—" if not x else (f"{statistics.median(x):.3g}" if m == "MfmaFlopsBF16" else
+                                            f"{statistics.median(x):.1f}"))
+        lines.append(f"| {k} | {n} | " + " | ".join(cells) + " |")
+    open(out_md, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def summarize_pmc(fetch_dir, write_dir, copy_bytes, out_json, out_md, cmd="", workload="ragged"):
     """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of a workload's decode kernel,
     scaled by what the same counters read for a plain device copy of known size."""
@@ -447,6 +498,26 @@ def summarize_pmc(fetch_dir, write_dir, copy_bytes, out_json, out_md, cmd="", wo
         lines.append(f"- {k}: fetched {v['fetch_bytes'] / 1e6:.2f} MB, written {v['write_bytes'] / 1e6:.2f} MB")
     open(out_md, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
+
+
+def measured_copy_tbps(nbytes: int = 1 << 30, reps: int = 5) -> float:
+    """HBM bandwidth of a plain device-to-device copy (the runtime's copy kernel) in
+    the same job: bytes read + written per second, best of `reps`, in TB/s."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").normal_()
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    best = float("inf")
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    del src, dst
+    return 2 * nbytes / (best * 1e-3) / 1e12
 
 
 def copy_calibration(nbytes: int, reps: int = 3):
@@ -673,12 +744,15 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
     ap.add_argument("--summarize-stats", nargs=2, metavar=("DIR", "OUT_MD"))
     ap.add_argument("--summarize-pmc", nargs=5, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_BYTES", "OUT_JSON", "OUT_MD"))
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("DIR", "OUT_MD"))
     ap.add_argument("--cmd", default="")
     args = ap.parse_args()
     if args.summarize_stats:
         return summarize_stats(*args.summarize_stats, cmd=args.cmd)
     if args.summarize_pmc:
         return summarize_pmc(*args.summarize_pmc, cmd=args.cmd, workload=args.workload)
+    if args.summarize_counters:
+        return summarize_counters(*args.summarize_counters, cmd=args.cmd, workload=args.workload)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the MLA decode path here is single-GPU (no sharding, no "
               "collectives); use --gpus 1.", file=sys.stderr)
