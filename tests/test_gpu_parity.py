@@ -132,6 +132,20 @@ def test_v2_ragged(v2_ragged, part):
     compare_all(case, step, TOL["bf16"])
 
 
+SHORT = [64] * 12 + [1] * 5 + [0, 130]
+
+
+@pytest.mark.parametrize("part", [(0, 17), (0, 20), (0, 29)])
+def test_v2_cost_stream_partition_short_sequences(part):
+    """Many one-page sequences, about as many parts as pages: the 2 extra cost
+    units between sequences leave some work items without any page (20 pages,
+    54 units: 2 of 20 items are empty for 20 or more parts)."""
+    case = direct_case(3, SHORT, max_pages=4, seed=91)
+    print(f"case: V2 bf16 lens={SHORT}, partition {part}", flush=True)
+    step = run_step(case, to_device(case), *part)
+    compare_all(case, step, TOL["bf16"])
+
+
 def test_v2_deterministic(v2_ragged):
     case, dev = v2_ragged
     print("case: V2 bf16 ragged, repeat bitwise", flush=True)
