@@ -97,6 +97,16 @@ def test_fused_batch_37_with_empty_sequences():
     _check(*_both(case, dev, (0, 9)), exact_heads=False)
 
 
+def test_fused_more_than_64_splits():
+    """79 splits of one sequence (64-token splits of 5000 tokens): the lse values
+    beyond the 64 lanes are read per split."""
+    lens = [5000, 70, 0, 640]
+    case = direct_case(3, lens, max_pages=80, seed=85)
+    dev = to_device(case)
+    print(f"case: V2 bf16 lens {lens}, split 64", flush=True)
+    _check(*_both(case, dev, (64, 0)), exact_heads=False)
+
+
 def test_fused_v2lite_16_heads():
     lens = [2, 70, 900, 129, 0, 4000]
     case = direct_case(6, lens, max_pages=64, seed=83)
