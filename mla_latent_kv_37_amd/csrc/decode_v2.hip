@@ -477,6 +477,10 @@ void decode_v2_kernel(V2DecodeArgs a) {
       // row dims; fragment reads run two k-steps ahead of the (dependent) MFMA chain
       const int jq = 2 * k + team;
       open_slot(jq);
+      // bf16: the score wavefront wins issue arbitration against its SIMD
+      // partner during this slot (1.3-1.8% less decode time in interleaved A/B
+      // runs; the fp8 kernel was 2% slower with it)
+      if constexpr (!kF8) __builtin_amdgcn_s_setprio(1);
       const uint32_t tb = tile_buf(k);
       f32x16 s = {};
       {
@@ -514,6 +518,7 @@ void decode_v2_kernel(V2DecodeArgs a) {
         f32x4 v = {s[4 * q4], s[4 * q4 + 1], s[4 * q4 + 2], s[4 * q4 + 3]};
         *reinterpret_cast<f32x4 MLA_LDS*>((char MLA_LDS*)(uintptr_t)(xs_of(opaque_lane()) + q4 * 1024)) = v;
       }
+      if constexpr (!kF8) __builtin_amdgcn_s_setprio(0);
       close_slot(jq);
 
       // ======== slot 2k + team + 1: softmax and O^T += V^T . P^T of tile k
