@@ -226,12 +226,19 @@ def run(args):
         if ev is not None:
             ev[1].record(stream)
         if q_len > 1:
-            # expand + decode + merge in one call
-            mk.decode_multi(step.d, q_lat_m, s["q_pe"].view(B, q_len, N_H, D_R), s["cache"].desc, scale, step.part,
-                            multi_ws, o_lat_m, lse_m)
-            if ev is not None:
-                ev[2].record(stream)
-            step.project(s["W_UV"])
+            if args.unfused:
+                # expand + decode + merge in one call, then the projection
+                mk.decode_multi(step.d, q_lat_m, s["q_pe"].view(B, q_len, N_H, D_R), s["cache"].desc, scale,
+                                step.part, multi_ws, o_lat_m, lse_m)
+                if ev is not None:
+                    ev[2].record(stream)
+                step.project(s["W_UV"])
+            else:
+                # expand + decode, then merge + projection in one launch
+                mk.decode_multi_out_proj(step.d, q_lat_m, s["q_pe"].view(B, q_len, N_H, D_R), s["cache"].desc, scale,
+                                         step.part, multi_ws, o_lat_m, s["W_UV"], step.o_heads, lse_m)
+                if ev is not None:
+                    ev[2].record(stream)
             if ev is not None:
                 ev[3].record(stream)
         else:
@@ -278,8 +285,11 @@ def run(args):
             one(args.warmup + args.steps + i, evs[i])
         torch.cuda.synchronize()
         step_evs = sorted(e[0].elapsed_time(e[4]) for e in evs)
-        names = (["absorb", "decode_multi", "out_proj", "-"] if q_len > 1 else
-                 ["absorb", "decode", "merge + out_proj" if args.unfused else "merge_out_proj", "-"])
+        if q_len > 1:
+            names = (["absorb", "decode_multi", "out_proj", "-"] if args.unfused else
+                     ["absorb", "decode_multi_out_proj", "-", "-"])
+        else:
+            names = ["absorb", "decode", "merge + out_proj" if args.unfused else "merge_out_proj", "-"]
         per_kernel = {n: sum(e[k].elapsed_time(e[k + 1]) for e in evs) / args.steps for k, n in enumerate(names)
                       if n != "-"}
         per_kernel_step_ms = sum(e[0].elapsed_time(e[4]) for e in evs) / args.steps
@@ -332,7 +342,7 @@ def run(args):
         res["kernel_events_step_ms"] = per_kernel_step_ms
         n = len(step_evs)
         res["kernel_events_step_ms_p10_p50_p90"] = [step_evs[n // 10], step_evs[n // 2], step_evs[(9 * n) // 10]]
-        dec_name = "decode_multi" if q_len > 1 else "decode"
+        dec_name = ("decode_multi" if args.unfused else "decode_multi_out_proj") if q_len > 1 else "decode"
         dec_s = per_kernel[dec_name] * 1e-3
         ach = alg["decode_bytes"] / dec_s / 1e9
         traffic = None
@@ -346,7 +356,9 @@ def run(args):
                            "kernel": ("decode_v2_kernel<true> (fp8 cache)" if cid == 5 else
                                       "decode_lite_kernel (16 heads, bf16 cache)" if n_h == 16 else
                                       "decode_v2_kernel<false> (bf16 cache)") +
-                                     (" + expand_kernel + merge_kernel (mla_decode_multi)" if q_len > 1 else ""),
+                                     ((" + expand_kernel + merge_kernel (mla_decode_multi)" if args.unfused else
+                                       " + expand_kernel + merge_proj_kernel (mla_decode_multi_out_proj; the "
+                                       "time includes the W^UV projection)") if q_len > 1 else ""),
                            "algorithmic_bytes_per_launch": alg["decode_bytes"],
                            "mean_launch_ms": per_kernel[dec_name],
                            "mfma_frac": alg["decode_flops"] / dec_s / (MFMA_BF16_PEAK_TFLOPS * 1e12)}
@@ -738,7 +750,8 @@ def main():
     ap.add_argument("--copies", type=int, default=2)
     ap.add_argument("--no-kernel-events", dest="kernel_events", action="store_false")
     ap.add_argument("--unfused", action="store_true",
-                    help="run mla_merge_splits + mla_out_proj instead of mla_merge_out_proj (comparison)")
+                    help="run mla_merge_splits + mla_out_proj (mla_decode_multi + mla_out_proj) instead of "
+                         "mla_merge_out_proj (mla_decode_multi_out_proj), for comparison")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")

@@ -216,6 +216,22 @@ mla_status_t mla_decode_multi(const mla_dims_t* dims, int32_t batch, int32_t q_l
                               void* o_lat, mla_dtype_t o_dt, float* lse, void* stream);
 
 /*
+ * mla_decode_multi followed by mla_out_proj over the batch * q_len rows, with
+ * the split merge and the W^UV projection in one launch (mla_merge_out_proj).
+ * o_lat / lse are written as by mla_decode_multi; o_heads: [batch, q_len,
+ * n_h * d_h] (out_dt), equal to mla_out_proj's result up to the order of fp32
+ * additions.  All arguments (those of the projection included) are validated
+ * before anything is enqueued.
+ */
+mla_status_t mla_decode_multi_out_proj(const mla_dims_t* dims, int32_t batch, int32_t q_len,
+                                       const void* q_lat, const void* q_pe, mla_dtype_t q_dt,
+                                       const mla_paged_cache_t* cache, float softmax_scale,
+                                       const mla_partition_t* part, void* workspace,
+                                       size_t workspace_bytes, void* o_lat, mla_dtype_t o_dt, float* lse,
+                                       const void* w_uv, mla_dtype_t w_dt, void* o_heads,
+                                       mla_dtype_t out_dt, void* stream);
+
+/*
  * o_heads[b, i*d_h + k] = sum_c W^UV[i*d_h + k, c] o_lat[b, i, c]  (W^UV applied
  * after attention, [DeepSeek-V2 explainer §2.2.2]).
  *   o_lat: [batch, n_h, d_c] (o_dt);  w_uv: [n_h * d_h, d_c] (w_dt);

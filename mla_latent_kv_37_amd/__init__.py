@@ -11,7 +11,7 @@ from __future__ import annotations
 
 from . import _lib
 from ._lib import (MLA_BF16, MLA_F32, MLA_FP8_E4M3, MlaError, absorb_q, build_info, cache_append,  # noqa: F401
-                   cache_store, decode, decode_multi, dims, lse_part_offset, make_cache, merge_out_proj,
+                   cache_store, decode, decode_multi, decode_multi_out_proj, dims, lse_part_offset, make_cache, merge_out_proj,
                    merge_splits, multi_workspace_size, out_proj, partition, partition_host, query_prep, query_prep_scratch_size,
                    status_string, workspace_size)
 

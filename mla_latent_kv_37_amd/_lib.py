@@ -20,7 +20,8 @@ MLA_F32, MLA_BF16, MLA_FP8_E4M3 = 0, 1, 2
 EXPORTS = ("mla_status_string", "mla_build_info", "mla_absorb_q", "mla_decode_workspace_size",
            "mla_lse_part_offset", "mla_decode", "mla_merge_splits", "mla_out_proj", "mla_cache_store",
            "mla_cache_append", "mla_query_prep_scratch_size", "mla_query_prep", "mla_partition_host",
-           "mla_decode_multi_workspace_size", "mla_decode_multi", "mla_merge_out_proj")
+           "mla_decode_multi_workspace_size", "mla_decode_multi", "mla_merge_out_proj",
+           "mla_decode_multi_out_proj")
 
 
 class MlaError(RuntimeError):
@@ -83,6 +84,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                                            ctypes.POINTER(I32)]),
         "mla_decode_multi": (ctypes.c_int, [PD, I32, I32, P, P, ctypes.c_int, PC, ctypes.c_float, PP, P, SZ, P,
                                             ctypes.c_int, P, P]),
+        "mla_decode_multi_out_proj": (ctypes.c_int, [PD, I32, I32, P, P, ctypes.c_int, PC, ctypes.c_float, PP, P, SZ,
+                                                     P, ctypes.c_int, P, P, ctypes.c_int, P, ctypes.c_int, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -210,6 +213,19 @@ def decode_multi(d: Dims, q_lat, q_pe, cache: PagedCache, softmax_scale: float, 
                                    ctypes.byref(part), _ptr(workspace), ws_bytes, _ptr(o_lat), dtype_code(o_lat),
                                    _ptr(lse), _stream(stream)), "mla_decode_multi")
     return o_lat
+
+
+def decode_multi_out_proj(d: Dims, q_lat, q_pe, cache: PagedCache, softmax_scale: float, part: Partition,
+                          workspace, o_lat, w_uv, o_heads, lse=None, stream=None):
+    """decode_multi(...) then out_proj over the B * q_len rows, the merge and the
+    projection in one launch; o_heads [B, q_len, n_h * d_h]."""
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load().mla_decode_multi_out_proj(ctypes.byref(d), q_lat.shape[0], q_lat.shape[1], _ptr(q_lat), _ptr(q_pe),
+                                            dtype_code(q_lat), ctypes.byref(cache), ctypes.c_float(softmax_scale),
+                                            ctypes.byref(part), _ptr(workspace), ws_bytes, _ptr(o_lat),
+                                            dtype_code(o_lat), _ptr(lse), _ptr(w_uv), dtype_code(w_uv), _ptr(o_heads),
+                                            dtype_code(o_heads), _stream(stream)), "mla_decode_multi_out_proj")
+    return o_heads
 
 
 def out_proj(d: Dims, o_lat, w_uv, o_heads, stream=None):

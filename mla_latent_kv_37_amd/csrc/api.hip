@@ -369,10 +369,28 @@ mla_status_t mla_decode_multi_workspace_size(const mla_dims_t* dims, int32_t bat
   return MLA_OK;
 }
 
-mla_status_t mla_decode_multi(const mla_dims_t* dims, int32_t batch, int32_t q_len, const void* q_lat,
-                              const void* q_pe, mla_dtype_t q_dt, const mla_paged_cache_t* cache,
-                              float softmax_scale, const mla_partition_t* part, void* workspace,
-                              size_t workspace_bytes, void* o_lat, mla_dtype_t o_dt, float* lse, void* stream) {
+namespace {
+
+// Arguments of the W^UV projection checked before anything is enqueued (the
+// fused call validates them too, but only after the decode has been launched).
+mla_status_t check_out_proj_args(const mla_dims_t* dims, mla_dtype_t o_dt, const void* w_uv, mla_dtype_t w_dt,
+                                 const void* o_heads, mla_dtype_t out_dt) {
+  if (!w_uv || !o_heads) return MLA_ERR_INVALID_ARG;
+  for (mla_dtype_t t : {o_dt, w_dt, out_dt})
+    if (t != MLA_F32 && t != MLA_BF16) return valid_dtype(t) ? MLA_ERR_UNSUPPORTED : MLA_ERR_INVALID_ARG;
+  if (!aligned16(w_uv) || !aligned16(o_heads)) return MLA_ERR_ALIGNMENT;
+  const bool v2 = dims->d_head == 128 && dims->d_latent == 512 && w_dt == MLA_BF16 && out_dt == MLA_BF16;
+  if (!v2 && dims->d_latent > kGenMaxLatent) return MLA_ERR_UNSUPPORTED;
+  return MLA_OK;
+}
+
+// expand + decode over the batch * q_len virtual sequences, then the merge
+// (w_uv == nullptr) or the merge + W^UV projection (mla_merge_out_proj).
+mla_status_t decode_multi_impl(const mla_dims_t* dims, int32_t batch, int32_t q_len, const void* q_lat,
+                               const void* q_pe, mla_dtype_t q_dt, const mla_paged_cache_t* cache,
+                               float softmax_scale, const mla_partition_t* part, void* workspace,
+                               size_t workspace_bytes, void* o_lat, mla_dtype_t o_dt, float* lse, const void* w_uv,
+                               mla_dtype_t w_dt, void* o_heads, mla_dtype_t out_dt, void* stream) {
   if (!cache) return MLA_ERR_INVALID_ARG;
   MultiLayout M;
   int n_slots = 0;
@@ -382,6 +400,8 @@ mla_status_t mla_decode_multi(const mla_dims_t* dims, int32_t batch, int32_t q_l
   if (!workspace || workspace_bytes < M.total) return MLA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return MLA_ERR_ALIGNMENT;
   if (o_dt != MLA_F32 && o_dt != MLA_BF16) return valid_dtype(o_dt) ? MLA_ERR_UNSUPPORTED : MLA_ERR_INVALID_ARG;
+  if (w_uv || o_heads)
+    if (mla_status_t s = check_out_proj_args(dims, o_dt, w_uv, w_dt, o_heads, out_dt)) return s;
   char* ws = static_cast<char*>(workspace);
   const int vb = batch * q_len;
   mla_paged_cache_t vc = *cache;
@@ -399,8 +419,32 @@ mla_status_t mla_decode_multi(const mla_dims_t* dims, int32_t batch, int32_t q_l
   if (mla_status_t s = decode_impl(dims, vb, q_lat, q_pe, q_dt, &vc, softmax_scale, part, dec_ws, M.dec_bytes, o_lat,
                                    o_dt, lse, stream, false))
     return s;
-  return mla_merge_splits(dims, vb, vc.seq_lens, cache->page_size, cache->max_pages_per_seq, part, dec_ws,
-                          M.dec_bytes, o_lat, o_dt, lse, stream);
+  if (!w_uv)
+    return mla_merge_splits(dims, vb, vc.seq_lens, cache->page_size, cache->max_pages_per_seq, part, dec_ws,
+                            M.dec_bytes, o_lat, o_dt, lse, stream);
+  return mla_merge_out_proj(dims, vb, vc.seq_lens, cache->page_size, cache->max_pages_per_seq, part, dec_ws,
+                            M.dec_bytes, o_lat, o_dt, lse, w_uv, w_dt, o_heads, out_dt, stream);
+}
+
+}  // namespace
+
+mla_status_t mla_decode_multi(const mla_dims_t* dims, int32_t batch, int32_t q_len, const void* q_lat,
+                              const void* q_pe, mla_dtype_t q_dt, const mla_paged_cache_t* cache,
+                              float softmax_scale, const mla_partition_t* part, void* workspace,
+                              size_t workspace_bytes, void* o_lat, mla_dtype_t o_dt, float* lse, void* stream) {
+  return decode_multi_impl(dims, batch, q_len, q_lat, q_pe, q_dt, cache, softmax_scale, part, workspace,
+                           workspace_bytes, o_lat, o_dt, lse, nullptr, MLA_BF16, nullptr, MLA_BF16, stream);
+}
+
+mla_status_t mla_decode_multi_out_proj(const mla_dims_t* dims, int32_t batch, int32_t q_len, const void* q_lat,
+                                       const void* q_pe, mla_dtype_t q_dt, const mla_paged_cache_t* cache,
+                                       float softmax_scale, const mla_partition_t* part, void* workspace,
+                                       size_t workspace_bytes, void* o_lat, mla_dtype_t o_dt, float* lse,
+                                       const void* w_uv, mla_dtype_t w_dt, void* o_heads, mla_dtype_t out_dt,
+                                       void* stream) {
+  if (!w_uv || !o_heads) return MLA_ERR_INVALID_ARG;
+  return decode_multi_impl(dims, batch, q_len, q_lat, q_pe, q_dt, cache, softmax_scale, part, workspace,
+                           workspace_bytes, o_lat, o_dt, lse, w_uv, w_dt, o_heads, out_dt, stream);
 }
 
 mla_status_t mla_out_proj(const mla_dims_t* dims, int32_t batch, const void* o_lat, mla_dtype_t o_dt, const void* w_uv,

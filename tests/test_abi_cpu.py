@@ -181,6 +181,54 @@ def test_multi_decode_workspace_and_validation(lib):
               1, None, None) == lib.MLA_OK
 
 
+def test_merge_out_proj_validation(lib):
+    """mla_merge_out_proj checks the arguments of both calls it replaces before
+    anything is enqueued."""
+    L = _raw(lib)
+    d = _v2(lib)
+    fake, odd = ctypes.c_void_p(0x10000), ctypes.c_void_p(0x10008)
+    B, mp = 8, 10
+    part = lib.partition(0, 40)
+    need, _ = lib.workspace_size(d, B, mp, 64, part)
+    mo = L.mla_merge_out_proj
+    args = lambda **k: dict(dict(batch=B, lens=fake, ws=fake, nb=need, o=fake, odt=1, w=fake, wdt=1, oh=fake,  # noqa: E731
+                                 ohdt=1), **k)
+
+    def call(a):
+        return mo(ctypes.byref(d), a["batch"], a["lens"], 64, mp, ctypes.byref(part), a["ws"], a["nb"], a["o"],
+                  a["odt"], None, a["w"], a["wdt"], a["oh"], a["ohdt"], None)
+    assert call(args(lens=None)) == lib.MLA_ERR_INVALID_ARG
+    assert call(args(w=None)) == lib.MLA_ERR_INVALID_ARG
+    assert call(args(oh=None)) == lib.MLA_ERR_INVALID_ARG
+    assert call(args(ohdt=lib.MLA_FP8_E4M3)) == lib.MLA_ERR_UNSUPPORTED
+    assert call(args(wdt=7)) == lib.MLA_ERR_INVALID_ARG
+    assert call(args(oh=odd)) == lib.MLA_ERR_ALIGNMENT
+    assert call(args(nb=need - 1)) == lib.MLA_ERR_WORKSPACE
+    assert call(args(batch=0)) == lib.MLA_OK
+
+
+def test_multi_out_proj_validation(lib):
+    """mla_decode_multi_out_proj rejects bad projection arguments before the
+    decode is enqueued."""
+    L = _raw(lib)
+    d = _v2(lib)
+    fake, odd = ctypes.c_void_p(0x10000), ctypes.c_void_p(0x10008)
+    B, q, mp = 8, 3, 10
+    part = lib.partition(0, 0)
+    cache = lib.PagedCache(0x10000, None, lib.MLA_BF16, 64, 100, 0x20000, mp, 0x30000)
+    need, _ = lib.multi_workspace_size(d, B, q, mp, 64, part)
+    f = L.mla_decode_multi_out_proj
+
+    def call(batch=B, w=fake, wdt=1, oh=fake, ohdt=1):
+        return f(ctypes.byref(d), batch, q, fake, fake, 1, ctypes.byref(cache), 0.07, ctypes.byref(part), fake, need,
+                 fake, 1, None, w, wdt, oh, ohdt, None)
+    assert call(w=None) == lib.MLA_ERR_INVALID_ARG
+    assert call(oh=None) == lib.MLA_ERR_INVALID_ARG
+    assert call(wdt=lib.MLA_FP8_E4M3) == lib.MLA_ERR_UNSUPPORTED
+    assert call(oh=odd) == lib.MLA_ERR_ALIGNMENT
+    assert call(batch=0) == lib.MLA_OK
+
+
 SEG_COST = 2   # extra cost units between consecutive non-empty sequences
 
 

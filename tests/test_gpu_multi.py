@@ -42,7 +42,7 @@ def _queries(case, q_len, seed, gain):
     return _round(q_c, case.act), _round(q_r, case.act)
 
 
-def _run_multi(case, dev, q_c, q_r, part):
+def _run_multi(case, dev, q_c, q_r, part, fused=False):
     import torch
     import mla_latent_kv_37_amd as mk
     d = case.dims
@@ -60,9 +60,14 @@ def _run_multi(case, dev, q_c, q_r, part):
     ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
     o_lat = torch.full((B, q_len, d.n_heads, d.d_latent), float("nan"), dtype=tdt, device="cuda")
     lse = torch.full((B, q_len, d.n_heads), float("nan"), dtype=torch.float32, device="cuda")
-    mk.decode_multi(dd, q_lat.view(B, q_len, d.n_heads, d.d_latent), q_pe, cache.desc, case.scale, p, ws, o_lat, lse)
-    o_heads = torch.empty((B * q_len, d.n_heads * d.d_head), dtype=tdt, device="cuda")
-    mk.out_proj(dd, o_lat.view(B * q_len, d.n_heads, d.d_latent), dev["W_UV"], o_heads)
+    o_heads = torch.full((B * q_len, d.n_heads * d.d_head), float("nan"), dtype=tdt, device="cuda")
+    if fused:
+        mk.decode_multi_out_proj(dd, q_lat.view(B, q_len, d.n_heads, d.d_latent), q_pe, cache.desc, case.scale, p, ws,
+                                 o_lat, dev["W_UV"], o_heads, lse)
+    else:
+        mk.decode_multi(dd, q_lat.view(B, q_len, d.n_heads, d.d_latent), q_pe, cache.desc, case.scale, p, ws, o_lat,
+                        lse)
+        mk.out_proj(dd, o_lat.view(B * q_len, d.n_heads, d.d_latent), dev["W_UV"], o_heads)
     torch.cuda.synchronize()
     return host(o_lat), host(lse), host(o_heads).reshape(B, q_len, d.n_heads, d.d_head)
 
@@ -170,3 +175,21 @@ def test_multi_v2lite_bf16(part):
     print(f"case: multi-token V2-Lite bf16, lens {lens}, q_len 2, partition {part}", flush=True)
     q_c, q_r = _queries(case, 2, seed=10, gain=20.0)
     _compare(case, q_c, q_r, _run_multi(case, dev, q_c, q_r, part), TOL["bf16"])
+
+
+@pytest.mark.parametrize("part", [(0, -1), (128, 0), (0, 0)])
+def test_multi_fused_out_proj(v2_ragged, part):
+    """mla_decode_multi_out_proj: o_lat / lse the same bits as mla_decode_multi,
+    o_heads within one bf16 step of mla_out_proj's, and against the oracle."""
+    case, dev = v2_ragged
+    print(f"case: multi-token V2 bf16 fused, lens {case.lens}, q_len 3, partition {part}", flush=True)
+    q_c, q_r = _queries(case, 3, seed=11, gain=1.0)
+    f = _run_multi(case, dev, q_c, q_r, part, fused=True)
+    u = _run_multi(case, dev, q_c, q_r, part, fused=False)
+    assert np.array_equal(f[0], u[0]), "o_lat differs"
+    assert np.array_equal(f[1], u[1]), "lse differs"
+    assert np.all(np.isfinite(f[2]))
+    err = np.abs(f[2] - u[2]).max() / np.abs(u[2]).max()
+    print(f"  o_heads fused vs unfused: {err:.3e} of max", flush=True)
+    assert err <= 2.0 ** -7
+    _compare(case, q_c, q_r, f, TOL["bf16"], SAMPLE_HEADS)
