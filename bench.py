@@ -159,6 +159,18 @@ def make_inputs(config_id: int, copies: int, device="cuda", q_len: int = 1):
 # CPU baseline: the oracle on a bounded sample of the same workload
 # ---------------------------------------------------------------------------
 
+def host_cpu_model() -> str:
+    """The host CPU's model name from /proc/cpuinfo ("unknown" where it is not readable)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(config_id: int, budget_s: float = 15.0):
     import numpy as np
     import oracle
@@ -189,6 +201,7 @@ def cpu_baseline(config_id: int, budget_s: float = 15.0):
         if elapsed >= budget_s:
             break
     return {"value": tokens / elapsed, "unit": "KV-tokens/s", "cores": cores, "kind": "oracle",
+            "cpu_model": host_cpu_model(), "affinity_cpus": len(os.sched_getaffinity(0)),
             "sample": f"oracle.attend (float64, non-absorbed, all {w.dims.n_heads} heads) on the first {nseq} sequences "
                       f"({tokens} cached tokens) of the same workload; {elapsed:.1f} s"}
 
