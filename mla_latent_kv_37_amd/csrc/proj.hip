@@ -129,21 +129,32 @@ __global__ __launch_bounds__(256) void absorb_v2_kernel(const uint16_t* __restri
     acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), b0, acc0, 0, 0, 0);
     acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), b1, acc1, 0, 0, 0);
   }
-  // D[col][b]: lane has b = lane%32 (+32 for acc1), cols 8(r/4) + 4h + r%4 of the wave's 32 columns
+  // D[col][b]: lane has b = lane%32 (+32 for acc1), cols 8(r/4) + 4h + r%4 of the
+  // wave's 32 columns.  The output tile (64 rows x 128 columns) goes through the
+  // freed weight area so that every global store is part of a whole 256-byte
+  // row piece: 16-byte chunk c of row r at slot c ^ (r & 15).
+  __syncthreads();   // every wavefront is done with the weight tile
+  uint16_t MLA_LDS* os = (uint16_t MLA_LDS*)ws;
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
-    const int bq = bt + 32 * half + (lane & 31);
-    if (bq < batch) {
-      const f32x16& acc = half ? acc1 : acc0;
-      uint16_t* o = out + (int64_t(bq) * n_heads + i) * kPL + cb + wave * 32 + 4 * h;
+    const f32x16& acc = half ? acc1 : acc0;
+    const int r = 32 * half + (lane & 31);
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        bf16x4 v;
+    for (int q4 = 0; q4 < 4; ++q4) {
+      bf16x4 v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (__bf16)acc[4 * q4 + e];
-        *reinterpret_cast<bf16x4*>(o + 8 * q4) = v;
-      }
+      for (int e = 0; e < 4; ++e) v[e] = (__bf16)acc[4 * q4 + e];
+      const int c = wave * 4 + q4;
+      *reinterpret_cast<bf16x4 MLA_LDS*>(os + r * 128 + ((c ^ (r & 15)) * 8) + 4 * h) = v;
     }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = tid + 256 * j, r = e >> 4, c = e & 15;
+    if (bt + r < batch)
+      *reinterpret_cast<bf16x8*>(out + (int64_t(bt + r) * n_heads + i) * kPL + cb + c * 8) =
+          *reinterpret_cast<const bf16x8 MLA_LDS*>(os + r * 128 + ((c ^ (r & 15)) * 8));
   }
 }
 
