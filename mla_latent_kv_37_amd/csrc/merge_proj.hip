@@ -15,16 +15,23 @@
 // Workgroup of 16 wavefronts for R = 16 or 32 sequences (32 when that still
 // gives at least one workgroup per compute unit: the fewer workgroups read each
 // head's W^UV, the less traffic).  Wavefront w = 4q + kb owns
-// output rows k = 32kb..32kb+31 and the contraction quarter c = 128q..128q+127,
-// whose W^UV fragments (8 KB) it loads first, so they arrive while the merge
-// runs.  Phase 1: wavefront w merges tile rows w, w + 16 (lane = 8 columns): a row's
+// output rows k = 32kb..32kb+31 and the contraction quarter c = 128q..128q+127.
+// Phase 0: the head's whole W^UV_i (128 rows x 1 KB) is copied into LDS by
+// direct-to-LDS loads issued before anything else (8 rows per wavefront; chunk
+// c of row k at slot c ^ (k & 15), so the fragment reads are conflict-free), so
+// the weight and the split partials stream from memory at the same time
+// (measured: 8.7% less time than loading the fragments into registers after
+// the merge).  Phase 1: wavefront w merges tile rows w, w + 16 (lane = 8 columns): a row's
 // split lse values are loaded lane-parallel together with its first 8 partials
 // (two memory round trips for up to 8 splits), into an LDS copy of the R rows
 // (bf16, 16-byte chunk j of row r at slot j ^ (r & 15): conflict-free for the
-// row writes and the MFMA operand reads).  Phase 2: 8 MFMAs per wavefront (for
+// row writes and the MFMA operand reads).  Phase 2: after the weight loads are
+// waited for, 8 MFMAs per wavefront (for
 // R = 16 the 32-wide batch operand repeats the 16 rows and only the first 16
 // columns are stored); quarters 1-3 pass their fp32 partial products through
-// LDS and quarter 0 adds them in order and stores bf16.
+// LDS (the weight area, once every wavefront has read its fragments) and
+// quarter 0 adds them in order and rounds to bf16 into LDS, from where the
+// output rows are stored whole.
 #include "kernels.cuh"
 
 namespace mla {
@@ -115,22 +122,37 @@ __device__ __forceinline__ bf16x8 mp_merge_row(const MergeArgs& a, int b, int he
 template <int R>
 __global__ __launch_bounds__(64 * kMPWaves) void merge_proj_kernel(MergeArgs a, const uint16_t* __restrict__ w,
                                                                    uint16_t* __restrict__ out, int batch) {
+  __shared__ __attribute__((aligned(1024))) char wl[kMPH * 1024];
   __shared__ __attribute__((aligned(1024))) char rows[R * 1024];
-  __shared__ __attribute__((aligned(1024))) float red[12 * 1024];
+  float MLA_LDS* const red = (float MLA_LDS*)(uintptr_t)uint32_t(reinterpret_cast<uintptr_t>(wl));
   const int i = blockIdx.x, bt = blockIdx.y * R;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, h = lane >> 5;
   const int kb = wave & 3, cq = wave >> 2;
-  // W^UV fragments of this wavefront: row 32kb + (lane & 31), columns 128cq + 16kk + 8h;
-  // loaded before the merge (R = 16) or after it (R = 32: two rows' merge state
-  // and the fragments do not fit the register budget together)
-  bf16x8 wa[8];
-  auto load_w = [&]() {
-    const bf16x8* wr = reinterpret_cast<const bf16x8*>(w + (int64_t(i) * kMPH + 32 * kb + (lane & 31)) * kMPL +
-                                                       128 * cq + 8 * h);
+  // W^UV_i into LDS: wavefront w copies rows 8w..8w+7, one 1 KB row per load;
+  // lane l of row k's load reads chunk l ^ (k & 15), which lands in slot l.
+  // Untracked by the compiler (inline assembly): waited for before the barrier
+  // that precedes the fragment reads.
+  const uint32_t w_lds = uint32_t(reinterpret_cast<uintptr_t>(wl));
+  {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const uint64_t base = reinterpret_cast<uint64_t>(w + int64_t(i) * kMPH * kMPL);
+    typedef int i32x4 __attribute__((ext_vector_type(4)));
+    i32x4 rsrc;
+    rsrc[0] = uniform(int(uint32_t(base)));
+    rsrc[1] = uniform(int(uint32_t(base >> 32) & 0xFFFFu));
+    rsrc[2] = kMPH * kMPL * 2;
+    rsrc[3] = int(0x00020000u);
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) wa[kk] = wr[2 * kk];
-  };
-  if (R == 16) load_w();
+    for (int j = 0; j < 8; ++j) {
+      const int k = 8 * wave + j;
+      const int voff = (ln ^ (k & 15)) * 16;
+      const int m0 = uniform(int(w_lds + uint32_t(k * 1024)));
+      const int soff = uniform(k * 1024);
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                   : : "s"(m0), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+    }
+  }
   const uint32_t rows_lds = uint32_t(reinterpret_cast<uintptr_t>(rows));
 #pragma unroll
   for (int r = wave; r < R; r += kMPWaves) {
@@ -138,8 +160,19 @@ __global__ __launch_bounds__(64 * kMPWaves) void merge_proj_kernel(MergeArgs a, 
     const bf16x8 o = b < batch ? mp_merge_row(a, b, i, lane) : bf16x8{};
     *reinterpret_cast<bf16x8 MLA_LDS*>((char MLA_LDS*)(uintptr_t)(rows_lds + mp_row_off(r, lane))) = o;
   }
-  if (R == 32) load_w();
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   __syncthreads();
+  // W^UV fragments of this wavefront: row 32kb + (lane & 31), columns 128cq + 16kk + 8h
+  bf16x8 wa[8];
+  {
+    const int kr = 32 * kb + (lane & 31);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const int c = 16 * cq + 2 * kk + h;
+      wa[kk] = *reinterpret_cast<const bf16x8 MLA_LDS*>(
+          (const char MLA_LDS*)(uintptr_t)(w_lds + uint32_t(kr * 1024 + ((c ^ (kr & 15)) * 16))));
+    }
+  }
   // o_lat^T fragment of k-step kk: row lane % R, columns 128cq + 16kk + 8h (chunk 16cq + 2kk + h)
   f32x16 acc = {};
 #pragma unroll
@@ -148,6 +181,7 @@ __global__ __launch_bounds__(64 * kMPWaves) void merge_proj_kernel(MergeArgs a, 
         (const char MLA_LDS*)(uintptr_t)(rows_lds + mp_row_off(lane & (R - 1), 16 * cq + 2 * kk + h)));
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[kk], bo, acc, 0, 0, 0);
   }
+  __syncthreads();   // every wavefront has read its weight fragments (red reuses that area)
   // red: quarter q (1..3) of row block kb at (4(q-1) + kb) * 1024 floats, [q4][lane] f32x4
   if (cq > 0) {
     float MLA_LDS* dst = (float MLA_LDS*)red + (4 * (cq - 1) + kb) * 1024 + lane * 4;
@@ -169,18 +203,28 @@ __global__ __launch_bounds__(64 * kMPWaves) void merge_proj_kernel(MergeArgs a, 
       }
     }
     // D[k][b]: lane holds b = lane & 31 (for R = 16 columns 16-31 repeat 0-15),
-    // k = 8(e/4) + 4h + e%4 of the row block
-    const int bq = bt + (lane & 31);
-    if ((lane & 31) < R && bq < batch) {
-      uint16_t* o = out + (int64_t(bq) * a.n_heads + i) * kMPH + 32 * kb + 4 * h;
+    // k = 8(e/4) + 4h + e%4 of the row block.  Staged in the (no longer read)
+    // row area as [b][128 k] bf16, 16-byte chunk c of row b at slot c ^ (b & 15),
+    // so that the global stores below are whole 256-byte rows.
+    const int b = lane & 31;
+    if (b < R) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         bf16x4 v;
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = (__bf16)acc[4 * q4 + e];
-        *reinterpret_cast<bf16x4*>(o + 8 * q4) = v;
+        const int c = 4 * kb + q4;
+        *reinterpret_cast<bf16x4 MLA_LDS*>((char MLA_LDS*)(uintptr_t)(rows_lds + uint32_t(b * 256 + ((c ^ (b & 15)) * 16) + 8 * h))) = v;
       }
     }
+  }
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (t < R * 16) {
+    const int r = t >> 4, c = t & 15;
+    if (bt + r < batch)
+      *reinterpret_cast<bf16x8*>(out + (int64_t(bt + r) * a.n_heads + i) * kMPH + c * 8) =
+          *reinterpret_cast<const bf16x8 MLA_LDS*>((const char MLA_LDS*)(uintptr_t)(rows_lds + uint32_t(r * 256 + ((c ^ (r & 15)) * 16))));
   }
 }
 
