@@ -52,7 +52,10 @@ def traffic_json(workload: str) -> str:
 WORKLOADS = {
     # name: (synth config id, description, partition (split_tokens, num_parts))
     "ragged": (3, "v2_bf16_ragged_b64_t1024-8192", (0, -1)),
-    "long": (4, "v2_bf16_long_b4_t131072_split4096", (4096, 0)),
+    # one work item per compute unit (64 per sequence); the fixed 4096-token
+    # split of the parity cases gives 128 items, half the compute units
+    # (--partition 4096 0)
+    "long": (4, "v2_bf16_long_b4_t131072", (0, -1)),
     "fp8": (5, "v2_fp8_b32_t16384", (0, -1)),
     "v2b1": (2, "v2_bf16_b1_t4096", (0, -1)),
     # the ragged batch with two new query tokens per sequence (causal within them)
@@ -214,6 +217,9 @@ def run(args):
     import torch
     import mla_latent_kv_37_amd as mk
     cid, wname, (split, parts) = WORKLOADS[args.workload]
+    if args.partition is not None:
+        split, parts = args.partition
+        wname += f"_part{split}x{parts}"
     q_len = Q_LEN.get(args.workload, 1)
     torch.cuda.set_device(0)
     mk._lib.load()
@@ -761,6 +767,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--workload", default="ragged", choices=sorted(WORKLOADS) + sorted(APPEND_WORKLOADS) + sorted(QUERY_WORKLOADS))
     ap.add_argument("--copies", type=int, default=2)
+    ap.add_argument("--partition", type=int, nargs=2, metavar=("SPLIT_TOKENS", "NUM_PARTS"), default=None,
+                    help="override the workload's partition (split_tokens, num_parts; -1 parts = one per compute unit)")
     ap.add_argument("--no-kernel-events", dest="kernel_events", action="store_false")
     ap.add_argument("--unfused", action="store_true",
                     help="run mla_merge_splits + mla_out_proj (mla_decode_multi + mla_out_proj) instead of "
