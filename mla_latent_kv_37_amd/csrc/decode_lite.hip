@@ -64,7 +64,9 @@ __host__ __device__ constexpr int lite_offset(int t, int c) {
 // The 18 loads of one tile: block (g, rb) = chunk group g (chunks 8g..8g+7) of
 // rows 8rb..8rb+7.  Lane l reads row 8rb + (l>>3), chunk 8g + ((l&7) ^ f(row)),
 // landing at LDS offset g*2048 + rb*1024 + 16*l.  Rows at or past `valid` read
-// as zeros (descriptor size).
+// as zeros (descriptor size).  The loads carry the non-temporal hint: the cache
+// is streamed once per step, and without the hint it evicts the data the step
+// reuses (measured: decode 66.0 -> 58.9 us, merge + out-proj 10.4 -> 9.3 us).
 __device__ __forceinline__ void lite_issue(const char* src, int valid, uint32_t buf) {
   int ln = threadIdx.x & 63;
   asm volatile("" : "+v"(ln));
@@ -86,7 +88,7 @@ __device__ __forceinline__ void lite_issue(const char* src, int valid, uint32_t 
       asm volatile(
           "s_mov_b32 m0, %0\n\t"
           "s_nop 0\n\t"
-          "buffer_load_dwordx4 %1, %2, %3 offen lds"
+          "buffer_load_dwordx4 %1, %2, %3 offen nt lds"
           :
           : "s"(m0), "v"(rb ? voff1 : voff0), "s"(rsrc), "s"(soff)
           : "memory", "m0");
