@@ -9,7 +9,9 @@ mla_merge_splits -> mla_out_proj, every input already resident in HBM.  The
 default workload is the ragged batch (B=64, cache lengths uniform in
 [1024, 8192], DeepSeek-V2 shapes, bf16 paged cache, pages in random order).
 Inputs are rotated over --copies full copies so that successive steps do not
-find their cache in the 256 MB Infinity Cache.
+find their cache in the 256 MB Infinity Cache, and W^UK / W^UV over at least
+512 MB of copies, so that every step reads its weights from HBM as a layer of a
+many-layer model does (--warm-weights reuses them).
 
 Prints one JSON line with the contract fields plus `roofline` (the decode
 kernel's algorithmic bytes per launch / its mean launch time, HIP events on the
@@ -237,8 +239,25 @@ def run(args):
         o_lat_m = step.o_lat.view(B, q_len, N_H, D_C)
         lse_m = step.lse.view(B, q_len, N_H)
 
+    # Weight copies rotated apart from the cache copies.  A layer's W^UK and W^UV
+    # were last read a whole forward pass earlier in a many-layer model, so by
+    # default every step reads its weights from HBM: the rotation holds at least
+    # 512 MB of weight copies (twice the 256 MB Infinity Cache).  --warm-weights
+    # reuses each input set's own weights instead.
+    if args.warm_weights:
+        wsets = [(st["W_UK"], st["W_UV"]) for st in sets]
+    else:
+        per_copy = sets[0]["W_UK"].numel() * 2 + sets[0]["W_UV"].numel() * 2
+        n_w = max(len(sets), -(-(512 << 20) // per_copy))
+        wsets = [(st["W_UK"], st["W_UV"]) for st in sets]
+        while len(wsets) < n_w:
+            wsets.append((sets[0]["W_UK"].clone(), sets[0]["W_UV"].clone()))
+    weight_rotation_mb = len(wsets) * (sets[0]["W_UK"].numel() + sets[0]["W_UV"].numel()) * 2 / 2**20
+
     def one(i, ev=None):
         s = sets[i % len(sets)]
+        w_uk, w_uv = wsets[i % len(wsets)]
+        s = dict(s, W_UK=w_uk, W_UV=w_uv)
         if ev is not None:
             ev[0].record(stream)
         step.absorb(s["q_nope"], s["W_UK"])
@@ -340,6 +359,8 @@ def run(args):
         "config": {"workload": wname, "batch": len(lens), "sum_cache_tokens": T, "cache_dtype": w.cache_dtype,
                    "heads": n_h, "d_latent": D_C, "d_rope": D_R, "page_size": 64,
                    "partition": {"split_tokens": split, "num_parts": parts}, "input_copies": args.copies,
+                   "weights": ("warm: each input set's own W^UK / W^UV" if args.warm_weights else
+                               f"cold: {len(wsets)} copies of W^UK / W^UV rotated ({weight_rotation_mb:.0f} MB)"),
                    "parallelism": "single GPU", "q_len": q_len},
     }
     step_s = ms_per_step * 1e-3
@@ -767,6 +788,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--workload", default="ragged", choices=sorted(WORKLOADS) + sorted(APPEND_WORKLOADS) + sorted(QUERY_WORKLOADS))
     ap.add_argument("--copies", type=int, default=2)
+    ap.add_argument("--warm-weights", action="store_true",
+                    help="reuse each input set's W^UK / W^UV (they may stay cached between steps)")
     ap.add_argument("--partition", type=int, nargs=2, metavar=("SPLIT_TOKENS", "NUM_PARTS"), default=None,
                     help="override the workload's partition (split_tokens, num_parts; -1 parts = one per compute unit)")
     ap.add_argument("--no-kernel-events", dest="kernel_events", action="store_false")
