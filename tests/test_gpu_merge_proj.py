@@ -140,3 +140,40 @@ def test_fused_against_oracle_sharp():
             err = rel_err(got, ref)
             print(f"  b={b} {name}: rel err {err:.3e}", flush=True)
             assert err <= TOL["bf16"], (b, name)
+
+
+def test_fused_batch_100_and_absorb_second_tile():
+    """100 sequences: four 32-row merge tiles (the last ragged) and two 64-row
+    absorb tiles (the second ragged); fused against unfused, and the absorbed
+    queries and outputs of rows in every tile against the oracle."""
+    import torch
+    rng = np.random.default_rng(9)
+    lens = [int(x) for x in rng.integers(0, 300, size=100)]
+    lens[0] = lens[64] = lens[99] = 0
+    lens[63], lens[65], lens[98] = 290, 1, 257
+    case = direct_case(3, lens, max_pages=5, seed=87)
+    dev = to_device(case)
+    print(f"case: V2 bf16 B=100 lens {lens}", flush=True)
+    fused, unfused = _both(case, dev, (0, -1))
+    _check(fused, unfused, exact_heads=False)
+    import mla_latent_kv_37_amd as mk
+    d = case.dims
+    step = mk.DecodeStep(d.n_heads, d.d_head, d.d_rope, d.d_latent, len(lens), dev["cache"].max_pages,
+                         dev["cache"].page_size, 0, -1, act_dtype=dev["dtype"])
+    step.absorb(dev["q_nope"], dev["W_UK"])
+    torch.cuda.synchronize()
+    q_lat = host(step.q_lat)
+    o_lat, lse, o_heads = (host(t) for t in fused)
+    heads = [0, 31, 64, 127]
+    for b in (64, 99):   # empty sequences: zero output, lse = -inf
+        assert np.all(o_lat[b] == 0) and np.all(np.isneginf(lse[b])), b
+    for b in (1, 63, 65, 98):
+        r = case.reference(b, heads=heads)
+        err = rel_err(q_lat[b][heads], r["q_lat"][heads])
+        print(f"  b={b} q_lat: rel err {err:.3e}", flush=True)
+        assert err <= TOL["bf16"], b
+        for name, got, ref in (("o_lat", o_lat[b][heads], r["o_lat"][heads]),
+                               ("o_heads", o_heads[b].reshape(d.n_heads, d.d_head)[heads], r["o_heads"][heads])):
+            err = rel_err(got, ref)
+            print(f"  b={b} {name}: rel err {err:.3e}", flush=True)
+            assert err <= TOL["bf16"], (b, name)
