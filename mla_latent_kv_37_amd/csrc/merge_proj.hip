@@ -43,19 +43,12 @@ __device__ __forceinline__ uint32_t mp_row_off(int r, int chunk) {
   return uint32_t(r * 1024 + ((chunk ^ (r & 15)) * 16));
 }
 
-// Merged (or single-split) row b of head `head`, 8 columns per lane; writes
-// o_lat / lse for sequences that were split or are empty, like merge_kernel.
-__device__ __forceinline__ bf16x8 mp_merge_row(const MergeArgs& a, int b, int head, int lane) {
+// Split slots of row b: [first, first + count); count 0 for an empty sequence.
+__device__ __forceinline__ void mp_splits(const MergeArgs& a, int b, int& first, int& count) {
   const int T = load_const(a.seq_lens, b);
-  const int64_t out_row = int64_t(b) * a.n_heads + head;
-  uint16_t* const orow = static_cast<uint16_t*>(a.o_lat) + out_row * kMPL + lane * 8;
-  bf16x8 o = {};
-  if (T <= 0) {
-    *reinterpret_cast<bf16x8*>(orow) = o;
-    if (lane == 0 && a.lse != nullptr) a.lse[out_row] = -INFINITY;
-    return o;
-  }
-  int first = 0, count = 1;
+  first = 0;
+  count = T > 0 ? 1 : 0;
+  if (T <= 0) return;
   if (a.pp.mode == PART_FIXED) {
     count = ceil_div(T, a.pp.split_tokens);
     first = b * a.pp.fixed_slots;
@@ -63,6 +56,44 @@ __device__ __forceinline__ bf16x8 mp_merge_row(const MergeArgs& a, int b, int he
     const int wf = load_const(a.meta, b), wl = load_const(a.meta, int64_t(a.pp.batch) + b);
     count = wl - wf + 1;
     first = wf + b;
+  }
+}
+
+// A wavefront with no row of its own (tiles with fewer rows than wavefronts)
+// reads split partials 8 + j, 8 + j + nh, ... of row b (the owner's first 8 go
+// out with its lse loads) and discards them, so that the owner's later 8-split
+// chunks find them in L2.  The owner's arithmetic is unchanged.
+__device__ __forceinline__ void mp_touch_row(const MergeArgs& a, int b, int head, int lane, int j, int nh) {
+  int first, count;
+  mp_splits(a, b, first, count);
+  if (count <= 8) return;
+  const int64_t stride = int64_t(a.n_heads) * kMPL;
+  const uint16_t* const src0 = static_cast<const uint16_t*>(a.o_part) + (int64_t(first) * a.n_heads + head) * kMPL + lane * 8;
+  uint32_t sink = 0;
+  int n = 0;
+  for (int s = 8 + j; s < count; s += nh) {
+    const bf16x8 x = *reinterpret_cast<const bf16x8*>(src0 + s * stride);
+    sink ^= __builtin_bit_cast(uint32_t, __builtin_shufflevector(x, x, 0, 1));
+    if (++n == 8) {
+      asm volatile("" : : "v"(sink));
+      n = 0;
+    }
+  }
+  asm volatile("" : : "v"(sink));
+}
+
+// Merged (or single-split) row b of head `head`, 8 columns per lane; writes
+// o_lat / lse for sequences that were split or are empty, like merge_kernel.
+__device__ __forceinline__ bf16x8 mp_merge_row(const MergeArgs& a, int b, int head, int lane) {
+  const int64_t out_row = int64_t(b) * a.n_heads + head;
+  uint16_t* const orow = static_cast<uint16_t*>(a.o_lat) + out_row * kMPL + lane * 8;
+  bf16x8 o = {};
+  int first, count;
+  mp_splits(a, b, first, count);
+  if (count == 0) {
+    *reinterpret_cast<bf16x8*>(orow) = o;
+    if (lane == 0 && a.lse != nullptr) a.lse[out_row] = -INFINITY;
+    return o;
   }
   // one work item covered the sequence: mla_decode wrote the final row
   if (count <= 1) return *reinterpret_cast<const bf16x8*>(orow);
@@ -154,6 +185,14 @@ __global__ __launch_bounds__(64 * kMPWaves) void merge_proj_kernel(MergeArgs a, 
     }
   }
   const uint32_t rows_lds = uint32_t(reinterpret_cast<uintptr_t>(rows));
+  {
+    const int nvalid = min(R, batch - bt);
+    if (nvalid < kMPWaves && wave >= nvalid) {
+      const int hw = wave - nvalid, r = hw % nvalid;
+      const int nh = (kMPWaves - nvalid - r + nvalid - 1) / nvalid;
+      mp_touch_row(a, bt + r, i, lane, hw / nvalid, nh);
+    }
+  }
 #pragma unroll
   for (int r = wave; r < R; r += kMPWaves) {
     const int b = bt + r;
