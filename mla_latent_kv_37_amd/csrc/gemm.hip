@@ -25,10 +25,13 @@ namespace mla {
 
 constexpr int kGemmTile = 64;    // weight rows and batch rows per workgroup
 constexpr int kGemmChunk = 64;   // k per chunk
-// chunks in flight per thread (registers): 2 rather than 8 leaves room for
-// more resident workgroups (query prep measured 52.5 us against 59.6 us)
-constexpr int kGemmDepth = 2;
-
+// kGemmDepth: chunks in flight per thread beyond the one being stored
+// (registers).  Few chunks leave room for more resident workgroups: 8 chunks
+// held 172 VGPRs (2 wavefronts per SIMD), 2 hold 66 and 1 holds 49 (5).
+// Measured: query prep (384 workgroups) 59.6 us with 8, 52.9 with 2, 50.6
+// with 1; the cache append (72 workgroups) and the fused query product (1152
+// workgroups) are faster with 2 (16.1 vs 18.0 us; 97.9 vs 105.7 us).
+template <int kGemmDepth>
 __global__ __launch_bounds__(256) void gemm_ws_mfma_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t lw[2][kGemmTile * kGemmChunk];
   __shared__ __attribute__((aligned(16))) uint16_t lx[2][kGemmTile * kGemmChunk];
@@ -77,8 +80,10 @@ __global__ __launch_bounds__(256) void gemm_ws_mfma_kernel(GemmArgs a) {
 #pragma unroll
     for (int d = 0; d < kGemmDepth; ++d) {
       const int c = c0 + d;
-      uint16_t MLA_LDS* bw = (uint16_t MLA_LDS*)lw[d & 1];
-      uint16_t MLA_LDS* bx = (uint16_t MLA_LDS*)lx[d & 1];
+      // chunk c goes to buffer c & 1: the buffer it overwrites was last read
+      // for chunk c - 2, before the barrier of chunk c - 1
+      uint16_t MLA_LDS* bw = (uint16_t MLA_LDS*)lw[c & 1];
+      uint16_t MLA_LDS* bx = (uint16_t MLA_LDS*)lx[c & 1];
       *reinterpret_cast<bf16x8 MLA_LDS*>(bw + so0) = rw0[d];
       *reinterpret_cast<bf16x8 MLA_LDS*>(bw + so1) = rw1[d];
       *reinterpret_cast<bf16x8 MLA_LDS*>(bx + so0) = rx0[d];
@@ -135,10 +140,14 @@ void gemm_ws_plan(GemmArgs& a, int max_slices) {
 }
 
 hipError_t launch_gemm_ws(const GemmArgs& a, hipStream_t st) {
-  if (a.use_mfma)
-    gemm_ws_mfma_kernel<<<dim3(a.N / kGemmTile, a.slices, ceil_div(a.batch, kGemmTile)), 256, 0, st>>>(a);
-  else
+  if (a.use_mfma) {
+    const dim3 grid(a.N / kGemmTile, a.slices, ceil_div(a.batch, kGemmTile));
+    const int64_t wgs = int64_t(grid.x) * grid.y * grid.z;
+    if (wgs >= 256 && wgs <= 512) gemm_ws_mfma_kernel<1><<<grid, 256, 0, st>>>(a);
+    else gemm_ws_mfma_kernel<2><<<grid, 256, 0, st>>>(a);
+  } else {
     gemm_ws_generic_kernel<<<dim3(a.batch, ceil_div(a.N, 256)), 256, 0, st>>>(a);
+  }
   return hipGetLastError();
 }
 
