@@ -12,9 +12,10 @@
 // ([DeepSeek-V2 explainer] §2.2.2: W^UV applied after attention), as
 // o^T [k x b] = W^UV_i [k x c] . o_lat^T [c x b] on v_mfma_f32_32x32x16_bf16.
 //
-// Workgroup of 16 wavefronts for R = 16 or 32 sequences (32 when that still
-// gives at least one workgroup per compute unit: the fewer workgroups read each
-// head's W^UV, the less traffic).  Wavefront w = 4q + kb owns
+// Workgroup of 16 wavefronts for R = 8, 16 or 32 sequences (the largest that
+// still gives about one workgroup per compute unit: the fewer workgroups read
+// each head's W^UV, the less traffic; 8 rows only for few heads, as in
+// V2-Lite, where it took the kernel from 9.4 to 8.8 us).  Wavefront w = 4q + kb owns
 // output rows k = 32kb..32kb+31 and the contraction quarter c = 128q..128q+127.
 // Phase 0: the head's whole W^UV_i (128 rows x 1 KB) is copied into LDS by
 // direct-to-LDS loads issued before anything else (8 rows per wavefront; chunk
@@ -27,7 +28,7 @@
 // (bf16, 16-byte chunk j of row r at slot j ^ (r & 15): conflict-free for the
 // row writes and the MFMA operand reads).  Phase 2: after the weight loads are
 // waited for, 8 MFMAs per wavefront (for
-// R = 16 the 32-wide batch operand repeats the 16 rows and only the first 16
+// R < 32 the 32-wide batch operand repeats the R rows and only the first R
 // columns are stored); quarters 1-3 pass their fp32 partial products through
 // LDS (the weight area, once every wavefront has read its fragments) and
 // quarter 0 adds them in order and rounds to bf16 into LDS, from where the
@@ -275,8 +276,10 @@ hipError_t launch_merge_proj(const MergeArgs& a, const void* w_uv, void* o_heads
   uint16_t* out = static_cast<uint16_t*>(o_heads);
   if (int64_t(a.n_heads) * ceil_div(batch, 32) >= cus)
     merge_proj_kernel<32><<<dim3(a.n_heads, ceil_div(batch, 32)), 64 * kMPWaves, 0, st>>>(a, w, out, batch);
-  else
+  else if (int64_t(a.n_heads) * ceil_div(batch, 16) >= cus / 2)
     merge_proj_kernel<16><<<dim3(a.n_heads, ceil_div(batch, 16)), 64 * kMPWaves, 0, st>>>(a, w, out, batch);
+  else
+    merge_proj_kernel<8><<<dim3(a.n_heads, ceil_div(batch, 8)), 64 * kMPWaves, 0, st>>>(a, w, out, batch);
   return hipGetLastError();
 }
 
