@@ -73,7 +73,7 @@ def decode_source_hash(workload: str = "ragged") -> str:
     traffic record is only reported for the code it was measured on)."""
     src = DECODE_KERNEL.get(workload, DEFAULT_DECODE_KERNEL)[0]
     h = hashlib.sha256()
-    for f in (src, "kernels.cuh", "mla_common.cuh", "partition.cuh"):
+    for f in (src, "kernels.h", "mla_common.h", "partition.h"):
         h.update(open(os.path.join(CSRC, f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -215,14 +215,24 @@ def cpu_baseline(config_id: int, budget_s: float = 15.0):
 # GPU timing
 # ---------------------------------------------------------------------------
 
-def run(args):
+def binding_roof(flops: float, nbytes: float):
+    """The roof that binds a kernel of `flops` and `nbytes` algorithmic work: the
+    larger of its HBM time (8 TB/s) and its bf16 MFMA time (2.5 PFLOP/s)."""
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+    t_mfma = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    return ("hbm", t_hbm) if t_hbm >= t_mfma else ("mfma", t_mfma)
+
+
+def run(args, workload=None, partition=None, cpu=True, copy_tbps=None):
     import torch
     import mla_latent_kv_37_amd as mk
-    cid, wname, (split, parts) = WORKLOADS[args.workload]
-    if args.partition is not None:
-        split, parts = args.partition
+    workload = workload or args.workload
+    partition = partition if partition is not None else args.partition
+    cid, wname, (split, parts) = WORKLOADS[workload]
+    if partition is not None:
+        split, parts = partition
         wname += f"_part{split}x{parts}"
-    q_len = Q_LEN.get(args.workload, 1)
+    q_len = Q_LEN.get(workload, 1)
     torch.cuda.set_device(0)
     mk._lib.load()
     w, lens, sets = make_inputs(cid, args.copies, q_len=q_len)
@@ -341,7 +351,8 @@ def run(args):
     w1.record(stream)
     torch.cuda.synchronize()
     warm_ms = w0.elapsed_time(w1) / args.steps
-    copy_tbps = measured_copy_tbps()
+    if copy_tbps is None:
+        copy_tbps = measured_copy_tbps()
     alg = algorithmic(lens, w.cache_dtype, q_len, n_h)
     T = sum(lens)
     value = T * args.steps / (total_ms * 1e-3)
@@ -369,12 +380,15 @@ def run(args):
     if q_len > 1:
         res["attended_kv_tokens_per_s"] = alg["attended_tokens"] / step_s
     res["step_TBps"] = alg["step_bytes"] / step_s / 1e12
+    res["step_TFLOPs"] = alg["step_flops"] / step_s / 1e12
+    step_bound, step_roof_s = binding_roof(alg["step_flops"], alg["step_bytes"])
     res["step_roofline"] = {
         "hbm_us": alg["step_bytes"] / (HBM_PEAK_GBS * 1e9) * 1e6,
         "mfma_us": alg["step_flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12) * 1e6,
+        "bound": step_bound,
+        # the step's time at the binding roof over its measured time
+        "frac_of_min_roof": step_roof_s / step_s,
     }
-    roof_us = max(res["step_roofline"].values())
-    res["step_roofline"]["frac_of_min_roof"] = roof_us / (ms_per_step * 1e3)
     res["warm_ms_per_step"] = warm_ms
     res["measured_copy_TBps"] = copy_tbps
     if per_kernel:
@@ -386,13 +400,22 @@ def run(args):
         dec_s = per_kernel[dec_name] * 1e-3
         ach = alg["decode_bytes"] / dec_s / 1e9
         traffic = None
-        if os.path.exists(traffic_json(args.workload)):
-            tj = json.load(open(traffic_json(args.workload)))
-            if tj.get("decode_source_sha") == decode_source_hash(args.workload) and tj.get("workload") == wname:
+        if os.path.exists(traffic_json(workload)):
+            tj = json.load(open(traffic_json(workload)))
+            if tj.get("decode_source_sha") == decode_source_hash(workload) and tj.get("workload") == wname:
                 traffic = tj.get("decode_bytes_per_launch")
         res["decode_frac_of_measured_copy"] = ach / (copy_tbps * 1e3)
-        res["roofline"] = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                           "frac": ach / HBM_PEAK_GBS, "traffic": traffic,
+        # the decode kernel against its binding roof: HBM for the bf16 cache at one
+        # query token (242 flop/B, under the 312 flop/B ridge); bf16 MFMA for the
+        # fp8 cache (467 flop/B) and for several new tokens per sequence
+        bound, _ = binding_roof(alg["decode_flops"], alg["decode_bytes"])
+        if bound == "hbm":
+            r_ach, r_peak, r_unit = ach, HBM_PEAK_GBS, "GB/s"
+        else:
+            r_ach, r_peak, r_unit = alg["decode_flops"] / dec_s / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
+        res["roofline"] = {"bound": bound, "achieved": r_ach, "peak": r_peak, "unit": r_unit,
+                           "frac": r_ach / r_peak, "traffic": traffic,
+                           "hbm_GBps": ach, "hbm_frac": ach / HBM_PEAK_GBS,
                            "kernel": ("decode_v2_kernel<true> (fp8 cache)" if cid == 5 else
                                       "decode_lite_kernel (16 heads, bf16 cache)" if n_h == 16 else
                                       "decode_v2_kernel<false> (bf16 cache)") +
@@ -400,12 +423,39 @@ def run(args):
                                        " + expand_kernel + merge_proj_kernel (mla_decode_multi_out_proj; the "
                                        "time includes the W^UV projection)") if q_len > 1 else ""),
                            "algorithmic_bytes_per_launch": alg["decode_bytes"],
+                           "algorithmic_flops_per_launch": alg["decode_flops"],
                            "mean_launch_ms": per_kernel[dec_name],
                            "mfma_frac": alg["decode_flops"] / dec_s / (MFMA_BF16_PEAK_TFLOPS * 1e12)}
     res["wall_s_timed"] = wall
-    if not args.no_cpu_baseline and q_len == 1:
+    if cpu and not args.no_cpu_baseline and q_len == 1:
         res["cpu_baseline"] = cpu_baseline(cid, args.cpu_budget)
+    del sets, wsets
+    torch.cuda.empty_cache()
     return res
+
+
+# the other workloads that the default run times as well (sub-objects of the one
+# JSON line): (name, workload, partition override)
+EXTRA_WORKLOADS = (
+    ("v2_bf16_b1_t4096", "v2b1", None),
+    ("v2_bf16_long_b4_t131072", "long", None),
+    ("v2_bf16_long_b4_t131072_split4096", "long", (4096, 0)),
+    ("v2_fp8_b32_t16384", "fp8", None),
+)
+
+
+def summary(r):
+    """The per-workload figures kept in the headline line's `other_workloads`."""
+    out = {k: r[k] for k in ("value", "unit", "ms_per_step", "query_tokens_per_s", "cache_tokens_per_s",
+                             "step_TBps", "step_TFLOPs", "step_roofline", "warm_ms_per_step") if k in r}
+    out["config"] = {k: r["config"][k] for k in ("workload", "batch", "sum_cache_tokens", "cache_dtype",
+                                                 "partition")}
+    if "roofline" in r:
+        out["roofline"] = {k: r["roofline"][k] for k in ("bound", "achieved", "peak", "unit", "frac", "hbm_GBps",
+                                                         "mean_launch_ms", "kernel")}
+    if "kernel_ms" in r:
+        out["kernel_ms"] = r["kernel_ms"]
+    return out
 
 
 # ---------------------------------------------------------------------------
@@ -797,6 +847,8 @@ def main():
                     help="run mla_merge_splits + mla_out_proj (mla_decode_multi + mla_out_proj) instead of "
                          "mla_merge_out_proj (mla_decode_multi_out_proj), for comparison")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="time the ragged workload alone (no other decode workloads first)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
     ap.add_argument("--summarize-stats", nargs=2, metavar=("DIR", "OUT_MD"))
@@ -820,6 +872,18 @@ def main():
         res = run_append(args)
     elif args.workload in QUERY_WORKLOADS:
         res = run_query(args)
+    elif args.workload == "ragged" and args.partition is None and not args.headline_only:
+        # The default run: the other decode workloads first (each with its own
+        # warm-up and K timed steps), then the headline ragged batch, so that the
+        # headline is timed at the clocks a GPU that has been decoding holds.
+        copy_tbps = measured_copy_tbps()
+        others = {}
+        for name, wl, part in EXTRA_WORKLOADS:
+            r = run(args, wl, part, cpu=False, copy_tbps=copy_tbps)
+            others[name] = summary(r)
+            print(f"# {name}: {r['ms_per_step'] * 1e3:.1f} us/step, {r['value'] / 1e9:.3f} G {r['unit']}", flush=True)
+        res = run(args, copy_tbps=copy_tbps)
+        res["other_workloads"] = others
     else:
         res = run(args)
     print(json.dumps(res), flush=True)

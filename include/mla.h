@@ -86,6 +86,10 @@ typedef struct {
  *            in [0, num_pages).
  *   seq_lens: [batch] int32, 0 <= seq_lens[b] <= max_pages_per_seq * page_size.
  * Slots past a sequence's length are never read (they may hold NaN).
+ * Input that breaks these rules does not make a kernel read or write outside
+ * the arrays: lengths are clamped to [0, max_pages_per_seq * page_size], and a
+ * page id outside [0, num_pages) reads as a page of zero rows (decode) or is
+ * skipped (cache store).  mla_validate_cache_host checks the rules on the host.
  */
 typedef struct {
   const void* kv;
@@ -324,6 +328,26 @@ mla_status_t mla_query_prep(const mla_dims_t* dims, int32_t d_model, int32_t d_q
                             const void* h, mla_dtype_t h_dt, const void* w_dq, const void* w_uq, const void* w_qr,
                             mla_dtype_t w_dt, const int32_t* positions, float rope_base, void* q_nope, void* q_pe,
                             mla_dtype_t out_dt, void* scratch, size_t scratch_bytes, void* stream);
+
+/*
+ * Host check (no device access) of a paged cache's metadata, on host copies of
+ * its block table and lengths [DeepSeek-V2 explainer §2.1.1 names the paged KV
+ * memory; the layout is that of mla_paged_cache_t above]:
+ *   - 0 <= seq_lens_host[b] <= max_pages_per_seq * page_size, and
+ *   - every block-table entry the kernels read for sequence b (the first
+ *     ceil(seq_lens_host[b] / page_size) of its row) is in [0, num_pages).
+ *   block_table_host: [batch, max_pages_per_seq] int32; seq_lens_host: [batch].
+ * Returns MLA_OK, or MLA_ERR_INVALID_ARG with *bad_seq (if not NULL) set to the
+ * first sequence that breaks a rule (-1 when the arguments themselves are
+ * invalid: null pointers, batch < 0, non-positive sizes).
+ * The device kernels never fault on such input (a length is clamped to its
+ * row, a page id outside the cache reads as a page of zero rows) but their
+ * results for it are meaningless; call this where lengths or tables come from
+ * untrusted code.
+ */
+mla_status_t mla_validate_cache_host(const int32_t* block_table_host, const int32_t* seq_lens_host,
+                                     int32_t batch, int32_t max_pages_per_seq, int32_t page_size,
+                                     int32_t num_pages, int32_t* bad_seq);
 
 /*
  * Host helper (no device access): for host copies of seq_lens, the workspace

@@ -21,7 +21,7 @@ EXPORTS = ("mla_status_string", "mla_build_info", "mla_absorb_q", "mla_decode_wo
            "mla_lse_part_offset", "mla_decode", "mla_merge_splits", "mla_out_proj", "mla_cache_store",
            "mla_cache_append", "mla_query_prep_scratch_size", "mla_query_prep", "mla_partition_host",
            "mla_decode_multi_workspace_size", "mla_decode_multi", "mla_merge_out_proj",
-           "mla_decode_multi_out_proj")
+           "mla_decode_multi_out_proj", "mla_validate_cache_host")
 
 
 class MlaError(RuntimeError):
@@ -80,6 +80,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                           ctypes.c_float, P, P, ctypes.c_int, P, SZ, P]),
         "mla_partition_host": (ctypes.c_int, [ctypes.POINTER(I32), I32, I32, I32, PP, ctypes.POINTER(I32),
                                               ctypes.POINTER(I32)]),
+        "mla_validate_cache_host": (ctypes.c_int, [ctypes.POINTER(I32), ctypes.POINTER(I32), I32, I32, I32, I32,
+                                                   ctypes.POINTER(I32)]),
         "mla_decode_multi_workspace_size": (ctypes.c_int, [PD, I32, I32, I32, I32, PP, ctypes.POINTER(SZ),
                                                            ctypes.POINTER(I32)]),
         "mla_decode_multi": (ctypes.c_int, [PD, I32, I32, P, P, ctypes.c_int, PC, ctypes.c_float, PP, P, SZ, P,
@@ -289,3 +291,18 @@ def partition_host(seq_lens, page_size: int, max_pages: int, part: Partition):
     _check(load().mla_partition_host(lens.ctypes.data_as(I32P), b, page_size, max_pages, ctypes.byref(part),
                                      first.ctypes.data_as(I32P), count.ctypes.data_as(I32P)), "mla_partition_host")
     return first, count
+
+
+def validate_cache_host(block_table, seq_lens, page_size: int, num_pages: int) -> Tuple[int, int]:
+    """Host check of a cache's block table and lengths (numpy or CPU arrays):
+    returns (status, first offending sequence or -1)."""
+    import numpy as np
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    if bt.ndim != 2 or lens.ndim != 1 or bt.shape[0] != lens.shape[0]:
+        raise ValueError("block_table must be [batch, max_pages] and seq_lens [batch]")
+    bad = ctypes.c_int32(-1)
+    I32P = ctypes.POINTER(ctypes.c_int32)
+    st = load().mla_validate_cache_host(bt.ctypes.data_as(I32P), lens.ctypes.data_as(I32P), lens.shape[0],
+                                        bt.shape[1], page_size, num_pages, ctypes.byref(bad))
+    return int(st), int(bad.value)

@@ -6,7 +6,27 @@
 #include <cstdint>
 #include <cstring>
 
-#include "kernels.cuh"
+#include "kernels.h"
+
+namespace mla {
+
+// Plan of the weight-streaming product (gemm.hip): the MFMA kernel for bf16
+// operands on whole 64 x 64 tiles, with k slices until tiles x slices fill the
+// chip about twice (two workgroups per compute unit).
+int gemm_ws_slices(int N, int K, int batch, int max_slices) {
+  if (N % kGemmTile != 0 || K % kGemmChunk != 0) return 1;
+  const int tiles = (N / kGemmTile) * ceil_div(batch > 1 ? batch : 1, kGemmTile);
+  for (int sl : {16, 8, 4, 2})
+    if (sl <= max_slices && K % (kGemmChunk * sl) == 0 && tiles * sl <= 512) return sl;
+  return 1;
+}
+
+void gemm_ws_plan(GemmArgs& a, int max_slices) {
+  a.use_mfma = a.x_dt == MLA_BF16 && a.w_dt == MLA_BF16 && a.N % kGemmTile == 0 && a.K % kGemmChunk == 0;
+  a.slices = a.use_mfma ? gemm_ws_slices(a.N, a.K, a.batch, max_slices) : 1;
+}
+
+}  // namespace mla
 
 namespace {
 
@@ -38,6 +58,10 @@ mla_status_t resolve(const mla_dims_t* /*dims*/, int32_t batch, int32_t max_page
   PartParams p{};
   p.page_size = page_size;
   p.batch = batch;
+  {
+    const int64_t mt = int64_t(max_pages) * page_size;
+    p.max_tokens = mt > INT32_MAX ? INT32_MAX : int(mt);
+  }
   const int split = part ? part->split_tokens : 0;
   const int parts = part ? part->num_parts : 0;
   if (split < 0) return MLA_ERR_INVALID_ARG;
@@ -254,6 +278,7 @@ mla_status_t decode_impl(const mla_dims_t* dims, int32_t batch, const void* q_la
     a.block_table = cache->block_table;
     a.seq_lens = cache->seq_lens;
     a.max_pages = cache->max_pages_per_seq;
+    a.num_pages = cache->num_pages;
     a.n_items = n_items;
     a.scale_log2 = softmax_scale * kLog2e;
     a.pp = pp;
@@ -275,6 +300,7 @@ mla_status_t decode_impl(const mla_dims_t* dims, int32_t batch, const void* q_la
     a.block_table = cache->block_table;
     a.seq_lens = cache->seq_lens;
     a.max_pages = cache->max_pages_per_seq;
+    a.num_pages = cache->num_pages;
     a.n_heads = dims->n_heads;
     a.d_rope = dims->d_rope;
     a.d_latent = dims->d_latent;
@@ -626,6 +652,27 @@ mla_status_t mla_query_prep(const mla_dims_t* dims, int32_t d_model, int32_t d_q
   f.out_dt = out_dt;
   if (e == hipSuccess) e = launch_query_finish(f, st);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status_t mla_validate_cache_host(const int32_t* block_table_host, const int32_t* seq_lens_host, int32_t batch,
+                                     int32_t max_pages_per_seq, int32_t page_size, int32_t num_pages,
+                                     int32_t* bad_seq) {
+  if (bad_seq) *bad_seq = -1;
+  if (batch < 0 || max_pages_per_seq < 1 || page_size < 1 || num_pages < 1) return MLA_ERR_INVALID_ARG;
+  if (batch > 0 && (!block_table_host || !seq_lens_host)) return MLA_ERR_INVALID_ARG;
+  const int64_t max_tokens = int64_t(max_pages_per_seq) * page_size;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int32_t T = seq_lens_host[b];
+    bool ok = T >= 0 && int64_t(T) <= max_tokens;
+    const int64_t np = ok ? (int64_t(T) + page_size - 1) / page_size : 0;
+    const int32_t* row = block_table_host + int64_t(b) * max_pages_per_seq;
+    for (int64_t p = 0; ok && p < np; ++p) ok = row[p] >= 0 && row[p] < num_pages;
+    if (!ok) {
+      if (bad_seq) *bad_seq = b;
+      return MLA_ERR_INVALID_ARG;
+    }
+  }
+  return MLA_OK;
 }
 
 mla_status_t mla_partition_host(const int32_t* seq_lens_host, int32_t batch, int32_t page_size,

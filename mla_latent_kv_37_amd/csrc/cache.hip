@@ -20,7 +20,7 @@
 //
 // The projection rows[b] = [W^DKV h_b ; W^KR h_b] of mla_cache_append is the
 // weight-streaming product of gemm.hip, in k slices that this kernel adds up.
-#include "kernels.cuh"
+#include "kernels.h"
 
 namespace mla {
 
@@ -33,11 +33,13 @@ __global__ __launch_bounds__(640) void cache_store_kernel(CacheStoreArgs a) {
   const int W = a.d_latent + a.d_rope;
   const int ng = (W + kGroup - 1) / kGroup;
   if (g >= ng) return;
+  // A position outside the block table or a page id outside the cache skips
+  // the cache write only: the projection slices are still summed into rows[b].
   const int pos = load_const(a.positions, b);
-  if (pos < 0 || pos >= a.max_pages * a.page_size) return;
-  const int page = load_const(a.block_table, int64_t(b) * a.max_pages + pos / a.page_size);
-  if (page < 0 || page >= a.num_pages) return;   // never write outside the cache
-  const int64_t row = int64_t(page) * a.page_size + pos % a.page_size;
+  const bool pos_ok = pos >= 0 && pos < a.max_pages * a.page_size;
+  const int page = pos_ok ? load_const(a.block_table, int64_t(b) * a.max_pages + pos / a.page_size) : -1;
+  const bool store = pos_ok && page >= 0 && page < a.num_pages;   // never write outside the cache
+  const int64_t row = int64_t(store ? page : 0) * a.page_size + (store ? pos % a.page_size : 0);
 
   const int c0 = g * kGroup + 2 * lane;
   const int gend = min(W, (g + 1) * kGroup);
@@ -57,7 +59,7 @@ __global__ __launch_bounds__(640) void cache_store_kernel(CacheStoreArgs a) {
       r0[0] = x0;
       r0[1] = x1;
     }
-    if (a.rope_base > 0.f && c0 >= a.d_latent) {
+    if (store && a.rope_base > 0.f && c0 >= a.d_latent) {
       const int k = (c0 - a.d_latent) >> 1;
       const double theta = pow(double(a.rope_base), -2.0 * k / double(a.d_rope));
       const double ang = double(pos) * theta;
@@ -67,6 +69,7 @@ __global__ __launch_bounds__(640) void cache_store_kernel(CacheStoreArgs a) {
       x1 = float(y1);
     }
   }
+  if (!store) return;
   if (a.kv_dt == MLA_F32) {
     if (live) {
       float* dst = static_cast<float*>(a.kv) + row * W + c0;

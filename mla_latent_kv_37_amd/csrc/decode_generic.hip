@@ -5,7 +5,7 @@
 //   s_j = (q_lat_i . c^KV_j + q^R_i . k^R_j) * scale        (absorbed score,
 //         [deepseek(2) 關鍵技術] §1 with [DeepSeek-V2 explainer] §2.2.2)
 // with an online softmax (running max m, running sum l) and o = sum_j p_j c^KV_j.
-#include "kernels.cuh"
+#include "kernels.h"
 
 namespace mla {
 
@@ -14,8 +14,10 @@ constexpr int kGenMaxRow = 1280;
 constexpr int kGenMaxCols = 4;  // d_latent <= 4 * 256
 
 
+// row < 0: a token of an out-of-range page, read as a zero row
 template <mla_dtype_t KV>
 __device__ __forceinline__ float cache_val(const GenericDecodeArgs& a, int64_t row, int c, int W, int ng) {
+  if (row < 0) return 0.f;
   float v = Elem<KV>::load(a.kv, row * W + c);
   if (KV == MLA_FP8_E4M3) v *= a.scales[row * ng + c / 128];
   return v;
@@ -66,7 +68,8 @@ __global__ __launch_bounds__(kGenThreads) void decode_generic_kernel(GenericDeco
       const int t = tt + tid;
       float s = -INFINITY;
       if (t < sg.t1) {
-        int64_t row = int64_t(bt[t / page]) * page + (t % page);
+        const int pid = bt[t / page];
+        const int64_t row = (pid >= 0 && pid < a.num_pages) ? int64_t(pid) * page + (t % page) : -1;
         rows[tid] = row;
         float acc = 0.f;
         for (int c = 0; c < W; ++c) acc += qs[c] * cache_val<KV>(a, row, c, W, ng);

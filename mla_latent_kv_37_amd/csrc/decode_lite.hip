@@ -7,7 +7,7 @@
 // only has to keep enough cache bytes in flight; the matrix work is small.
 //
 // Work decomposition.  A work item is a list of (sequence, token range)
-// segments (partition.cuh; ranges start on page boundaries).  One workgroup of
+// segments (partition.h; ranges start on page boundaries).  One workgroup of
 // 4 wavefronts (one per SIMD) serves an item; wavefront w takes quarter w
 // (tokens 16w..16w+15) of every page of the range and keeps its own online
 // softmax over them, so the tile loop has no barrier.  At the end of a segment
@@ -34,7 +34,7 @@
 //
 // Softmax in the log2 domain, with the running max raised lazily (rescale only
 // when it grows by more than 8), as in the 128-head kernel.
-#include "kernels.cuh"
+#include "kernels.h"
 
 namespace mla {
 
@@ -149,16 +149,22 @@ __global__ __launch_bounds__(kLThreads) void decode_lite_kernel(V2DecodeArgs a) 
     // page can have an empty quarter)
     const int last_valid = len - (npages - 1) * kLPage - kLTileTok * wave;
     const int ntl = last_valid > 0 ? npages : npages - 1;
+    // a page id outside [0, num_pages) reads as a page of zero rows (no
+    // address outside the cache is formed)
     auto tile_valid = [&](int k) { return k < npages - 1 ? kLTileTok : min(kLTileTok, last_valid); };
+    auto dma_valid = [&](int k) {   // rows the tile loads read (0: a zero tile)
+      return unsigned(load_const(bt, k)) < unsigned(a.num_pages) ? tile_valid(k) : 0;
+    };
     auto tile_src = [&](int k) {
-      return kv + int64_t(load_const(bt, k)) * kLPageBytes + wave * kLTileBytes;
+      const int pid = load_const(bt, k);
+      return kv + int64_t(unsigned(pid) < unsigned(a.num_pages) ? pid : 0) * kLPageBytes + wave * kLTileBytes;
     };
     auto tile_buf = [&](int k) { return buf0 + uint32_t((k & 1) * kLTileBytes); };
 
     // every wavefront is done with the previous segment's LDS use
     __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
     raw_barrier();
-    if (ntl > 0) lite_issue(tile_src(0), tile_valid(0), tile_buf(0));
+    if (ntl > 0) lite_issue(tile_src(0), dma_valid(0), tile_buf(0));
     // Q^T fragments (B operand): head hd, dims 32s + 8g .. +7 of [q_lat | q_pe]
     bf16x8 qf[18];
     {
@@ -173,7 +179,7 @@ __global__ __launch_bounds__(kLThreads) void decode_lite_kernel(V2DecodeArgs a) 
     // that the query registers are ready, so it puts no wait for them inside the
     // tile loop (where it would drain the tile prefetch)
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    if (ntl > 1) lite_issue(tile_src(1), tile_valid(1), tile_buf(1));
+    if (ntl > 1) lite_issue(tile_src(1), dma_valid(1), tile_buf(1));
     f32x4 acc[32];
 #pragma unroll
     for (int n = 0; n < 32; ++n) acc[n] = f32x4{};
@@ -238,7 +244,7 @@ __global__ __launch_bounds__(kLThreads) void decode_lite_kernel(V2DecodeArgs a) 
       // the buffer's reads are done before the next tile's loads overwrite it
       if (k + 2 < ntl) {
         __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
-        lite_issue(tile_src(k + 2), tile_valid(k + 2), tb);
+        lite_issue(tile_src(k + 2), dma_valid(k + 2), tb);
       }
     }
 

@@ -9,7 +9,7 @@
 //   O^T [512 x heads]   += V^T [512 x tokens] . P^T [tokens x heads]
 //
 // Work decomposition.  A work item is a list of (sequence, token range)
-// segments (partition.cuh); one workgroup of 8 wavefronts serves one work item
+// segments (partition.h); one workgroup of 8 wavefronts serves one work item
 // for all 128 heads.  Wavefronts w and w+4 run on the same SIMD.  Pair
 // p = w >> 1 (wavefronts 2p, 2p+1) owns heads 32p..32p+31; member d = w & 1
 // multiplies half of the 576 row dims for the scores (latent dims
@@ -49,7 +49,7 @@
 // FMA).  The running max is raised lazily: the accumulators are rescaled only
 // when a head's max grows by more than 8 (a factor 256), which keeps every
 // probability <= 256 in bf16 and fp32 and skips almost every rescale.
-#include "kernels.cuh"
+#include "kernels.h"
 
 namespace mla {
 
@@ -222,7 +222,11 @@ __device__ __forceinline__ void issue_tile_f8(const char* codes, const float* sc
   rc[3] = int(kBufferFlags);
   rs[0] = uniform(int(uint32_t(sb)));
   rs[1] = uniform(int(uint32_t(sb >> 32) & 0xFFFFu));
-  rs[2] = uniform(valid * kF8Groups * 4);
+  // whole 16-byte lane loads: the last valid row's scales end mid-load when
+  // valid % 4 != 0, so the range is rounded up (to at most the tile's 640
+  // bytes, inside the page); the extra scales belong to rows >= valid, which
+  // the dequantisation writes as zeros whatever they hold
+  rs[2] = uniform((valid * kF8Groups * 4 + 15) & ~15);
   rs[3] = int(kBufferFlags);
   const int i0 = f8_first_load(wave), nl = f8_num_loads(wave);
 #pragma unroll
@@ -252,8 +256,10 @@ __device__ __forceinline__ void wait_tile_f8(int wave, bool newer_in_flight) {
 // Dequantise a staged tile into a bf16 tile buffer.  Item i (0..2303) is one
 // bf16 chunk (8 values) of one row; 16 consecutive items cover 8 consecutive
 // chunks of one chunk group in 2 consecutive rows, so a 16-lane group of the
-// 16-byte LDS writes hits 16 distinct bank quads.
-__device__ __forceinline__ void convert_tile_f8(uint32_t stage, uint32_t buf) {
+// 16-byte LDS writes hits 16 distinct bank quads.  Rows t >= valid (past the
+// sequence end) are written as zeros, not code * scale: their staged scales
+// may be anything.
+__device__ __forceinline__ void convert_tile_f8(uint32_t stage, uint32_t buf, int valid) {
 #pragma unroll
   for (int r = 0; r < 5; ++r) {
     const int i = r * kDecThreads + int(threadIdx.x);
@@ -273,6 +279,7 @@ __device__ __forceinline__ void convert_tile_f8(uint32_t stage, uint32_t buf) {
       v[2] = (__bf16)(f1[0] * sc); v[3] = (__bf16)(f1[1] * sc);
       v[4] = (__bf16)(f2[0] * sc); v[5] = (__bf16)(f2[1] * sc);
       v[6] = (__bf16)(f3[0] * sc); v[7] = (__bf16)(f3[1] * sc);
+      if (t >= valid) v = bf16x8{};
       *reinterpret_cast<bf16x8 MLA_LDS*>((char MLA_LDS*)(uintptr_t)(buf + uint32_t(tile_offset(t, c)))) = v;
     }
   }
@@ -368,13 +375,18 @@ void decode_v2_kernel(V2DecodeArgs a) {
     auto stage_buf = [&](int k) {
       return tiles_lds + uint32_t(kBufs * kTileBytes + (k % kF8NumBuf) * kF8StageBytes);
     };
+    // A page id outside [0, num_pages) is read as a page of zero rows: the
+    // loads then use page 0's address with an empty range.
     auto issue = [&](int k, int page_id) {
+      const bool ok = unsigned(page_id) < unsigned(a.num_pages);
+      const int pid = ok ? page_id : 0;
+      const int dv = ok ? tile_valid(k) : 0;
       if constexpr (kF8) {
-        const char* codes = kv + (int64_t(page_id) * kV2Page + (k & 1) * kTileTok) * kV2Row;
-        const float* sc = a.scales + (int64_t(page_id) * kV2Page + (k & 1) * kTileTok) * kF8Groups;
-        issue_tile_f8(codes, sc, tile_valid(k), stage_buf(k), wave);
+        const char* codes = kv + (int64_t(pid) * kV2Page + (k & 1) * kTileTok) * kV2Row;
+        const float* sc = a.scales + (int64_t(pid) * kV2Page + (k & 1) * kTileTok) * kF8Groups;
+        issue_tile_f8(codes, sc, dv, stage_buf(k), wave);
       } else {
-        issue_tile(tile_src(k, page_id), tile_valid(k), tile_buf(k), wave);
+        issue_tile(tile_src(k, pid), dv, tile_buf(k), wave);
       }
     };
 
@@ -422,7 +434,7 @@ void decode_v2_kernel(V2DecodeArgs a) {
     if constexpr (kF8) {
       // tile 0's staged codes visible to all, dequantised before slot 0
       raw_barrier();
-      convert_tile_f8(stage_buf(0), tile_buf(0));
+      convert_tile_f8(stage_buf(0), tile_buf(0), tile_valid(0));
     }
     if (kF8 && ntiles > 1) issue(1, page_first);
     // page of the next tile to issue (tile 2); loaded a slot before its use
@@ -450,7 +462,7 @@ void decode_v2_kernel(V2DecodeArgs a) {
         __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
         raw_barrier();
         if ((j & 1) && tc < ntiles) {
-          convert_tile_f8(stage_buf(tc), tile_buf(tc));
+          convert_tile_f8(stage_buf(tc), tile_buf(tc), tile_valid(tc));
         }
       } else {
         if ((j & 1) == 0 && j >= 2 && j / 2 < ntiles) wait_tile(wave, j / 2 + 1 < ntiles);

@@ -19,12 +19,10 @@
 // flight) publishes it.  Batch rows past the end are clamped to the last row
 // and not stored; batches above 64 take more workgroups along z, which read
 // the weights again (from the caches when they run together).
-#include "kernels.cuh"
+#include "kernels.h"
 
 namespace mla {
 
-constexpr int kGemmTile = 64;    // weight rows and batch rows per workgroup
-constexpr int kGemmChunk = 64;   // k per chunk
 // kGemmDepth: chunks in flight per thread beyond the one being stored
 // (registers).  Few chunks leave room for more resident workgroups: 8 chunks
 // held 172 VGPRs (2 wavefronts per SIMD), 2 hold 66 and 1 holds 49 (5).
@@ -123,20 +121,6 @@ __global__ __launch_bounds__(256) void gemm_ws_generic_kernel(GemmArgs a) {
   for (int k = 0; k < a.K; ++k)
     acc = __builtin_fmaf(load_any(a.x, int64_t(b) * a.K + k, a.x_dt), load_any(w, wr + k, a.w_dt), acc);
   a.out[int64_t(b) * a.N + n] = acc;
-}
-
-int gemm_ws_slices(int N, int K, int batch, int max_slices) {
-  if (N % kGemmTile != 0 || K % kGemmChunk != 0) return 1;
-  // k slices until tiles x slices fill the chip about twice (two workgroups per CU)
-  const int tiles = (N / kGemmTile) * ceil_div(max(batch, 1), kGemmTile);
-  for (int sl : {16, 8, 4, 2})
-    if (sl <= max_slices && K % (kGemmChunk * sl) == 0 && tiles * sl <= 512) return sl;
-  return 1;
-}
-
-void gemm_ws_plan(GemmArgs& a, int max_slices) {
-  a.use_mfma = a.x_dt == MLA_BF16 && a.w_dt == MLA_BF16 && a.N % kGemmTile == 0 && a.K % kGemmChunk == 0;
-  a.slices = a.use_mfma ? gemm_ws_slices(a.N, a.K, a.batch, max_slices) : 1;
 }
 
 hipError_t launch_gemm_ws(const GemmArgs& a, hipStream_t st) {

@@ -2,7 +2,7 @@
 // the kernel translation units.
 #pragma once
 
-#include "partition.cuh"
+#include "partition.h"
 
 namespace mla {
 
@@ -16,6 +16,7 @@ struct GenericDecodeArgs {
   const int32_t* block_table;
   const int32_t* seq_lens;
   int max_pages;
+  int num_pages;           // page ids outside [0, num_pages) read as empty pages
   int n_heads, d_rope, d_latent;
   float scale;
   PartParams pp;
@@ -36,6 +37,7 @@ struct V2DecodeArgs {
   const int32_t* block_table;
   const int32_t* seq_lens;
   int max_pages;
+  int num_pages;           // page ids outside [0, num_pages) read as empty pages
   int n_items;
   float scale_log2;        // softmax_scale * log2(e)
   PartParams pp;
@@ -102,9 +104,12 @@ struct QueryFinishArgs {
   mla_dtype_t out_dt;
 };
 
+constexpr int kGemmTile = 64;    // weight-streaming product: weight rows and batch rows per workgroup
+constexpr int kGemmChunk = 64;   // and k per chunk
 constexpr int kGemmMaxSlices = 8;      // k slices of mla_cache_append's projection (its scratch holds 8)
 constexpr int kQueryMaxSlices = 16;    // k slices of mla_query_prep's products
-// k slices of the MFMA plan for an N x K bf16 product over `batch` rows (1 for every other plan)
+// k slices of the MFMA plan for an N x K bf16 product over `batch` rows (1 for
+// every other plan); host code, in api.hip
 int gemm_ws_slices(int N, int K, int batch, int max_slices);
 void gemm_ws_plan(GemmArgs& a, int max_slices);   // chooses slices (<= max_slices) and the kernel
 hipError_t launch_gemm_ws(const GemmArgs& a, hipStream_t st);

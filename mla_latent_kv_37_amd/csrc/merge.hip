@@ -5,7 +5,7 @@
 // printed on the pages.  Partials are stored in the output dtype.  One
 // wavefront per (sequence, head); each lane owns d_c/64 consecutive columns
 // (8 for d_c = 512: one 16-byte load per partial in bf16, two in fp32).
-#include "kernels.cuh"
+#include "kernels.h"
 
 namespace mla {
 
@@ -19,7 +19,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(MergeArgs a) {
   const int head = blockIdx.y * kMergeWaves + threadIdx.x / 64;
   const int lane = threadIdx.x % 64;
   if (head >= a.n_heads) return;
-  const int T = load_const(a.seq_lens, b);
+  const int T = clamp_len(load_const(a.seq_lens, b), a.pp);
   const int64_t out_row = (int64_t(b) * a.n_heads + head);
   if (T <= 0) {
     for (int c = lane; c < a.d_latent; c += 64) store_any(a.o_lat, out_row * a.d_latent + c, 0.f, a.o_dt);

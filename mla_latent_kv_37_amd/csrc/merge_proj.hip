@@ -33,7 +33,7 @@
 // LDS (the weight area, once every wavefront has read its fragments) and
 // quarter 0 adds them in order and rounds to bf16 into LDS, from where the
 // output rows are stored whole.
-#include "kernels.cuh"
+#include "kernels.h"
 
 namespace mla {
 
@@ -46,7 +46,7 @@ __device__ __forceinline__ uint32_t mp_row_off(int r, int chunk) {
 
 // Split slots of row b: [first, first + count); count 0 for an empty sequence.
 __device__ __forceinline__ void mp_splits(const MergeArgs& a, int b, int& first, int& count) {
-  const int T = load_const(a.seq_lens, b);
+  const int T = clamp_len(load_const(a.seq_lens, b), a.pp);
   first = 0;
   count = T > 0 ? 1 : 0;
   if (T <= 0) return;

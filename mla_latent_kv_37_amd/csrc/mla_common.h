@@ -76,9 +76,18 @@ struct PartParams {
   int fixed_slots;    // PART_FIXED: slots per sequence S
   int page_size;
   int batch;
+  int max_tokens;     // max_pages_per_seq * page_size: longer lengths are read as this
 };
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// A sequence length as the kernels use it: clamped to [0, max_pages * page_size],
+// so that no kernel reads past the sequence's block-table row whatever seq_lens
+// holds (lengths outside that range are invalid input; mla_validate_cache_host
+// reports them).
+__host__ __device__ __forceinline__ int clamp_len(int T, const PartParams& pp) {
+  return T < 0 ? 0 : (T > pp.max_tokens ? pp.max_tokens : T);
+}
 
 // Read-only int32 metadata (block table, lengths) through the constant address
 // space: scalar loads, counted by lgkmcnt, so waiting for them never waits for

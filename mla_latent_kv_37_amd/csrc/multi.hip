@@ -16,7 +16,7 @@
 //
 // expand_kernel writes the virtual lengths and block table (one workgroup per
 // virtual sequence).
-#include "kernels.cuh"
+#include "kernels.h"
 
 namespace mla {
 

@@ -3,7 +3,7 @@
 // Three partitions (mla_partition_t):
 //   whole:    item b = sequence b.
 //   fixed:    item b*S + s = tokens [s*L, min((s+1)*L, T_b)) of sequence b.
-//   balanced: the cost stream of mla_common.cuh (the pages of all sequences in
+//   balanced: the cost stream of mla_common.h (the pages of all sequences in
 //             sequence order, kSegCost units between consecutive non-empty
 //             sequences; C units) is cut into W = min(num_parts, total pages)
 //             contiguous parts; item w takes units [floor(w*C/W),
@@ -16,7 +16,7 @@
 //             (parts are at least one unit long).
 #pragma once
 
-#include "mla_common.cuh"
+#include "mla_common.h"
 
 namespace mla {
 
@@ -59,7 +59,7 @@ struct SegmentIter {
     if (pp.mode != PART_BALANCED) return;
     const int B = pp.batch, page = pp.page_size;
     const int lane = threadIdx.x & 63;
-    auto pages_of = [&](int i) { return i < B ? ceil_div(max(seq_lens[i], 0), page) : 0; };
+    auto pages_of = [&](int i) { return i < B ? ceil_div(clamp_len(seq_lens[i], pp), page) : 0; };
     // total pages P and non-empty sequences m of the batch
     int P = 0, m = 0;
     for (int base = 0; base < B; base += 64) {
@@ -102,7 +102,7 @@ struct SegmentIter {
     if (pp.mode == PART_WHOLE) {
       done = true;
       if (item >= B) return false;
-      const int T = load_const(seq_lens, item);
+      const int T = clamp_len(load_const(seq_lens, item), pp);
       if (T <= 0) return false;
       sg = Segment{item, 0, T, -1, true};
       return true;
@@ -111,14 +111,14 @@ struct SegmentIter {
       done = true;
       const int bb = item / pp.fixed_slots, sp = item % pp.fixed_slots;
       if (bb >= B) return false;
-      const int T = load_const(seq_lens, bb);
+      const int T = clamp_len(load_const(seq_lens, bb), pp);
       const int n = ceil_div(T, pp.split_tokens);
       if (sp >= n) return false;
       sg = Segment{bb, sp * pp.split_tokens, min(T, (sp + 1) * pp.split_tokens), item, n == 1};
       return true;
     }
     while (b < B && S < p1) {
-      const int T = max(load_const(seq_lens, b), 0);
+      const int T = clamp_len(load_const(seq_lens, b), pp);
       const int np = ceil_div(T, page);
       const int64_t Sb = S;
       const int bb = b;

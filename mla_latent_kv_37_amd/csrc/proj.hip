@@ -7,7 +7,7 @@
 // Both are weight-streaming products (each weight element is used B times), so
 // they are bound by HBM; the V2-shape kernels run them on MFMA so the matrix
 // work stays far below the time to stream the 16.8 MB weight.
-#include "kernels.cuh"
+#include "kernels.h"
 
 namespace mla {
 

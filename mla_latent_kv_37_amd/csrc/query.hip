@@ -8,7 +8,7 @@
 //   query_finish_kernel - adds the k slices of [q^C ; q^R], rotates each head's
 //                        q^R pairs (2k, 2k+1) by pos * base^(-2k/d_h^R) (angle in
 //                        fp64) and writes q_nope [B, n_h, d_h], q_pe [B, n_h, d_h^R].
-#include "kernels.cuh"
+#include "kernels.h"
 
 namespace mla {
 

@@ -1,0 +1,207 @@
+// Host-only check of libmla's C-ABI layer (api.hip compiled for the host alone)
+// under AddressSanitizer and UndefinedBehaviorSanitizer.  The kernel launchers
+// and the two HIP device queries that api.hip uses are replaced by stubs that
+// record their calls, so argument validation, partition resolution, workspace
+// sizing and the host partition helper run without a GPU.  Every check prints
+// nothing on success; the first failure prints its line and exits 1.  A
+// sanitizer finding aborts the process (the test builds with
+// -fno-sanitize-recover).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <random>
+#include <vector>
+
+#include "../mla_latent_kv_37_amd/csrc/kernels.h"
+
+static int g_launches = 0;
+static mla::V2DecodeArgs g_v2{};
+static int g_fails = 0;
+
+#define CHECK(cond)                                                         \
+  do {                                                                      \
+    if (!(cond)) {                                                          \
+      std::fprintf(stderr, "host_abi_check:%d: failed: %s\n", __LINE__, #cond); \
+      ++g_fails;                                                            \
+    }                                                                       \
+  } while (0)
+
+// ---- stubs: kernel launchers (api.hip's only route to the device) ----
+namespace mla {
+hipError_t launch_decode_generic(const GenericDecodeArgs&, int, hipStream_t) { ++g_launches; return hipSuccess; }
+hipError_t launch_decode_v2(const V2DecodeArgs& a, hipStream_t) { ++g_launches; g_v2 = a; return hipSuccess; }
+hipError_t launch_decode_lite(const V2DecodeArgs& a, hipStream_t) { ++g_launches; g_v2 = a; return hipSuccess; }
+hipError_t launch_cache_store(const CacheStoreArgs&, int, hipStream_t) { ++g_launches; return hipSuccess; }
+hipError_t launch_gemm_ws(const GemmArgs&, hipStream_t) { ++g_launches; return hipSuccess; }
+hipError_t launch_reduce_cast(const float*, int, int64_t, void*, mla_dtype_t, hipStream_t) { ++g_launches; return hipSuccess; }
+hipError_t launch_query_finish(const QueryFinishArgs&, hipStream_t) { ++g_launches; return hipSuccess; }
+hipError_t launch_merge(const MergeArgs&, int, hipStream_t) { ++g_launches; return hipSuccess; }
+hipError_t launch_merge_proj(const MergeArgs&, const void*, void*, int, hipStream_t) { ++g_launches; return hipSuccess; }
+hipError_t launch_expand(const int32_t*, const int32_t*, int, int, int, int32_t*, int32_t*, hipStream_t) {
+  ++g_launches;
+  return hipSuccess;
+}
+hipError_t launch_absorb_generic(const void*, mla_dtype_t, const void*, mla_dtype_t, void*, mla_dtype_t, int, int, int,
+                                 int, hipStream_t) {
+  ++g_launches;
+  return hipSuccess;
+}
+hipError_t launch_outproj_generic(const void*, mla_dtype_t, const void*, mla_dtype_t, void*, mla_dtype_t, int, int, int,
+                                  int, hipStream_t) {
+  ++g_launches;
+  return hipSuccess;
+}
+hipError_t launch_absorb_v2(const void*, const void*, void*, int, int, hipStream_t) { ++g_launches; return hipSuccess; }
+hipError_t launch_outproj_v2(const void*, bool, const void*, void*, int, int, hipStream_t) {
+  ++g_launches;
+  return hipSuccess;
+}
+}  // namespace mla
+
+// ---- stubs: the device queries behind num_parts < 0 (a 256-CU device) ----
+extern "C" hipError_t hipGetDevice(int* d) {
+  *d = 0;
+  return hipSuccess;
+}
+extern "C" hipError_t hipDeviceGetAttribute(int* v, hipDeviceAttribute_t attr, int) {
+  *v = attr == hipDeviceAttributeMultiprocessorCount ? 256 : 0;
+  return hipSuccess;
+}
+
+// stand-ins for device pointers: the ABI layer never dereferences them
+static void* dev(uintptr_t k) { return reinterpret_cast<void*>(0x100000 + 256 * k); }
+static int32_t* idev(uintptr_t k) { return static_cast<int32_t*>(dev(k)); }
+
+static void check_partitions(std::mt19937& rng) {
+  for (int trial = 0; trial < 400; ++trial) {
+    const int B = 1 + int(rng() % 70), page = 64, maxp = 1 + int(rng() % 40);
+    std::vector<int32_t> lens(B), first(B), count(B);
+    for (int b = 0; b < B; ++b) lens[b] = (rng() % 5 == 0) ? 0 : int(rng() % (maxp * page + 1));
+    const int mode = int(rng() % 3);
+    mla_partition_t part{0, 0};
+    if (mode == 1) part.split_tokens = page * (1 + int(rng() % 6));
+    if (mode == 2) part.num_parts = 1 + int(rng() % 300);
+    CHECK(mla_partition_host(lens.data(), B, page, maxp, &part, first.data(), count.data()) == MLA_OK);
+    size_t ws = 0;
+    int32_t slots = 0;
+    mla_dims_t d{128, 128, 64, 512};
+    CHECK(mla_decode_workspace_size(&d, B, maxp, page, &part, &ws, &slots) == MLA_OK);
+    // every non-empty sequence is covered; split slots are in range and disjoint
+    std::vector<int> owner(size_t(slots > 0 ? slots : 1), -1);
+    for (int b = 0; b < B; ++b) {
+      if (lens[b] == 0) {
+        CHECK(count[b] == 0);
+        continue;
+      }
+      CHECK(count[b] >= 1);
+      CHECK(count[b] <= (lens[b] + page - 1) / page);
+      if (count[b] == 1 && mode != 1) continue;   // final output straight from mla_decode
+      for (int s = first[b]; s < first[b] + count[b]; ++s) {
+        CHECK(s >= 0 && s < slots);
+        if (s >= 0 && s < slots) {
+          CHECK(owner[size_t(s)] == -1);
+          owner[size_t(s)] = b;
+        }
+      }
+    }
+    // validation of a cache built for these lengths
+    std::vector<int32_t> bt(size_t(B) * maxp);
+    const int num_pages = B * maxp;
+    for (size_t i = 0; i < bt.size(); ++i) bt[i] = int32_t(rng() % num_pages);
+    int32_t bad = 7;
+    CHECK(mla_validate_cache_host(bt.data(), lens.data(), B, maxp, page, num_pages, &bad) == MLA_OK && bad == -1);
+    const int b = int(rng() % B);
+    if (lens[b] > 0) {
+      bt[size_t(b) * maxp + size_t(rng() % ((lens[b] + page - 1) / page))] = num_pages;
+      CHECK(mla_validate_cache_host(bt.data(), lens.data(), B, maxp, page, num_pages, &bad) == MLA_ERR_INVALID_ARG);
+      CHECK(bad >= 0 && bad <= b);
+    }
+  }
+}
+
+static void check_decode_validation() {
+  mla_dims_t d{128, 128, 64, 512};
+  int32_t* bt = static_cast<int32_t*>(dev(1));
+  int32_t* lens = static_cast<int32_t*>(dev(2));
+  mla_paged_cache_t c{dev(3), nullptr, MLA_BF16, 64, 1000, bt, 40, lens};
+  mla_partition_t whole{0, 0}, bal{0, -1}, fixed{128, 0}, odd{100, 0};
+  size_t ws = 0;
+  int32_t slots = 0;
+  CHECK(mla_decode_workspace_size(&d, 64, 40, 64, &bal, &ws, &slots) == MLA_OK && slots == 256 + 64 && ws > 0);
+  const float scale = 0.0721688f;
+  int before = g_launches;
+  // valid calls launch the 128-head kernel with the resolved arguments
+  CHECK(mla_decode(&d, 64, dev(4), dev(5), MLA_BF16, &c, scale, &bal, dev(6), ws, dev(7), MLA_BF16, nullptr,
+                   nullptr) == MLA_OK);
+  CHECK(g_launches == before + 1);
+  CHECK(g_v2.n_items == 256 && g_v2.num_pages == 1000 && g_v2.pp.max_tokens == 40 * 64 && g_v2.max_pages == 40);
+  CHECK(mla_decode(&d, 64, dev(4), dev(5), MLA_BF16, &c, scale, &whole, nullptr, 0, dev(7), MLA_BF16, nullptr,
+                   nullptr) == MLA_OK);
+  before = g_launches;
+  // invalid calls launch nothing
+  CHECK(mla_decode(&d, 64, dev(4), dev(5), MLA_BF16, &c, scale, &bal, nullptr, 0, dev(7), MLA_BF16, nullptr, nullptr) ==
+        MLA_ERR_WORKSPACE);
+  CHECK(mla_decode(&d, 64, dev(4), dev(5), MLA_BF16, &c, scale, &bal, dev(6), ws - 1, dev(7), MLA_BF16, nullptr,
+                   nullptr) == MLA_ERR_WORKSPACE);
+  CHECK(mla_decode(&d, 64, dev(4), dev(5), MLA_BF16, &c, scale, &odd, dev(6), ws, dev(7), MLA_BF16, nullptr,
+                   nullptr) == MLA_ERR_INVALID_ARG);
+  CHECK(mla_decode(&d, 64, reinterpret_cast<char*>(dev(4)) + 2, dev(5), MLA_BF16, &c, scale, &whole, nullptr, 0,
+                   dev(7), MLA_BF16, nullptr, nullptr) == MLA_ERR_ALIGNMENT);
+  CHECK(mla_decode(&d, 64, dev(4), dev(5), MLA_F32, &c, scale, &whole, nullptr, 0, dev(7), MLA_BF16, nullptr,
+                   nullptr) == MLA_ERR_UNSUPPORTED);
+  CHECK(mla_decode(&d, 64, dev(4), dev(5), MLA_BF16, &c, -1.f, &whole, nullptr, 0, dev(7), MLA_BF16, nullptr,
+                   nullptr) == MLA_ERR_INVALID_ARG);
+  CHECK(mla_decode(&d, -1, dev(4), dev(5), MLA_BF16, &c, scale, &whole, nullptr, 0, dev(7), MLA_BF16, nullptr,
+                   nullptr) == MLA_ERR_INVALID_ARG);
+  CHECK(mla_decode(nullptr, 64, dev(4), dev(5), MLA_BF16, &c, scale, &whole, nullptr, 0, dev(7), MLA_BF16, nullptr,
+                   nullptr) == MLA_ERR_INVALID_ARG);
+  mla_paged_cache_t f8 = c;
+  f8.dtype = MLA_FP8_E4M3;
+  CHECK(mla_decode(&d, 64, dev(4), dev(5), MLA_BF16, &f8, scale, &whole, nullptr, 0, dev(7), MLA_BF16, nullptr,
+                   nullptr) == MLA_ERR_INVALID_ARG);   // fp8 without scales
+  mla_paged_cache_t nopages = c;
+  nopages.num_pages = 0;
+  CHECK(mla_decode(&d, 64, dev(4), dev(5), MLA_BF16, &nopages, scale, &whole, nullptr, 0, dev(7), MLA_BF16, nullptr,
+                   nullptr) == MLA_ERR_INVALID_ARG);
+  CHECK(mla_merge_splits(&d, 64, lens, 64, 40, &fixed, nullptr, 0, dev(7), MLA_BF16, nullptr, nullptr) ==
+        MLA_ERR_WORKSPACE);
+  CHECK(mla_merge_out_proj(&d, 64, lens, 64, 40, &bal, dev(6), ws, dev(7), MLA_BF16, nullptr, nullptr, MLA_BF16,
+                           dev(8), MLA_BF16, nullptr) == MLA_ERR_INVALID_ARG);   // no W^UV
+  CHECK(mla_absorb_q(&d, 64, dev(4), MLA_FP8_E4M3, dev(5), MLA_BF16, dev(6), MLA_BF16, nullptr) ==
+        MLA_ERR_UNSUPPORTED);
+  CHECK(mla_out_proj(&d, 64, dev(4), MLA_BF16, nullptr, MLA_BF16, dev(6), MLA_BF16, nullptr) == MLA_ERR_INVALID_ARG);
+  // multi-token decode: the projection's arguments are checked before the decode is enqueued
+  size_t mws = 0;
+  CHECK(mla_decode_multi_workspace_size(&d, 64, 3, 40, 64, &bal, &mws, &slots) == MLA_OK && mws > 0);
+  CHECK(mla_decode_multi_out_proj(&d, 64, 3, dev(4), dev(5), MLA_BF16, &c, scale, &bal, dev(6), mws, dev(7),
+                                  MLA_BF16, nullptr, dev(8), MLA_FP8_E4M3, dev(9), MLA_BF16, nullptr) ==
+        MLA_ERR_UNSUPPORTED);
+  CHECK(mla_decode_multi(&d, 64, 0, dev(4), dev(5), MLA_BF16, &c, scale, &bal, dev(6), mws, dev(7), MLA_BF16, nullptr,
+                         nullptr) == MLA_ERR_INVALID_ARG);
+  // cache writers
+  CHECK(mla_cache_store(&d, 8, dev(4), MLA_FP8_E4M3, idev(5), 0.f, &c, nullptr) == MLA_ERR_UNSUPPORTED);
+  CHECK(mla_cache_store(&d, 8, dev(4), MLA_BF16, idev(5), -1.f, &c, nullptr) == MLA_ERR_INVALID_ARG);
+  mla_dims_t odd_dims{4, 16, 7, 32};
+  CHECK(mla_cache_store(&odd_dims, 8, dev(4), MLA_BF16, idev(5), 0.f, &c, nullptr) == MLA_ERR_UNSUPPORTED);
+  CHECK(mla_query_prep(&d, 5120, 1536, 8, dev(4), MLA_BF16, dev(5), dev(6), dev(7), MLA_BF16, idev(8), 1e4f, dev(9),
+                       dev(10), MLA_BF16, nullptr, 0, nullptr) == MLA_ERR_WORKSPACE);
+  CHECK(g_launches == before);
+  // huge sizes: no overflow in the workspace arithmetic (sizes are size_t)
+  CHECK(mla_decode_workspace_size(&d, 1 << 20, 1 << 10, 64, &fixed, &ws, &slots) == MLA_OK);
+  CHECK(ws >= size_t(slots) * 128 * 512 * 4);
+  CHECK(mla_query_prep_scratch_size(&d, 1536, 1 << 16) > 0);
+}
+
+int main() {
+  std::mt19937 rng(12345);
+  check_partitions(rng);
+  check_decode_validation();
+  if (g_fails) {
+    std::fprintf(stderr, "host_abi_check: %d failures\n", g_fails);
+    return 1;
+  }
+  std::printf("host_abi_check: ok (%d stub launches)\n", g_launches);
+  return 0;
+}

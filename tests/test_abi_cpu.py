@@ -294,3 +294,32 @@ def test_partition_host_fixed_and_whole(lib):
     assert count.tolist() == [0, 1, 1, 1, 1]
     with pytest.raises(lib.MlaError):
         lib.partition_host(np.array([5000], dtype=np.int32), 64, 2, lib.partition(0, 0))
+
+
+def test_validate_cache_host(lib):
+    """Host check of block-table ids and lengths: accepts a consistent cache and
+    names the first sequence that breaks a rule."""
+    rng = np.random.default_rng(5)
+    B, maxp, page, num_pages = 6, 4, 64, 30
+    bt = rng.integers(0, num_pages, (B, maxp)).astype(np.int32)
+    lens = np.array([0, 1, 64, 65, 255, 256], dtype=np.int32)
+    assert lib.validate_cache_host(bt, lens, page, num_pages) == (lib.MLA_OK, -1)
+    # entries past a sequence's pages are not read: anything goes there
+    bt2 = bt.copy()
+    bt2[1, 1:] = -7
+    bt2[0, :] = 10 ** 6
+    assert lib.validate_cache_host(bt2, lens, page, num_pages) == (lib.MLA_OK, -1)
+    # a read entry outside [0, num_pages)
+    for bad_id in (-1, num_pages, 2 ** 31 - 1):
+        bt3 = bt.copy()
+        bt3[3, 1] = bad_id
+        assert lib.validate_cache_host(bt3, lens, page, num_pages) == (lib.MLA_ERR_INVALID_ARG, 3)
+    # lengths outside [0, max_pages * page]
+    for bad_len, b in ((-1, 2), (maxp * page + 1, 4)):
+        l2 = lens.copy()
+        l2[b] = bad_len
+        assert lib.validate_cache_host(bt, l2, page, num_pages) == (lib.MLA_ERR_INVALID_ARG, b)
+    # invalid arguments themselves
+    assert lib.validate_cache_host(bt, lens, 0, num_pages) == (lib.MLA_ERR_INVALID_ARG, -1)
+    assert lib.validate_cache_host(bt, lens, page, 0) == (lib.MLA_ERR_INVALID_ARG, -1)
+    assert lib.validate_cache_host(bt[:0], lens[:0], page, num_pages) == (lib.MLA_OK, -1)

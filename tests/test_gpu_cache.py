@@ -216,6 +216,10 @@ def test_cache_append_v2(model, kind):
     h, w_dkv, w_kr = to_bf16(rng.normal(size=(batch, dims.d_model))), to_bf16(W["W_DKV"]), to_bf16(W["W_KR"])
     pos = rng.integers(0, max_pages * PAGE, batch).astype(np.int32)
     perm = _targets(rng, pos, max_pages, num_pages)
+    # skipped sequences: their cache slot is not written, but rows[b] still
+    # holds the summed projection
+    pos[3] = -1                              # negative position
+    perm[7, pos[7] // PAGE] = num_pages      # page id outside the cache
     kv, scales, bt, cache = _device_cache(kind, num_pages, width, perm)
     t = lambda x: torch.from_numpy(x.astype(np.float32)).cuda().to(torch.bfloat16)  # noqa: E731
     rows = torch.empty((8, batch, width), dtype=torch.float32, device="cuda")
@@ -224,11 +228,19 @@ def test_cache_append_v2(model, kind):
     rows_gpu = rows[0].cpu().numpy()
     ref_c, ref_r = h @ w_dkv.T, h @ w_kr.T          # the projections, float64
     ref = np.concatenate([ref_c, ref_r], axis=1)
-    err = np.abs(rows_gpu - ref).max() / np.abs(ref).max()
-    print(f"rows rel err {err:.3e}", flush=True)
-    assert err <= 1e-4
+    for b in range(batch):                          # every sequence, the skipped ones included
+        err = np.abs(rows_gpu[b] - ref[b]).max() / np.abs(ref[b]).max()
+        assert err <= 1e-4, f"rows[{b}] rel err {err:.3e}"
     got = _stored_values(kind, kv, scales, perm, pos, num_pages, width)
+    assert got[3] is None and got[7] is None
+    # nothing outside the written slots changed (the skipped sequences wrote nothing)
+    written = {int(perm[b, pos[b] // PAGE]) * PAGE + int(pos[b]) % PAGE for b in range(batch) if got[b] is not None}
+    kvb = _host_bytes(kv, num_pages * PAGE)
+    untouched = np.array([r for r in range(num_pages * PAGE) if r not in written])
+    assert np.all(kvb[untouched] == SENTINEL)
     for b in range(batch):
+        if got[b] is None:
+            continue
         if kind == "bf16":
             want = ostore.bf16_bits_to_f64(ostore.f32_to_bf16_bits(rows_gpu[b, :dc]))
         else:

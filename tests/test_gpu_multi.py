@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 import oracle
-from _cases import TOL, direct_case, from_h_case, host, rel_err, to_device
+from _cases import TOL, Worst, compare_seq, direct_case, from_h_case, host, rel_err, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -73,11 +73,12 @@ def _run_multi(case, dev, q_c, q_r, part, fused=False):
 
 
 def _compare(case, q_c, q_r, got, tol, heads=None):
+    """Each (sequence, new token) against the oracle: vectors per token, lse against
+    its derived bound over the rows that token sees."""
     o_lat, lse, o_heads = got
     d = case.dims
-    hs = list(range(d.n_heads)) if heads is None else list(heads)
-    refs = {"o_lat": [], "lse": [], "o_heads": []}
-    gots = {"o_lat": [], "lse": [], "o_heads": []}
+    q_len = q_c.shape[1]
+    worst = Worst()
     for b, T in enumerate(case.lens):
         rows = case.stored_rows(b)
         res = oracle.attend_new_tokens(q_c[b], q_r[b], rows[:, :d.d_latent], rows[:, d.d_latent:], case.W_UK,
@@ -87,13 +88,9 @@ def _compare(case, q_c, q_r, got, tol, heads=None):
                 # no visible token: zero output, lse = -inf
                 assert np.all(o_lat[b, t] == 0) and np.all(np.isneginf(lse[b, t])), (b, t)
                 continue
-            refs["o_lat"].append(r["o_lat"][hs]); gots["o_lat"].append(o_lat[b, t][hs])
-            refs["lse"].append(r["lse"][hs]); gots["lse"].append(lse[b, t][hs])
-            refs["o_heads"].append(r["o_heads"][hs]); gots["o_heads"].append(o_heads[b, t][hs])
-    for k in refs:
-        err = rel_err(np.stack(gots[k]), np.stack(refs[k]))
-        print(f"  {k}: rel err {err:.3e} (tol {tol:g})", flush=True)
-        assert err <= tol, k
+            compare_seq(case, b, r, {"o_lat": o_lat[b, t], "lse": lse[b, t], "o_heads": o_heads[b, t]}, tol, heads,
+                        worst, tag=f"b={b},t={t}", rows=rows[:T - q_len + t + 1], q_pe=q_r[b, t])
+    worst.report(tol)
 
 
 @pytest.fixture(scope="module")

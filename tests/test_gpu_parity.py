@@ -10,7 +10,8 @@ import numpy as np
 import pytest
 
 import oracle
-from _cases import TOL, direct_case, from_h_case, host, rel_err, run_step, to_device
+from _cases import (TOL, Worst, check_lse, check_vec, compare_seq, direct_case, from_h_case, host, lse_tolerance,
+                    run_step, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -26,33 +27,45 @@ def _gpu():
 
 
 def check(name, got, ref, tol):
-    err = rel_err(got, ref)
+    err = check_vec(name, got, ref, tol)
     print(f"  {name}: rel err {err:.3e} (tol {tol:g})", flush=True)
-    assert np.all(np.isfinite(np.asarray(got)[np.isfinite(ref)])), f"{name}: non-finite output"
-    assert err <= tol, f"{name}: {err:.3e} > {tol:g}"
 
 
-def compare_all(case, step, tol, heads=None):
-    """Compare q_lat, o_lat, lse and o_heads of every sequence with the oracle."""
+def compare_all(case, step, tol, heads=None, seqs=None):
+    """Compare q_lat, o_lat, lse and o_heads of every sequence (or of `seqs`) with
+    the oracle: vectors per sequence against tol * max|ref| of that sequence,
+    lse against its derived absolute bound (_cases.lse_tolerance)."""
     q_lat, o_lat, lse, o_heads = host(step.q_lat), host(step.o_lat), host(step.lse), host(step.o_heads)
     d = case.dims
-    refs = {"q_lat": [], "o_lat": [], "lse": [], "o_heads": []}
-    gots = {"q_lat": [], "o_lat": [], "lse": [], "o_heads": []}
-    for b, T in enumerate(case.lens):
-        if T == 0:
+    worst = Worst()
+    for b in (range(len(case.lens)) if seqs is None else seqs):
+        if case.lens[b] == 0:
             assert np.all(o_lat[b] == 0) and np.all(np.isneginf(lse[b])), "empty sequence must give o=0, lse=-inf"
             continue
         r = case.reference(b, heads=heads)
-        hs = list(range(d.n_heads)) if heads is None else list(heads)
-        refs["q_lat"].append(r["q_lat"][hs]); gots["q_lat"].append(q_lat[b][hs])
-        refs["o_lat"].append(r["o_lat"][hs]); gots["o_lat"].append(o_lat[b][hs])
-        refs["lse"].append(r["lse"][hs]); gots["lse"].append(lse[b][hs])
-        oh = o_heads[b].reshape(d.n_heads, d.d_head)
-        refs["o_heads"].append(r["o_heads"][hs]); gots["o_heads"].append(oh[hs])
-    for k in refs:
-        if refs[k]:
-            check(k, np.stack(gots[k]), np.stack(refs[k]), tol)
-    return refs
+        got = {"q_lat": q_lat[b], "o_lat": o_lat[b], "lse": lse[b],
+               "o_heads": o_heads[b].reshape(d.n_heads, d.d_head)}
+        compare_seq(case, b, r, got, tol, heads, worst)
+    worst.report(tol)
+
+
+def check_partials(case, step, tol, chunk, lens):
+    """Per-split partials (o_s, lse_s) of fixed splits against the oracle's chunks."""
+    o_part, lse_part = step.partials()
+    o_part, lse_part = host(o_part), host(lse_part)
+    S = step.num_slots // len(lens)
+    dc = case.dims.d_latent
+    worst = Worst()
+    for b, T in enumerate(lens):
+        parts = case.reference(b, chunk=chunk)
+        if len(parts) == 1:
+            continue
+        rows = case.stored_rows(b)
+        for s, p in enumerate(parts):
+            worst.add("o_part", check_vec(f"o_part[b={b},s={s}]", o_part[b * S + s], p["o_lat"], tol))
+            bound = lse_tolerance(case, p["q_lat"], case.q_pe[b], rows[s * chunk:(s + 1) * chunk], p["lse"])
+            worst.add("lse_part", check_lse(f"lse_part[b={b},s={s}]", lse_part[b * S + s], p["lse"], bound))
+    worst.report(tol)
 
 
 # ---------------------------------------------------------------------------
@@ -167,17 +180,7 @@ def test_v2_split_partials(gain):
     dev = to_device(case)
     step = run_step(case, dev, 256, 0)
     compare_all(case, step, TOL["bf16"])
-    o_part, lse_part = step.partials()
-    o_part, lse_part = host(o_part), host(lse_part)
-    S = step.num_slots // len(lens)
-    for b, T in enumerate(lens):
-        parts = case.reference(b, chunk=256)
-        if len(parts) == 1:
-            continue
-        got_o = np.stack([o_part[b * S + s] for s in range(len(parts))])
-        got_l = np.stack([lse_part[b * S + s] for s in range(len(parts))])
-        check(f"o_part[b={b}]", got_o, np.stack([p["o_lat"] for p in parts]), TOL["bf16"])
-        check(f"lse_part[b={b}]", got_l, np.stack([p["lse"] for p in parts]), TOL["bf16"])
+    check_partials(case, step, TOL["bf16"], 256, lens)
     if gain > 1:
         spread = max(np.ptp(case.reference(b)["lse"]) for b in range(len(lens)))
         print(f"  lse spread across heads {spread:.2f} (sharp softmax exercised)", flush=True)
@@ -195,6 +198,17 @@ def test_v2_fp8_small():
     for part in [(0, 0), (0, 6), (128, 0)]:
         step = run_step(case, dev, *part)
         compare_all(case, step, TOL["fp8"])
+
+
+def test_v2_fp8_short_tails():
+    """Sequences of 1-5 and 33-36 tokens: the last row's scales end inside a 16-byte
+    load whenever T % 4 != 0; each sequence is checked against its own values."""
+    lens = [1, 2, 3, 4, 5, 33, 34, 35, 36]
+    print(f"case: V2 fp8 short tails lens={lens}", flush=True)
+    case = direct_case(5, lens, max_pages=2, seed=77)
+    dev = to_device(case)
+    for part in [(0, 0), (0, 3)]:
+        compare_all(case, run_step(case, dev, *part), TOL["fp8"])
 
 
 FP8_RAGGED = [31, 32, 33, 64, 95, 129, 200, 700, 1100, 5]
@@ -230,19 +244,12 @@ def test_v2_fp8_sharp():
 # full sizes, in the launch configuration the benchmark times
 # ---------------------------------------------------------------------------
 
-SAMPLE_HEADS = [0, 37, 64, 127]
-
-
 def _sampled(case, step, tol, seqs):
-    o_lat, lse, o_heads = host(step.o_lat), host(step.lse), host(step.o_heads)
+    """All 128 heads of the sampled sequences against the oracle; finite values and
+    o_lat inside the convex hull of the cached latents at every (sequence, head)."""
+    o_lat, lse = host(step.o_lat), host(step.lse)
     d = case.dims
-    for b in seqs:
-        r = case.reference(b, heads=SAMPLE_HEADS)
-        check(f"o_lat[b={b}]", o_lat[b][SAMPLE_HEADS], r["o_lat"][SAMPLE_HEADS], tol)
-        check(f"lse[b={b}]", lse[b][SAMPLE_HEADS], r["lse"][SAMPLE_HEADS], tol)
-        oh = o_heads[b].reshape(d.n_heads, d.d_head)
-        check(f"o_heads[b={b}]", oh[SAMPLE_HEADS], r["o_heads"][SAMPLE_HEADS], tol)
-    # properties at every (sequence, head): finite, o_lat a convex combination of cached latents
+    compare_all(case, step, tol, seqs=seqs)
     assert np.all(np.isfinite(o_lat)) and np.all(np.isfinite(lse))
     for b in range(len(case.lens)):
         rows = case.stored_rows(b)[:, : d.d_latent]
@@ -261,12 +268,24 @@ def test_fullsize_ragged_b64():
     _sampled(case, step, TOL["bf16"], seqs=[0, 17, 63])
 
 
-def test_fullsize_long_b4_split4096():
-    print("case: full-size long B=4 T=131072 split 4096", flush=True)
+@pytest.fixture(scope="module")
+def long_b4():
     case = direct_case(4, [131072] * 4, max_pages=2048)
-    dev = to_device(case)
-    step = run_step(case, dev, 4096, 0)
-    _sampled(case, step, TOL["bf16"], seqs=[0, 3])
+    return case, to_device(case)
+
+
+def test_fullsize_long_b4_split4096(long_b4):
+    print("case: full-size long B=4 T=131072 split 4096", flush=True)
+    case, dev = long_b4
+    _sampled(case, run_step(case, dev, 4096, 0), TOL["bf16"], seqs=[0, 3])
+
+
+def test_fullsize_long_b4_bench_partition(long_b4):
+    """The benchmark's launch configuration for the long workload: one work item
+    per compute unit (64 splits of each 131,072-token sequence)."""
+    print("case: full-size long B=4 T=131072, one work item per compute unit", flush=True)
+    case, dev = long_b4
+    _sampled(case, run_step(case, dev, 0, -1), TOL["bf16"], seqs=[0, 3])
 
 
 def test_fullsize_fp8_b32():
