@@ -330,6 +330,27 @@ mla_status_t mla_query_prep(const mla_dims_t* dims, int32_t d_model, int32_t d_q
                             mla_dtype_t out_dt, void* scratch, size_t scratch_bytes, void* stream);
 
 /*
+ * mla_decode followed by mla_merge_splits without a caller workspace, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  The split partials
+ * live in a library-owned device array of MLA_NOALLOC_SCRATCH_BYTES per GPU
+ * (held until the process ends), packed at the output dtype's size; a
+ * partition whose partials need more returns MLA_ERR_WORKSPACE before
+ * anything is enqueued (see mla_decode_workspace_size for the fp32-sized
+ * public layout; here bf16 output needs half of its o_part area).  The call
+ * allocates nothing.  All calls on one GPU share its array: calls that
+ * overlap in time on one GPU (other streams or host threads) race and must be
+ * serialised by the caller.  Arguments and results are those of mla_decode +
+ * mla_merge_splits: o_lat / lse hold every sequence's final output.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES (48u << 20)
+mla_status_t mla_decode_noalloc(const mla_dims_t* dims, int32_t batch,
+                                const void* q_lat, const void* q_pe, mla_dtype_t q_dt,
+                                const mla_paged_cache_t* cache, float softmax_scale,
+                                const mla_partition_t* part,
+                                void* o_lat, mla_dtype_t o_dt, float* lse, void* stream);
+
+/*
  * Host check (no device access) of a paged cache's metadata, on host copies of
  * its block table and lengths [DeepSeek-V2 explainer §2.1.1 names the paged KV
  * memory; the layout is that of mla_paged_cache_t above]:

@@ -21,7 +21,7 @@ EXPORTS = ("mla_status_string", "mla_build_info", "mla_absorb_q", "mla_decode_wo
            "mla_lse_part_offset", "mla_decode", "mla_merge_splits", "mla_out_proj", "mla_cache_store",
            "mla_cache_append", "mla_query_prep_scratch_size", "mla_query_prep", "mla_partition_host",
            "mla_decode_multi_workspace_size", "mla_decode_multi", "mla_merge_out_proj",
-           "mla_decode_multi_out_proj", "mla_validate_cache_host")
+           "mla_decode_multi_out_proj", "mla_validate_cache_host", "mla_decode_noalloc")
 
 
 class MlaError(RuntimeError):
@@ -80,6 +80,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                           ctypes.c_float, P, P, ctypes.c_int, P, SZ, P]),
         "mla_partition_host": (ctypes.c_int, [ctypes.POINTER(I32), I32, I32, I32, PP, ctypes.POINTER(I32),
                                               ctypes.POINTER(I32)]),
+        "mla_decode_noalloc": (ctypes.c_int, [PD, I32, P, P, ctypes.c_int, PC, ctypes.c_float, PP, P, ctypes.c_int, P,
+                                              P]),
         "mla_validate_cache_host": (ctypes.c_int, [ctypes.POINTER(I32), ctypes.POINTER(I32), I32, I32, I32, I32,
                                                    ctypes.POINTER(I32)]),
         "mla_decode_multi_workspace_size": (ctypes.c_int, [PD, I32, I32, I32, I32, PP, ctypes.POINTER(SZ),
@@ -184,6 +186,15 @@ def decode(d: Dims, q_lat, q_pe, cache: PagedCache, softmax_scale: float, part: 
                              ctypes.byref(cache), ctypes.c_float(softmax_scale), ctypes.byref(part), _ptr(workspace),
                              ws_bytes, _ptr(o_lat), dtype_code(o_lat), _ptr(lse), _stream(stream)), "mla_decode")
     return o_lat
+
+
+def decode_noalloc(d: Dims, q_lat, q_pe, cache: PagedCache, softmax_scale: float, part: Partition, o_lat,
+                   lse=None, stream=None):
+    """mla_decode + mla_merge_splits with the split partials in the library's own device array."""
+    _check(load().mla_decode_noalloc(ctypes.byref(d), q_lat.shape[0], _ptr(q_lat), _ptr(q_pe), dtype_code(q_lat),
+                                     ctypes.byref(cache), ctypes.c_float(softmax_scale), ctypes.byref(part),
+                                     _ptr(o_lat), dtype_code(o_lat), _ptr(lse), _stream(stream)), "mla_decode_noalloc")
+    return o_lat, lse
 
 
 def merge_splits(d: Dims, seq_lens, page_size: int, max_pages: int, part: Partition, workspace, o_lat, lse=None,

@@ -6,7 +6,7 @@
 #include <cstdint>
 #include <cstring>
 
-#include "kernels.h"
+#include "api_internal.h"
 
 namespace mla {
 
@@ -108,11 +108,14 @@ struct WsLayout {
   size_t o_part, lse_part, meta, total;
 };
 
-WsLayout ws_layout(const mla_dims_t* d, int n_slots, int batch, bool balanced) {
+// o_elem: bytes per partial element.  The public workspace is sized for fp32
+// (sizeof(float)) so that one size serves either output dtype; the
+// no-allocation entry point packs partials at the output dtype's own size.
+WsLayout ws_layout(const mla_dims_t* d, int n_slots, int batch, bool balanced, size_t o_elem = sizeof(float)) {
   WsLayout L{};
   if (n_slots == 0) return L;
   L.o_part = 0;
-  L.lse_part = align256(size_t(n_slots) * d->n_heads * d->d_latent * sizeof(float));
+  L.lse_part = align256(size_t(n_slots) * d->n_heads * d->d_latent * o_elem);
   L.meta = L.lse_part + align256(size_t(n_slots) * d->n_heads * sizeof(float));
   L.total = L.meta + (balanced ? align256(size_t(2) * batch * sizeof(int32_t)) : 0);
   return L;
@@ -236,13 +239,13 @@ size_t mla_lse_part_offset(const mla_dims_t* dims, int32_t num_slots) {
 
 }  // extern "C"
 
-namespace {
+namespace mla {
 
 // mla_decode's checks and launch; with dry = true only the checks.
 mla_status_t decode_impl(const mla_dims_t* dims, int32_t batch, const void* q_lat, const void* q_pe,
                          mla_dtype_t q_dt, const mla_paged_cache_t* cache, float softmax_scale,
                          const mla_partition_t* part, void* workspace, size_t workspace_bytes, void* o_lat,
-                         mla_dtype_t o_dt, float* lse, void* stream, bool dry) {
+                         mla_dtype_t o_dt, float* lse, void* stream, bool dry, size_t o_elem) {
   if (mla_status_t s = check_dims(dims)) return s;
   if (!cache || !q_lat || !o_lat || (dims->d_rope > 0 && !q_pe)) return MLA_ERR_INVALID_ARG;
   if (!cache->kv || !cache->block_table || !cache->seq_lens) return MLA_ERR_INVALID_ARG;
@@ -260,7 +263,7 @@ mla_status_t decode_impl(const mla_dims_t* dims, int32_t batch, const void* q_la
   int n_items = 0, n_slots = 0;
   if (mla_status_t s = resolve(dims, batch, cache->max_pages_per_seq, cache->page_size, part, &pp, &n_items, &n_slots))
     return s;
-  const WsLayout L = ws_layout(dims, n_slots, batch, pp.mode == PART_BALANCED);
+  const WsLayout L = ws_layout(dims, n_slots, batch, pp.mode == PART_BALANCED, o_elem);
   if (L.total > 0 && (workspace == nullptr || workspace_bytes < L.total)) return MLA_ERR_WORKSPACE;
   if (L.total > 0 && !aligned16(workspace)) return MLA_ERR_ALIGNMENT;
   const bool fast = is_v2(dims) && cache->page_size == 64 && q_dt == MLA_BF16 &&
@@ -327,6 +330,51 @@ mla_status_t decode_impl(const mla_dims_t* dims, int32_t batch, const void* q_la
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
+// mla_merge_splits' checks and launch (o_elem as for decode_impl).
+mla_status_t merge_impl(const mla_dims_t* dims, int32_t batch, const int32_t* seq_lens, int32_t page_size,
+                        int32_t max_pages_per_seq, const mla_partition_t* part, const void* workspace,
+                        size_t workspace_bytes, void* o_lat, mla_dtype_t o_dt, float* lse, void* stream,
+                        size_t o_elem) {
+  if (mla_status_t s = check_dims(dims)) return s;
+  if (!seq_lens || !o_lat) return MLA_ERR_INVALID_ARG;
+  if (o_dt != MLA_F32 && o_dt != MLA_BF16) return valid_dtype(o_dt) ? MLA_ERR_UNSUPPORTED : MLA_ERR_INVALID_ARG;
+  if (!aligned16(o_lat)) return MLA_ERR_ALIGNMENT;
+  PartParams pp;
+  int n_items = 0, n_slots = 0;
+  if (mla_status_t s = resolve(dims, batch, max_pages_per_seq, page_size, part, &pp, &n_items, &n_slots)) return s;
+  const WsLayout L = ws_layout(dims, n_slots, batch, pp.mode == PART_BALANCED, o_elem);
+  if (L.total > 0 && (workspace == nullptr || workspace_bytes < L.total)) return MLA_ERR_WORKSPACE;
+  if (batch == 0) return MLA_OK;
+  const char* ws = static_cast<const char*>(workspace);
+  MergeArgs a{};
+  a.seq_lens = seq_lens;
+  a.pp = pp;
+  a.n_heads = dims->n_heads;
+  a.d_latent = dims->d_latent;
+  a.o_part = L.total ? static_cast<const void*>(ws + L.o_part) : nullptr;
+  a.lse_part = L.total ? reinterpret_cast<const float*>(ws + L.lse_part) : nullptr;
+  a.meta = (L.total && pp.mode == PART_BALANCED) ? reinterpret_cast<const int32_t*>(ws + L.meta) : nullptr;
+  a.o_lat = o_lat;
+  a.o_dt = o_dt;
+  a.lse = lse;
+  const hipError_t e = launch_merge(a, batch, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status_t decode_workspace_layout(const mla_dims_t* dims, int32_t batch, int32_t max_pages_per_seq,
+                                     int32_t page_size, const mla_partition_t* part, size_t o_elem, size_t* bytes) {
+  if (mla_status_t s = check_dims(dims)) return s;
+  PartParams pp;
+  int n_items = 0, n_slots = 0;
+  if (mla_status_t s = resolve(dims, batch, max_pages_per_seq, page_size, part, &pp, &n_items, &n_slots)) return s;
+  *bytes = ws_layout(dims, n_slots, batch, pp.mode == PART_BALANCED, o_elem).total;
+  return MLA_OK;
+}
+
+}  // namespace mla
+
+namespace {
+
 // mla_decode_multi workspace: virtual lengths, virtual block table, then the
 // workspace of the decode over batch * q_len virtual sequences.
 struct MultiLayout {
@@ -361,36 +409,14 @@ mla_status_t mla_decode(const mla_dims_t* dims, int32_t batch, const void* q_lat
                         const mla_partition_t* part, void* workspace, size_t workspace_bytes, void* o_lat,
                         mla_dtype_t o_dt, float* lse, void* stream) {
   return decode_impl(dims, batch, q_lat, q_pe, q_dt, cache, softmax_scale, part, workspace, workspace_bytes, o_lat,
-                     o_dt, lse, stream, false);
+                     o_dt, lse, stream, false, sizeof(float));
 }
 
 mla_status_t mla_merge_splits(const mla_dims_t* dims, int32_t batch, const int32_t* seq_lens, int32_t page_size,
                               int32_t max_pages_per_seq, const mla_partition_t* part, const void* workspace,
                               size_t workspace_bytes, void* o_lat, mla_dtype_t o_dt, float* lse, void* stream) {
-  if (mla_status_t s = check_dims(dims)) return s;
-  if (!seq_lens || !o_lat) return MLA_ERR_INVALID_ARG;
-  if (o_dt != MLA_F32 && o_dt != MLA_BF16) return valid_dtype(o_dt) ? MLA_ERR_UNSUPPORTED : MLA_ERR_INVALID_ARG;
-  if (!aligned16(o_lat)) return MLA_ERR_ALIGNMENT;
-  PartParams pp;
-  int n_items = 0, n_slots = 0;
-  if (mla_status_t s = resolve(dims, batch, max_pages_per_seq, page_size, part, &pp, &n_items, &n_slots)) return s;
-  const WsLayout L = ws_layout(dims, n_slots, batch, pp.mode == PART_BALANCED);
-  if (L.total > 0 && (workspace == nullptr || workspace_bytes < L.total)) return MLA_ERR_WORKSPACE;
-  if (batch == 0) return MLA_OK;
-  const char* ws = static_cast<const char*>(workspace);
-  MergeArgs a{};
-  a.seq_lens = seq_lens;
-  a.pp = pp;
-  a.n_heads = dims->n_heads;
-  a.d_latent = dims->d_latent;
-  a.o_part = L.total ? static_cast<const void*>(ws + L.o_part) : nullptr;
-  a.lse_part = L.total ? reinterpret_cast<const float*>(ws + L.lse_part) : nullptr;
-  a.meta = (L.total && pp.mode == PART_BALANCED) ? reinterpret_cast<const int32_t*>(ws + L.meta) : nullptr;
-  a.o_lat = o_lat;
-  a.o_dt = o_dt;
-  a.lse = lse;
-  const hipError_t e = launch_merge(a, batch, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+  return merge_impl(dims, batch, seq_lens, page_size, max_pages_per_seq, part, workspace, workspace_bytes, o_lat,
+                    o_dt, lse, stream, sizeof(float));
 }
 
 mla_status_t mla_decode_multi_workspace_size(const mla_dims_t* dims, int32_t batch, int32_t q_len,
@@ -445,7 +471,7 @@ mla_status_t decode_multi_impl(const mla_dims_t* dims, int32_t batch, int32_t q_
   vc.block_table = reinterpret_cast<const int32_t*>(ws + M.bt);
   void* dec_ws = M.dec_bytes ? static_cast<void*>(ws + M.dec) : nullptr;
   if (mla_status_t s = decode_impl(dims, vb, q_lat, q_pe, q_dt, &vc, softmax_scale, part, dec_ws, M.dec_bytes, o_lat,
-                                   o_dt, lse, stream, true))
+                                   o_dt, lse, stream, true, sizeof(float)))
     return s;
   if (batch == 0) return MLA_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -453,7 +479,7 @@ mla_status_t decode_multi_impl(const mla_dims_t* dims, int32_t batch, int32_t q_
                     reinterpret_cast<int32_t*>(ws + M.lens), reinterpret_cast<int32_t*>(ws + M.bt), st) != hipSuccess)
     return MLA_ERR_HIP;
   if (mla_status_t s = decode_impl(dims, vb, q_lat, q_pe, q_dt, &vc, softmax_scale, part, dec_ws, M.dec_bytes, o_lat,
-                                   o_dt, lse, stream, false))
+                                   o_dt, lse, stream, false, sizeof(float)))
     return s;
   if (!w_uv)
     return mla_merge_splits(dims, vb, vc.seq_lens, cache->page_size, cache->max_pages_per_seq, part, dec_ws,

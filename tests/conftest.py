@@ -14,8 +14,10 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # Run GPU tests in a stable order: probes/ABI first, full-size last.
+    # Run GPU tests in a stable order: probes/ABI first, full-size next to last,
+    # the no-allocation entry point's test last (it shares a device array that
+    # the library keeps until the process ends)
     def key(item):
         name = item.nodeid
-        return (2 if "fullsize" in name else 1 if item.get_closest_marker("gpu") else 0)
+        return (3 if "no_alloc" in name else 2 if "fullsize" in name else 1 if item.get_closest_marker("gpu") else 0)
     items.sort(key=key)

@@ -323,3 +323,20 @@ def test_validate_cache_host(lib):
     assert lib.validate_cache_host(bt, lens, 0, num_pages) == (lib.MLA_ERR_INVALID_ARG, -1)
     assert lib.validate_cache_host(bt, lens, page, 0) == (lib.MLA_ERR_INVALID_ARG, -1)
     assert lib.validate_cache_host(bt[:0], lens[:0], page, num_pages) == (lib.MLA_OK, -1)
+
+
+def test_noalloc_rejects_before_touching_the_device(lib):
+    """mla_decode_noalloc checks the partition's partials against its fixed 48 MiB
+    array (and the output dtype) before any device access."""
+    import ctypes
+    l = lib.load()
+    d = _v2(lib)
+    fake = ctypes.c_void_p(0x100000)
+    cache = lib.PagedCache(fake, None, lib.MLA_BF16, 64, 1000, fake, 40, fake)
+    big = lib.partition(0, 4096)     # 4096 + 64 slots of 128 KB bf16 partials
+    st = l.mla_decode_noalloc(ctypes.byref(d), 64, fake, fake, lib.MLA_BF16, ctypes.byref(cache),
+                              ctypes.c_float(0.07), ctypes.byref(big), fake, lib.MLA_BF16, None, None)
+    assert st == lib.MLA_ERR_WORKSPACE
+    st = l.mla_decode_noalloc(ctypes.byref(d), 64, fake, fake, lib.MLA_BF16, ctypes.byref(cache),
+                              ctypes.c_float(0.07), ctypes.byref(big), fake, lib.MLA_FP8_E4M3, None, None)
+    assert st == lib.MLA_ERR_UNSUPPORTED
