@@ -32,14 +32,6 @@ namespace {
 
 using namespace mla;
 
-// The bf16-cache decode kernel: decode_v2 (32-head pairs) unless the library is
-// built with MLA_DECODE_BF16_V3 defined (64-head teams, decode_v3.hip).
-#ifdef MLA_DECODE_BF16_V3
-constexpr bool kDecodeBf16V2 = false;
-#else
-constexpr bool kDecodeBf16V2 = true;
-#endif
-
 constexpr int kGenMaxLatent = 1024;
 constexpr int kGenMaxRow = 1280;
 constexpr int kGenMaxHead = 1024;
@@ -299,9 +291,7 @@ mla_status_t decode_impl(const mla_dims_t* dims, int32_t batch, const void* q_la
     a.o_lat = o_lat;
     a.o_dt = o_dt;
     a.lse = lse;
-    if (!fast) e = launch_decode_lite(a, st);
-    else if (cache->dtype == MLA_BF16 && !kDecodeBf16V2) e = launch_decode_v3(a, st);
-    else e = launch_decode_v2(a, st);
+    e = fast ? launch_decode_v2(a, st) : launch_decode_lite(a, st);
   } else {
     GenericDecodeArgs a{};
     a.q_lat = q_lat;

@@ -91,8 +91,6 @@ struct GemmArgs {
 };
 
 hipError_t launch_decode_v2(const V2DecodeArgs& a, hipStream_t st);
-// bf16 cache, 128 heads: 64-head teams with dimension-quarter score blocks
-hipError_t launch_decode_v3(const V2DecodeArgs& a, hipStream_t st);
 // 16 heads, d_c = 512, d_rope = 64, page 64, bf16 cache and queries (same arguments)
 hipError_t launch_decode_lite(const V2DecodeArgs& a, hipStream_t st);
 hipError_t launch_cache_store(const CacheStoreArgs& a, int batch, hipStream_t st);
