@@ -306,6 +306,20 @@ def run(args, workload=None, partition=None, cpu=True, copy_tbps=None):
         if ev is not None:
             ev[4].record(stream)
 
+    # Settle: back-to-back steps for args.settle seconds before the warm-up
+    # steps.  The GPU's clocks ramp up over the first few hundred steps after
+    # idle (the same step takes ~157 us after 10 steps and ~128 us from ~1000
+    # on), and the first pass over the rotated weight copies pays first-touch
+    # TLB misses; a decode server runs in the settled state.  Untimed and
+    # reported as settle_steps.
+    settle_steps = 0
+    if args.settle > 0:
+        t_end = time.perf_counter() + args.settle
+        while time.perf_counter() < t_end:
+            for _ in range(25):
+                one(settle_steps)
+                settle_steps += 1
+            torch.cuda.synchronize()
     for i in range(args.warmup):
         one(i)
     torch.cuda.synchronize()
@@ -365,7 +379,8 @@ def run(args, workload=None, partition=None, cpu=True, copy_tbps=None):
         value = B * q_len * args.steps / (total_ms * 1e-3)
     res = {
         "metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "settle_steps": settle_steps, "settle_s": args.settle,
+        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wname, "batch": len(lens), "sum_cache_tokens": T, "cache_dtype": w.cache_dtype,
                    "heads": n_h, "d_latent": D_C, "d_rope": D_R, "page_size": 64,
@@ -447,7 +462,8 @@ EXTRA_WORKLOADS = (
 def summary(r):
     """The per-workload figures kept in the headline line's `other_workloads`."""
     out = {k: r[k] for k in ("value", "unit", "ms_per_step", "query_tokens_per_s", "cache_tokens_per_s",
-                             "step_TBps", "step_TFLOPs", "step_roofline", "warm_ms_per_step") if k in r}
+                             "step_TBps", "step_TFLOPs", "step_roofline", "warm_ms_per_step", "steps", "warmup",
+                             "settle_steps") if k in r}
     out["config"] = {k: r["config"][k] for k in ("workload", "batch", "sum_cache_tokens", "cache_dtype",
                                                  "partition")}
     if "roofline" in r:
@@ -846,6 +862,8 @@ def main():
     ap.add_argument("--unfused", action="store_true",
                     help="run mla_merge_splits + mla_out_proj (mla_decode_multi + mla_out_proj) instead of "
                          "mla_merge_out_proj (mla_decode_multi_out_proj), for comparison")
+    ap.add_argument("--settle", type=float, default=0.5,
+                    help="seconds of untimed back-to-back steps before the warm-up steps (clock ramp, TLB warm-up)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--headline-only", action="store_true",
                     help="time the ragged workload alone (no other decode workloads first)")

@@ -205,8 +205,9 @@ mla_status_t mla_merge_splits(const mla_dims_t* dims, int32_t batch,
  *   o_lat: [batch, q_len, n_h, d_c] (o_dt), lse: [batch, q_len, n_h] or NULL.
  * One call runs the whole attention, merge included: each (sequence, new
  * token) pair is a virtual sequence of mla_decode's batch * q_len, with the
- * partition `part` applied to the virtual batch; the virtual lengths and block
- * table live in the workspace.  Same cache and dtype rules as mla_decode.
+ * partition `part` applied to the virtual batch; the virtual lengths live in
+ * the workspace, and virtual sequence b*q_len + t reads sequence b's
+ * block-table row in place.  Same cache and dtype rules as mla_decode.
  *   workspace: mla_decode_multi_workspace_size(...) bytes, 16-B aligned (never 0).
  */
 mla_status_t mla_decode_multi_workspace_size(const mla_dims_t* dims, int32_t batch, int32_t q_len,

@@ -237,7 +237,7 @@ namespace mla {
 mla_status_t decode_impl(const mla_dims_t* dims, int32_t batch, const void* q_lat, const void* q_pe,
                          mla_dtype_t q_dt, const mla_paged_cache_t* cache, float softmax_scale,
                          const mla_partition_t* part, void* workspace, size_t workspace_bytes, void* o_lat,
-                         mla_dtype_t o_dt, float* lse, void* stream, bool dry, size_t o_elem) {
+                         mla_dtype_t o_dt, float* lse, void* stream, bool dry, size_t o_elem, int bt_div) {
   if (mla_status_t s = check_dims(dims)) return s;
   if (!cache || !q_lat || !o_lat || (dims->d_rope > 0 && !q_pe)) return MLA_ERR_INVALID_ARG;
   if (!cache->kv || !cache->block_table || !cache->seq_lens) return MLA_ERR_INVALID_ARG;
@@ -282,6 +282,7 @@ mla_status_t decode_impl(const mla_dims_t* dims, int32_t batch, const void* q_la
     a.seq_lens = cache->seq_lens;
     a.max_pages = cache->max_pages_per_seq;
     a.num_pages = cache->num_pages;
+    a.bt_div = bt_div;
     a.n_items = n_items;
     a.scale_log2 = softmax_scale * kLog2e;
     a.pp = pp;
@@ -304,6 +305,7 @@ mla_status_t decode_impl(const mla_dims_t* dims, int32_t batch, const void* q_la
     a.seq_lens = cache->seq_lens;
     a.max_pages = cache->max_pages_per_seq;
     a.num_pages = cache->num_pages;
+    a.bt_div = bt_div;
     a.n_heads = dims->n_heads;
     a.d_rope = dims->d_rope;
     a.d_latent = dims->d_latent;
@@ -368,7 +370,7 @@ namespace {
 // mla_decode_multi workspace: virtual lengths, virtual block table, then the
 // workspace of the decode over batch * q_len virtual sequences.
 struct MultiLayout {
-  size_t lens, bt, dec, dec_bytes, total;
+  size_t lens, dec, dec_bytes, total;
 };
 
 mla_status_t multi_layout(const mla_dims_t* dims, int32_t batch, int32_t q_len, int32_t max_pages,
@@ -382,8 +384,7 @@ mla_status_t multi_layout(const mla_dims_t* dims, int32_t batch, int32_t q_len, 
   if (mla_status_t s = resolve(dims, int(vb), max_pages, page_size, part, &pp, &n_items, n_slots)) return s;
   MultiLayout m{};
   m.lens = 0;
-  m.bt = align256(size_t(vb) * sizeof(int32_t));
-  m.dec = m.bt + align256(size_t(vb) * max_pages * sizeof(int32_t));
+  m.dec = align256(size_t(vb) * sizeof(int32_t));
   m.dec_bytes = ws_layout(dims, *n_slots, int(vb), pp.mode == PART_BALANCED).total;
   m.total = m.dec + m.dec_bytes;
   *M = m;
@@ -399,7 +400,7 @@ mla_status_t mla_decode(const mla_dims_t* dims, int32_t batch, const void* q_lat
                         const mla_partition_t* part, void* workspace, size_t workspace_bytes, void* o_lat,
                         mla_dtype_t o_dt, float* lse, void* stream) {
   return decode_impl(dims, batch, q_lat, q_pe, q_dt, cache, softmax_scale, part, workspace, workspace_bytes, o_lat,
-                     o_dt, lse, stream, false, sizeof(float));
+                     o_dt, lse, stream, false, sizeof(float), 1);
 }
 
 mla_status_t mla_merge_splits(const mla_dims_t* dims, int32_t batch, const int32_t* seq_lens, int32_t page_size,
@@ -458,18 +459,16 @@ mla_status_t decode_multi_impl(const mla_dims_t* dims, int32_t batch, int32_t q_
   const int vb = batch * q_len;
   mla_paged_cache_t vc = *cache;
   vc.seq_lens = reinterpret_cast<const int32_t*>(ws + M.lens);
-  vc.block_table = reinterpret_cast<const int32_t*>(ws + M.bt);
   void* dec_ws = M.dec_bytes ? static_cast<void*>(ws + M.dec) : nullptr;
   if (mla_status_t s = decode_impl(dims, vb, q_lat, q_pe, q_dt, &vc, softmax_scale, part, dec_ws, M.dec_bytes, o_lat,
-                                   o_dt, lse, stream, true, sizeof(float)))
+                                   o_dt, lse, stream, true, sizeof(float), q_len))
     return s;
   if (batch == 0) return MLA_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (launch_expand(cache->seq_lens, cache->block_table, batch, q_len, cache->max_pages_per_seq,
-                    reinterpret_cast<int32_t*>(ws + M.lens), reinterpret_cast<int32_t*>(ws + M.bt), st) != hipSuccess)
+  if (launch_expand(cache->seq_lens, batch, q_len, reinterpret_cast<int32_t*>(ws + M.lens), st) != hipSuccess)
     return MLA_ERR_HIP;
   if (mla_status_t s = decode_impl(dims, vb, q_lat, q_pe, q_dt, &vc, softmax_scale, part, dec_ws, M.dec_bytes, o_lat,
-                                   o_dt, lse, stream, false, sizeof(float)))
+                                   o_dt, lse, stream, false, sizeof(float), q_len))
     return s;
   if (!w_uv)
     return mla_merge_splits(dims, vb, vc.seq_lens, cache->page_size, cache->max_pages_per_seq, part, dec_ws,

@@ -12,7 +12,7 @@ namespace mla {
 mla_status_t decode_impl(const mla_dims_t* dims, int32_t batch, const void* q_lat, const void* q_pe,
                          mla_dtype_t q_dt, const mla_paged_cache_t* cache, float softmax_scale,
                          const mla_partition_t* part, void* workspace, size_t workspace_bytes, void* o_lat,
-                         mla_dtype_t o_dt, float* lse, void* stream, bool dry, size_t o_elem);
+                         mla_dtype_t o_dt, float* lse, void* stream, bool dry, size_t o_elem, int bt_div);
 
 // mla_merge_splits' checks and launch, with the same o_elem convention.
 mla_status_t merge_impl(const mla_dims_t* dims, int32_t batch, const int32_t* seq_lens, int32_t page_size,

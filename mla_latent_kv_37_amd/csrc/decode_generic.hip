@@ -63,7 +63,7 @@ __global__ __launch_bounds__(kGenThreads) void decode_generic_kernel(GenericDeco
     float o[kGenMaxCols];
 #pragma unroll
     for (int k = 0; k < kGenMaxCols; ++k) o[k] = 0.f;
-    const int32_t* bt = a.block_table + int64_t(b) * a.max_pages;
+    const int32_t* bt = a.block_table + int64_t(b / a.bt_div) * a.max_pages;
     for (int tt = sg.t0; tt < sg.t1; tt += kGenThreads) {
       const int t = tt + tid;
       float s = -INFINITY;

@@ -141,7 +141,7 @@ __global__ __launch_bounds__(kLThreads) void decode_lite_kernel(V2DecodeArgs a) 
   while (it.next(sg)) {
     const int b = uniform(sg.b);
     const int t0 = uniform(sg.t0), t1 = uniform(sg.t1);
-    const int32_t* bt = a.block_table + int64_t(b) * a.max_pages + t0 / kLPage;
+    const int32_t* bt = a.block_table + int64_t(b / a.bt_div) * a.max_pages + t0 / kLPage;
     const char* kv = static_cast<const char*>(a.kv);
     const int len = t1 - t0;
     const int npages = ceil_div(len, kLPage);

@@ -118,18 +118,23 @@ __device__ __forceinline__ void wait_tile_f8(int wave, bool newer_in_flight) {
 }
 
 // Dequantise a staged tile into a bf16 tile buffer.  Item i (0..2303) is one
-// bf16 chunk (8 values) of one row; 16 consecutive items cover 8 consecutive
-// chunks of one chunk group in 2 consecutive rows, so a 16-lane group of the
-// 16-byte LDS writes hits 16 distinct bank quads.  Rows t >= valid (past the
-// sequence end) are written as zeros, not code * scale: their staged scales
-// may be anything.
+// bf16 chunk (8 values) of one row; the 16 consecutive items of group
+// grp = i >> 4 cover the 8 chunks of chunk group grp >> 4 in rows
+// 2(grp & 15) and 2(grp & 15) + 1, so a 16-lane group of the 16-byte LDS writes
+// hits 16 distinct bank quads, and every address is shifts and masks of the
+// thread id (recomputed per tile from an opaque copy of it: held across the
+// tile loop, these addresses were the registers the kernel spilled).  Rows
+// t >= valid (past the sequence end) are written as zeros, not code * scale:
+// their staged scales may be anything.
 __device__ __forceinline__ void convert_tile_f8(uint32_t stage, uint32_t buf, int valid) {
+  int tx = int(threadIdx.x);
+  asm volatile("" : "+v"(tx));
 #pragma unroll
   for (int r = 0; r < 5; ++r) {
-    const int i = r * kDecThreads + int(threadIdx.x);
+    const int i = r * kDecThreads + tx;
     if (r < 4 || i < kTileTok * (kV2Row / 8)) {
       const int grp = i >> 4;
-      const int t = 2 * (grp / 9) + ((i >> 3) & 1), c = 8 * (grp % 9) + (i & 7);
+      const int t = 2 * (grp & 15) + ((i >> 3) & 1), c = 8 * (grp >> 4) + (i & 7);
       typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
       const u32x2 code = *reinterpret_cast<const u32x2 MLA_LDS*>((const char MLA_LDS*)(uintptr_t)(stage + uint32_t(t * kV2Row + c * 8)));
       const float sc = *reinterpret_cast<const float MLA_LDS*>(
@@ -215,7 +220,7 @@ void decode_v2_kernel(V2DecodeArgs a) {
   while (it.next(sg)) {
     const int b = uniform(sg.b);
     const int t0 = uniform(sg.t0), t1 = uniform(sg.t1);   // t0 is a multiple of the page size
-    const int32_t* bt = a.block_table + int64_t(b) * a.max_pages + t0 / kV2Page;
+    const int32_t* bt = a.block_table + int64_t(b / a.bt_div) * a.max_pages + t0 / kV2Page;
     const char* kv = static_cast<const char*>(a.kv);
     const int ntiles = ceil_div(t1 - t0, kTileTok);
     auto tile_src = [&](int k, int page_id) -> const char* {

@@ -17,6 +17,7 @@ struct GenericDecodeArgs {
   const int32_t* seq_lens;
   int max_pages;
   int num_pages;           // page ids outside [0, num_pages) read as empty pages
+  int bt_div;              // sequence b reads block-table row b / bt_div (q_len of a multi-token decode, else 1)
   int n_heads, d_rope, d_latent;
   float scale;
   PartParams pp;
@@ -38,6 +39,7 @@ struct V2DecodeArgs {
   const int32_t* seq_lens;
   int max_pages;
   int num_pages;           // page ids outside [0, num_pages) read as empty pages
+  int bt_div;              // sequence b reads block-table row b / bt_div (q_len of a multi-token decode, else 1)
   int n_items;
   float scale_log2;        // softmax_scale * log2(e)
   PartParams pp;
@@ -119,8 +121,7 @@ hipError_t launch_query_finish(const QueryFinishArgs& a, hipStream_t st);
 hipError_t launch_merge(const MergeArgs& a, int batch, hipStream_t st);
 // merge of split partials + W^UV projection (d_h 128, d_c 512, bf16)
 hipError_t launch_merge_proj(const MergeArgs& a, const void* w_uv, void* o_heads, int batch, hipStream_t st);
-hipError_t launch_expand(const int32_t* seq_lens, const int32_t* block_table, int batch, int q_len, int max_pages,
-                         int32_t* lens_out, int32_t* bt_out, hipStream_t st);
+hipError_t launch_expand(const int32_t* seq_lens, int batch, int q_len, int32_t* lens_out, hipStream_t st);
 hipError_t launch_absorb_generic(const void* q, mla_dtype_t q_dt, const void* w, mla_dtype_t w_dt, void* out,
                                  mla_dtype_t o_dt, int batch, int n_heads, int d_head, int d_latent, hipStream_t st);
 hipError_t launch_outproj_generic(const void* o, mla_dtype_t o_dt, const void* w, mla_dtype_t w_dt, void* out,

@@ -68,10 +68,10 @@ extern "C" mla_status_t mla_decode_noalloc(const mla_dims_t* dims, int32_t batch
     if (mla_status_t s = scratch_ptr(&ws)) return s;
   // every argument is checked before anything is enqueued
   if (mla_status_t s = decode_impl(dims, batch, q_lat, q_pe, q_dt, cache, softmax_scale, part, ws, need, o_lat, o_dt,
-                                   lse, stream, true, o_elem))
+                                   lse, stream, true, o_elem, 1))
     return s;
   if (mla_status_t s = decode_impl(dims, batch, q_lat, q_pe, q_dt, cache, softmax_scale, part, ws, need, o_lat, o_dt,
-                                   lse, stream, false, o_elem))
+                                   lse, stream, false, o_elem, 1))
     return s;
   return merge_impl(dims, batch, cache->seq_lens, cache->page_size, cache->max_pages_per_seq, part, ws, need, o_lat,
                     o_dt, lse, stream, o_elem);

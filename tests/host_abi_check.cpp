@@ -39,7 +39,7 @@ hipError_t launch_reduce_cast(const float*, int, int64_t, void*, mla_dtype_t, hi
 hipError_t launch_query_finish(const QueryFinishArgs&, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_merge(const MergeArgs&, int, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_merge_proj(const MergeArgs&, const void*, void*, int, hipStream_t) { ++g_launches; return hipSuccess; }
-hipError_t launch_expand(const int32_t*, const int32_t*, int, int, int, int32_t*, int32_t*, hipStream_t) {
+hipError_t launch_expand(const int32_t*, int, int, int32_t*, hipStream_t) {
   ++g_launches;
   return hipSuccess;
 }
