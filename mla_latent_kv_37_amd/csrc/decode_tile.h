@@ -56,9 +56,9 @@ __device__ __forceinline__ int dma_voff(int wave, int lane) {
   return row * kRowBytes + (((lane & 7) ^ swz_f(row)) * 16);
 }
 
-// Issue this wavefront's loads of one tile.  With or without the scalar offset
-// in the hardware range check, a row is in range exactly when it is below
-// `valid`, so rows past the sequence end read as zeros.
+// Tile loads.  With or without the scalar offset in the hardware range check,
+// a row is in range exactly when it is below `valid`, so rows past the
+// sequence end read as zeros.
 // The loads carry the non-temporal hint: the cache is streamed once per step,
 // and without the hint it pushes the step's reused data (the weights, the
 // absorbed queries, the split partials) out of the caches (measured: 3.6 us
@@ -68,22 +68,31 @@ __device__ __forceinline__ int dma_voff(int wave, int lane) {
 // completion is waited for explicitly (vmcnt) before the barrier that publishes
 // a tile.  The compiler's own vmcnt waits for other loads stay correct, only
 // possibly stricter, since these loads are not counted by it.
-__device__ __forceinline__ void issue_tile(const char* src, int valid, uint32_t buf, int wave) {
-  // per-lane offset, recomputed at each use from an opaque lane id instead of
-  // being held in a register across the tile loop
-  int ln = threadIdx.x & 63;
-  asm volatile("" : "+v"(ln));
-  const int voff = dma_voff(wave, ln);
-  const uint64_t base = reinterpret_cast<uint64_t>(src);
+// TileRowLoad: the loads of one tile's row block rb (rows 8rb..8rb+7, all 9
+// chunk groups), 9 one-block loads.  `init` sets up the buffer descriptor and the per-lane
+// offset, `group` issues chunk group g, so that a caller can spread the 9
+// issues over other work.
+struct TileRowLoad {
   i32x4 rsrc;
-  rsrc[0] = uniform(int(uint32_t(base)));
-  rsrc[1] = uniform(int(uint32_t(base >> 32) & 0xFFFFu));  // stride 0
-  rsrc[2] = uniform(valid * kRowBytes);
-  rsrc[3] = int(kBufferFlags);
-  if (wave < 4) return;
-#pragma unroll
-  for (int g = 0; g < 9; ++g) {
-    const int m0 = uniform(int(buf + uint32_t((4 * g + (wave & 3)) * 1024)));
+  int voff;
+  uint32_t buf;
+  int rb;
+  __device__ __forceinline__ void init(const char* src, int valid, uint32_t buf_, int rb_) {
+    // per-lane offset, recomputed at each use from an opaque lane id instead of
+    // being held in a register across the tile loop
+    int ln = threadIdx.x & 63;
+    asm volatile("" : "+v"(ln));
+    voff = dma_voff(rb_, ln);
+    const uint64_t base = reinterpret_cast<uint64_t>(src);
+    rsrc[0] = uniform(int(uint32_t(base)));
+    rsrc[1] = uniform(int(uint32_t(base >> 32) & 0xFFFFu));  // stride 0
+    rsrc[2] = uniform(valid * kRowBytes);
+    rsrc[3] = int(kBufferFlags);
+    buf = buf_;
+    rb = rb_;
+  }
+  __device__ __forceinline__ void group(int g) const {
+    const int m0 = uniform(int(buf + uint32_t((4 * g + rb) * 1024)));
     const int soff = uniform(g * 128);
     asm volatile(
         "s_mov_b32 m0, %0\n\t"
@@ -93,6 +102,16 @@ __device__ __forceinline__ void issue_tile(const char* src, int valid, uint32_t 
         : "s"(m0), "v"(voff), "s"(rsrc), "s"(soff)
         : "memory", "m0");
   }
+};
+
+// All of one tile's loads of this wavefront in an 8-wavefront workgroup
+// (team Y, wavefronts 4-7, loads row block wave - 4)
+__device__ __forceinline__ void issue_tile(const char* src, int valid, uint32_t buf, int wave) {
+  if (wave < 4) return;
+  TileRowLoad ld;
+  ld.init(src, valid, buf, wave & 3);
+#pragma unroll
+  for (int g = 0; g < 9; ++g) ld.group(g);
 }
 
 // wait until this wavefront's loads of the tile before the newest are done

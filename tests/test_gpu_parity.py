@@ -10,6 +10,7 @@ import numpy as np
 import pytest
 
 import oracle
+import synth
 from _cases import (TOL, Worst, check_lse, check_vec, compare_seq, direct_case, from_h_case, host, lse_tolerance,
                     run_step, to_device)
 
@@ -184,6 +185,49 @@ def test_v2_split_partials(gain):
     if gain > 1:
         spread = max(np.ptp(case.reference(b)["lse"]) for b in range(len(lens)))
         print(f"  lse spread across heads {spread:.2f} (sharp softmax exercised)", flush=True)
+
+
+def test_v2_max_jump_past_reference():
+    """A token whose score exceeds every score of its segment's first tile by far
+    more than 64 log2 units.  The bf16 kernel fixes each head's reference max at
+    a segment's first tile and lets later probabilities exceed 1; past that
+    bound it recomputes the segment with the exact maximum.  Row 300 of sequence
+    0 and row 40 of sequence 1 are c * sign pattern of head 0's absorbed query
+    (latent and RoPE parts), so head 0's softmax is nearly one-hot there; the
+    rows sit in the first tile's segment under every partition below."""
+    from oracle.mla import head_rows
+    from _cases import case_from_rows
+    lens = [700, 1500]
+    cid = 3
+    inp = synth.direct_inputs_for(cid, seed=21, lens=lens)
+    w = inp["workload"]
+    rows = [r.copy() for r in inp["rows"]]
+    base = case_from_rows(w.dims, rows, inp["q_nope"], inp["q_pe"], inp["W_UK"], inp["W_UV"], "bf16", "bf16",
+                          synth.rng_for(cid, synth.S_PERM, 21), max_pages=32)
+    d = w.dims
+    log2e = 1.0 / math.log(2.0)
+    for b, t_star in ((0, 300), (1, 40)):
+        q_lat0 = head_rows(base.W_UK, 0, d.d_head).T @ base.q_nope[b, 0]
+        pattern = np.concatenate([np.sign(q_lat0), np.sign(base.q_pe[b, 0])])
+        r0 = oracle.attend_head(base.q_nope[b, 0], base.q_pe[b, 0], base.stored_rows(b)[:32, :d.d_latent],
+                                base.stored_rows(b)[:32, d.d_latent:], base.W_UK, base.W_UV, 0, base.scale)
+        l1 = np.abs(q_lat0).sum() + np.abs(base.q_pe[b, 0]).sum()
+        # smallest power of two that puts the jump past 96 log2 units (exact in bf16)
+        need = (96.0 / log2e + r0["s"].max()) / (base.scale * l1)
+        c = 2.0 ** math.ceil(math.log2(max(need, 1.0)))
+        rows[b][t_star] = (c * pattern).astype(np.float32)
+    case = case_from_rows(w.dims, rows, inp["q_nope"], inp["q_pe"], inp["W_UK"], inp["W_UV"], "bf16", "bf16",
+                          synth.rng_for(cid, synth.S_PERM, 21), max_pages=32)
+    for b, t_star in ((0, 300), (1, 40)):
+        r = oracle.attend_head(case.q_nope[b, 0], case.q_pe[b, 0], case.stored_rows(b)[:, :d.d_latent],
+                               case.stored_rows(b)[:, d.d_latent:], case.W_UK, case.W_UV, 0, case.scale)
+        jump = (r["s"][t_star] - r["s"][:32].max()) * log2e
+        print(f"  seq {b}: token {t_star} score jump over the first tile {jump:.1f} log2 units", flush=True)
+        assert jump > 64.0 and r["p"][t_star] > 0.99
+    dev = to_device(case)
+    for part in [(0, 0), (256, 0), (0, -1)]:
+        print(f"case: V2 bf16 max jump lens={lens} part={part}", flush=True)
+        compare_all(case, run_step(case, dev, *part), TOL["bf16"])
 
 
 # ---------------------------------------------------------------------------
