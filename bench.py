@@ -487,7 +487,7 @@ def _db(d):
 
 
 def _short(name: str) -> str:
-    name = name.split("(")[0]
+    name = name.replace("(anonymous namespace)::", "").split("(")[0]
     for pre in ("void ", "mla::"):
         name = name.replace(pre, "")
     return name[:60]
