@@ -230,6 +230,44 @@ def test_v2_max_jump_past_reference():
         compare_all(case, run_step(case, dev, *part), TOL["bf16"])
 
 
+@pytest.mark.parametrize("cfg", [3, 5], ids=["bf16", "fp8"])
+def test_v2_bad_page_ids_and_overlong_lengths(cfg):
+    """A block-table entry outside [0, num_pages) reads as a page of zero rows
+    (score 0 and value 0: those tokens are still attended), and a length above
+    max_pages_per_seq * page_size is clamped to it.  Sequence 1's third page id
+    is set past the cache; sequence 2 fills its block-table row (11 pages) and its
+    length is raised by 100.  References: the oracle on the rows the kernel
+    reads (sequence 1 with tokens 128-191 zero; sequence 2 at its true length)."""
+    import torch
+    lens = [300, 700, 704]
+    case = direct_case(cfg, lens, max_pages=11, seed=33)
+    dev = to_device(case)
+    num_pages = case.cache.kv.shape[0]
+    bt = case.cache.block_table.copy()
+    bt[1, 2] = num_pages + 5
+    sl = case.cache.seq_lens.copy()
+    sl[2] += 100
+    dev["cache"].block_table.copy_(torch.from_numpy(bt))
+    dev["cache"].seq_lens.copy_(torch.from_numpy(sl))
+    d = case.dims
+    rows1 = case.stored_rows(1).copy()
+    rows1[128:192] = 0.0
+    ref1 = oracle.attend(case.q_nope[1], case.q_pe[1], rows1[:, :d.d_latent], rows1[:, d.d_latent:], case.W_UK,
+                         case.W_UV, case.scale)
+    tol = TOL["fp8" if cfg == 5 else "bf16"]
+    for part in [(0, 0), (128, 0), (0, -1)]:
+        print(f"case: V2 {'fp8' if cfg == 5 else 'bf16'} bad page id / long length lens={lens} part={part}",
+              flush=True)
+        step = run_step(case, dev, *part)
+        q_lat, o_lat, lse, o_heads = host(step.q_lat), host(step.o_lat), host(step.lse), host(step.o_heads)
+        worst = Worst()
+        for b, ref, rows in ((0, case.reference(0), None), (1, ref1, rows1), (2, case.reference(2), None)):
+            got = {"q_lat": q_lat[b], "o_lat": o_lat[b], "lse": lse[b],
+                   "o_heads": o_heads[b].reshape(d.n_heads, d.d_head)}
+            compare_seq(case, b, ref, got, tol, None, worst, rows=rows)
+        worst.report(tol)
+
+
 # ---------------------------------------------------------------------------
 # fp8 E4M3 cache with 1x128 group scales
 # ---------------------------------------------------------------------------
