@@ -43,8 +43,8 @@ N_H, D_H, D_R, D_C = 128, 128, 64, 512
 ROW_BYTES_BF16 = (D_C + D_R) * 2
 CSRC = os.path.join(ROOT, "mla_latent_kv_37_amd", "csrc")
 # the decode kernel of each workload: (source file, name fragment in rocprofv3 output)
-DECODE_KERNEL = {"lite": ("decode_lite.hip", "decode_lite"), "fp8": ("decode_v2.hip", "decode_v2")}
-DEFAULT_DECODE_KERNEL = ("decode_wide.hip", "decode_wide")   # bf16 cache at 128 heads
+DECODE_KERNEL = {"lite": ("decode_lite.hip", "decode_lite")}
+DEFAULT_DECODE_KERNEL = ("decode_wide.hip", "decode_wide")   # bf16 and fp8 caches at 128 heads
 
 
 def traffic_json(workload: str) -> str:
@@ -431,9 +431,9 @@ def run(args, workload=None, partition=None, cpu=True, copy_tbps=None):
         res["roofline"] = {"bound": bound, "achieved": r_ach, "peak": r_peak, "unit": r_unit,
                            "frac": r_ach / r_peak, "traffic": traffic,
                            "hbm_GBps": ach, "hbm_frac": ach / HBM_PEAK_GBS,
-                           "kernel": ("decode_v2_kernel<true> (fp8 cache)" if cid == 5 else
+                           "kernel": ("decode_wide_kernel<true> (fp8 cache, one wavefront per SIMD)" if cid == 5 else
                                       "decode_lite_kernel (16 heads, bf16 cache)" if n_h == 16 else
-                                      "decode_wide_kernel (bf16 cache, one wavefront per SIMD)") +
+                                      "decode_wide_kernel<false> (bf16 cache, one wavefront per SIMD)") +
                                      ((" + expand_kernel + merge_kernel (mla_decode_multi)" if args.unfused else
                                        " + expand_kernel + merge_proj_kernel (mla_decode_multi_out_proj; the "
                                        "time includes the W^UV projection)") if q_len > 1 else ""),

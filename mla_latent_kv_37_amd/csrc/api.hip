@@ -183,8 +183,8 @@ const char* mla_status_string(mla_status_t s) {
 }
 
 const char* mla_build_info(void) {
-  return "libmla gfx950: absorb(v2 mfma, generic), decode(v2 bf16 one-wavefront-per-SIMD mfma, v2 fp8-dequant mfma "
-         "ping-pong, 16-head bf16 mfma, "
+  return "libmla gfx950: absorb(v2 mfma, generic), decode(v2 bf16 / fp8-dequant one-wavefront-per-SIMD mfma, "
+         "16-head bf16 mfma, "
          "generic f32/bf16/fp8), "
          "cache store (f32/bf16/fp8 1x128), cache append and query prep (weight-streaming mfma / generic "
          "products), "
@@ -294,8 +294,7 @@ mla_status_t decode_impl(const mla_dims_t* dims, int32_t batch, const void* q_la
     a.o_dt = o_dt;
     a.lse = lse;
     if (!fast) e = launch_decode_lite(a, st);
-    else if (a.kv_dt == MLA_BF16) e = launch_decode_wide(a, st);
-    else e = launch_decode_v2(a, st);
+    else e = launch_decode_wide(a, st);   // bf16 and fp8 caches
   } else {
     GenericDecodeArgs a{};
     a.q_lat = q_lat;

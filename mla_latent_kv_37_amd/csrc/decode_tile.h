@@ -173,6 +173,112 @@ __device__ __forceinline__ void issue_query_pe(const uint16_t* src, uint32_t qpe
 }
 
 
+// ---------------------------------------------------------------------------
+// fp8 cache (OCP E4M3 codes, one fp32 scale per token per 128-channel group;
+// the stored value is code * scale).  A tile's codes (32 rows x 576 B, one
+// contiguous run inside a page) and scales (32 x 5 fp32) are copied into an LDS
+// staging buffer, then dequantised once into the bf16 tile layout above, which
+// the score and PV steps read unchanged.
+constexpr int kF8TileBytes = kTileTok * kV2Row;       // 18432
+constexpr int kF8Groups = 5;                          // scale groups per row
+constexpr int kF8StageBytes = kF8TileBytes + 1024;    // codes, then scales (640 B used)
+constexpr int kF8Items = kTileTok * (kV2Row / 8);     // 2304 bf16 chunks of 8 values per tile
+
+// Loads of one staged tile: 18 one-KB code blocks and one scale block, by
+// wavefronts 0-3 (5 each for wavefronts 0-2, 4 for wavefront 3; load i: codes
+// block i for i < 18, the scales for i = 18).  Rows past `valid` read as zeros
+// (codes and scales).  Non-temporal, like the bf16 tile loads.
+__device__ __forceinline__ int f8_first_load(int wave) { return 5 * (wave & 3); }
+__device__ __forceinline__ int f8_num_loads(int wave) { return wave >= 4 ? 0 : (wave < 3 ? 5 : 4); }
+
+__device__ __forceinline__ void issue_tile_f8(const char* codes, const float* scales, int valid, uint32_t stage,
+                                              int wave) {
+  int ln = threadIdx.x & 63;
+  asm volatile("" : "+v"(ln));
+  const int voff = ln * 16;
+  const uint64_t cb = reinterpret_cast<uint64_t>(codes), sb = reinterpret_cast<uint64_t>(scales);
+  i32x4 rc, rs;
+  rc[0] = uniform(int(uint32_t(cb)));
+  rc[1] = uniform(int(uint32_t(cb >> 32) & 0xFFFFu));
+  rc[2] = uniform(valid * kV2Row);
+  rc[3] = int(kBufferFlags);
+  rs[0] = uniform(int(uint32_t(sb)));
+  rs[1] = uniform(int(uint32_t(sb >> 32) & 0xFFFFu));
+  // whole 16-byte lane loads: the last valid row's scales end mid-load when
+  // valid % 4 != 0, so the range is rounded up (to at most the tile's 640
+  // bytes, inside the page); the extra scales belong to rows >= valid, which
+  // the dequantisation writes as zeros whatever they hold
+  rs[2] = uniform((valid * kF8Groups * 4 + 15) & ~15);
+  rs[3] = int(kBufferFlags);
+  const int i0 = f8_first_load(wave), nl = f8_num_loads(wave);
+#pragma unroll
+  for (int j = 0; j < 5; ++j) {
+    if (j < nl) {
+      const int i = i0 + j;
+      const int m0 = uniform(int(stage + uint32_t(i * 1024)));
+      if (i < 18) {
+        const int soff = uniform(i * 1024);
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
+                     : : "s"(m0), "v"(voff), "s"(rc), "s"(soff) : "memory", "m0");
+      } else {
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+                     : : "s"(m0), "v"(voff), "s"(rs) : "memory", "m0");
+      }
+    }
+  }
+}
+
+// Dequantise item i (0..2303) of a staged tile into a bf16 tile buffer: one
+// bf16 chunk (8 values) of one row.  The 16 consecutive items of group
+// grp = i >> 4 cover the 8 chunks of chunk group grp >> 4 in rows
+// 2(grp & 15) and 2(grp & 15) + 1, so a 16-lane group of the 16-byte LDS writes
+// hits 16 distinct bank quads, and every address is shifts and masks of i.
+// Each value is code * scale in fp32, rounded to bf16.  Rows t >= valid (past
+// the sequence end) are written as zeros, not code * scale: their staged
+// scales may be anything.
+// The two halves: the LDS reads of an item (its 8 codes and its scale), and
+// the conversion and write, so that a caller can issue the reads of several
+// items well before their conversion.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+struct F8Item {
+  u32x2 code;
+  float sc;
+};
+__device__ __forceinline__ void f8_item_pos(int i, int& t, int& c) {
+  const int grp = i >> 4;
+  t = 2 * (grp & 15) + ((i >> 3) & 1);
+  c = 8 * (grp >> 4) + (i & 7);
+}
+__device__ __forceinline__ F8Item read_item_f8(uint32_t stage, int i) {
+  int t, c;
+  f8_item_pos(i, t, c);
+  F8Item x;
+  x.code = *reinterpret_cast<const u32x2 MLA_LDS*>((const char MLA_LDS*)(uintptr_t)(stage + uint32_t(t * kV2Row + c * 8)));
+  x.sc = *reinterpret_cast<const float MLA_LDS*>(
+      (const char MLA_LDS*)(uintptr_t)(stage + uint32_t(kF8TileBytes + (t * kF8Groups + (c >> 4)) * 4)));
+  return x;
+}
+__device__ __forceinline__ void write_item_f8(const F8Item& x, uint32_t buf, int valid, int i) {
+  int t, c;
+  f8_item_pos(i, t, c);
+  const u32x2 code = x.code;
+  const float sc = x.sc;
+  const auto f0 = __builtin_amdgcn_cvt_pk_f32_fp8(int(code[0]), false);
+  const auto f1 = __builtin_amdgcn_cvt_pk_f32_fp8(int(code[0]), true);
+  const auto f2 = __builtin_amdgcn_cvt_pk_f32_fp8(int(code[1]), false);
+  const auto f3 = __builtin_amdgcn_cvt_pk_f32_fp8(int(code[1]), true);
+  bf16x8 v;
+  v[0] = (__bf16)(f0[0] * sc); v[1] = (__bf16)(f0[1] * sc);
+  v[2] = (__bf16)(f1[0] * sc); v[3] = (__bf16)(f1[1] * sc);
+  v[4] = (__bf16)(f2[0] * sc); v[5] = (__bf16)(f2[1] * sc);
+  v[6] = (__bf16)(f3[0] * sc); v[7] = (__bf16)(f3[1] * sc);
+  if (t >= valid) v = bf16x8{};
+  *reinterpret_cast<bf16x8 MLA_LDS*>((char MLA_LDS*)(uintptr_t)(buf + uint32_t(tile_offset(t, c)))) = v;
+}
+__device__ __forceinline__ void convert_item_f8(uint32_t stage, uint32_t buf, int valid, int i) {
+  write_item_f8(read_item_f8(stage, i), buf, valid, i);
+}
+
 __device__ __forceinline__ bf16x8 lds_read_b128(uint32_t addr) {
   return *reinterpret_cast<const bf16x8 MLA_LDS*>((const char MLA_LDS*)(uintptr_t)addr);
 }

@@ -50,8 +50,15 @@ constexpr int kVAhead = 8;        // V^T fragment reads in flight ahead of the P
 constexpr float kRefSlack = 64.f; // log2 units a head's max may exceed its reference
 constexpr int kStageBytes = kWideWaves * 32768;   // epilogue staging (bf16 output)
 constexpr int kFlagOffset = kStageBytes;          // redo flags, past the staging area
+// fp8 cache: three bf16 tile buffers (tiles k, k+1 and k+2, which is written
+// by the dequantisation during tile k's PV phase) and two staging buffers of
+// codes and scales; the RoPE query is held in registers instead of LDS
+constexpr int kWideF8Bufs = 3;
+constexpr int kWideF8Area = kWideF8Bufs * kTileBytes + 2 * kF8StageBytes;
 static_assert(kWideBufs * kTileBytes + kQpeBytes <= 160 * 1024, "LDS budget");
-static_assert(kFlagOffset + 16 <= kWideBufs * kTileBytes, "flags inside the tile area");
+static_assert(kWideF8Area <= 160 * 1024, "LDS budget (fp8)");
+static_assert(kFlagOffset + 16 <= kWideBufs * kTileBytes && kFlagOffset + 16 <= kWideF8Area,
+              "flags inside the tile area");
 
 __device__ __forceinline__ bf16x8 pack_half(const f32x16& p, int base) {
   bf16x8 r;
@@ -77,10 +84,57 @@ __device__ __forceinline__ void score_mfma(f32x16& acc, bf16x8 a, bf16x8 b, bool
 }
 __device__ __forceinline__ void score_settle() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
 
+// fp8 dequantisation with 256 threads: item r*256 + tx (r = 0..8) of a staged
+// tile is row t = 2((tx>>4)&15) + ((tx>>3)&1), chunk c = 8r + (tx&7) (the item
+// order of convert_item_f8), so a thread's row and chunk slot are the same for
+// all 9 of its items and every address is a per-thread base plus an immediate:
+// codes at t*576 + 8(tx&7) + 64r, the scale at 18432 + 20t + 4(r>>1), the bf16
+// chunk at tile_offset(t, tx&7) + 4096r.
+struct F8Thread {
+  uint32_t code_off, scale_off, write_off;
+  int row;
+};
+__device__ __forceinline__ F8Thread f8_thread(int tx) {
+  F8Thread p;
+  const int t = 2 * ((tx >> 4) & 15) + ((tx >> 3) & 1), x = tx & 7;
+  p.row = t;
+  p.code_off = uint32_t(t * kV2Row + 8 * x);
+  p.scale_off = uint32_t(kF8TileBytes + t * kF8Groups * 4);
+  p.write_off = uint32_t(tile_offset(t, x));
+  return p;
+}
+__device__ __forceinline__ F8Item f8_read(uint32_t stage, const F8Thread& p, int r) {
+  F8Item x;
+  x.code = *reinterpret_cast<const u32x2 MLA_LDS*>((const char MLA_LDS*)(uintptr_t)(stage + p.code_off + uint32_t(64 * r)));
+  x.sc = *reinterpret_cast<const float MLA_LDS*>(
+      (const char MLA_LDS*)(uintptr_t)(stage + p.scale_off + uint32_t(4 * (r >> 1))));
+  return x;
+}
+// code * scale in fp32, rounded to bf16 (as convert_item_f8); rows past the
+// sequence end as zeros
+__device__ __forceinline__ void f8_write(const F8Item& x, uint32_t buf, const F8Thread& p, bool row_ok, int r) {
+  const auto f0 = __builtin_amdgcn_cvt_pk_f32_fp8(int(x.code[0]), false);
+  const auto f1 = __builtin_amdgcn_cvt_pk_f32_fp8(int(x.code[0]), true);
+  const auto f2 = __builtin_amdgcn_cvt_pk_f32_fp8(int(x.code[1]), false);
+  const auto f3 = __builtin_amdgcn_cvt_pk_f32_fp8(int(x.code[1]), true);
+  const float sc = x.sc;
+  bf16x8 v;
+  v[0] = (__bf16)(f0[0] * sc); v[1] = (__bf16)(f0[1] * sc);
+  v[2] = (__bf16)(f1[0] * sc); v[3] = (__bf16)(f1[1] * sc);
+  v[4] = (__bf16)(f2[0] * sc); v[5] = (__bf16)(f2[1] * sc);
+  v[6] = (__bf16)(f3[0] * sc); v[7] = (__bf16)(f3[1] * sc);
+  if (!row_ok) v = bf16x8{};
+  *reinterpret_cast<bf16x8 MLA_LDS*>((char MLA_LDS*)(uintptr_t)(buf + p.write_off + uint32_t(4096 * r))) = v;
+}
+
+// kF8: fp8 cache (tiles staged as codes and scales, dequantised once into the
+// bf16 tile layout); else bf16 cache.
+template <bool kF8>
 __global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_wide_kernel(V2DecodeArgs a) {
-  __shared__ __attribute__((aligned(2048))) char tiles_raw[kWideBufs * kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char qpe_raw[kQpeBytes];
+  constexpr int kTileArea = kF8 ? kWideF8Area : kWideBufs * kTileBytes;
+  __shared__ __attribute__((aligned(2048))) char tiles_raw[kTileArea];
+  __shared__ __attribute__((aligned(1024))) char qpe_raw[kF8 ? 16 : kQpeBytes];
   // XCD-aware item order (as in decode_v2.hip): block x runs on XCD x % 8
   const int n_items = a.n_items;
   const int item = (n_items & 7) == 0 ? int(blockIdx.x & 7) * (n_items >> 3) + int(blockIdx.x >> 3) : int(blockIdx.x);
@@ -114,7 +168,17 @@ void decode_wide_kernel(V2DecodeArgs a) {
     const char* kv = static_cast<const char*>(a.kv);
     const int ntiles = ceil_div(t1 - t0, kTileTok);
     auto tile_valid = [&](int k) { return min(kTileTok, t1 - t0 - k * kTileTok); };
-    auto tile_buf = [&](int k) { return tiles_lds + uint32_t((k & (kWideBufs - 1)) * kTileBytes); };
+    auto tile_buf = [&](int k) {
+      return tiles_lds + uint32_t((kF8 ? k % kWideF8Bufs : k & (kWideBufs - 1)) * kTileBytes);
+    };
+    // fp8: staging buffer of tile k, and the issue of its loads (a page id
+    // outside [0, num_pages) reads as zero codes and scales)
+    auto stage_buf = [&](int k) { return tiles_lds + uint32_t(kWideF8Bufs * kTileBytes + (k & 1) * kF8StageBytes); };
+    auto issue_f8 = [&](int k, int page_id) {
+      const bool ok = unsigned(page_id) < unsigned(a.num_pages);
+      const int64_t row0 = int64_t(ok ? page_id : 0) * kV2Page + (k & 1) * kTileTok;
+      issue_tile_f8(kv + row0 * kV2Row, a.scales + row0 * kF8Groups, ok ? tile_valid(k) : 0, stage_buf(k), wave);
+    };
     // this wavefront's row block of tile k; a page id outside [0, num_pages)
     // reads as a page of zero rows (page 0's address, empty range)
     auto start_tile = [&](TileRowLoad& ld, int k, int page_id) {
@@ -134,10 +198,12 @@ void decode_wide_kernel(V2DecodeArgs a) {
     const int page0 = load_const(bt, 0);
     const int page1 = ntiles > 2 ? load_const(bt, 1) : 0;
     // Query: this wavefront's 32 heads x 512 latent dims in four 128-dim passes
-    // through a 16 KB staging area per wavefront in tile buffers 2-3 (free
-    // until tile 2 is issued), two passes at a time; the RoPE query of all heads
-    // into its own area (blocks 2w, 2w+1, 2w+8, 2w+9 by wavefront w).
-    const uint32_t qstage = tiles_lds + uint32_t(2 * kTileBytes + wave * 16384);
+    // through a 16 KB staging area per wavefront (bf16: tile buffers 2-3, free
+    // until tile 2 is issued; fp8: tile buffers 1-2, free until tile 1 is
+    // dequantised), two passes at a time; the RoPE query of all heads into its
+    // own area (blocks 2w, 2w+1, 2w+8, 2w+9 by wavefront w), or for fp8 this
+    // wavefront's heads into registers.
+    const uint32_t qstage = tiles_lds + uint32_t((kF8 ? 1 : 2) * kTileBytes + wave * 16384);
     const uint16_t* const qsrc = a.q_lat + (int64_t(b) * kV2Heads + wave * 32) * kV2Lat;
     const uint16_t* const qpe_src = a.q_pe + int64_t(b) * kV2Heads * kV2Rope;
     // latent query slices (MFMA B operand): qf[st] holds dims 16st + 8(lane>>5)
@@ -154,16 +220,29 @@ void decode_wide_kernel(V2DecodeArgs a) {
           qf[8 * (pass0 + p) + t] = lds_read_b128(qstage + uint32_t(p * 8192 + r * 256 + ((c ^ (r & 15)) * 16)));
         }
     };
+    // fp8: RoPE query slices of head 32w + (lane&31) (MFMA B operand of the last
+    // four k-steps: dims 8(2j + (lane>>5)) .. +8)
+    bf16x8 qpe_r[4];
     issue_query_pass(qsrc, qstage);
     issue_query_pass(qsrc + 128, qstage + 8192);
-    issue_query_pe(qpe_src, qpe_lds, wave);
-    issue_query_pe(qpe_src, qpe_lds, wave + 4);
-    load_tile(0, page0);
-    if (ntiles > 1) {
-      load_tile(1, page0);
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(18));   // query passes 0-1 and RoPE query
+    if constexpr (kF8) {
+      const int ln = opaque_lane();
+      const uint16_t* const qp = qpe_src + (wave * 32 + (ln & 31)) * kV2Rope + 8 * (ln >> 5);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) qpe_r[j] = *reinterpret_cast<const bf16x8*>(qp + 16 * j);
+      issue_f8(0, page0);
+      if (ntiles > 1) issue_f8(1, page0);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     } else {
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(9));
+      issue_query_pe(qpe_src, qpe_lds, wave);
+      issue_query_pe(qpe_src, qpe_lds, wave + 4);
+      load_tile(0, page0);
+      if (ntiles > 1) {
+        load_tile(1, page0);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(18));   // query passes 0-1 and RoPE query
+      } else {
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(9));
+      }
     }
     read_query(0);
     __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));   // read before the area is refilled
@@ -175,7 +254,31 @@ void decode_wide_kernel(V2DecodeArgs a) {
     // so that it puts no waits for them inside the tile loop
     __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
     raw_barrier();   // tiles 0-1 and the RoPE query complete; staging areas free
-    if (ntiles > 2) load_tile(2, page1);
+    if constexpr (kF8) {
+      // tiles 0-1 dequantised by all threads; then staging buffer 0 takes tile 2
+      {
+        const F8Thread p = f8_thread(wave * 64 + opaque_lane());
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          if (kt < ntiles) {
+            const bool row_ok = p.row < tile_valid(kt);
+            F8Item x[3];   // reads two items ahead of each conversion
+            x[0] = f8_read(stage_buf(kt), p, 0);
+            x[1] = f8_read(stage_buf(kt), p, 1);
+#pragma unroll
+            for (int r = 0; r < 9; ++r) {
+              if (r + 2 < 9) x[(r + 2) % 3] = f8_read(stage_buf(kt), p, r + 2);
+              f8_write(x[r % 3], tile_buf(kt), p, row_ok, r);
+            }
+          }
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
+      raw_barrier();
+      if (ntiles > 2) issue_f8(2, page1);
+    } else {
+      if (ntiles > 2) load_tile(2, page1);
+    }
 
     // ---- score MFMAs of tile kt into sn, k-steps in order; the K fragments
     // (and for the RoPE steps the query fragments) are read kKAhead steps ahead.
@@ -201,9 +304,9 @@ void decode_wide_kernel(V2DecodeArgs a) {
         const int nx = st + kKAhead;
         if (nx < kScoreSteps) {
           kr[st % kKAhead] = lds_read_b128(kaddr(nx));
-          if (nx >= 32) qr[nx - 32] = lds_read_b128(qaddr(nx - 32));
+          if (!kF8 && nx >= 32) qr[nx - 32] = lds_read_b128(qaddr(nx - 32));
         }
-        score_mfma(sn, kc, st < 32 ? qf[st] : qr[st - 32], st == 0);
+        score_mfma(sn, kc, st < 32 ? qf[st] : kF8 ? qpe_r[st - 32] : qr[st - 32], st == 0);
         between(st);
         __builtin_amdgcn_sched_barrier(0);   // keep each step's order
       }
@@ -244,6 +347,11 @@ void decode_wide_kernel(V2DecodeArgs a) {
       }
       const bool more = k + 1 < ntiles;
       const bool load3 = k + 3 < ntiles;
+      // fp8: tile k+3's codes into the staging buffer that tile k+1's held
+      // (dequantised in the previous tile's PV phase, before the barrier)
+      if constexpr (kF8) {
+        if (load3) issue_f8(k + 3, page3);
+      }
 
       bf16x8 pk0, pk1;
       auto softmax_step = [&](int st) {
@@ -290,18 +398,47 @@ void decode_wide_kernel(V2DecodeArgs a) {
         for (int i = 0; i < kVAhead; ++i) vr[i] = vfrag(i);
       }
 
-      // ======== phase B: O^T += V^T . P^T of tile k | loads of tile k+3
+      // ======== phase B: O^T += V^T . P^T of tile k | bf16: loads of tile k+3;
+      // fp8: dequantisation of tile k+2 (9 items per thread)
       {
+        const bool conv = kF8 && k + 2 < ntiles;
+        if constexpr (kF8) {
+          if (k == 0 && conv) {
+            // tile 2's codes (issued before the loop; tile 3's stay in flight)
+            if (!load3) __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+            else if (wave < 3) __builtin_amdgcn_s_waitcnt(waitcnt_vm(5));
+            else __builtin_amdgcn_s_waitcnt(waitcnt_vm(4));
+            raw_barrier();
+          }
+        }
         TileRowLoad ld3;
-        if (load3) start_tile(ld3, k + 3, page3);
+        if (!kF8 && load3) start_tile(ld3, k + 3, page3);
+        F8Item f8x[3];   // fp8: ring of the items whose reads are in flight
+        // (computed whether or not this tile converts: a conditional definition
+        // leaves the compiler carrying and spilling both versions)
+        F8Thread f8p = f8_thread(wave * 64 + opaque_lane());   // (no register holds the thread id)
+        const bool f8_row_ok = f8p.row < tile_valid(k + 2);
+        const uint32_t f8_stage = stage_buf(k + 2), f8_buf = tile_buf(k + 2);
 #pragma unroll
         for (int st = 0; st < kPvSteps; ++st) {
           const bf16x8 vc = vr[st % kVAhead];
           if (st + kVAhead < kPvSteps) vr[st % kVAhead] = vfrag(st + kVAhead);
           const int mt = st & 15;
           acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vc, st < 16 ? pk0 : pk1, acc[mt], 0, 0, 0);
+          if constexpr (kF8) {
+            // item r's reads go out at step 3r - 5 (at least 0), its conversion
+            // at step 3r + 1: two items' reads in flight ahead of each conversion
+#pragma unroll
+            for (int r = 0; r < 9; ++r) {
+              if (conv && st == (3 * r - 5 < 0 ? 0 : 3 * r - 5)) f8x[r % 3] = f8_read(f8_stage, f8p, r);
+            }
+          }
           if (st % 3 == 1 && st / 3 < 9) {
-            if (load3) ld3.group(st / 3);
+            if constexpr (kF8) {
+              if (conv) f8_write(f8x[(st / 3) % 3], f8_buf, f8p, f8_row_ok, st / 3);
+            } else {
+              if (load3) ld3.group(st / 3);
+            }
           }
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -315,8 +452,8 @@ void decode_wide_kernel(V2DecodeArgs a) {
       // next tile into a wait for all.
       page3 = k + 4 < ntiles ? load_const(bt, (k + 4) >> 1) : 0;
       if (k + 2 < ntiles) {
-        if (load3) __builtin_amdgcn_s_waitcnt(waitcnt_vm(9));
-        else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        if (!kF8 && load3) __builtin_amdgcn_s_waitcnt(waitcnt_vm(9));
+        else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // fp8: tile k+3's codes
       }
       __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
       if (k + 2 < ntiles) raw_barrier();
@@ -402,8 +539,9 @@ void decode_wide_kernel(V2DecodeArgs a) {
 }  // namespace
 
 hipError_t launch_decode_wide(const V2DecodeArgs& a, hipStream_t st) {
-  if (a.kv_dt != MLA_BF16) return hipErrorInvalidValue;
-  decode_wide_kernel<<<a.n_items, kWideThreads, 0, st>>>(a);
+  if (a.kv_dt == MLA_FP8_E4M3) decode_wide_kernel<true><<<a.n_items, kWideThreads, 0, st>>>(a);
+  else if (a.kv_dt == MLA_BF16) decode_wide_kernel<false><<<a.n_items, kWideThreads, 0, st>>>(a);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
