@@ -1,4 +1,4 @@
-// Paged-cache tile staging shared by the 128-head decode kernels (V2 shapes:
+// Paged-cache tile staging of the 128-head decode kernel (V2 shapes:
 // 576-wide rows [c^KV | k^R], 64-token pages, bf16): the LDS tile layout, the
 // direct-to-LDS tile and query loads, and the LDS fragment reads.
 //
@@ -22,12 +22,7 @@ constexpr int kRowBytes = kV2Row * 2;                 // 1152
 constexpr int kPageBytes = kV2Page * kRowBytes;       // 73728
 constexpr int kTileTok = 32;
 constexpr int kTileBytes = kTileTok * kRowBytes;      // 36864
-constexpr int kNumBuf = 3;
-constexpr int kWaves = 8;
-constexpr int kDecThreads = 64 * kWaves;
-constexpr int kXsBytes = kWaves * 4096;               // partial-score exchange area
 constexpr int kQpeBytes = kV2Heads * kV2Rope * 2;     // RoPE part of the query, 16 KB
-constexpr float kRescaleSlack = 8.0f;                 // log2 units
 constexpr uint32_t kBufferFlags = 0x00020000u;        // raw buffer, 32-bit data format
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -41,13 +36,8 @@ __host__ __device__ constexpr int tile_offset(int t, int c) {
 }
 
 // Tile loads: block i = 4g + rb holds rows 8rb..8rb+7 of chunk group g (chunks
-// 8g..8g+7).  Wavefront 4 + rb (team Y) loads row block rb of all 9 chunk
-// groups: 36 one-block loads per tile.  Issuing them costs ~100 clocks per load
-// (the address unit takes one every ~16 clocks from the whole workgroup), so
-// they go out where that wait is off the critical path: in odd slots, right
-// after team Y's score MFMAs and before it publishes its partial scores, while
-// team X runs the longer softmax and PV (measured: 3% less decode time than
-// issuing them from team X at the start of its softmax slot).  Lane l of a block load
+// 8g..8g+7); a tile is 36 one-block loads, row block rb of all 9 chunk groups
+// being one wavefront's share.  Lane l of a block load
 // reads row 8rb + (l>>3), logical chunk 8g + ((l&7) ^ f(row)), so that it lands
 // at LDS offset i*1024 + 16*l; its byte offset in the tile is the per-lane
 // `voff` (fixed per wavefront) plus g*128 (the scalar offset).
@@ -103,23 +93,6 @@ struct TileRowLoad {
         : "memory", "m0");
   }
 };
-
-// All of one tile's loads of this wavefront in an 8-wavefront workgroup
-// (team Y, wavefronts 4-7, loads row block wave - 4)
-__device__ __forceinline__ void issue_tile(const char* src, int valid, uint32_t buf, int wave) {
-  if (wave < 4) return;
-  TileRowLoad ld;
-  ld.init(src, valid, buf, wave & 3);
-#pragma unroll
-  for (int g = 0; g < 9; ++g) ld.group(g);
-}
-
-// wait until this wavefront's loads of the tile before the newest are done
-// (team X issues none: it only waits for its other loads, if any)
-__device__ __forceinline__ void wait_tile(int wave, bool newer_in_flight) {
-  if (!newer_in_flight || wave < 4) __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-  else __builtin_amdgcn_s_waitcnt(waitcnt_vm(9));
-}
 
 // Query staging.  A wavefront's latent query (32 heads x 256 dims, 16 KB) is
 // copied into LDS in two passes of 128 dims (8 KB: 32 rows of 256 B) by
@@ -182,14 +155,13 @@ __device__ __forceinline__ void issue_query_pe(const uint16_t* src, uint32_t qpe
 constexpr int kF8TileBytes = kTileTok * kV2Row;       // 18432
 constexpr int kF8Groups = 5;                          // scale groups per row
 constexpr int kF8StageBytes = kF8TileBytes + 1024;    // codes, then scales (640 B used)
-constexpr int kF8Items = kTileTok * (kV2Row / 8);     // 2304 bf16 chunks of 8 values per tile
 
 // Loads of one staged tile: 18 one-KB code blocks and one scale block, by
 // wavefronts 0-3 (5 each for wavefronts 0-2, 4 for wavefront 3; load i: codes
 // block i for i < 18, the scales for i = 18).  Rows past `valid` read as zeros
 // (codes and scales).  Non-temporal, like the bf16 tile loads.
 __device__ __forceinline__ int f8_first_load(int wave) { return 5 * (wave & 3); }
-__device__ __forceinline__ int f8_num_loads(int wave) { return wave >= 4 ? 0 : (wave < 3 ? 5 : 4); }
+__device__ __forceinline__ int f8_num_loads(int wave) { return wave < 3 ? 5 : 4; }
 
 __device__ __forceinline__ void issue_tile_f8(const char* codes, const float* scales, int valid, uint32_t stage,
                                               int wave) {
@@ -228,56 +200,15 @@ __device__ __forceinline__ void issue_tile_f8(const char* codes, const float* sc
   }
 }
 
-// Dequantise item i (0..2303) of a staged tile into a bf16 tile buffer: one
-// bf16 chunk (8 values) of one row.  The 16 consecutive items of group
-// grp = i >> 4 cover the 8 chunks of chunk group grp >> 4 in rows
-// 2(grp & 15) and 2(grp & 15) + 1, so a 16-lane group of the 16-byte LDS writes
-// hits 16 distinct bank quads, and every address is shifts and masks of i.
-// Each value is code * scale in fp32, rounded to bf16.  Rows t >= valid (past
-// the sequence end) are written as zeros, not code * scale: their staged
-// scales may be anything.
-// The two halves: the LDS reads of an item (its 8 codes and its scale), and
-// the conversion and write, so that a caller can issue the reads of several
-// items well before their conversion.
+// The LDS reads of one dequantisation item (one bf16 chunk of 8 values of one
+// row): its 8 codes and its row's group scale.  Each value is code * scale in
+// fp32, rounded to bf16; rows past the sequence end are written as zeros, not
+// code * scale, since their staged scales may be anything.
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 struct F8Item {
   u32x2 code;
   float sc;
 };
-__device__ __forceinline__ void f8_item_pos(int i, int& t, int& c) {
-  const int grp = i >> 4;
-  t = 2 * (grp & 15) + ((i >> 3) & 1);
-  c = 8 * (grp >> 4) + (i & 7);
-}
-__device__ __forceinline__ F8Item read_item_f8(uint32_t stage, int i) {
-  int t, c;
-  f8_item_pos(i, t, c);
-  F8Item x;
-  x.code = *reinterpret_cast<const u32x2 MLA_LDS*>((const char MLA_LDS*)(uintptr_t)(stage + uint32_t(t * kV2Row + c * 8)));
-  x.sc = *reinterpret_cast<const float MLA_LDS*>(
-      (const char MLA_LDS*)(uintptr_t)(stage + uint32_t(kF8TileBytes + (t * kF8Groups + (c >> 4)) * 4)));
-  return x;
-}
-__device__ __forceinline__ void write_item_f8(const F8Item& x, uint32_t buf, int valid, int i) {
-  int t, c;
-  f8_item_pos(i, t, c);
-  const u32x2 code = x.code;
-  const float sc = x.sc;
-  const auto f0 = __builtin_amdgcn_cvt_pk_f32_fp8(int(code[0]), false);
-  const auto f1 = __builtin_amdgcn_cvt_pk_f32_fp8(int(code[0]), true);
-  const auto f2 = __builtin_amdgcn_cvt_pk_f32_fp8(int(code[1]), false);
-  const auto f3 = __builtin_amdgcn_cvt_pk_f32_fp8(int(code[1]), true);
-  bf16x8 v;
-  v[0] = (__bf16)(f0[0] * sc); v[1] = (__bf16)(f0[1] * sc);
-  v[2] = (__bf16)(f1[0] * sc); v[3] = (__bf16)(f1[1] * sc);
-  v[4] = (__bf16)(f2[0] * sc); v[5] = (__bf16)(f2[1] * sc);
-  v[6] = (__bf16)(f3[0] * sc); v[7] = (__bf16)(f3[1] * sc);
-  if (t >= valid) v = bf16x8{};
-  *reinterpret_cast<bf16x8 MLA_LDS*>((char MLA_LDS*)(uintptr_t)(buf + uint32_t(tile_offset(t, c)))) = v;
-}
-__device__ __forceinline__ void convert_item_f8(uint32_t stage, uint32_t buf, int valid, int i) {
-  write_item_f8(read_item_f8(stage, i), buf, valid, i);
-}
 
 __device__ __forceinline__ bf16x8 lds_read_b128(uint32_t addr) {
   return *reinterpret_cast<const bf16x8 MLA_LDS*>((const char MLA_LDS*)(uintptr_t)addr);

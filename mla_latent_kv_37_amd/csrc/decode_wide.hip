@@ -1,8 +1,8 @@
 // MLA decode at DeepSeek-V2 shapes over a bf16 cache, one wavefront per SIMD.
 //
-// The operation, the work items (partition.h), the split partials and the LDS
-// tile layout (decode_tile.h) are those of decode_v2.hip; what differs is the
-// division of the work inside a workgroup.  A workgroup has 4 wavefronts, one
+// One workgroup per work item (partition.h); a segment of a split sequence
+// writes its bf16 partial and lse, a whole sequence its final rows; tiles sit
+// in LDS in the layout of decode_tile.h.  A workgroup has 4 wavefronts, one
 // per SIMD, and wavefront w owns heads 32w..32w+31 entirely: all 576 dims of
 // their scores and all 512 output columns.  Per 32-token tile it computes
 //   S^T [32 tokens x 32 heads] = K [32 x 576] . Q^T [576 x 32]    (36 MFMAs)
@@ -85,8 +85,8 @@ __device__ __forceinline__ void score_mfma(f32x16& acc, bf16x8 a, bf16x8 b, bool
 __device__ __forceinline__ void score_settle() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
 
 // fp8 dequantisation with 256 threads: item r*256 + tx (r = 0..8) of a staged
-// tile is row t = 2((tx>>4)&15) + ((tx>>3)&1), chunk c = 8r + (tx&7) (the item
-// order of convert_item_f8), so a thread's row and chunk slot are the same for
+// tile is row t = 2((tx>>4)&15) + ((tx>>3)&1), chunk c = 8r + (tx&7) (a
+// 16-lane group of the 16-byte LDS writes then hits 16 distinct bank quads), so a thread's row and chunk slot are the same for
 // all 9 of its items and every address is a per-thread base plus an immediate:
 // codes at t*576 + 8(tx&7) + 64r, the scale at 18432 + 20t + 4(r>>1), the bf16
 // chunk at tile_offset(t, tx&7) + 4096r.
@@ -110,8 +110,7 @@ __device__ __forceinline__ F8Item f8_read(uint32_t stage, const F8Thread& p, int
       (const char MLA_LDS*)(uintptr_t)(stage + p.scale_off + uint32_t(4 * (r >> 1))));
   return x;
 }
-// code * scale in fp32, rounded to bf16 (as convert_item_f8); rows past the
-// sequence end as zeros
+// code * scale in fp32, rounded to bf16; rows past the sequence end as zeros
 __device__ __forceinline__ void f8_write(const F8Item& x, uint32_t buf, const F8Thread& p, bool row_ok, int r) {
   const auto f0 = __builtin_amdgcn_cvt_pk_f32_fp8(int(x.code[0]), false);
   const auto f1 = __builtin_amdgcn_cvt_pk_f32_fp8(int(x.code[0]), true);
@@ -135,7 +134,7 @@ void decode_wide_kernel(V2DecodeArgs a) {
   constexpr int kTileArea = kF8 ? kWideF8Area : kWideBufs * kTileBytes;
   __shared__ __attribute__((aligned(2048))) char tiles_raw[kTileArea];
   __shared__ __attribute__((aligned(1024))) char qpe_raw[kF8 ? 16 : kQpeBytes];
-  // XCD-aware item order (as in decode_v2.hip): block x runs on XCD x % 8
+  // XCD-aware item order: block x runs on XCD x % 8
   const int n_items = a.n_items;
   const int item = (n_items & 7) == 0 ? int(blockIdx.x & 7) * (n_items >> 3) + int(blockIdx.x >> 3) : int(blockIdx.x);
   if (item >= n_items) return;

@@ -92,8 +92,8 @@ struct GemmArgs {
   bool use_mfma;           // set by gemm_ws_plan
 };
 
-hipError_t launch_decode_v2(const V2DecodeArgs& a, hipStream_t st);
-// bf16 cache only: one wavefront per SIMD (decode_wide.hip)
+// 128 heads, d_c = 512, d_rope = 64, page 64, bf16 queries, bf16 or fp8 cache:
+// one wavefront per SIMD (decode_wide.hip)
 hipError_t launch_decode_wide(const V2DecodeArgs& a, hipStream_t st);
 // 16 heads, d_c = 512, d_rope = 64, page 64, bf16 cache and queries (same arguments)
 hipError_t launch_decode_lite(const V2DecodeArgs& a, hipStream_t st);

@@ -177,6 +177,45 @@ def attend_new_tokens(q_c: np.ndarray, q_r: np.ndarray, c_kv: np.ndarray, k_r: n
     return out
 
 
+def prefill_head(q_c_i: np.ndarray, q_r_i: np.ndarray, c_kv: np.ndarray, k_r: np.ndarray,
+                 W_UK: np.ndarray, W_UV: np.ndarray, i: int, scale: Optional[float] = None):
+    """Head i of the attention of a sequence's q_len newest tokens, all at once.
+
+    The same quantity as attend_new_tokens, written as matrices: the keys
+    k_{j,i} = [W^UK_i c^KV_j; k^R_j] and values v_{j,i} = W^UV_i c^KV_j of all T
+    cached rows are formed once ([V2-explainer] §2.2.1 and §2.2.2), the score
+    matrix S[t, j] = [q^C_{t,i}; q^R_{t,i}] . k_{j,i} * scale ([Key-tech] §1)
+    keeps, for new token t at position T - q_len + t, the rows j <= T - q_len + t
+    (the sum over earlier positions of [Key-tech] §1), each kept row of S is
+    soft-maxed and O = P V.  This is the prompt-processing (prefill) shape:
+    with q_len = T every cached token is new.
+    q_c_i [q_len, d_h], q_r_i [q_len, d_r], c_kv [T, d_c], k_r [T, d_r].
+    Returns dict(o [q_len, d_h], lse [q_len]); a token with no visible row gets
+    o = 0 and lse = -inf.
+    """
+    q_len, d_h = q_c_i.shape
+    T = c_kv.shape[0]
+    if scale is None:
+        scale = softmax_scale(d_h, q_r_i.shape[1])
+    k = np.concatenate([c_kv @ head_rows(W_UK, i, d_h).T, k_r], axis=1)   # [T, d_h + d_r]
+    v = c_kv @ head_rows(W_UV, i, d_h).T                                  # [T, d_h]
+    q = np.concatenate([q_c_i, q_r_i], axis=1)                            # [q_len, d_h + d_r]
+    s = (q @ k.T) * scale                                                 # [q_len, T]
+    visible = np.arange(T)[None, :] <= (T - q_len + np.arange(q_len))[:, None]
+    s = np.where(visible, s, -np.inf)
+    o = np.zeros((q_len, d_h))
+    lse = np.full(q_len, -np.inf)
+    for t in range(q_len):
+        if not visible[t].any():
+            continue
+        m = s[t].max()
+        e = np.exp(s[t] - m)
+        z = e.sum()
+        o[t] = (e / z) @ v
+        lse[t] = m + math.log(z)
+    return {"o": o, "lse": lse}
+
+
 def chunk_partials(q_c, q_r, c_kv, k_r, W_UK, W_UV, chunk: int, scale=None, heads=None):
     """Attention restricted to each chunk [s*chunk, min((s+1)*chunk, T)) of the cache.
 

@@ -31,7 +31,6 @@ static int g_fails = 0;
 // ---- stubs: kernel launchers (api.hip's only route to the device) ----
 namespace mla {
 hipError_t launch_decode_generic(const GenericDecodeArgs&, int, hipStream_t) { ++g_launches; return hipSuccess; }
-hipError_t launch_decode_v2(const V2DecodeArgs& a, hipStream_t) { ++g_launches; g_v2 = a; return hipSuccess; }
 hipError_t launch_decode_wide(const V2DecodeArgs& a, hipStream_t) { ++g_launches; g_v2 = a; return hipSuccess; }
 hipError_t launch_decode_lite(const V2DecodeArgs& a, hipStream_t) { ++g_launches; g_v2 = a; return hipSuccess; }
 hipError_t launch_cache_store(const CacheStoreArgs&, int, hipStream_t) { ++g_launches; return hipSuccess; }

@@ -129,6 +129,56 @@ def test_new_tokens_match_torch_sdpa_causal_mask(q_len, T):
             np.testing.assert_allclose(res[t]["o_heads"][i], o[t], rtol=1e-12, atol=1e-14)
 
 
+@pytest.mark.parametrize("q_len,T", [(9, 9), (4, 21), (6, 3), (1, 7)])
+def test_prefill_head_matches_per_token_attention(q_len, T):
+    """The matrix form (prefill_head) against the per-token loop of
+    attend_new_tokens, head by head: the same visible rows, outputs and lse,
+    with T < q_len included (tokens that see nothing: zeros and -inf)."""
+    rng = np.random.default_rng(200 + 10 * q_len + T)
+    n_h, d_h, d_r, d_c = 3, 4, 2, 6
+    q_c = rng.normal(size=(q_len, n_h, d_h)) * 2.0
+    q_r = rng.normal(size=(q_len, n_h, d_r)) * 2.0
+    c_kv, k_r = rng.normal(size=(T, d_c)), rng.normal(size=(T, d_r))
+    W_UK, W_UV = rng.normal(size=(n_h * d_h, d_c)) * 0.5, rng.normal(size=(n_h * d_h, d_c)) * 0.5
+    res = oracle.attend_new_tokens(q_c, q_r, c_kv, k_r, W_UK, W_UV)
+    for i in range(n_h):
+        r = oracle.prefill_head(q_c[:, i], q_r[:, i], c_kv, k_r, W_UK, W_UV, i)
+        for t in range(q_len):
+            np.testing.assert_allclose(r["o"][t], res[t]["o_heads"][i], rtol=1e-12, atol=1e-14)
+            if np.isneginf(res[t]["lse"][i]):
+                assert np.isneginf(r["lse"][t])
+            else:
+                np.testing.assert_allclose(r["lse"][t], res[t]["lse"][i], rtol=1e-13)
+
+
+def test_prefill_head_full_prompt_is_causal_sdpa():
+    """q_len = T (a whole prompt): torch's scaled_dot_product_attention with
+    is_causal=True on the up-projected keys and values, in float64; and the first
+    token's output is its own value row (softmax over a single row)."""
+    torch = pytest.importorskip("torch")
+    import torch.nn.functional as F
+    rng = np.random.default_rng(7)
+    T, n_h, d_h, d_r, d_c = 11, 2, 4, 2, 6
+    q_c, q_r = rng.normal(size=(T, n_h, d_h)), rng.normal(size=(T, n_h, d_r))
+    c_kv, k_r = rng.normal(size=(T, d_c)), rng.normal(size=(T, d_r))
+    W_UK, W_UV = rng.normal(size=(n_h * d_h, d_c)), rng.normal(size=(n_h * d_h, d_c))
+    scale = 1.0 / math.sqrt(d_h + d_r)
+    c = torch.from_numpy(c_kv)
+    for i in range(n_h):
+        r = oracle.prefill_head(q_c[:, i], q_r[:, i], c_kv, k_r, W_UK, W_UV, i)
+        wk = torch.from_numpy(W_UK[i * d_h:(i + 1) * d_h])
+        wv = torch.from_numpy(W_UV[i * d_h:(i + 1) * d_h])
+        k = torch.cat([c @ wk.T, torch.from_numpy(k_r)], dim=1)
+        v = c @ wv.T
+        q = torch.cat([torch.from_numpy(q_c[:, i]), torch.from_numpy(q_r[:, i])], dim=1)
+        o = F.scaled_dot_product_attention(q[None, None], k[None, None], v[None, None], is_causal=True,
+                                           scale=scale)[0, 0].numpy()
+        np.testing.assert_allclose(r["o"], o, rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(r["o"][0], v[0].numpy(), rtol=1e-13)
+        s00 = float(np.dot(np.concatenate([q_c[0, i], q_r[0, i]]), k[0].numpy())) * scale
+        np.testing.assert_allclose(r["lse"][0], s00, rtol=1e-13)
+
+
 def test_new_tokens_shorter_cache_than_q_len():
     """T < q_len: the first q_len - T new tokens see no row (lse -inf, zero output);
     the others see rows 0 .. T - q_len + t."""
