@@ -352,6 +352,51 @@ mla_status_t mla_decode_noalloc(const mla_dims_t* dims, int32_t batch,
                                 void* o_lat, mla_dtype_t o_dt, float* lse, void* stream);
 
 /*
+ * Prefill: attention of a batch of new prompt tokens over their sequences'
+ * paged caches, in the non-absorbed form [DeepSeek-V2 explainer §2.2.1: per
+ * head, k^C_{j,i} = W^UK_i c^KV_j and v_{j,i} = W^UV_i c^KV_j; deepseek(2) 關鍵技術
+ * §1: s = [q^C_i; q^R_i] . [k^C_{j,i}; k^R_j] * softmax_scale, softmax over the
+ * positions up to the query's own, o_i = sum_j p_j v_{j,i}].  Keys and values
+ * are up-projected once per cached token (into the workspace), so the
+ * attention runs at d_h + d_h^R = 192 score dims and d_h = 128 output dims
+ * instead of the absorbed 576 / 512: the cheaper form once a sequence has more
+ * than a few hundred new tokens.  The new tokens of sequence b are rows
+ * [q_offsets[b], q_offsets[b+1]) of q_nope / q_pe / o_heads, and they are the
+ * last q_len_b = q_offsets[b+1] - q_offsets[b] of its seq_lens[b] cached tokens
+ * (already written to the cache, e.g. by mla_cache_append): new token t sits
+ * at position seq_lens[b] - q_len_b + t and attends to cache positions
+ * 0 .. seq_lens[b] - q_len_b + t (none when that is negative: zeros, lse -inf).
+ * Earlier cached tokens (a prefix from an earlier chunk) are attended too.
+ *   q_offsets: [batch + 1] int32, device; non-decreasing, q_offsets[batch] <= total_q.
+ *   total_q: rows of q_nope / q_pe / o_heads / lse (host value).
+ *   max_q_len: host bound on every q_len_b (tokens past it are not computed).
+ *   q_nope: [total_q, n_h, d_h], q_pe: [total_q, n_h, d_rope] (RoPE applied), q_dt.
+ *   total_kv: host bound on the sum of the (clamped) seq_lens; the gathered and
+ *       up-projected rows are sized by it (if the sum exceeds it, the later
+ *       sequences' trailing positions are not attended).
+ *   w_uk, w_uv: [n_h * d_h, d_c] (w_dt), W^UK and W^UV as on the pages.
+ *   o_heads: [total_q, n_h, d_h] (out_dt) = [o_1; ...; o_nh] per token, the
+ *       input of W^O; lse: [total_q, n_h] fp32 (natural log) or NULL.
+ *   workspace: mla_prefill_workspace_size(...) bytes, 256-B aligned: the
+ *       gathered rows (bf16, an fp8 cache dequantised), then the up-projected
+ *       keys and values ([2 n_h, rows, d_h] bf16, about 64 KB per cached token
+ *       at 128 heads).
+ * Supported: d_h = 128, d_c = 512, d_rope = 64, page_size = 64, any n_h;
+ * q_dt = w_dt = out_dt = MLA_BF16; bf16 or fp8 cache (others:
+ * MLA_ERR_UNSUPPORTED).  total_kv < 2^24.  fp32 accumulation; keys, values
+ * and probabilities are rounded to bf16 before their products.
+ */
+mla_status_t mla_prefill_workspace_size(const mla_dims_t* dims, int32_t batch, int64_t total_kv,
+                                        size_t* bytes);
+mla_status_t mla_prefill(const mla_dims_t* dims, int32_t batch, const int32_t* q_offsets,
+                         int32_t total_q, int32_t max_q_len,
+                         const void* q_nope, const void* q_pe, mla_dtype_t q_dt,
+                         const mla_paged_cache_t* cache, int64_t total_kv,
+                         const void* w_uk, const void* w_uv, mla_dtype_t w_dt,
+                         float softmax_scale, void* workspace, size_t workspace_bytes,
+                         void* o_heads, mla_dtype_t out_dt, float* lse, void* stream);
+
+/*
  * Host check (no device access) of a paged cache's metadata, on host copies of
  * its block table and lengths [DeepSeek-V2 explainer §2.1.1 names the paged KV
  * memory; the layout is that of mla_paged_cache_t above]:

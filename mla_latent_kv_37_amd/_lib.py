@@ -21,7 +21,8 @@ EXPORTS = ("mla_status_string", "mla_build_info", "mla_absorb_q", "mla_decode_wo
            "mla_lse_part_offset", "mla_decode", "mla_merge_splits", "mla_out_proj", "mla_cache_store",
            "mla_cache_append", "mla_query_prep_scratch_size", "mla_query_prep", "mla_partition_host",
            "mla_decode_multi_workspace_size", "mla_decode_multi", "mla_merge_out_proj",
-           "mla_decode_multi_out_proj", "mla_validate_cache_host", "mla_decode_noalloc")
+           "mla_decode_multi_out_proj", "mla_validate_cache_host", "mla_decode_noalloc",
+           "mla_prefill_workspace_size", "mla_prefill")
 
 
 class MlaError(RuntimeError):
@@ -90,6 +91,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                             ctypes.c_int, P, P]),
         "mla_decode_multi_out_proj": (ctypes.c_int, [PD, I32, I32, P, P, ctypes.c_int, PC, ctypes.c_float, PP, P, SZ,
                                                      P, ctypes.c_int, P, P, ctypes.c_int, P, ctypes.c_int, P]),
+        "mla_prefill_workspace_size": (ctypes.c_int, [PD, I32, ctypes.c_int64, ctypes.POINTER(SZ)]),
+        "mla_prefill": (ctypes.c_int, [PD, I32, P, I32, I32, P, P, ctypes.c_int, PC, ctypes.c_int64, P, P,
+                                       ctypes.c_int, ctypes.c_float, P, SZ, P, ctypes.c_int, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -238,6 +242,26 @@ def decode_multi_out_proj(d: Dims, q_lat, q_pe, cache: PagedCache, softmax_scale
                                             ctypes.byref(part), _ptr(workspace), ws_bytes, _ptr(o_lat),
                                             dtype_code(o_lat), _ptr(lse), _ptr(w_uv), dtype_code(w_uv), _ptr(o_heads),
                                             dtype_code(o_heads), _stream(stream)), "mla_decode_multi_out_proj")
+    return o_heads
+
+
+def prefill_workspace_size(d: Dims, batch: int, total_kv: int) -> int:
+    nbytes = ctypes.c_size_t(0)
+    _check(load().mla_prefill_workspace_size(ctypes.byref(d), batch, total_kv, ctypes.byref(nbytes)),
+           "mla_prefill_workspace_size")
+    return nbytes.value
+
+
+def prefill(d: Dims, q_offsets, total_q: int, max_q_len: int, q_nope, q_pe, cache: PagedCache, total_kv: int,
+            w_uk, w_uv, softmax_scale: float, workspace, o_heads, lse=None, stream=None):
+    """Non-absorbed attention of new prompt tokens: q_offsets [B+1] int32 (rows of sequence b's new tokens),
+    q_nope [total_q, n_h, d_h], q_pe [total_q, n_h, d_r], o_heads [total_q, n_h, d_h], lse [total_q, n_h]."""
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load().mla_prefill(ctypes.byref(d), q_offsets.shape[0] - 1, _ptr(q_offsets), total_q, max_q_len,
+                              _ptr(q_nope), _ptr(q_pe), dtype_code(q_nope), ctypes.byref(cache), total_kv,
+                              _ptr(w_uk), _ptr(w_uv), dtype_code(w_uk), ctypes.c_float(softmax_scale),
+                              _ptr(workspace), ws_bytes, _ptr(o_heads), dtype_code(o_heads), _ptr(lse),
+                              _stream(stream)), "mla_prefill")
     return o_heads
 
 

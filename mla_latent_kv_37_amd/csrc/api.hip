@@ -479,6 +479,32 @@ mla_status_t decode_multi_impl(const mla_dims_t* dims, int32_t batch, int32_t q_
                             M.dec_bytes, o_lat, o_dt, lse, w_uv, w_dt, o_heads, out_dt, stream);
 }
 
+// mla_prefill workspace: sequence offsets, gathered rows, up-projected keys
+// and values (see PrefillArgs)
+struct PrefillLayout {
+  size_t cu, rows, kv, total;
+  int cap_rows;
+};
+
+constexpr int64_t kPrefillMaxKv = (int64_t(1) << 24) - 1;
+
+mla_status_t prefill_layout(const mla_dims_t* dims, int32_t batch, int64_t total_kv, PrefillLayout* L) {
+  if (mla_status_t s = check_dims(dims)) return s;
+  if (batch < 0 || total_kv < 0) return MLA_ERR_INVALID_ARG;
+  if (dims->d_head != 128 || dims->d_latent != 512 || dims->d_rope != 64) return MLA_ERR_UNSUPPORTED;
+  if (total_kv > kPrefillMaxKv || dims->n_heads > 65536) return MLA_ERR_UNSUPPORTED;
+  PrefillLayout l{};
+  // rows: every position a 32-row tile of a sequence can touch (up to 31 past
+  // the last row), in whole 256-row tiles of the up-projection
+  l.cap_rows = int(((total_kv + 32 + 255) / 256) * 256);
+  l.cu = 0;
+  l.rows = align256(size_t(batch + 1) * sizeof(int32_t));
+  l.kv = l.rows + align256(size_t(l.cap_rows) * 576 * 2);
+  l.total = l.kv + size_t(2) * dims->n_heads * size_t(l.cap_rows) * 128 * 2;
+  *L = l;
+  return MLA_OK;
+}
+
 }  // namespace
 
 mla_status_t mla_decode_multi(const mla_dims_t* dims, int32_t batch, int32_t q_len, const void* q_lat,
@@ -741,6 +767,73 @@ mla_status_t mla_partition_host(const int32_t* seq_lens_host, int32_t batch, int
     if (np > 0) S += np + kSegCost;
   }
   return MLA_OK;
+}
+
+mla_status_t mla_prefill_workspace_size(const mla_dims_t* dims, int32_t batch, int64_t total_kv, size_t* bytes) {
+  if (!bytes) return MLA_ERR_INVALID_ARG;
+  PrefillLayout L;
+  if (mla_status_t s = prefill_layout(dims, batch, total_kv, &L)) return s;
+  *bytes = L.total;
+  return MLA_OK;
+}
+
+mla_status_t mla_prefill(const mla_dims_t* dims, int32_t batch, const int32_t* q_offsets, int32_t total_q,
+                         int32_t max_q_len, const void* q_nope, const void* q_pe, mla_dtype_t q_dt,
+                         const mla_paged_cache_t* cache, int64_t total_kv, const void* w_uk, const void* w_uv,
+                         mla_dtype_t w_dt, float softmax_scale, void* workspace, size_t workspace_bytes,
+                         void* o_heads, mla_dtype_t out_dt, float* lse, void* stream) {
+  PrefillLayout L;
+  if (mla_status_t s = prefill_layout(dims, batch, total_kv, &L)) return s;
+  if (total_q < 0 || max_q_len < 0 || cache == nullptr || !q_offsets) return MLA_ERR_INVALID_ARG;
+  if (!q_nope || !q_pe || !w_uk || !w_uv || !o_heads) return MLA_ERR_INVALID_ARG;
+  if (!cache->kv || !cache->block_table || !cache->seq_lens) return MLA_ERR_INVALID_ARG;
+  if (cache->page_size < 1 || cache->max_pages_per_seq < 1 || cache->num_pages < 1) return MLA_ERR_INVALID_ARG;
+  if (!(softmax_scale > 0.f) || !(softmax_scale < 1e30f)) return MLA_ERR_INVALID_ARG;
+  for (mla_dtype_t t : {q_dt, w_dt, out_dt, cache->dtype})
+    if (!valid_dtype(t)) return MLA_ERR_INVALID_ARG;
+  if (q_dt != MLA_BF16 || w_dt != MLA_BF16 || out_dt != MLA_BF16) return MLA_ERR_UNSUPPORTED;
+  if (cache->dtype == MLA_F32 || cache->page_size != 64) return MLA_ERR_UNSUPPORTED;
+  if (cache->dtype == MLA_FP8_E4M3 && !cache->scales) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(q_nope) || !aligned16(q_pe) || !aligned16(w_uk) || !aligned16(w_uv) || !aligned16(o_heads) ||
+      !aligned16(cache->kv))
+    return MLA_ERR_ALIGNMENT;
+  if (!workspace || workspace_bytes < L.total) return MLA_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return MLA_ERR_ALIGNMENT;
+  const int64_t n_qblk = (int64_t(max_q_len) + 255) / 256;
+  if (int64_t(batch) * n_qblk * dims->n_heads > INT32_MAX) return MLA_ERR_UNSUPPORTED;
+  if (batch == 0 || total_q == 0) return MLA_OK;
+
+  PrefillArgs a{};
+  a.batch = batch;
+  a.n_heads = dims->n_heads;
+  {
+    const int64_t mt = int64_t(cache->max_pages_per_seq) * cache->page_size;
+    a.max_tokens = mt > INT32_MAX ? INT32_MAX : int(mt);
+  }
+  a.max_pages = cache->max_pages_per_seq;
+  a.num_pages = cache->num_pages;
+  a.total_kv = total_kv;
+  a.cap_rows = L.cap_rows;
+  a.total_q = total_q;
+  a.n_qblk = int(n_qblk);
+  a.seq_lens = cache->seq_lens;
+  a.block_table = cache->block_table;
+  a.q_off = q_offsets;
+  a.kv = cache->kv;
+  a.scales = cache->scales;
+  a.kv_dt = cache->dtype;
+  a.q_nope = static_cast<const uint16_t*>(q_nope);
+  a.q_pe = static_cast<const uint16_t*>(q_pe);
+  a.w_uk = static_cast<const uint16_t*>(w_uk);
+  a.w_uv = static_cast<const uint16_t*>(w_uv);
+  a.scale_log2 = softmax_scale * kLog2e;
+  char* ws = static_cast<char*>(workspace);
+  a.cu = reinterpret_cast<int32_t*>(ws + L.cu);
+  a.c_rows = reinterpret_cast<uint16_t*>(ws + L.rows);
+  a.kv_up = reinterpret_cast<uint16_t*>(ws + L.kv);
+  a.out = static_cast<uint16_t*>(o_heads);
+  a.lse = lse;
+  return launch_prefill(a, static_cast<hipStream_t>(stream)) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
 }  // extern "C"

@@ -108,6 +108,35 @@ struct QueryFinishArgs {
   mla_dtype_t out_dt;
 };
 
+// prefill (prefill.hip): d_h 128, d_c 512, d_rope 64, page 64, bf16 queries,
+// weights and outputs, bf16 or fp8 cache
+struct PrefillArgs {
+  int batch, n_heads;
+  int max_tokens;          // max_pages * page_size: longer lengths are read as this
+  int max_pages, num_pages;
+  int64_t total_kv;        // capacity of the gathered rows (sum of the lengths)
+  int cap_rows;            // rows of the gathered and up-projected arrays (multiple of 256)
+  int total_q;             // rows of q_nope / q_pe / out
+  int n_qblk;              // 256-token blocks per sequence (ceil(max_q_len / 256))
+  const int32_t* seq_lens; // [batch]
+  const int32_t* block_table;
+  const int32_t* q_off;    // [batch + 1]
+  const void* kv;
+  const float* scales;
+  mla_dtype_t kv_dt;
+  const uint16_t* q_nope;  // [total_q, n_h, 128]
+  const uint16_t* q_pe;    // [total_q, n_h, 64]
+  const uint16_t* w_uk;    // [n_h * 128, 512]
+  const uint16_t* w_uv;
+  float scale_log2;        // softmax scale * log2(e)
+  int32_t* cu;             // workspace: [batch + 1] first row of each sequence
+  uint16_t* c_rows;        // workspace: [cap_rows, 576] gathered rows
+  uint16_t* kv_up;         // workspace: [2 n_h, cap_rows, 128] up-projected keys, then values
+  uint16_t* out;           // [total_q, n_h, 128]
+  float* lse;              // [total_q, n_h] or null
+};
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st);
+
 constexpr int kGemmTile = 64;    // weight-streaming product: weight rows and batch rows per workgroup
 constexpr int kGemmChunk = 64;   // and k per chunk
 constexpr int kGemmMaxSlices = 8;      // k slices of mla_cache_append's projection (its scratch holds 8)

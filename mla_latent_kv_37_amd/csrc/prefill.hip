@@ -1,0 +1,447 @@
+// MLA prefill: attention of a batch of new prompt tokens over their sequences'
+// paged latent cache, in the non-absorbed form.
+//
+// For a long run of new tokens the absorbed form (scores against the 576-wide
+// cached rows, outputs in the 512-wide latent space) costs 2 x 1088 flops per
+// (query, cached token, head); up-projecting the keys and values once,
+//   k^C_{j,i} = W^UK_i c^KV_j,  v_{j,i} = W^UV_i c^KV_j   (DeepSeek-V2 explainer
+//   (一文通透DeepSeek-V2) §2.2.1, the per-head keys and values of the latent),
+// costs 2 x 2 x 512 x 128 flops per (cached token, head) once, and the
+// attention itself 2 x (192 + 128) per (query, cached token, head) with
+//   s = [q^C_i; q^R_i] . [k^C_{j,i}; k^R_j] / sqrt(d_h + d_h^R)
+// (deepseek(2)——deepseek 關鍵技術 §1; a new token at position p attends to the
+// cached positions 0..p).  Past a few hundred new tokens per sequence the
+// up-projection is the cheaper route (the V2 technical report describes
+// prompt processing in this form; the absorbed form is the decode's).
+//
+// Four launches, in stream order, all on one workspace (api.hip lays it out):
+//   scan:    cu[b] = sum of the clamped lengths of sequences < b (int32).
+//   gather:  C[g] = the cached row [c^KV | k^R] of global token g (sequence b,
+//            position g - cu[b]) in bf16, dequantised for an fp8 cache; rows
+//            past the batch's tokens and rows of a page id outside the cache
+//            are zeros.  C is dense, so the two kernels after it need no
+//            block table.
+//   kv:      KV[s][g] = W_s . c^KV_g for the 2 n_h slabs s of 128 output
+//            features (slab i < n_h: W^UK_i, slab n_h + i: W^UV_i), a dense
+//            product [2 n_h 128 x 512] x [512 x rows] on MFMA.
+//   attn:    per (head, block of 256 new tokens of one sequence), causal
+//            attention over the keys [KV[i][g] | C[g][512:576]] and values
+//            KV[n_h + i][g] with an online softmax, on MFMA.
+#include "decode_tile.h"
+
+namespace mla {
+namespace {
+
+constexpr int kPfHead = 128, kPfLat = 512, kPfRope = 64, kPfRow = 576, kPfPage = 64;
+constexpr int kPfRowBytes = kPfRow * 2;   // 1152: one gathered row of C
+
+// ---------------------------------------------------------------------------
+// scan: one workgroup of 256 threads walks the batch 256 sequences at a time.
+__global__ __launch_bounds__(256) void prefill_scan_kernel(PrefillArgs a) {
+  __shared__ int part[4];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  int64_t run = 0;
+  for (int base = 0; base < a.batch; base += 256) {
+    const int b = base + int(threadIdx.x);
+    int T = b < a.batch ? a.seq_lens[b] : 0;
+    T = T < 0 ? 0 : (T > a.max_tokens ? a.max_tokens : T);
+    // inclusive scan within the wavefront, then across the 4 wavefronts
+    int v = T;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(v, off, 64);
+      if (lane >= off) v += t;
+    }
+    if (lane == 63) part[wave] = v;
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += part[w];
+    const int64_t excl = run + before + v - T;
+    if (b < a.batch) a.cu[b] = int(excl < a.total_kv ? excl : a.total_kv);
+    run += part[0] + part[1] + part[2] + part[3];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) a.cu[a.batch] = int(run < a.total_kv ? run : a.total_kv);
+}
+
+// ---------------------------------------------------------------------------
+// gather: workgroup x fills rows 32x..32x+31 of C (72 chunks of 8 values each).
+__global__ __launch_bounds__(256) void prefill_gather_kernel(PrefillArgs a) {
+  __shared__ int64_t src_row[32];   // cache row (page * page_size + slot), -1: zeros
+  const int g0 = blockIdx.x * 32;
+  if (threadIdx.x < 32) {
+    const int g = g0 + int(threadIdx.x);
+    int64_t row = -1;
+    if (g < a.cu[a.batch]) {
+      // the sequence holding global token g: the last b with cu[b] <= g
+      int lo = 0, hi = a.batch;   // cu[lo] <= g < cu[hi]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (a.cu[mid] <= g) lo = mid;
+        else hi = mid;
+      }
+      const int j = g - a.cu[lo];
+      const int page = a.block_table[int64_t(lo) * a.max_pages + j / kPfPage];
+      if (unsigned(page) < unsigned(a.num_pages)) row = int64_t(page) * kPfPage + (j % kPfPage);
+    }
+    src_row[threadIdx.x] = row;
+  }
+  __syncthreads();
+  uint16_t* out = a.c_rows + int64_t(g0) * kPfRow;
+  for (int e = threadIdx.x; e < 32 * 72; e += 256) {
+    const int t = e / 72, c = e % 72;
+    const int64_t row = src_row[t];
+    bf16x8 v = bf16x8{};
+    if (row >= 0) {
+      if (a.kv_dt == MLA_BF16) {
+        v = *reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(a.kv) + row * kPfRow + c * 8);
+      } else {
+        // fp8: code * scale of the token's 128-channel group, in fp32, rounded to bf16
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 code = *reinterpret_cast<const u32x2*>(static_cast<const uint8_t*>(a.kv) + row * kPfRow + c * 8);
+        const float sc = a.scales[row * 5 + (c >> 4)];
+        const auto f0 = __builtin_amdgcn_cvt_pk_f32_fp8(int(code[0]), false);
+        const auto f1 = __builtin_amdgcn_cvt_pk_f32_fp8(int(code[0]), true);
+        const auto f2 = __builtin_amdgcn_cvt_pk_f32_fp8(int(code[1]), false);
+        const auto f3 = __builtin_amdgcn_cvt_pk_f32_fp8(int(code[1]), true);
+        v[0] = (__bf16)(f0[0] * sc); v[1] = (__bf16)(f0[1] * sc);
+        v[2] = (__bf16)(f1[0] * sc); v[3] = (__bf16)(f1[1] * sc);
+        v[4] = (__bf16)(f2[0] * sc); v[5] = (__bf16)(f2[1] * sc);
+        v[6] = (__bf16)(f3[0] * sc); v[7] = (__bf16)(f3[1] * sc);
+      }
+    }
+    *reinterpret_cast<bf16x8*>(out + t * kPfRow + c * 8) = v;
+  }
+}
+
+// One direct-to-LDS load: 64 lanes x 16 bytes from per-lane global addresses
+// into 1 KB of LDS at `lds` (lane l's bytes at lds + 16 l).  Inline assembly,
+// so the compiler does not track it: its completion is waited for with an
+// explicit vmcnt before the barrier that publishes the data.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+  const int m0 = uniform(int(lds));
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(m0), "v"(src)
+               : "memory", "m0");
+}
+
+// ---------------------------------------------------------------------------
+// kv: KV^T tile [256 features x 256 rows] per workgroup, K = 512 in 16 chunks of
+// 32.  8 wavefronts (2 per SIMD): wavefront w computes features 128(w&1) ..+127
+// x rows 64(w>>1) ..+63 as 4 x 2 blocks of v_mfma_f32_32x32x16_bf16 (A = weight
+// rows, B = C rows, so a lane's accumulator holds one row's runs of 4
+// consecutive features).  Each chunk's operands (256 weight rows and 256 C
+// rows, 64 B of each) sit in one of 4 LDS stages, 3 chunks ahead of use; row r's
+// 16-byte piece p at r*64 + ((p ^ ((r>>2)&3)) * 16), so that the fragment
+// reads (16 rows of one piece per 16 lanes) hit distinct banks.
+constexpr int kKvTile = 256, kKvChunk = 32, kKvChunks = kPfLat / kKvChunk, kKvStages = 4;
+constexpr int kKvHalf = kKvTile * kKvChunk * 2;   // 16 KB: one operand of a stage
+constexpr int kKvStage = 2 * kKvHalf;
+
+__global__ __launch_bounds__(512) void prefill_kv_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(1024))) char lds_raw[kKvStages * kKvStage];
+  const uint32_t lds = uint32_t(reinterpret_cast<uintptr_t>(lds_raw));
+  const int f0 = blockIdx.x * kKvTile, g0 = blockIdx.y * kKvTile;
+  const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63, h = lane >> 5;
+  const int nk = a.n_heads * kPfHead;
+
+  // loads: wavefront w fills 16-row blocks 2w and 2w+1 of both operands; lane
+  // l reads row 16i + (l>>2), logical piece (l&3) ^ ((l>>4)&3)
+  const int lp = (lane & 3) ^ ((lane >> 4) & 3);
+  const char* asrc[2];
+  const char* bsrc[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = 16 * (2 * wave + j) + (lane >> 2);
+    const int f = f0 + r;
+    const uint16_t* w = f < nk ? a.w_uk + int64_t(f) * kPfLat : a.w_uv + int64_t(f - nk) * kPfLat;
+    asrc[j] = reinterpret_cast<const char*>(w) + lp * 16;
+    bsrc[j] = reinterpret_cast<const char*>(a.c_rows + int64_t(g0 + r) * kPfRow) + lp * 16;
+  }
+  auto issue = [&](int c) {
+    const uint32_t sb = lds + uint32_t((c % kKvStages) * kKvStage);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      dma16(asrc[j] + c * 64, sb + uint32_t((2 * wave + j) * 1024));
+      dma16(bsrc[j] + c * 64, sb + uint32_t(kKvHalf + (2 * wave + j) * 1024));
+    }
+  };
+
+  const int fw = wave & 1, tw = wave >> 1;
+  const int sw = (lane >> 2) & 3;
+  const uint32_t a_row = uint32_t((128 * fw + (lane & 31)) * 64);
+  const uint32_t b_row = uint32_t(kKvHalf + (64 * tw + (lane & 31)) * 64);
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int n = 0; n < 2; ++n) acc[m][n] = f32x16{};
+
+  issue(0);
+  issue(1);
+  issue(2);
+#pragma unroll
+  for (int c = 0; c < kKvChunks; ++c) {
+    // this wavefront's loads of chunk c are done (those of the next ones may
+    // still be in flight: 4 per chunk), then the barrier publishes chunk c and
+    // frees the stage of chunk c-1 for chunk c+3
+    const int later = (c + 2 < kKvChunks ? 2 : kKvChunks - 1 - c);
+    if (later == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(8));
+    else if (later == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(4));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    raw_barrier();
+    if (c + 3 < kKvChunks) issue(c + 3);
+    const uint32_t sb = lds + uint32_t((c % kKvStages) * kKvStage);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const uint32_t pofs = uint32_t(((2 * s + h) ^ sw) * 16);
+      bf16x8 af[4], bf[2];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) af[m] = lds_read_b128(sb + a_row + uint32_t(m * 2048) + pofs);
+#pragma unroll
+      for (int n = 0; n < 2; ++n) bf[n] = lds_read_b128(sb + b_row + uint32_t(n * 2048) + pofs);
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int n = 0; n < 2; ++n) acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[m], bf[n], acc[m][n], 0, 0, 0);
+    }
+  }
+
+  // stores: feature 32m + 8(i>>2) + 4h + (i&3) of slab 2x + fw, row g0 + 64tw + 32n + (lane&31)
+  const int slab = 2 * blockIdx.x + fw;
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    const int g = g0 + 64 * tw + 32 * n + (lane & 31);
+    uint16_t* dst = a.kv_up + (int64_t(slab) * a.cap_rows + g) * kPfHead + 4 * h;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (__bf16)acc[m][n][4 * q + e];
+        *reinterpret_cast<bf16x4*>(dst + 32 * m + 8 * q) = v;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// attn: workgroup (head i, block of 256 new tokens of sequence b), 8 wavefronts
+// of 32 new tokens each.  Per 32-token tile of cached positions, wavefront w
+//   S^T [32 positions x 32 tokens] = K [32 x 192] . Q^T [192 x 32]   (12 MFMAs)
+//   O^T [128 x 32 tokens]        += V^T [128 x 32] . P^T [32 x 32]   (8 MFMAs)
+// with Q^T in registers and K, V from LDS (the tile layout of decode_tile.h:
+// K = 24 chunks, 16 of k^C then 8 of k^R; V = 16 chunks).  A lane holds one new
+// token (column lane&31) and 16 of the tile's positions (8(r>>2) + 4h + (r&3)
+// in register r), so a token's softmax is a reduction over its lane pair.
+// Online softmax in the log2 domain with a lazy rescale: a token's reference
+// max moves (and its O^T and row sum are rescaled) only when the tile's max
+// exceeds it by more than kPfSlack, so probabilities stay below 2^kPfSlack.
+constexpr int kPaWaves = 8, kPaQ = 32 * kPaWaves, kPaTok = 32, kPaBufs = 4;
+constexpr int kPaKBytes = 3 * 4096, kPaVBytes = 2 * 4096, kPaTileBytes = kPaKBytes + kPaVBytes;
+constexpr float kPfSlack = 8.f;
+
+__global__ __launch_bounds__(512) void prefill_attn_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(2048))) char lds_raw[kPaBufs * kPaTileBytes];
+  const uint32_t lds = uint32_t(reinterpret_cast<uintptr_t>(lds_raw));
+  const int head = blockIdx.x;
+  const int b = blockIdx.y / a.n_qblk;
+  const int qb = a.n_qblk - 1 - int(blockIdx.y % a.n_qblk);   // longest blocks first
+  const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63, h = lane >> 5;
+
+  int T0 = load_const(a.seq_lens, b);
+  T0 = T0 < 0 ? 0 : (T0 > a.max_tokens ? a.max_tokens : T0);
+  const int cu = load_const(a.cu, b);
+  const int T = min(T0, load_const(a.cu, b + 1) - cu);   // rows the scan placed (capacity)
+  int qo = load_const(a.q_off, b), qn = load_const(a.q_off, b + 1) - qo;
+  qo = max(qo, 0);
+  qn = max(0, min(qn, a.total_q - qo));
+  if (kPaQ * qb >= qn) return;
+  const int p0 = T0 - qn;   // position of new token 0
+  // last visible position of the workgroup, of this wavefront and of this lane
+  const int tq_last = min(qn, kPaQ * (qb + 1)) - 1;
+  const int p_last = min(p0 + tq_last, T - 1);
+  const int ntiles = p_last >= 0 ? p_last / kPaTok + 1 : 0;
+  const int t_base = kPaQ * qb + 32 * wave;
+  const int w_last = t_base < qn ? min(p0 + min(qn - 1, t_base + 31), T - 1) : -1;
+  const int w_tiles = w_last >= 0 ? w_last / kPaTok + 1 : 0;
+  const int w_first = min(p0 + t_base, T - 1);   // first token's last visible position
+  const int t = t_base + (lane & 31);
+  const bool q_ok = t < qn;
+  const int lim = min(p0 + t, T - 1);            // this token sees positions 0..lim
+
+  // Q^T fragments: k-step st holds dims 16st + 8h .. +7 of token t (q^C for
+  // st < 8, q^R for st >= 8)
+  bf16x8 qf[12];
+  {
+    const int64_t qrow = int64_t(qo + (q_ok ? t : 0)) * a.n_heads + head;
+    const uint16_t* qc = a.q_nope + qrow * kPfHead + 8 * h;
+    const uint16_t* qr = a.q_pe + qrow * kPfRope + 8 * h;
+#pragma unroll
+    for (int st = 0; st < 12; ++st) {
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(st < 8 ? qc + 16 * st : qr + 16 * (st - 8));
+      qf[st] = q_ok ? v : bf16x8{};
+    }
+  }
+
+  // tile loads: 20 one-KB blocks (block 4g + rb: rows 8rb..8rb+7 of chunk
+  // group g; groups 0-1 k^C, 2 k^R, 3-4 V); wavefront w issues blocks w, w+8
+  // and (w < 4) w+16.  Lane l reads row 8rb + (l>>3), logical chunk
+  // 8g' + ((l&7) ^ f(row)) of its source row.
+  const int n_my = wave < 4 ? 3 : 2;
+  const uint16_t* kc_base = a.kv_up + (int64_t(head) * a.cap_rows + cu) * kPfHead;
+  const uint16_t* v_base = a.kv_up + (int64_t(a.n_heads + head) * a.cap_rows + cu) * kPfHead;
+  const uint16_t* kr_base = a.c_rows + int64_t(cu) * kPfRow + kPfLat;
+  auto issue = [&](int k) {
+    const uint32_t tb = lds + uint32_t((k % kPaBufs) * kPaTileBytes);
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      if (j < n_my) {
+        const int i = wave + 8 * j;
+        const int g = i >> 2, rb = i & 3;
+        const int row = 8 * rb + (lane >> 3);
+        const int ch = (lane & 7) ^ swz_f(row);
+        const int pos = k * kPaTok + row;
+        const uint16_t* src;
+        uint32_t dst;
+        if (g < 2) {
+          src = kc_base + int64_t(pos) * kPfHead + 8 * (8 * g + ch);
+          dst = tb + uint32_t(i * 1024);
+        } else if (g == 2) {
+          src = kr_base + int64_t(pos) * kPfRow + 8 * ch;
+          dst = tb + uint32_t(i * 1024);
+        } else {
+          src = v_base + int64_t(pos) * kPfHead + 8 * (8 * (g - 3) + ch);
+          dst = tb + uint32_t(kPaKBytes + (i - 12) * 1024);
+        }
+        dma16(src, dst);
+      }
+    }
+  };
+
+  const int kb0 = tile_offset(lane & 31, h);
+  // V^T fragment (transposing reads) of column tile mt, token half ks: rows
+  // 4h + (j>>2) and 8 + 4h + (j>>2) (j = lane & 15) of chunk 2((lane>>4)&1) +
+  // ((j>>1)&1), byte (j&1)*8; the second row's address is the first's ^ 0x410;
+  // then ^ 64*(mt&1) + (mt>>1)*4096 + ks*2048
+  const int vb0 = tile_offset(4 * h + ((lane & 15) >> 2), 2 * ((lane >> 4) & 1) + ((lane >> 1) & 1)) + (lane & 1) * 8;
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) acc[m] = f32x16{};
+  float m_run = -INFINITY, lsum = 0.f;
+
+  for (int k = 0; k < min(ntiles, 3); ++k) issue(k);
+  for (int k = 0; k < ntiles; ++k) {
+    const int later = min(ntiles - 1 - k, 2);   // tiles after k with loads in flight
+    if (later == 2) {
+      if (wave < 4) __builtin_amdgcn_s_waitcnt(waitcnt_vm(6));
+      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(4));
+    } else if (later == 1) {
+      if (wave < 4) __builtin_amdgcn_s_waitcnt(waitcnt_vm(3));
+      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(2));
+    } else {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    }
+    raw_barrier();
+    if (k + 3 < ntiles) issue(k + 3);
+    if (k >= w_tiles) continue;   // past this wavefront's last visible position
+
+    const uint32_t tb = lds + uint32_t((k % kPaBufs) * kPaTileBytes);
+    // scores
+    f32x16 s = f32x16{};
+    {
+      const uint32_t kl = tb + uint32_t(kb0);
+#pragma unroll
+      for (int st = 0; st < 12; ++st) {
+        const bf16x8 kf = lds_read_b128((kl ^ uint32_t(32 * (st & 3))) + uint32_t((st >> 2) * 4096));
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[st], s, 0, 0, 0);
+      }
+    }
+    // scale, causal mask, tile max
+    const int j0 = k * kPaTok;
+    const bool diag = j0 + kPaTok - 1 > w_first;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float x = s[r] * a.scale_log2;
+      s[r] = (diag && j0 + 8 * (r >> 2) + 4 * h + (r & 3) > lim) ? -INFINITY : x;
+    }
+    float mx = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    {
+      const auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(sw2[0]), __uint_as_float(sw2[1]));
+    }
+    const bool need = mx > m_run + kPfSlack;   // (false while mx is -inf)
+    if (__any(need)) {
+      const float m_new = need ? mx : m_run;
+      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;   // exp2(-inf) = 0
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[m][r] *= alpha;
+      lsum *= alpha;
+      m_run = m_new;
+    }
+    const float mref = m_run == -INFINITY ? 0.f : m_run;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(s[r] - mref);
+    {
+      const float u0 = (s[0] + s[1]) + (s[2] + s[3]), u1 = (s[4] + s[5]) + (s[6] + s[7]);
+      const float u2 = (s[8] + s[9]) + (s[10] + s[11]), u3 = (s[12] + s[13]) + (s[14] + s[15]);
+      lsum += (u0 + u1) + (u2 + u3);
+    }
+    bf16x8 pk[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pk[ks][e] = (__bf16)s[8 * ks + e];
+    // O^T += V^T . P^T
+    const uint32_t vl = tb + uint32_t(kPaKBytes + vb0);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const uint32_t a0 = (vl ^ uint32_t(64 * (mt & 1))) + uint32_t((mt >> 1) * 4096 + ks * 2048);
+        const bf16x8 vf = lds_read_tr_pair(a0, a0 ^ 0x410u);
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pk[ks], acc[mt], 0, 0, 0);
+      }
+  }
+
+  // epilogue: the token's row sum over both lanes of its pair; o = O / sum,
+  // lse = ln(sum) + m (natural log); a token that sees no position gets zeros
+  // and -inf
+  {
+    const auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum), false, false);
+    lsum = __uint_as_float(sw2[0]) + __uint_as_float(sw2[1]);
+  }
+  if (!q_ok) return;
+  const bool any = lsum > 0.f;
+  const float inv = any ? 1.f / lsum : 0.f;
+  uint16_t* dst = a.out + (int64_t(qo + t) * a.n_heads + head) * kPfHead + 4 * h;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      bf16x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[mt][4 * q + e] * inv);
+      *reinterpret_cast<bf16x4*>(dst + 32 * mt + 8 * q) = v;
+    }
+  if (a.lse != nullptr && h == 0)
+    a.lse[int64_t(qo + t) * a.n_heads + head] = any ? (m_run + __log2f(lsum)) * kLn2 : -INFINITY;
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
+  prefill_scan_kernel<<<1, 256, 0, st>>>(a);
+  prefill_gather_kernel<<<a.cap_rows / 32, 256, 0, st>>>(a);
+  prefill_kv_kernel<<<dim3(2 * a.n_heads * kPfHead / kKvTile, a.cap_rows / kKvTile), 512, 0, st>>>(a);
+  if (a.batch > 0 && a.n_qblk > 0) prefill_attn_kernel<<<dim3(a.n_heads, a.batch * a.n_qblk), 512, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -18,6 +18,7 @@
 
 static int g_launches = 0;
 static mla::V2DecodeArgs g_v2{};
+static mla::PrefillArgs g_pf{};
 static int g_fails = 0;
 
 #define CHECK(cond)                                                         \
@@ -33,6 +34,7 @@ namespace mla {
 hipError_t launch_decode_generic(const GenericDecodeArgs&, int, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_decode_wide(const V2DecodeArgs& a, hipStream_t) { ++g_launches; g_v2 = a; return hipSuccess; }
 hipError_t launch_decode_lite(const V2DecodeArgs& a, hipStream_t) { ++g_launches; g_v2 = a; return hipSuccess; }
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t) { ++g_launches; g_pf = a; return hipSuccess; }
 hipError_t launch_cache_store(const CacheStoreArgs&, int, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_gemm_ws(const GemmArgs&, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_reduce_cast(const float*, int, int64_t, void*, mla_dtype_t, hipStream_t) { ++g_launches; return hipSuccess; }
@@ -194,10 +196,38 @@ static void check_decode_validation() {
   CHECK(mla_query_prep_scratch_size(&d, 1536, 1 << 16) > 0);
 }
 
+static void check_prefill_validation() {
+  mla_dims_t d{128, 128, 64, 512};
+  int32_t* bt = static_cast<int32_t*>(dev(1));
+  int32_t* lens = static_cast<int32_t*>(dev(2));
+  mla_paged_cache_t c{dev(3), nullptr, MLA_BF16, 64, 1000, bt, 40, lens};
+  size_t ws = 0;
+  CHECK(mla_prefill_workspace_size(&d, 4, 5000, &ws) == MLA_OK);
+  const int cap = ((5000 + 32 + 255) / 256) * 256;
+  CHECK(ws == 256 + size_t(cap) * 1152 + size_t(2) * 128 * cap * 256);
+  char* wsp = static_cast<char*>(dev(6));
+  int before = g_launches;
+  CHECK(mla_prefill(&d, 4, idev(9), 3000, 1000, dev(4), dev(5), MLA_BF16, &c, 5000, dev(7), dev(8), MLA_BF16, 0.07f,
+                    wsp, ws, dev(10), MLA_BF16, nullptr, nullptr) == MLA_OK);
+  CHECK(g_launches == before + 1);
+  CHECK(g_pf.cap_rows == cap && g_pf.n_qblk == 4 && g_pf.total_q == 3000 && g_pf.max_tokens == 40 * 64);
+  CHECK(reinterpret_cast<char*>(g_pf.cu) == wsp && reinterpret_cast<char*>(g_pf.c_rows) == wsp + 256);
+  CHECK(reinterpret_cast<char*>(g_pf.kv_up) == wsp + 256 + size_t(cap) * 1152);
+  before = g_launches;
+  CHECK(mla_prefill(&d, 4, idev(9), 3000, 1000, dev(4), dev(5), MLA_BF16, &c, 5000, dev(7), dev(8), MLA_BF16, 0.07f,
+                    wsp, ws - 1, dev(10), MLA_BF16, nullptr, nullptr) == MLA_ERR_WORKSPACE);
+  CHECK(mla_prefill(&d, 4, nullptr, 3000, 1000, dev(4), dev(5), MLA_BF16, &c, 5000, dev(7), dev(8), MLA_BF16, 0.07f,
+                    wsp, ws, dev(10), MLA_BF16, nullptr, nullptr) == MLA_ERR_INVALID_ARG);
+  CHECK(mla_prefill(&d, 4, idev(9), 3000, 1000, dev(4), dev(5), MLA_BF16, &c, int64_t(1) << 24, dev(7), dev(8),
+                    MLA_BF16, 0.07f, wsp, ws, dev(10), MLA_BF16, nullptr, nullptr) == MLA_ERR_UNSUPPORTED);
+  CHECK(g_launches == before);
+}
+
 int main() {
   std::mt19937 rng(12345);
   check_partitions(rng);
   check_decode_validation();
+  check_prefill_validation();
   if (g_fails) {
     std::fprintf(stderr, "host_abi_check: %d failures\n", g_fails);
     return 1;

@@ -145,6 +145,53 @@ def test_validation_errors_before_any_device_access(lib):
               None) == lib.MLA_ERR_INVALID_ARG
 
 
+def test_prefill_workspace_and_validation(lib):
+    """mla_prefill: workspace = offsets + gathered rows + up-projected keys and
+    values, sized by total_kv; every argument error is reported before launch."""
+    L = _raw(lib)
+    d = _v2(lib)
+    cap = ((1000 + 32 + 255) // 256) * 256
+    expect = 256 + cap * 576 * 2 + 2 * 128 * cap * 128 * 2
+    assert lib.prefill_workspace_size(d, 3, 1000) == expect
+    sz = ctypes.c_size_t(0)
+    assert L.mla_prefill_workspace_size(ctypes.byref(d), 3, -1, ctypes.byref(sz)) == lib.MLA_ERR_INVALID_ARG
+    assert L.mla_prefill_workspace_size(ctypes.byref(d), 3, 1 << 24, ctypes.byref(sz)) == lib.MLA_ERR_UNSUPPORTED
+    d_other = lib.dims(16, 192, 64, 512)
+    assert L.mla_prefill_workspace_size(ctypes.byref(d_other), 3, 10, ctypes.byref(sz)) == lib.MLA_ERR_UNSUPPORTED
+    fake = ctypes.c_void_p(0x10000)
+    odd = ctypes.c_void_p(0x10008)
+    ws = ctypes.c_void_p(0x100000)
+    cache = lib.PagedCache(0x10000, None, lib.MLA_BF16, 64, 100, 0x20000, 16, 0x30000)
+    pf = L.mla_prefill
+
+    def call(**kw):
+        args = dict(dims=ctypes.byref(d), batch=3, qoff=fake, total_q=100, max_q=64, qn=fake, qp=fake, q_dt=1,
+                    cache=ctypes.byref(cache), total_kv=1000, wuk=fake, wuv=fake, w_dt=1, scale=0.07, ws=ws,
+                    ws_bytes=expect, out=fake, out_dt=1, lse=None)
+        args.update(kw)
+        return pf(*args.values(), None)
+
+    assert call(ws_bytes=expect - 1) == lib.MLA_ERR_WORKSPACE
+    assert call(ws=None) == lib.MLA_ERR_WORKSPACE
+    assert call(ws=ctypes.c_void_p(0x100010)) == lib.MLA_ERR_ALIGNMENT
+    assert call(qoff=None) == lib.MLA_ERR_INVALID_ARG
+    assert call(wuv=None) == lib.MLA_ERR_INVALID_ARG
+    assert call(scale=0.0) == lib.MLA_ERR_INVALID_ARG
+    assert call(total_q=-1) == lib.MLA_ERR_INVALID_ARG
+    assert call(q_dt=lib.MLA_F32) == lib.MLA_ERR_UNSUPPORTED
+    assert call(out_dt=lib.MLA_F32) == lib.MLA_ERR_UNSUPPORTED
+    assert call(out=odd) == lib.MLA_ERR_ALIGNMENT
+    c_f32 = lib.PagedCache(0x10000, None, lib.MLA_F32, 64, 100, 0x20000, 16, 0x30000)
+    assert call(cache=ctypes.byref(c_f32)) == lib.MLA_ERR_UNSUPPORTED
+    c_pg = lib.PagedCache(0x10000, None, lib.MLA_BF16, 32, 100, 0x20000, 16, 0x30000)
+    assert call(cache=ctypes.byref(c_pg)) == lib.MLA_ERR_UNSUPPORTED
+    c_f8 = lib.PagedCache(0x10000, None, lib.MLA_FP8_E4M3, 64, 100, 0x20000, 16, 0x30000)
+    assert call(cache=ctypes.byref(c_f8)) == lib.MLA_ERR_INVALID_ARG
+    # nothing to do: no launch, no device access
+    assert call(batch=0) == lib.MLA_OK
+    assert call(total_q=0) == lib.MLA_OK
+
+
 def test_multi_decode_workspace_and_validation(lib):
     """mla_decode_multi: the workspace holds the virtual lengths (B * q_len) before
     the decode workspace of the virtual batch (virtual sequences read their
