@@ -3,6 +3,8 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload ragged|long|fp8|v2b1]
     python bench.py --workload append_bf16|append_fp8     (cache append step, reported apart)
+    python bench.py --workload prefill_b4_t4096|prefill_b1_t16384|prefill_chunk_b4_t8192_q1024
+                                                          (non-absorbed prefill, reported apart)
 
 A step is one full MLA decode step over the batch: mla_absorb_q -> mla_decode ->
 mla_merge_splits -> mla_out_proj, every input already resident in HBM.  The
@@ -656,6 +658,13 @@ def copy_calibration(nbytes: int, reps: int = 3):
 # ---------------------------------------------------------------------------
 
 APPEND_WORKLOADS = {"append_bf16": "bf16", "append_fp8": "fp8"}
+# prefill: (batch, cached tokens per sequence, new tokens per sequence, cache dtype)
+PREFILL_WORKLOADS = {
+    "prefill_b4_t4096": (4, 4096, 4096, "bf16"),
+    "prefill_b1_t16384": (1, 16384, 16384, "bf16"),
+    "prefill_chunk_b4_t8192_q1024": (4, 8192, 1024, "bf16"),
+    "prefill_fp8_b4_t4096": (4, 4096, 4096, "fp8"),
+}
 QUERY_WORKLOADS = ("query_prep", "query_lat", "query_lat_fused", "query_lite")
 D_MODEL = 5120
 D_QLATENT = 1536
@@ -798,6 +807,88 @@ def run_query_lite(args):
     }
 
 
+def prefill_flops(batch: int, T: int, q_len: int, n_h: int = N_H):
+    """Algorithmic flops of one mla_prefill call: the up-projection of every
+    cached row (2 x 512 x 2 n_h d_h) and, per head, the score and output
+    products over the visible positions (2 x (192 + 128) per query-position
+    pair; new token t of a sequence sees T - q_len + t + 1 positions)."""
+    visible = batch * (q_len * (T - q_len) + q_len * (q_len + 1) // 2)
+    return 2.0 * batch * T * D_C * 2 * n_h * D_H + 2.0 * n_h * visible * (D_H + D_R + D_H)
+
+
+def run_prefill(args, name=None):
+    """mla_prefill over synthetic V2-shaped inputs: B sequences of T cached
+    tokens whose last q_len are new (prompt processing; q_len < T is a chunk
+    after a cached prefix), pages in random order.  The call is timed whole
+    (HIP events around each call on its stream: scan, gather, up-projection
+    and attention); the roofline is MFMA-bound on the algorithmic flops."""
+    import numpy as np
+    import torch
+    import synth
+    import mla_latent_kv_37_amd as mk
+    name = name or args.workload
+    B, T, Q, cdt = PREFILL_WORKLOADS[name]
+    torch.cuda.set_device(0)
+    mk._lib.load()
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1234)
+    pages = (T + 63) // 64
+    rows = torch.randn(B * pages, 64, D_C + D_R, device="cuda", generator=g) * synth.V2_SD_LATENT
+    if cdt == "bf16":
+        kv, scales = rows.to(torch.bfloat16), None
+    else:
+        # 1 x 128 groups: scale = max|x| / 448 per token and group, codes = x / scale in E4M3
+        r = torch.nn.functional.pad(rows, (0, 640 - (D_C + D_R))).view(B * pages, 64, 5, 128)
+        scales = (r.abs().amax(dim=-1) / 448.0).clamp_min(1e-12).contiguous()
+        kv = (r / scales[..., None]).view(B * pages, 64, 640)[..., : D_C + D_R].to(torch.float8_e4m3fn).contiguous()
+    bt = torch.randperm(B * pages, device="cuda", generator=g).to(torch.int32).view(B, pages)
+    lens = torch.full((B,), T, dtype=torch.int32, device="cuda")
+    cache = mk.make_cache(kv, bt, lens, 64, scales)
+    q_off = torch.arange(B + 1, dtype=torch.int32, device="cuda") * Q
+    n = B * Q
+    sdq = synth.V2_SD_QUERY
+    qn = (torch.randn(n, N_H, D_H, device="cuda", generator=g) * sdq).to(torch.bfloat16)
+    qp = (torch.randn(n, N_H, D_R, device="cuda", generator=g) * sdq).to(torch.bfloat16)
+    wuk = (torch.randn(N_H * D_H, D_C, device="cuda", generator=g) * synth.V2_SIGMA_W).to(torch.bfloat16)
+    wuv = (torch.randn(N_H * D_H, D_C, device="cuda", generator=g) * synth.V2_SIGMA_W).to(torch.bfloat16)
+    d = mk.dims(N_H, D_H, D_R, D_C)
+    total_kv = B * T
+    ws = torch.empty(mk.prefill_workspace_size(d, B, total_kv), dtype=torch.uint8, device="cuda")
+    out = torch.empty(n, N_H, D_H, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(n, N_H, dtype=torch.float32, device="cuda")
+    scale = 1.0 / math.sqrt(D_H + D_R)
+
+    def fn():
+        mk.prefill(d, q_off, n, Q, qn, qp, cache, total_kv, wuk, wuv, scale, ws, out, lse)
+    steps, warm = max(1, min(args.steps, 50)), max(1, min(args.warmup, 10))
+    for _ in range(warm):
+        fn()
+    stream = torch.cuda.current_stream()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        evs[i][0].record(stream)
+        fn()
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    times = sorted(e[0].elapsed_time(e[1]) for e in evs)
+    ms = times[len(times) // 2]
+    fl = prefill_flops(B, T, Q)
+    ach = fl / (ms * 1e-3) / 1e12
+    return {
+        "metric": "MLA prefill new tokens/s (non-absorbed, causal, 128 heads)",
+        "value": n / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warm,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": name, "batch": B, "cached_tokens_per_seq": T, "new_tokens_per_seq": Q,
+                   "cache_dtype": cdt, "timing": "median of per-call HIP events"},
+        "roofline": {"bound": "mfma", "achieved": ach, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": ach / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "mla_prefill (scan + gather + prefill_kv_kernel + prefill_attn_kernel), whole call",
+                     "algorithmic_flops_per_launch": fl, "mean_launch_ms": sum(times) / len(times)},
+    }
+
+
 def run_append(args):
     import numpy as np
     import torch
@@ -852,7 +943,8 @@ def main():
     # 1000 warmup steps reach the steady state that a serving loop runs at
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=1000)
-    ap.add_argument("--workload", default="ragged", choices=sorted(WORKLOADS) + sorted(APPEND_WORKLOADS) + sorted(QUERY_WORKLOADS))
+    ap.add_argument("--workload", default="ragged",
+                    choices=sorted(WORKLOADS) + sorted(APPEND_WORKLOADS) + sorted(QUERY_WORKLOADS) + sorted(PREFILL_WORKLOADS))
     ap.add_argument("--copies", type=int, default=2)
     ap.add_argument("--warm-weights", action="store_true",
                     help="reuse each input set's W^UK / W^UV (they may stay cached between steps)")
@@ -888,6 +980,8 @@ def main():
         copy_calibration(args.copy_calibration)
     if args.workload in APPEND_WORKLOADS:
         res = run_append(args)
+    elif args.workload in PREFILL_WORKLOADS:
+        res = run_prefill(args)
     elif args.workload in QUERY_WORKLOADS:
         res = run_query(args)
     elif args.workload == "ragged" and args.partition is None and not args.headline_only:
@@ -900,6 +994,11 @@ def main():
             r = run(args, wl, part, cpu=False, copy_tbps=copy_tbps)
             others[name] = summary(r)
             print(f"# {name}: {r['ms_per_step'] * 1e3:.1f} us/step, {r['value'] / 1e9:.3f} G {r['unit']}", flush=True)
+        pf = run_prefill(args, "prefill_b4_t4096")
+        others["prefill_b4_t4096"] = {k: pf[k] for k in ("metric", "value", "unit", "ms_per_step", "steps", "warmup",
+                                                         "config", "roofline")}
+        print(f"# prefill_b4_t4096: {pf['ms_per_step'] * 1e3:.1f} us/call, {pf['value'] / 1e6:.3f} M tokens/s, "
+              f"{pf['roofline']['achieved']:.0f} TFLOP/s", flush=True)
         res = run(args, copy_tbps=copy_tbps)
         res["other_workloads"] = others
     else:

@@ -238,16 +238,49 @@ __global__ __launch_bounds__(512) void prefill_kv_kernel(PrefillArgs a) {
 // Online softmax in the log2 domain with a lazy rescale: a token's reference
 // max moves (and its O^T and row sum are rescaled) only when the tile's max
 // exceeds it by more than kPfSlack, so probabilities stay below 2^kPfSlack.
-constexpr int kPaWaves = 8, kPaQ = 32 * kPaWaves, kPaTok = 32, kPaBufs = 4;
+constexpr int kPaWaves = 8, kPaQ = 32 * kPaWaves, kPaTok = 32;
+// tile buffers: tiles k and k+1 are read while tiles k+2 .. k+kPaBufs-1 load
+constexpr int kPaBufs = 6, kPaLead = kPaBufs - 1;
 constexpr int kPaKBytes = 3 * 4096, kPaVBytes = 2 * 4096, kPaTileBytes = kPaKBytes + kPaVBytes;
 constexpr float kPfSlack = 8.f;
+constexpr int kPaKAhead = 6;   // K fragment reads in flight ahead of the score MFMAs
+
+// s_waitcnt vmcnt(n) for a wave-uniform n in [0, 15]
+__device__ __forceinline__ void wait_vm(int n) {
+  switch (n) {
+#define MLA_VM_CASE(i) case i: __builtin_amdgcn_s_waitcnt(waitcnt_vm(i)); break;
+    MLA_VM_CASE(1) MLA_VM_CASE(2) MLA_VM_CASE(3) MLA_VM_CASE(4) MLA_VM_CASE(5) MLA_VM_CASE(6) MLA_VM_CASE(7)
+    MLA_VM_CASE(8) MLA_VM_CASE(9) MLA_VM_CASE(10) MLA_VM_CASE(11) MLA_VM_CASE(12) MLA_VM_CASE(13) MLA_VM_CASE(14)
+    MLA_VM_CASE(15)
+#undef MLA_VM_CASE
+    default: __builtin_amdgcn_s_waitcnt(waitcnt_vm(0)); break;
+  }
+}
 
 __global__ __launch_bounds__(512) void prefill_attn_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(2048))) char lds_raw[kPaBufs * kPaTileBytes];
   const uint32_t lds = uint32_t(reinterpret_cast<uintptr_t>(lds_raw));
-  const int head = blockIdx.x;
-  const int b = blockIdx.y / a.n_qblk;
-  const int qb = a.n_qblk - 1 - int(blockIdx.y % a.n_qblk);   // longest blocks first
+  // Order: block x runs on XCD x % 8.  Each XCD takes its heads (x % 8,
+  // x % 8 + 8, ...) two at a time, and a pair's token blocks longest first
+  // (the blocks of both heads and of every sequence at one block index, then
+  // the next lower index), so that the workgroups resident on an XCD read the
+  // keys and values of two heads, which its L2 then serves, and the last
+  // blocks to start are short ones.
+  const int per_head = a.batch * a.n_qblk;
+  int head, b, qb;
+  if ((a.n_heads & 15) == 0) {
+    const int j = int(blockIdx.x) >> 3;
+    const int grp = j / (2 * per_head), idx = j % (2 * per_head);
+    const int rest = idx % (2 * a.batch);
+    head = int(blockIdx.x & 7) + 8 * (2 * grp + (rest & 1));
+    b = rest >> 1;
+    qb = a.n_qblk - 1 - idx / (2 * a.batch);
+  } else {
+    head = int(blockIdx.x) / per_head;
+    const int r = int(blockIdx.x) % per_head;
+    b = r % a.batch;
+    qb = a.n_qblk - 1 - r / a.batch;
+  }
   const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63, h = lane >> 5;
 
   int T0 = load_const(a.seq_lens, b);
@@ -293,31 +326,31 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(PrefillArgs a) {
   const uint16_t* kc_base = a.kv_up + (int64_t(head) * a.cap_rows + cu) * kPfHead;
   const uint16_t* v_base = a.kv_up + (int64_t(a.n_heads + head) * a.cap_rows + cu) * kPfHead;
   const uint16_t* kr_base = a.c_rows + int64_t(cu) * kPfRow + kPfLat;
-  auto issue = [&](int k) {
+  auto issue_block = [&](int k, int j) {   // block wave + 8j of tile k
     const uint32_t tb = lds + uint32_t((k % kPaBufs) * kPaTileBytes);
-#pragma unroll
-    for (int j = 0; j < 3; ++j) {
-      if (j < n_my) {
-        const int i = wave + 8 * j;
-        const int g = i >> 2, rb = i & 3;
-        const int row = 8 * rb + (lane >> 3);
-        const int ch = (lane & 7) ^ swz_f(row);
-        const int pos = k * kPaTok + row;
-        const uint16_t* src;
-        uint32_t dst;
-        if (g < 2) {
-          src = kc_base + int64_t(pos) * kPfHead + 8 * (8 * g + ch);
-          dst = tb + uint32_t(i * 1024);
-        } else if (g == 2) {
-          src = kr_base + int64_t(pos) * kPfRow + 8 * ch;
-          dst = tb + uint32_t(i * 1024);
-        } else {
-          src = v_base + int64_t(pos) * kPfHead + 8 * (8 * (g - 3) + ch);
-          dst = tb + uint32_t(kPaKBytes + (i - 12) * 1024);
-        }
-        dma16(src, dst);
-      }
+    const int i = wave + 8 * j;
+    const int g = i >> 2, rb = i & 3;
+    const int row = 8 * rb + (lane >> 3);
+    const int ch = (lane & 7) ^ swz_f(row);
+    const int pos = k * kPaTok + row;
+    const uint16_t* src;
+    uint32_t dst;
+    if (g < 2) {
+      src = kc_base + int64_t(pos) * kPfHead + 8 * (8 * g + ch);
+      dst = tb + uint32_t(i * 1024);
+    } else if (g == 2) {
+      src = kr_base + int64_t(pos) * kPfRow + 8 * ch;
+      dst = tb + uint32_t(i * 1024);
+    } else {
+      src = v_base + int64_t(pos) * kPfHead + 8 * (8 * (g - 3) + ch);
+      dst = tb + uint32_t(kPaKBytes + (i - 12) * 1024);
     }
+    dma16(src, dst);
+  };
+  auto issue = [&](int k) {
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+      if (j < n_my) issue_block(k, j);
   };
 
   const int kb0 = tile_offset(lane & 31, h);
@@ -326,88 +359,130 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(PrefillArgs a) {
   // ((j>>1)&1), byte (j&1)*8; the second row's address is the first's ^ 0x410;
   // then ^ 64*(mt&1) + (mt>>1)*4096 + ks*2048
   const int vb0 = tile_offset(4 * h + ((lane & 15) >> 2), 2 * ((lane >> 4) & 1) + ((lane >> 1) & 1)) + (lane & 1) * 8;
+  auto tile_buf = [&](int k) { return lds + uint32_t((k % kPaBufs) * kPaTileBytes); };
+  auto kfrag = [&](uint32_t tb, int st) {
+    return lds_read_b128(((tb + uint32_t(kb0)) ^ uint32_t(32 * (st & 3))) + uint32_t((st >> 2) * 4096));
+  };
+  auto vfrag = [&](uint32_t tb, int st) {   // PV step st: token half st >> 2, column tile st & 3
+    const int ks = st >> 2, mt = st & 3;
+    const uint32_t a0 = ((tb + uint32_t(kPaKBytes + vb0)) ^ uint32_t(64 * (mt & 1))) + uint32_t((mt >> 1) * 4096 + ks * 2048);
+    return lds_read_tr_pair(a0, a0 ^ 0x410u);
+  };
 
   f32x16 acc[4];
 #pragma unroll
   for (int m = 0; m < 4; ++m) acc[m] = f32x16{};
   float m_run = -INFINITY, lsum = 0.f;
 
-  for (int k = 0; k < min(ntiles, 3); ++k) issue(k);
-  for (int k = 0; k < ntiles; ++k) {
-    const int later = min(ntiles - 1 - k, 2);   // tiles after k with loads in flight
-    if (later == 2) {
-      if (wave < 4) __builtin_amdgcn_s_waitcnt(waitcnt_vm(6));
-      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(4));
-    } else if (later == 1) {
-      if (wave < 4) __builtin_amdgcn_s_waitcnt(waitcnt_vm(3));
-      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(2));
-    } else {
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    }
-    raw_barrier();
-    if (k + 3 < ntiles) issue(k + 3);
-    if (k >= w_tiles) continue;   // past this wavefront's last visible position
+  // Software pipeline of tile k (per wavefront; the workgroup's tiles go on
+  // past a wavefront's own range, where it only loads and waits):
+  //   mask and max of S(k), lazy rescale of O^T
+  //   phase A: the 12 score MFMAs of tile k+1, with the exponentials, the bf16
+  //            packing and the row sums of P(k) between them and the first V^T
+  //            reads of tile k during the last ones
+  //   phase B: the 8 PV MFMAs of tile k, with this wavefront's loads of tile
+  //            k+5 between them (into the buffer of tile k-1)
+  //   wait for this wavefront's loads of tile k+2, barrier (tile k+2 complete;
+  //     every wavefront is done with tile k, whose buffer takes tile k+6)
+  for (int k = 0; k < min(ntiles, kPaLead); ++k) issue(k);
+  // tiles 0 and 1 complete (the loads of the later ones stay in flight)
+  wait_vm(n_my * max(0, min(ntiles, kPaLead) - 2));
+  raw_barrier();
+  f32x16 s = f32x16{};
+  if (w_tiles > 0) {
+    const uint32_t tb = tile_buf(0);
+#pragma unroll
+    for (int st = 0; st < 12; ++st) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(tb, st), qf[st], s, 0, 0, 0);
+  }
 
-    const uint32_t tb = lds + uint32_t((k % kPaBufs) * kPaTileBytes);
-    // scores
-    f32x16 s = f32x16{};
-    {
-      const uint32_t kl = tb + uint32_t(kb0);
+  for (int k = 0; k < ntiles; ++k) {
+    const bool load3 = k + kPaLead < ntiles;   // tile k+kPaLead, into tile k-1's buffer
+    if (k < w_tiles) {
+      const uint32_t tb = tile_buf(k);
+      // causal mask (only where the tile reaches past the wavefront's first
+      // token's last position) and the tile max
+      const int j0 = k * kPaTok;
+      if (j0 + kPaTok - 1 > w_first) {
 #pragma unroll
-      for (int st = 0; st < 12; ++st) {
-        const bf16x8 kf = lds_read_b128((kl ^ uint32_t(32 * (st & 3))) + uint32_t((st >> 2) * 4096));
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[st], s, 0, 0, 0);
+        for (int r = 0; r < 16; ++r)
+          s[r] = (j0 + 8 * (r >> 2) + 4 * h + (r & 3) > lim) ? -INFINITY : s[r];
       }
-    }
-    // scale, causal mask, tile max
-    const int j0 = k * kPaTok;
-    const bool diag = j0 + kPaTok - 1 > w_first;
+      float mx = s[0];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float x = s[r] * a.scale_log2;
-      s[r] = (diag && j0 + 8 * (r >> 2) + 4 * h + (r & 3) > lim) ? -INFINITY : x;
-    }
-    float mx = s[0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-    {
-      const auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx = fmaxf(__uint_as_float(sw2[0]), __uint_as_float(sw2[1]));
-    }
-    const bool need = mx > m_run + kPfSlack;   // (false while mx is -inf)
-    if (__any(need)) {
-      const float m_new = need ? mx : m_run;
-      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;   // exp2(-inf) = 0
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[m][r] *= alpha;
-      lsum *= alpha;
-      m_run = m_new;
-    }
-    const float mref = m_run == -INFINITY ? 0.f : m_run;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(s[r] - mref);
-    {
-      const float u0 = (s[0] + s[1]) + (s[2] + s[3]), u1 = (s[4] + s[5]) + (s[6] + s[7]);
-      const float u2 = (s[8] + s[9]) + (s[10] + s[11]), u3 = (s[12] + s[13]) + (s[14] + s[15]);
-      lsum += (u0 + u1) + (u2 + u3);
-    }
-    bf16x8 pk[2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pk[ks][e] = (__bf16)s[8 * ks + e];
-    // O^T += V^T . P^T
-    const uint32_t vl = tb + uint32_t(kPaKBytes + vb0);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const uint32_t a0 = (vl ^ uint32_t(64 * (mt & 1))) + uint32_t((mt >> 1) * 4096 + ks * 2048);
-        const bf16x8 vf = lds_read_tr_pair(a0, a0 ^ 0x410u);
-        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pk[ks], acc[mt], 0, 0, 0);
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+      {
+        const auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = fmaxf(__uint_as_float(sw2[0]), __uint_as_float(sw2[1])) * a.scale_log2;
       }
+      const bool need = mx > m_run + kPfSlack;   // (false while mx is -inf)
+      if (__any(need)) {
+        const float m_new = need ? mx : m_run;
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;   // exp2(-inf) = 0
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[m][r] *= alpha;
+        lsum *= alpha;
+        m_run = m_new;
+      }
+      const float mref = m_run == -INFINITY ? 0.f : m_run;
+
+      // ======== phase A: scores of tile k+1 (computed also past the
+      // wavefront's range, where they are not used: no branch inside the
+      // pipeline), softmax of tile k in 11 pieces between them
+      bf16x8 pk[2];
+      bf16x8 vr[4];
+      f32x16 sn;
+      {
+        const uint32_t tn = tile_buf(k + 1);
+        bf16x8 kr[kPaKAhead];
+#pragma unroll
+        for (int i = 0; i < kPaKAhead; ++i) kr[i] = kfrag(tn, i);
+#pragma unroll
+        for (int st = 0; st < 12; ++st) {
+          const bf16x8 kc = kr[st % kPaKAhead];
+          if (st + kPaKAhead < 12) kr[st % kPaKAhead] = kfrag(tn, st + kPaKAhead);
+          sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc, qf[st], st == 0 ? f32x16{} : sn, 0, 0, 0);
+          // (each piece is pinned where it is written: left alone, the
+          // compiler sinks the exponentials next to their use in phase B)
+          if (st < 8) {
+            s[2 * st] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * st], a.scale_log2, -mref));
+            s[2 * st + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * st + 1], a.scale_log2, -mref));
+            asm volatile("" : "+v"(s[2 * st]), "+v"(s[2 * st + 1]));
+          } else if (st < 10) {
+            const int ks = st - 8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pk[ks][e] = (__bf16)s[8 * ks + e];
+            asm volatile("" : "+v"(pk[ks]));
+          } else if (st == 10) {
+            const float u0 = (s[0] + s[1]) + (s[2] + s[3]), u1 = (s[4] + s[5]) + (s[6] + s[7]);
+            const float u2 = (s[8] + s[9]) + (s[10] + s[11]), u3 = (s[12] + s[13]) + (s[14] + s[15]);
+            lsum += (u0 + u1) + (u2 + u3);
+          }
+          if (st >= 8) vr[st - 8] = vfrag(tb, st - 8);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+
+      // ======== phase B: O^T += V^T . P^T of tile k | loads of tile k+5
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        const bf16x8 vc = vr[st % 4];
+        if (st + 4 < 8) vr[st % 4] = vfrag(tb, st + 4);
+        acc[st & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vc, pk[st >> 2], acc[st & 3], 0, 0, 0);
+        if (load3 && (st & 1) == 0 && (st >> 1) < n_my) issue_block(k + kPaLead, st >> 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      s = sn;
+    } else if (load3) {
+      issue(k + kPaLead);
+    }
+
+    // ---- tile k+2 complete for every wavefront (the later tiles' loads stay in flight)
+    if (k + 2 < ntiles) {
+      wait_vm(n_my * (min(ntiles - 1, k + kPaLead) - (k + 2)));
+      raw_barrier();
+    }
   }
 
   // epilogue: the token's row sum over both lanes of its pair; o = O / sum,
@@ -440,7 +515,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   prefill_scan_kernel<<<1, 256, 0, st>>>(a);
   prefill_gather_kernel<<<a.cap_rows / 32, 256, 0, st>>>(a);
   prefill_kv_kernel<<<dim3(2 * a.n_heads * kPfHead / kKvTile, a.cap_rows / kKvTile), 512, 0, st>>>(a);
-  if (a.batch > 0 && a.n_qblk > 0) prefill_attn_kernel<<<dim3(a.n_heads, a.batch * a.n_qblk), 512, 0, st>>>(a);
+  if (a.batch > 0 && a.n_qblk > 0) prefill_attn_kernel<<<a.n_heads * a.batch * a.n_qblk, 512, 0, st>>>(a);
   return hipGetLastError();
 }
 
