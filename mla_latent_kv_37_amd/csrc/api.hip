@@ -492,7 +492,7 @@ mla_status_t prefill_layout(const mla_dims_t* dims, int32_t batch, int64_t total
   if (mla_status_t s = check_dims(dims)) return s;
   if (batch < 0 || total_kv < 0) return MLA_ERR_INVALID_ARG;
   if (dims->d_head != 128 || dims->d_latent != 512 || dims->d_rope != 64) return MLA_ERR_UNSUPPORTED;
-  if (total_kv > kPrefillMaxKv || dims->n_heads > 65536) return MLA_ERR_UNSUPPORTED;
+  if (total_kv > kPrefillMaxKv || dims->n_heads > 32768) return MLA_ERR_UNSUPPORTED;
   PrefillLayout l{};
   // rows: every position a 32-row tile of a sequence can touch (up to 31 past
   // the last row), in whole 256-row tiles of the up-projection

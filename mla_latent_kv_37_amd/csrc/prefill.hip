@@ -126,6 +126,27 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
                : "memory", "m0");
 }
 
+// Output staging.  An MFMA accumulator tile holds, in lane (r, h) = (lane&31,
+// lane>>5), row r's columns 8j + 4h .. +3 in registers 4j .. 4j+3 of each
+// 32-column block: stored as they are, every global write would be 8 bytes
+// scattered over 32 rows.  Instead a wavefront writes its rows (256 B each,
+// bf16) into its own LDS area, chunk c (16 B) of row r at r*256 + ((c ^ (r&15))
+// * 16), and then writes them out 4 whole rows per instruction.
+__device__ __forceinline__ void stage_block(uint32_t area, int row, int h, int blk, const f32x16& v, float mul) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    bf16x4 x;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = (__bf16)(v[4 * j + e] * mul);
+    const int c = 4 * blk + j;
+    *reinterpret_cast<bf16x4 MLA_LDS*>((char MLA_LDS*)(uintptr_t)(area + uint32_t(row * 256 + ((c ^ (row & 15)) * 16) + 8 * h))) = x;
+  }
+}
+// row r of the staged rows (4 per call, lane l: row 4i + (l>>4), chunk l&15)
+__device__ __forceinline__ bf16x8 staged_chunk(uint32_t area, int row, int c) {
+  return lds_read_b128(area + uint32_t(row * 256 + ((c ^ (row & 15)) * 16)));
+}
+
 // ---------------------------------------------------------------------------
 // kv: KV^T tile [256 features x 256 rows] per workgroup, K = 512 in 16 chunks of
 // 32.  8 wavefronts (2 per SIMD): wavefront w computes features 128(w&1) ..+127
@@ -142,7 +163,11 @@ constexpr int kKvStage = 2 * kKvHalf;
 __global__ __launch_bounds__(512) void prefill_kv_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds_raw[kKvStages * kKvStage];
   const uint32_t lds = uint32_t(reinterpret_cast<uintptr_t>(lds_raw));
-  const int f0 = blockIdx.x * kKvTile, g0 = blockIdx.y * kKvTile;
+  // Row tiles vary fastest: block x runs on XCD x % 8, so an XCD holds the
+  // same few row tiles of C (256 KB each) for the whole launch, from its L2,
+  // while the weight tiles stream past once per XCD.
+  const int ft = int(blockIdx.y);
+  const int f0 = ft * kKvTile, g0 = int(blockIdx.x) * kKvTile;
   const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63, h = lane >> 5;
   const int nk = a.n_heads * kPfHead;
 
@@ -178,51 +203,71 @@ __global__ __launch_bounds__(512) void prefill_kv_kernel(PrefillArgs a) {
 #pragma unroll
     for (int n = 0; n < 2; ++n) acc[m][n] = f32x16{};
 
-  issue(0);
-  issue(1);
-  issue(2);
+  // fragments of one chunk: k-step s, 4 weight and 2 row fragments
+  struct Frags {
+    bf16x8 a[2][4], b[2][2];
+  };
+  auto read_step = [&](Frags& f, int c, int s) {
+    const uint32_t sb = lds + uint32_t((c % kKvStages) * kKvStage);
+    const uint32_t pofs = uint32_t(((2 * s + h) ^ sw) * 16);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) f.a[s][m] = lds_read_b128(sb + a_row + uint32_t(m * 2048) + pofs);
+#pragma unroll
+    for (int n = 0; n < 2; ++n) f.b[s][n] = lds_read_b128(sb + b_row + uint32_t(n * 2048) + pofs);
+  };
+
+  // Chunk c's fragments are read into registers during chunk c-1's MFMAs, so
+  // the MFMAs never wait for LDS; the barrier at the top of iteration c
+  // publishes chunk c+1 and tells that every wavefront holds chunk c in
+  // registers, so chunk c+4 may overwrite its stage.
+#pragma unroll
+  for (int c = 0; c < kKvStages; ++c) issue(c);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(4 * (kKvStages - 1)));
+  raw_barrier();
+  Frags cur;
+  read_step(cur, 0, 0);
+  read_step(cur, 0, 1);
 #pragma unroll
   for (int c = 0; c < kKvChunks; ++c) {
-    // this wavefront's loads of chunk c are done (those of the next ones may
-    // still be in flight: 4 per chunk), then the barrier publishes chunk c and
-    // frees the stage of chunk c-1 for chunk c+3
-    const int later = (c + 2 < kKvChunks ? 2 : kKvChunks - 1 - c);
-    if (later == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(8));
-    else if (later == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(4));
-    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    raw_barrier();
-    if (c + 3 < kKvChunks) issue(c + 3);
-    const uint32_t sb = lds + uint32_t((c % kKvStages) * kKvStage);
+    Frags nxt;
+    if (c + 1 < kKvChunks) {
+      const int later = min(c + kKvStages - 1, kKvChunks - 1) - (c + 1);   // chunks issued after c+1
+      if (later == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(8));
+      else if (later == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(4));
+      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
+      raw_barrier();
+      if (c + kKvStages < kKvChunks) issue(c + kKvStages);
+      read_step(nxt, c + 1, 0);
+    }
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const uint32_t pofs = uint32_t(((2 * s + h) ^ sw) * 16);
-      bf16x8 af[4], bf[2];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) af[m] = lds_read_b128(sb + a_row + uint32_t(m * 2048) + pofs);
-#pragma unroll
-      for (int n = 0; n < 2; ++n) bf[n] = lds_read_b128(sb + b_row + uint32_t(n * 2048) + pofs);
 #pragma unroll
       for (int m = 0; m < 4; ++m)
 #pragma unroll
-        for (int n = 0; n < 2; ++n) acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[m], bf[n], acc[m][n], 0, 0, 0);
+        for (int n = 0; n < 2; ++n)
+          acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.a[s][m], cur.b[s][n], acc[m][n], 0, 0, 0);
+      if (s == 0 && c + 1 < kKvChunks) read_step(nxt, c + 1, 1);
     }
+    if (c + 1 < kKvChunks) cur = nxt;
   }
 
-  // stores: feature 32m + 8(i>>2) + 4h + (i&3) of slab 2x + fw, row g0 + 64tw + 32n + (lane&31)
-  const int slab = 2 * blockIdx.x + fw;
+  // stores: the wavefront's 64 rows x 128 features of slab 2 ft + fw are one
+  // contiguous 16 KB block (rows g0 + 64 tw ..), staged through the LDS area
+  // of the (finished) operand stages
+  __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
+  raw_barrier();
+  const uint32_t area = lds + uint32_t(wave * 16384);
 #pragma unroll
-  for (int n = 0; n < 2; ++n) {
-    const int g = g0 + 64 * tw + 32 * n + (lane & 31);
-    uint16_t* dst = a.kv_up + (int64_t(slab) * a.cap_rows + g) * kPfHead + 4 * h;
+  for (int n = 0; n < 2; ++n)
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int m = 0; m < 4; ++m) stage_block(area, 32 * n + (lane & 31), h, m, acc[m][n], 1.f);
+  __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
+  uint16_t* dst = a.kv_up + (int64_t(2 * ft + fw) * a.cap_rows + g0 + 64 * tw) * kPfHead;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        bf16x4 v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (__bf16)acc[m][n][4 * q + e];
-        *reinterpret_cast<bf16x4*>(dst + 32 * m + 8 * q) = v;
-      }
+  for (int i = 0; i < 16; ++i) {
+    const int row = 4 * i + (lane >> 4), c = lane & 15;
+    *reinterpret_cast<bf16x8*>(dst + row * kPfHead + c * 8) = staged_chunk(area, row, c);
   }
 }
 
@@ -492,21 +537,27 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(PrefillArgs a) {
     const auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum), false, false);
     lsum = __uint_as_float(sw2[0]) + __uint_as_float(sw2[1]);
   }
-  if (!q_ok) return;
   const bool any = lsum > 0.f;
   const float inv = any ? 1.f / lsum : 0.f;
-  uint16_t* dst = a.out + (int64_t(qo + t) * a.n_heads + head) * kPfHead + 4 * h;
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      bf16x4 v;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[mt][4 * q + e] * inv);
-      *reinterpret_cast<bf16x4*>(dst + 32 * mt + 8 * q) = v;
-    }
-  if (a.lse != nullptr && h == 0)
+  if (q_ok && a.lse != nullptr && h == 0)
     a.lse[int64_t(qo + t) * a.n_heads + head] = any ? (m_run + __log2f(lsum)) * kLn2 : -INFINITY;
+  // outputs: the wavefront's 32 token rows (256 B each) staged through its 8 KB
+  // of LDS, then written 4 whole rows per instruction (the tile buffers are
+  // free once every wavefront has left the loop)
+  __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
+  raw_barrier();              // (no tile loads are in flight after the loop)
+  if (t_base >= qn) return;   // (wave-uniform: no token of this wavefront is valid)
+  const uint32_t area = lds + uint32_t(wave * 8192);
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) stage_block(area, lane & 31, h, mt, acc[mt], inv);
+  __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int row = 4 * i + (lane >> 4), c = lane & 15;
+    if (t_base + row < qn)
+      *reinterpret_cast<bf16x8*>(a.out + (int64_t(qo + t_base + row) * a.n_heads + head) * kPfHead + c * 8) =
+          staged_chunk(area, row, c);
+  }
 }
 
 }  // namespace
@@ -514,7 +565,7 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(PrefillArgs a) {
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   prefill_scan_kernel<<<1, 256, 0, st>>>(a);
   prefill_gather_kernel<<<a.cap_rows / 32, 256, 0, st>>>(a);
-  prefill_kv_kernel<<<dim3(2 * a.n_heads * kPfHead / kKvTile, a.cap_rows / kKvTile), 512, 0, st>>>(a);
+  prefill_kv_kernel<<<dim3(a.cap_rows / kKvTile, 2 * a.n_heads * kPfHead / kKvTile), 512, 0, st>>>(a);
   if (a.batch > 0 && a.n_qblk > 0) prefill_attn_kernel<<<a.n_heads * a.batch * a.n_qblk, 512, 0, st>>>(a);
   return hipGetLastError();
 }
