@@ -799,7 +799,7 @@ mla_status_t mla_prefill(const mla_dims_t* dims, int32_t batch, const int32_t* q
     return MLA_ERR_ALIGNMENT;
   if (!workspace || workspace_bytes < L.total) return MLA_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return MLA_ERR_ALIGNMENT;
-  const int64_t n_qblk = (int64_t(max_q_len) + 255) / 256;
+  const int64_t n_qblk = (int64_t(max_q_len) + 127) / 128;   // (blocks of at least 128 new tokens)
   if (int64_t(batch) * n_qblk * dims->n_heads > INT32_MAX) return MLA_ERR_UNSUPPORTED;
   if (batch == 0 || total_q == 0) return MLA_OK;
 
@@ -815,7 +815,7 @@ mla_status_t mla_prefill(const mla_dims_t* dims, int32_t batch, const int32_t* q
   a.total_kv = total_kv;
   a.cap_rows = L.cap_rows;
   a.total_q = total_q;
-  a.n_qblk = int(n_qblk);
+  a.max_q_len = max_q_len;
   a.seq_lens = cache->seq_lens;
   a.block_table = cache->block_table;
   a.q_off = q_offsets;

@@ -117,7 +117,8 @@ struct PrefillArgs {
   int64_t total_kv;        // capacity of the gathered rows (sum of the lengths)
   int cap_rows;            // rows of the gathered and up-projected arrays (multiple of 256)
   int total_q;             // rows of q_nope / q_pe / out
-  int n_qblk;              // 256-token blocks per sequence (ceil(max_q_len / 256))
+  int max_q_len;           // bound on every sequence's new tokens
+  int n_qblk;              // token blocks per sequence (set by launch_prefill)
   const int32_t* seq_lens; // [batch]
   const int32_t* block_table;
   const int32_t* q_off;    // [batch + 1]

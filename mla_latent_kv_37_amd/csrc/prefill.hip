@@ -286,6 +286,9 @@ __global__ __launch_bounds__(512) void prefill_kv_kernel(PrefillArgs a) {
 // Online softmax in the log2 domain with a lazy rescale: a token's reference
 // max moves (and its O^T and row sum are rescaled) only when the tile's max
 // exceeds it by more than kPfSlack, so probabilities stay below 2^kPfSlack.
+// (4 wavefronts per workgroup, two workgroups per compute unit with 4 buffers
+// each, measured 54% slower: twice the tile loads per token, and no gain from
+// the independent barriers)
 constexpr int kPaWaves = 8, kPaQ = 32 * kPaWaves, kPaTok = 32;
 // tile buffers: tiles k and k+1 are read while tiles k+2 .. k+kPaBufs-1 load
 constexpr int kPaBufs = 6, kPaLead = kPaBufs - 1;
@@ -305,7 +308,7 @@ __device__ __forceinline__ void wait_vm(int n) {
   }
 }
 
-__global__ __launch_bounds__(512) void prefill_attn_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(64 * kPaWaves) void prefill_attn_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(2048))) char lds_raw[kPaBufs * kPaTileBytes];
   const uint32_t lds = uint32_t(reinterpret_cast<uintptr_t>(lds_raw));
   // Order: block x runs on XCD x % 8.  Each XCD takes its heads (x % 8,
@@ -370,13 +373,13 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(PrefillArgs a) {
   // group g; groups 0-1 k^C, 2 k^R, 3-4 V); wavefront w issues blocks w, w+8
   // and (w < 4) w+16.  Lane l reads row 8rb + (l>>3), logical chunk
   // 8g' + ((l&7) ^ f(row)) of its source row.
-  const int n_my = wave < 4 ? 3 : 2;
+  const int n_my = (20 - wave + kPaWaves - 1) / kPaWaves;   // blocks wave, wave + kPaWaves, ..
   const uint16_t* kc_base = a.kv_up + (int64_t(head) * a.cap_rows + cu) * kPfHead;
   const uint16_t* v_base = a.kv_up + (int64_t(a.n_heads + head) * a.cap_rows + cu) * kPfHead;
   const uint16_t* kr_base = a.c_rows + int64_t(cu) * kPfRow + kPfLat;
   auto issue_block = [&](int k, int j) {   // block wave + 8j of tile k
     const uint32_t tb = lds + uint32_t((k % kPaBufs) * kPaTileBytes);
-    const int i = wave + 8 * j;
+    const int i = wave + kPaWaves * j;
     const int g = i >> 2, rb = i & 3;
     const int row = 8 * rb + (lane >> 3);
     const int ch = (lane & 7) ^ swz_f(row);
@@ -397,7 +400,7 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(PrefillArgs a) {
   };
   auto issue = [&](int k) {
 #pragma unroll
-    for (int j = 0; j < 3; ++j)
+    for (int j = 0; j < (20 + kPaWaves - 1) / kPaWaves; ++j)
       if (j < n_my) issue_block(k, j);
   };
 
@@ -518,7 +521,7 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(PrefillArgs a) {
         const bf16x8 vc = vr[st % 4];
         if (st + 4 < 8) vr[st % 4] = vfrag(tb, st + 4);
         acc[st & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vc, pk[st >> 2], acc[st & 3], 0, 0, 0);
-        if (load3 && (st & 1) == 0 && (st >> 1) < n_my) issue_block(k + kPaLead, st >> 1);
+        if (load3 && st < n_my) issue_block(k + kPaLead, st);
         __builtin_amdgcn_sched_barrier(0);
       }
       s = sn;
@@ -569,7 +572,9 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   prefill_scan_kernel<<<1, 256, 0, st>>>(a);
   prefill_gather_kernel<<<a.cap_rows / 32, 256, 0, st>>>(a);
   prefill_kv_kernel<<<dim3(a.cap_rows / kKvTile, 2 * a.n_heads * kPfHead / kKvTile), 512, 0, st>>>(a);
-  if (a.batch > 0 && a.n_qblk > 0) prefill_attn_kernel<<<a.n_heads * a.batch * a.n_qblk, 512, 0, st>>>(a);
+  PrefillArgs b = a;
+  b.n_qblk = (a.max_q_len + kPaQ - 1) / kPaQ;
+  if (b.batch > 0 && b.n_qblk > 0) prefill_attn_kernel<<<b.n_heads * b.batch * b.n_qblk, 64 * kPaWaves, 0, st>>>(b);
   return hipGetLastError();
 }
 

@@ -210,7 +210,7 @@ static void check_prefill_validation() {
   CHECK(mla_prefill(&d, 4, idev(9), 3000, 1000, dev(4), dev(5), MLA_BF16, &c, 5000, dev(7), dev(8), MLA_BF16, 0.07f,
                     wsp, ws, dev(10), MLA_BF16, nullptr, nullptr) == MLA_OK);
   CHECK(g_launches == before + 1);
-  CHECK(g_pf.cap_rows == cap && g_pf.n_qblk == 4 && g_pf.total_q == 3000 && g_pf.max_tokens == 40 * 64);
+  CHECK(g_pf.cap_rows == cap && g_pf.max_q_len == 1000 && g_pf.total_q == 3000 && g_pf.max_tokens == 40 * 64);
   CHECK(reinterpret_cast<char*>(g_pf.cu) == wsp && reinterpret_cast<char*>(g_pf.c_rows) == wsp + 256);
   CHECK(reinterpret_cast<char*>(g_pf.kv_up) == wsp + 256 + size_t(cap) * 1152);
   before = g_launches;
