@@ -41,11 +41,14 @@ def _queries(case, q_lens, seed, gain):
     return _round(q_c, "bf16"), _round(q_r, "bf16")
 
 
-def _run(case, dev, q_lens, q_c, q_r, total_kv=None, max_q_len=None):
+def _run(case, dev, q_lens, q_c, q_r, total_kv=None, max_q_len=None, extra_rows=0):
     import torch
     import mla_latent_kv_37_amd as mk
     d = case.dims
     dd = mk.dims(d.n_heads, d.d_head, d.d_rope, d.d_latent)
+    if extra_rows:
+        q_c = np.concatenate([q_c, np.zeros((extra_rows,) + q_c.shape[1:])])
+        q_r = np.concatenate([q_r, np.zeros((extra_rows,) + q_r.shape[1:])])
     n = q_c.shape[0]
     q_off = torch.tensor(np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32), device="cuda")
     t = lambda x: torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda().to(torch.bfloat16)  # noqa: E731
@@ -88,6 +91,8 @@ def _compare(case, q_lens, q_c, q_r, got, tol, heads):
     worst_o = worst_l = 0.0
     row0 = 0
     for b, (T, ql) in enumerate(zip(case.lens, q_lens)):
+        if ql == 0:
+            continue
         rows = case.stored_rows(b)
         c_kv, k_r = rows[:, :d.d_latent], rows[:, d.d_latent:]
         qs = slice(row0, row0 + ql)
@@ -233,3 +238,18 @@ def test_prefill_bad_page_ids_read_as_zero_rows():
         for t in (0, 63, 64, 100, 149):
             assert rel_err(out[t, i], r["o"][t]) <= TOL["bf16"], (i, t)
     torch.cuda.synchronize()
+
+
+def test_prefill_empty_sequences_and_spare_rows():
+    """Sequences with no new tokens, an empty cache, and rows of q / o_heads past
+    the last sequence's tokens: the spare rows stay untouched (NaN), the others
+    match the oracle."""
+    lens = [0, 50, 200, 7, 0]
+    q_lens = [0, 50, 0, 7, 0]
+    case = direct_case(3, lens, max_pages=4, seed=87)
+    dev = to_device(case)
+    q_c, q_r = _queries(case, q_lens, seed=18, gain=1.0)
+    out, lse = _run(case, dev, q_lens, q_c, q_r, extra_rows=5)
+    n = sum(q_lens)
+    assert np.all(np.isnan(out[n:])) and np.all(np.isnan(lse[n:]))
+    _compare(case, q_lens, q_c, q_r, (out[:n], lse[:n]), TOL["bf16"], HEADS)
