@@ -377,26 +377,35 @@ __global__ __launch_bounds__(64 * kPaWaves) void prefill_attn_kernel(PrefillArgs
   const uint16_t* kc_base = a.kv_up + (int64_t(head) * a.cap_rows + cu) * kPfHead;
   const uint16_t* v_base = a.kv_up + (int64_t(a.n_heads + head) * a.cap_rows + cu) * kPfHead;
   const uint16_t* kr_base = a.c_rows + int64_t(cu) * kPfRow + kPfLat;
-  auto issue_block = [&](int k, int j) {   // block wave + 8j of tile k
-    const uint32_t tb = lds + uint32_t((k % kPaBufs) * kPaTileBytes);
-    const int i = wave + kPaWaves * j;
+  // per block j of this wavefront: the source of tile 0, the step from tile to
+  // tile (uniform) and the LDS offset in a tile buffer, computed once (1.4%
+  // less attention time than computing each address at its issue)
+  constexpr int kMaxMy = (20 + kPaWaves - 1) / kPaWaves;
+  const char* src0[kMaxMy];
+  int64_t step[kMaxMy];
+  uint32_t doff[kMaxMy];
+#pragma unroll
+  for (int j = 0; j < kMaxMy; ++j) {
+    const int i = min(wave + kPaWaves * j, 19);
     const int g = i >> 2, rb = i & 3;
     const int row = 8 * rb + (lane >> 3);
     const int ch = (lane & 7) ^ swz_f(row);
-    const int pos = k * kPaTok + row;
-    const uint16_t* src;
-    uint32_t dst;
     if (g < 2) {
-      src = kc_base + int64_t(pos) * kPfHead + 8 * (8 * g + ch);
-      dst = tb + uint32_t(i * 1024);
+      src0[j] = reinterpret_cast<const char*>(kc_base + int64_t(row) * kPfHead + 8 * (8 * g + ch));
+      step[j] = int64_t(kPaTok) * kPfHead * 2;
+      doff[j] = uint32_t(i * 1024);
     } else if (g == 2) {
-      src = kr_base + int64_t(pos) * kPfRow + 8 * ch;
-      dst = tb + uint32_t(i * 1024);
+      src0[j] = reinterpret_cast<const char*>(kr_base + int64_t(row) * kPfRow + 8 * ch);
+      step[j] = int64_t(kPaTok) * kPfRow * 2;
+      doff[j] = uint32_t(i * 1024);
     } else {
-      src = v_base + int64_t(pos) * kPfHead + 8 * (8 * (g - 3) + ch);
-      dst = tb + uint32_t(kPaKBytes + (i - 12) * 1024);
+      src0[j] = reinterpret_cast<const char*>(v_base + int64_t(row) * kPfHead + 8 * (8 * (g - 3) + ch));
+      step[j] = int64_t(kPaTok) * kPfHead * 2;
+      doff[j] = uint32_t(kPaKBytes + (i - 12) * 1024);
     }
-    dma16(src, dst);
+  }
+  auto issue_block = [&](int k, int j) {   // block wave + kPaWaves j of tile k
+    dma16(src0[j] + k * step[j], lds + uint32_t((k % kPaBufs) * kPaTileBytes) + doff[j]);
   };
   auto issue = [&](int k) {
 #pragma unroll
