@@ -20,6 +20,7 @@ Nothing here is "parity unpinned".
 """
 from . import mla, storage  # noqa: F401
 from .mla import (attend, attend_head, attend_new_tokens, chunk_partials, forward_from_h, merge_partials,  # noqa: F401
-                  out_project, prefill_head, project_cache, project_query, rope, softmax_scale)
+                  out_project, prefill_head, project_cache, project_query, rope, rope_theta, softmax_scale,
+                  yarn_attention_factor, yarn_theta)
 from .storage import (bf16_bits_to_f64, dequantize_rows, e4m3fn_to_f64,  # noqa: F401
                       f32_to_bf16_bits, f64_to_e4m3fn, gather_sequence, quantize_e4m3_groups, stored_rows_f64)

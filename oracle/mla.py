@@ -55,6 +55,44 @@ def rope(x: np.ndarray, pos, base: float = ROPE_BASE) -> np.ndarray:
     return out
 
 
+def yarn_theta(d: int, base: float, scale: float, alpha: float, beta: float, orig_ctx: int) -> np.ndarray:
+    """RoPE frequencies after YaRN context extension ([V2-explainer] §3.1.3 gives
+    s = 40, alpha = 1, beta = 32 and applies YaRN to the RoPE-carrying key k^R;
+    the ramp is the YaRN definition the page refers to): pair k's plain
+    frequency theta_k = base^(-2k/d) turns r_k = orig_ctx * theta_k / (2 pi)
+    times over the original context; gamma_k = clip((r_k - alpha) / (beta -
+    alpha), 0, 1); the new frequency is (1 - gamma_k) theta_k / s + gamma_k theta_k
+    (slow pairs interpolated by s, fast pairs unchanged, a linear ramp between).
+    scale = 1 gives the plain frequencies."""
+    k = np.arange(d // 2, dtype=np.float64)
+    theta = base ** (-2.0 * k / d)
+    if scale == 1.0:
+        return theta
+    r = orig_ctx * theta / (2.0 * math.pi)
+    gamma = np.clip((r - alpha) / (beta - alpha), 0.0, 1.0)
+    return (1.0 - gamma) * theta / scale + gamma * theta
+
+
+def rope_theta(x: np.ndarray, pos, theta: np.ndarray) -> np.ndarray:
+    """Rotate consecutive pairs (x[2k], x[2k+1]) by angle pos * theta[k]."""
+    x = np.asarray(x, dtype=np.float64)
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * theta
+    c, s = np.cos(ang), np.sin(ang)
+    x0, x1 = x[..., 0::2], x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = x0 * c - x1 * s
+    out[..., 1::2] = x0 * s + x1 * c
+    return out
+
+
+def yarn_attention_factor(scale: float) -> float:
+    """The softmax-scale multiplier of YaRN in MLA: the page's length factor
+    sqrt(t) = 0.0707 ln s + 1, applied to both sides of the dot product, so the
+    scores are multiplied by t = (0.0707 ln s + 1)^2 ([V2-explainer] §3.1.3)."""
+    f = 0.0707 * math.log(scale) + 1.0 if scale > 1.0 else 1.0
+    return f * f
+
+
 # ---------------------------------------------------------------------------
 # projections from the hidden state h
 # ---------------------------------------------------------------------------

@@ -450,3 +450,58 @@ def test_group_quantizer_properties():
         err = np.abs(deq[:, sl] - x)
         bound = np.maximum(np.abs(x) * 2.0 ** -4, scales[:, g:g + 1].astype(np.float64) * 2.0 ** -10) * (1 + 1e-6)
         assert np.all(err <= bound)
+
+
+# ---------------------------------------------------------------------------
+# YaRN-extended RoPE frequencies ([V2-explainer] §3.1.3: s = 40, alpha = 1,
+# beta = 32, original context 4K, target 160K)
+# ---------------------------------------------------------------------------
+
+def test_yarn_reduces_to_plain_rope_at_scale_one():
+    rng = np.random.default_rng(31)
+    x = rng.normal(size=(5, 64))
+    pos = rng.integers(0, 200000, size=5)
+    theta = oracle.yarn_theta(64, 10000.0, 1.0, 1.0, 32.0, 4096)
+    np.testing.assert_array_equal(theta, 10000.0 ** (-2.0 * np.arange(32) / 64))
+    np.testing.assert_allclose(oracle.rope_theta(x, pos, theta), oracle.rope(x, pos), rtol=0, atol=0)
+    assert oracle.yarn_attention_factor(1.0) == 1.0
+
+
+def test_yarn_slow_pairs_interpolate_fast_pairs_stay():
+    """Pairs turning fewer than alpha times over the original context are
+    interpolated by s (rotating position m*s equals the plain rotation at m);
+    pairs turning more than beta times keep their frequency; the pages' s = 40
+    over a 4K context reaches the stated 160K target."""
+    d, base, s, a, b, L = 64, 10000.0, 40.0, 1.0, 32.0, 4096
+    plain = base ** (-2.0 * np.arange(d // 2) / d)
+    theta = oracle.yarn_theta(d, base, s, a, b, L)
+    r = L * plain / (2 * math.pi)
+    slow, fast = r <= a, r >= b
+    assert slow.any() and fast.any() and (~slow & ~fast).any()
+    np.testing.assert_allclose(theta[slow], plain[slow] / s, rtol=1e-15)
+    np.testing.assert_array_equal(theta[fast], plain[fast])
+    mid = ~slow & ~fast
+    assert np.all(theta[mid] < plain[mid]) and np.all(theta[mid] > plain[mid] / s)
+    assert np.all(np.diff(theta) < 0)          # still strictly decreasing frequencies
+    rng = np.random.default_rng(32)
+    x = rng.normal(size=(d,))
+    m = 1234
+    got = oracle.rope_theta(x, m * s, theta)
+    ref = oracle.rope(x, m, base)
+    for k in np.nonzero(slow)[0]:
+        np.testing.assert_allclose(got[2 * k:2 * k + 2], ref[2 * k:2 * k + 2], rtol=1e-9, atol=1e-12)
+    assert s * L >= 160 * 1000
+
+
+def test_yarn_ramp_midpoint_and_attention_factor():
+    """A pair placed exactly half-way up the ramp (r = (alpha + beta) / 2) gets
+    the mean of the interpolated and plain frequencies; the attention factor
+    grows with s from 1 at s = 1."""
+    d, base, s, a, b = 64, 10000.0, 40.0, 1.0, 32.0
+    plain = base ** (-2.0 * np.arange(d // 2) / d)
+    k = 10
+    L = 2 * math.pi * ((a + b) / 2) / plain[k]        # r_k = 16.5 exactly
+    theta = oracle.yarn_theta(d, base, s, a, b, L)
+    np.testing.assert_allclose(theta[k], plain[k] * (1 + 1 / s) / 2, rtol=1e-13)
+    f = [oracle.yarn_attention_factor(v) for v in (1.0, 2.0, 40.0, 100.0)]
+    assert f[0] == 1.0 and all(u < w for u, w in zip(f, f[1:]))
