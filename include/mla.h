@@ -331,6 +331,50 @@ mla_status_t mla_query_prep(const mla_dims_t* dims, int32_t d_model, int32_t d_q
                             mla_dtype_t out_dt, void* scratch, size_t scratch_bytes, void* stream);
 
 /*
+ * RoPE frequencies for the cache and query writers, with YaRN context
+ * extension [DeepSeek-V2 explainer §3.1.3: YaRN on the decoupled key k^R, scale
+ * s = 40, alpha = 1, beta = 32, from a 4K to a 160K context].  Pair k of the
+ * d_rope-wide RoPE slice turns at theta_k = base^(-2k/d_rope) radians per
+ * position; with yarn_scale s > 1, with r_k = yarn_orig_ctx * theta_k / (2 pi)
+ * its turns over the original context and gamma_k = clip((r_k - yarn_alpha) /
+ * (yarn_beta - yarn_alpha), 0, 1), it turns at (1 - gamma_k) theta_k / s +
+ * gamma_k theta_k instead (the YaRN ramp: slow pairs interpolated, fast pairs
+ * kept).  Both the cached k^R (mla_cache_*_rope) and the query's q^R
+ * (mla_query_prep_rope) must use the same parameters.  The matching softmax
+ * scale is mla_yarn_attention_factor(s) / sqrt(d_h + d_rope).
+ *   base >= 0 (0: no rotation); yarn_scale >= 1 (1: plain RoPE, the other
+ *   fields ignored); when yarn_scale > 1: 0 <= yarn_alpha < yarn_beta,
+ *   yarn_orig_ctx >= 1.  Anything else: MLA_ERR_INVALID_ARG.
+ * mla_cache_store / mla_cache_append / mla_query_prep are these calls with
+ * {rope_base, 1, 0, 0, 0}.
+ */
+typedef struct {
+  float base;
+  float yarn_scale;
+  float yarn_alpha;
+  float yarn_beta;
+  int32_t yarn_orig_ctx;
+} mla_rope_t;
+
+mla_status_t mla_cache_store_rope(const mla_dims_t* dims, int32_t batch, const void* rows, mla_dtype_t rows_dt,
+                                  const int32_t* positions, const mla_rope_t* rope, const mla_paged_cache_t* cache,
+                                  void* stream);
+mla_status_t mla_cache_append_rope(const mla_dims_t* dims, int32_t d_model, int32_t batch, const void* h,
+                                   mla_dtype_t h_dt, const void* w_dkv, const void* w_kr, mla_dtype_t w_dt,
+                                   float* rows, const int32_t* positions, const mla_rope_t* rope,
+                                   const mla_paged_cache_t* cache, void* stream);
+mla_status_t mla_query_prep_rope(const mla_dims_t* dims, int32_t d_model, int32_t d_qlatent, int32_t batch,
+                                 const void* h, mla_dtype_t h_dt, const void* w_dq, const void* w_uq,
+                                 const void* w_qr, mla_dtype_t w_dt, const int32_t* positions,
+                                 const mla_rope_t* rope, void* q_nope, void* q_pe, mla_dtype_t out_dt, void* scratch,
+                                 size_t scratch_bytes, void* stream);
+
+/* YaRN's attention factor in MLA [DeepSeek-V2 explainer §3.1.3: the length
+ * factor sqrt(t) = 0.0707 ln s + 1 on each side of the dot product]: returns
+ * t = (0.0707 ln s + 1)^2, the multiplier of the softmax scale (1 for s <= 1). */
+float mla_yarn_attention_factor(float yarn_scale);
+
+/*
  * mla_decode followed by mla_merge_splits without a caller workspace, for
  * callers that cannot allocate device memory (code under HIP graph capture,
  * tight serving loops, harnesses that forbid hipMalloc).  The split partials

@@ -13,7 +13,7 @@ from . import _lib
 from ._lib import (MLA_BF16, MLA_F32, MLA_FP8_E4M3, MlaError, absorb_q, build_info, cache_append,  # noqa: F401
                    cache_store, decode, decode_multi, decode_noalloc, decode_multi_out_proj, dims, lse_part_offset, make_cache, merge_out_proj,
                    merge_splits, multi_workspace_size, out_proj, partition, partition_host, prefill, prefill_workspace_size,
-                   query_prep, query_prep_scratch_size,
+                   query_prep, query_prep_scratch_size, rope, yarn_attention_factor,
                    status_string, validate_cache_host, workspace_size)
 
 __all__ = ["DecodeStep", "DeviceCache", "upload_cache"]

@@ -22,7 +22,8 @@ EXPORTS = ("mla_status_string", "mla_build_info", "mla_absorb_q", "mla_decode_wo
            "mla_cache_append", "mla_query_prep_scratch_size", "mla_query_prep", "mla_partition_host",
            "mla_decode_multi_workspace_size", "mla_decode_multi", "mla_merge_out_proj",
            "mla_decode_multi_out_proj", "mla_validate_cache_host", "mla_decode_noalloc",
-           "mla_prefill_workspace_size", "mla_prefill")
+           "mla_prefill_workspace_size", "mla_prefill", "mla_cache_store_rope", "mla_cache_append_rope",
+           "mla_query_prep_rope", "mla_yarn_attention_factor")
 
 
 class MlaError(RuntimeError):
@@ -34,6 +35,12 @@ class MlaError(RuntimeError):
 class Dims(ctypes.Structure):
     _fields_ = [("n_heads", ctypes.c_int32), ("d_head", ctypes.c_int32),
                 ("d_rope", ctypes.c_int32), ("d_latent", ctypes.c_int32)]
+
+
+class Rope(ctypes.Structure):
+    """mla_rope_t: RoPE base and YaRN parameters (yarn_scale 1 = plain RoPE)."""
+    _fields_ = [("base", ctypes.c_float), ("yarn_scale", ctypes.c_float), ("yarn_alpha", ctypes.c_float),
+                ("yarn_beta", ctypes.c_float), ("yarn_orig_ctx", ctypes.c_int32)]
 
 
 class PagedCache(ctypes.Structure):
@@ -92,6 +99,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "mla_decode_multi_out_proj": (ctypes.c_int, [PD, I32, I32, P, P, ctypes.c_int, PC, ctypes.c_float, PP, P, SZ,
                                                      P, ctypes.c_int, P, P, ctypes.c_int, P, ctypes.c_int, P]),
         "mla_prefill_workspace_size": (ctypes.c_int, [PD, I32, ctypes.c_int64, ctypes.POINTER(SZ)]),
+        "mla_cache_store_rope": (ctypes.c_int, [PD, I32, P, ctypes.c_int, P, ctypes.POINTER(Rope), PC, P]),
+        "mla_cache_append_rope": (ctypes.c_int, [PD, I32, I32, P, ctypes.c_int, P, P, ctypes.c_int, P, P,
+                                                 ctypes.POINTER(Rope), PC, P]),
+        "mla_query_prep_rope": (ctypes.c_int, [PD, I32, I32, I32, P, ctypes.c_int, P, P, P, ctypes.c_int, P,
+                                               ctypes.POINTER(Rope), P, P, ctypes.c_int, P, SZ, P]),
+        "mla_yarn_attention_factor": (ctypes.c_float, [ctypes.c_float]),
         "mla_prefill": (ctypes.c_int, [PD, I32, P, I32, I32, P, P, ctypes.c_int, PC, ctypes.c_int64, P, P,
                                        ctypes.c_int, ctypes.c_float, P, SZ, P, ctypes.c_int, P, P]),
     }
@@ -283,16 +296,38 @@ def merge_out_proj(d: Dims, seq_lens, page_size: int, max_pages: int, part: Part
     return o_heads
 
 
-def cache_store(d: Dims, rows, positions, cache: PagedCache, rope_base: float = 0.0, stream=None):
-    """Write rows [B, d_c+d_rope] (f32/bf16) at token positions [B] (int32, device) into the cache."""
+def rope(base: float, yarn_scale: float = 1.0, yarn_alpha: float = 0.0, yarn_beta: float = 0.0,
+         yarn_orig_ctx: int = 0) -> Rope:
+    return Rope(base, yarn_scale, yarn_alpha, yarn_beta, yarn_orig_ctx)
+
+
+def yarn_attention_factor(yarn_scale: float) -> float:
+    return load().mla_yarn_attention_factor(ctypes.c_float(yarn_scale))
+
+
+def cache_store(d: Dims, rows, positions, cache: PagedCache, rope_base: float = 0.0, stream=None, rope=None):
+    """Write rows [B, d_c+d_rope] (f32/bf16) at token positions [B] (int32, device) into the cache.
+    rope: an mla_rope_t (Rope) instead of rope_base (YaRN frequencies)."""
+    if rope is not None:
+        _check(load().mla_cache_store_rope(ctypes.byref(d), rows.shape[0], _ptr(rows), dtype_code(rows),
+                                           _ptr(positions), ctypes.byref(rope), ctypes.byref(cache), _stream(stream)),
+               "mla_cache_store_rope")
+        return
     _check(load().mla_cache_store(ctypes.byref(d), rows.shape[0], _ptr(rows), dtype_code(rows), _ptr(positions),
                                   ctypes.c_float(rope_base), ctypes.byref(cache), _stream(stream)), "mla_cache_store")
 
 
-def cache_append(d: Dims, h, w_dkv, w_kr, rows, positions, cache: PagedCache, rope_base: float, stream=None):
+def cache_append(d: Dims, h, w_dkv, w_kr, rows, positions, cache: PagedCache, rope_base: float, stream=None,
+                 rope=None):
     """rows = [W^DKV h ; W^KR h], then cache_store(rows, positions, rope_base).
 
     rows: fp32 scratch [8, B, d_c+d_rope]; rows[0] holds the projected rows afterwards."""
+    if rope is not None:
+        _check(load().mla_cache_append_rope(ctypes.byref(d), h.shape[1], h.shape[0], _ptr(h), dtype_code(h),
+                                            _ptr(w_dkv), _ptr(w_kr), dtype_code(w_dkv), _ptr(rows), _ptr(positions),
+                                            ctypes.byref(rope), ctypes.byref(cache), _stream(stream)),
+               "mla_cache_append_rope")
+        return
     _check(load().mla_cache_append(ctypes.byref(d), h.shape[1], h.shape[0], _ptr(h), dtype_code(h), _ptr(w_dkv),
                                    _ptr(w_kr), dtype_code(w_dkv), _ptr(rows), _ptr(positions),
                                    ctypes.c_float(rope_base), ctypes.byref(cache), _stream(stream)), "mla_cache_append")
@@ -303,11 +338,17 @@ def query_prep_scratch_size(d: Dims, d_qlatent: int, batch: int) -> int:
 
 
 def query_prep(d: Dims, h, w_dq, w_uq, w_qr, positions, q_nope, q_pe, scratch, rope_base: float = 10000.0,
-               stream=None):
+               stream=None, rope=None):
     """c^Q = W^DQ h, q_nope = W^UQ c^Q, q_pe = RoPE(W^QR c^Q) per head; shapes [B, d], [d_q, d],
     [n_h d_h, d_q], [n_h d_r, d_q], positions [B] int32, outputs [B, n_h, d_h], [B, n_h, d_r]."""
     nbytes = scratch.numel() * scratch.element_size()
     d_qlatent = 0 if w_dq is None else w_dq.shape[0]   # 0: query not compressed (w_uq, w_qr act on h)
+    if rope is not None:
+        _check(load().mla_query_prep_rope(ctypes.byref(d), h.shape[1], d_qlatent, h.shape[0], _ptr(h), dtype_code(h),
+                                          _ptr(w_dq), _ptr(w_uq), _ptr(w_qr), dtype_code(w_uq), _ptr(positions),
+                                          ctypes.byref(rope), _ptr(q_nope), _ptr(q_pe), dtype_code(q_nope),
+                                          _ptr(scratch), nbytes, _stream(stream)), "mla_query_prep_rope")
+        return q_nope, q_pe
     _check(load().mla_query_prep(ctypes.byref(d), h.shape[1], d_qlatent, h.shape[0], _ptr(h), dtype_code(h),
                                  _ptr(w_dq), _ptr(w_uq), _ptr(w_qr), dtype_code(w_uq), _ptr(positions),
                                  ctypes.c_float(rope_base), _ptr(q_nope), _ptr(q_pe), dtype_code(q_nope),

@@ -3,6 +3,7 @@
 // memory; every check runs before the first launch.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdint>
 #include <cstring>
 
@@ -113,13 +114,30 @@ WsLayout ws_layout(const mla_dims_t* d, int n_slots, int batch, bool balanced, s
   return L;
 }
 
+// RoPE parameters of an mla_rope_t (NULL: invalid) or a plain base
+mla_status_t rope_params(const mla_rope_t* r, RopeParams* out) {
+  if (r == nullptr) return MLA_ERR_INVALID_ARG;
+  if (!(r->base >= 0.f) || !(r->base < 1e30f)) return MLA_ERR_INVALID_ARG;
+  if (!(r->yarn_scale >= 1.f) || !(r->yarn_scale < 1e30f)) return MLA_ERR_INVALID_ARG;
+  RopeParams p{r->base, 1.f, 0.f, 0.f, 0.f};
+  if (r->yarn_scale > 1.f) {
+    if (!(r->yarn_beta > r->yarn_alpha) || !(r->yarn_alpha >= 0.f) || !(r->yarn_beta < 1e30f) ||
+        r->yarn_orig_ctx < 1)
+      return MLA_ERR_INVALID_ARG;
+    p = RopeParams{r->base, r->yarn_scale, r->yarn_alpha, r->yarn_beta, float(r->yarn_orig_ctx)};
+  }
+  *out = p;
+  return MLA_OK;
+}
+
 // checks shared by the cache-store entry points; fills the store arguments
 mla_status_t store_args(const mla_dims_t* dims, int32_t batch, const void* rows, mla_dtype_t rows_dt,
-                        const int32_t* positions, float rope_base, const mla_paged_cache_t* cache,
+                        const int32_t* positions, const mla_rope_t* rope, const mla_paged_cache_t* cache,
                         CacheStoreArgs* a) {
   if (mla_status_t s = check_dims(dims)) return s;
   if (batch < 0 || cache == nullptr) return MLA_ERR_INVALID_ARG;
-  if (!(rope_base >= 0.f)) return MLA_ERR_INVALID_ARG;
+  RopeParams rp;
+  if (mla_status_t s = rope_params(rope, &rp)) return s;
   if (rows_dt != MLA_F32 && rows_dt != MLA_BF16) return valid_dtype(rows_dt) ? MLA_ERR_UNSUPPORTED : MLA_ERR_INVALID_ARG;
   if (!valid_dtype(cache->dtype)) return MLA_ERR_INVALID_ARG;
   const int W = dims->d_latent + dims->d_rope;
@@ -133,7 +151,7 @@ mla_status_t store_args(const mla_dims_t* dims, int32_t batch, const void* rows,
   a->rows = rows;
   a->rows_dt = rows_dt;
   a->positions = positions;
-  a->rope_base = rope_base;
+  a->rope = rp;
   a->kv = const_cast<void*>(cache->kv);
   a->scales = const_cast<float*>(cache->scales);
   a->kv_dt = cache->dtype;
@@ -592,8 +610,15 @@ mla_status_t mla_merge_out_proj(const mla_dims_t* dims, int32_t batch, const int
 mla_status_t mla_cache_store(const mla_dims_t* dims, int32_t batch, const void* rows, mla_dtype_t rows_dt,
                              const int32_t* positions, float rope_base, const mla_paged_cache_t* cache,
                              void* stream) {
+  const mla_rope_t r{rope_base, 1.f, 0.f, 0.f, 0};
+  return mla_cache_store_rope(dims, batch, rows, rows_dt, positions, &r, cache, stream);
+}
+
+mla_status_t mla_cache_store_rope(const mla_dims_t* dims, int32_t batch, const void* rows, mla_dtype_t rows_dt,
+                                  const int32_t* positions, const mla_rope_t* rope, const mla_paged_cache_t* cache,
+                                  void* stream) {
   CacheStoreArgs a{};
-  if (mla_status_t s = store_args(dims, batch, rows, rows_dt, positions, rope_base, cache, &a)) return s;
+  if (mla_status_t s = store_args(dims, batch, rows, rows_dt, positions, rope, cache, &a)) return s;
   if (batch == 0) return MLA_OK;
   a.batch = batch;
   a.n_partials = 1;
@@ -605,8 +630,16 @@ mla_status_t mla_cache_append(const mla_dims_t* dims, int32_t d_model, int32_t b
                               mla_dtype_t h_dt, const void* w_dkv, const void* w_kr, mla_dtype_t w_dt, float* rows,
                               const int32_t* positions, float rope_base, const mla_paged_cache_t* cache,
                               void* stream) {
+  const mla_rope_t r{rope_base, 1.f, 0.f, 0.f, 0};
+  return mla_cache_append_rope(dims, d_model, batch, h, h_dt, w_dkv, w_kr, w_dt, rows, positions, &r, cache, stream);
+}
+
+mla_status_t mla_cache_append_rope(const mla_dims_t* dims, int32_t d_model, int32_t batch, const void* h,
+                                   mla_dtype_t h_dt, const void* w_dkv, const void* w_kr, mla_dtype_t w_dt,
+                                   float* rows, const int32_t* positions, const mla_rope_t* rope,
+                                   const mla_paged_cache_t* cache, void* stream) {
   CacheStoreArgs a{};
-  if (mla_status_t s = store_args(dims, batch, rows, MLA_F32, positions, rope_base, cache, &a)) return s;
+  if (mla_status_t s = store_args(dims, batch, rows, MLA_F32, positions, rope, cache, &a)) return s;
   if (d_model < 1) return MLA_ERR_INVALID_ARG;
   if ((h_dt != MLA_F32 && h_dt != MLA_BF16) || (w_dt != MLA_F32 && w_dt != MLA_BF16))
     return valid_dtype(h_dt) && valid_dtype(w_dt) ? MLA_ERR_UNSUPPORTED : MLA_ERR_INVALID_ARG;
@@ -642,8 +675,26 @@ mla_status_t mla_query_prep(const mla_dims_t* dims, int32_t d_model, int32_t d_q
                             const void* h, mla_dtype_t h_dt, const void* w_dq, const void* w_uq, const void* w_qr,
                             mla_dtype_t w_dt, const int32_t* positions, float rope_base, void* q_nope, void* q_pe,
                             mla_dtype_t out_dt, void* scratch, size_t scratch_bytes, void* stream) {
+  const mla_rope_t r{rope_base, 1.f, 0.f, 0.f, 0};
+  return mla_query_prep_rope(dims, d_model, d_qlatent, batch, h, h_dt, w_dq, w_uq, w_qr, w_dt, positions, &r, q_nope,
+                             q_pe, out_dt, scratch, scratch_bytes, stream);
+}
+
+float mla_yarn_attention_factor(float yarn_scale) {
+  if (!(yarn_scale > 1.f)) return 1.f;
+  const double f = 0.0707 * std::log(double(yarn_scale)) + 1.0;
+  return float(f * f);
+}
+
+mla_status_t mla_query_prep_rope(const mla_dims_t* dims, int32_t d_model, int32_t d_qlatent, int32_t batch,
+                                 const void* h, mla_dtype_t h_dt, const void* w_dq, const void* w_uq,
+                                 const void* w_qr, mla_dtype_t w_dt, const int32_t* positions,
+                                 const mla_rope_t* rope, void* q_nope, void* q_pe, mla_dtype_t out_dt, void* scratch,
+                                 size_t scratch_bytes, void* stream) {
   if (mla_status_t s = check_dims(dims)) return s;
-  if (batch < 0 || d_model < 1 || d_qlatent < 0 || !(rope_base >= 0.f)) return MLA_ERR_INVALID_ARG;
+  RopeParams rp;
+  if (mla_status_t s = rope_params(rope, &rp)) return s;
+  if (batch < 0 || d_model < 1 || d_qlatent < 0) return MLA_ERR_INVALID_ARG;
   const bool compressed = d_qlatent > 0;
   for (mla_dtype_t t : {h_dt, w_dt, out_dt})
     if (t != MLA_F32 && t != MLA_BF16) return valid_dtype(t) ? MLA_ERR_UNSUPPORTED : MLA_ERR_INVALID_ARG;
@@ -699,7 +750,7 @@ mla_status_t mla_query_prep(const mla_dims_t* dims, int32_t d_model, int32_t d_q
   f.d_head = dims->d_head;
   f.d_rope = dims->d_rope;
   f.positions = positions;
-  f.rope_base = rope_base;
+  f.rope = rp;
   f.q_nope = q_nope;
   f.q_pe = q_pe;
   f.out_dt = out_dt;

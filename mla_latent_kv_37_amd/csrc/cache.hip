@@ -59,9 +59,9 @@ __global__ __launch_bounds__(640) void cache_store_kernel(CacheStoreArgs a) {
       r0[0] = x0;
       r0[1] = x1;
     }
-    if (store && a.rope_base > 0.f && c0 >= a.d_latent) {
+    if (store && a.rope.base > 0.f && c0 >= a.d_latent) {
       const int k = (c0 - a.d_latent) >> 1;
-      const double theta = pow(double(a.rope_base), -2.0 * k / double(a.d_rope));
+      const double theta = rope_theta(k, a.d_rope, a.rope);
       const double ang = double(pos) * theta;
       const double c = cos(ang), s = sin(ang);
       const double y0 = double(x0) * c - double(x1) * s, y1 = double(x0) * s + double(x1) * c;

@@ -68,7 +68,7 @@ struct CacheStoreArgs {
   const void* rows;        // [B, d_c + d_rope]
   mla_dtype_t rows_dt;
   const int32_t* positions;
-  float rope_base;
+  RopeParams rope;
   void* kv;
   float* scales;
   mla_dtype_t kv_dt;
@@ -102,7 +102,7 @@ struct QueryFinishArgs {
   const float* slices;     // [n_slices, batch, n_h * (d_h + d_rope)] fp32
   int n_slices, batch, n_heads, d_head, d_rope;
   const int32_t* positions;
-  float rope_base;
+  RopeParams rope;
   void* q_nope;            // [batch, n_h, d_h]
   void* q_pe;              // [batch, n_h, d_rope]
   mla_dtype_t out_dt;

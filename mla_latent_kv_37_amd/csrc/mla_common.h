@@ -81,6 +81,27 @@ struct PartParams {
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// RoPE frequencies (mla_rope_t in mla.h): pair k of a d-wide RoPE slice turns
+// at theta_k = base^(-2k/d) per position; with YaRN (scale s > 1) the pairs
+// that turn fewer than alpha times over the original context are slowed by s,
+// those turning more than beta times are kept, with a linear ramp in the
+// number of turns between (the YaRN context extension the V2 explainer §3.1.3
+// applies to the RoPE-carrying key).  fp64, as the angle that uses it.
+struct RopeParams {
+  float base;       // 0: no rotation
+  float yarn_scale; // <= 1: plain RoPE
+  float yarn_alpha, yarn_beta;
+  float yarn_orig_ctx;
+};
+__device__ __forceinline__ double rope_theta(int k, int d, const RopeParams& r) {
+  const double theta = pow(double(r.base), -2.0 * k / double(d));
+  if (!(r.yarn_scale > 1.f)) return theta;
+  const double turns = double(r.yarn_orig_ctx) * theta / (2.0 * 3.141592653589793);
+  double g = (turns - double(r.yarn_alpha)) / (double(r.yarn_beta) - double(r.yarn_alpha));
+  g = g < 0.0 ? 0.0 : (g > 1.0 ? 1.0 : g);
+  return (1.0 - g) * theta / double(r.yarn_scale) + g * theta;
+}
+
 // A sequence length as the kernels use it: clamped to [0, max_pages * page_size],
 // so that no kernel reads past the sequence's block-table row whatever seq_lens
 // holds (lengths outside that range are invalid input; mla_validate_cache_host

@@ -40,9 +40,9 @@ __global__ __launch_bounds__(256) void query_finish_kernel(QueryFinishArgs a) {
     return;
   }
   const int r = c - nc, j = r % a.d_rope;                   // j even: pair j/2 of a head
-  if (a.rope_base > 0.f) {
+  if (a.rope.base > 0.f) {
     const int pos = load_const(a.positions, b);
-    const double theta = pow(double(a.rope_base), -double(j) / double(a.d_rope));
+    const double theta = rope_theta(j >> 1, a.d_rope, a.rope);
     const double ang = double(pos) * theta;
     const double cs = cos(ang), sn = sin(ang);
     const double y0 = double(x0) * cs - double(x1) * sn, y1 = double(x0) * sn + double(x1) * cs;

@@ -387,3 +387,28 @@ def test_noalloc_rejects_before_touching_the_device(lib):
     st = l.mla_decode_noalloc(ctypes.byref(d), 64, fake, fake, lib.MLA_BF16, ctypes.byref(cache),
                               ctypes.c_float(0.07), ctypes.byref(big), fake, lib.MLA_FP8_E4M3, None, None)
     assert st == lib.MLA_ERR_UNSUPPORTED
+
+
+def test_rope_parameters_validation_and_yarn_factor(lib):
+    """mla_rope_t is checked before anything is enqueued; the YaRN attention
+    factor matches the oracle's (the page's length factor, squared)."""
+    import oracle
+    L = _raw(lib)
+    d = _v2(lib)
+    fake = ctypes.c_void_p(0x10000)
+    cache = lib.PagedCache(0x10000, None, lib.MLA_BF16, 64, 100, 0x20000, 16, 0x30000)
+    cs = L.mla_cache_store_rope
+    ok = lib.rope(10000.0, 40.0, 1.0, 32.0, 4096)
+    assert cs(ctypes.byref(d), 0, fake, lib.MLA_F32, fake, ctypes.byref(ok), ctypes.byref(cache), None) == lib.MLA_OK
+    for bad in (lib.rope(-1.0), lib.rope(1e4, 0.5), lib.rope(1e4, 40.0, 32.0, 1.0, 4096),
+                lib.rope(1e4, 40.0, 1.0, 32.0, 0), lib.rope(float("nan")), lib.rope(1e4, float("inf"), 1.0, 32.0, 4096)):
+        assert cs(ctypes.byref(d), 1, fake, lib.MLA_F32, fake, ctypes.byref(bad), ctypes.byref(cache),
+                  None) == lib.MLA_ERR_INVALID_ARG
+    assert cs(ctypes.byref(d), 1, fake, lib.MLA_F32, fake, None, ctypes.byref(cache), None) == lib.MLA_ERR_INVALID_ARG
+    qp = L.mla_query_prep_rope
+    need = L.mla_query_prep_scratch_size(ctypes.byref(d), 1536, 4)
+    bad = lib.rope(1e4, 40.0, 5.0, 5.0, 4096)
+    assert qp(ctypes.byref(d), 5120, 1536, 4, fake, 1, fake, fake, fake, 1, fake, ctypes.byref(bad), fake, fake, 1,
+              fake, need, None) == lib.MLA_ERR_INVALID_ARG
+    for s in (1.0, 2.0, 40.0, 100.0):
+        assert abs(lib.yarn_attention_factor(s) - oracle.yarn_attention_factor(s)) <= 1e-6

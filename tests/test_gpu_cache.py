@@ -278,3 +278,34 @@ def test_cache_append_tiny_f32():
     for b in range(batch):
         full = np.concatenate([c_kv[b], k_r[b]])
         assert np.abs(got[b] - full).max() <= 1e-5 * np.abs(full).max()
+
+
+@pytest.mark.parametrize("kind", ["bf16", "fp8"])
+def test_cache_store_yarn(kind):
+    """k^R rotated with the YaRN frequencies of [V2-explainer] §3.1.3 (s = 40,
+    alpha = 1, beta = 32, original context 4096) through mla_cache_store_rope,
+    at positions up to 160K; the latent part is stored as without RoPE."""
+    import torch
+    import mla_latent_kv_37_amd as mk
+    d, width, dc = mk.dims(128, 128, 64, 512), 576, 512
+    rng = np.random.default_rng(22)
+    batch, max_pages = 16, 2560
+    num_pages = batch + 4
+    pos = np.concatenate([[0, 1, 4095, 4096, max_pages * PAGE - 1], rng.integers(0, max_pages * PAGE, batch - 5)])
+    pos = pos.astype(np.int32)
+    print(f"case: cache store with YaRN RoPE, {kind}, positions up to {max_pages * PAGE - 1}", flush=True)
+    perm = _targets(rng, pos, max_pages, num_pages)
+    rows32 = (rng.normal(size=(batch, width)) * 0.4).astype(np.float32)
+    kv, scales, bt, cache = _device_cache(kind, num_pages, width, perm)
+    mk.cache_store(d, torch.from_numpy(rows32).cuda(), torch.from_numpy(pos).cuda(), cache,
+                   rope=mk.rope(10000.0, 40.0, 1.0, 32.0, 4096))
+    torch.cuda.synchronize()
+    got = _stored_values(kind, kv, scales, perm, pos, num_pages, width)
+    theta = oracle.yarn_theta(64, 10000.0, 40.0, 1.0, 32.0, 4096)
+    differs = 0
+    for b in range(batch):
+        ref = np.concatenate([rows32[b, :dc].astype(np.float64), oracle.rope_theta(rows32[b, dc:], pos[b], theta)])
+        _check_rope_part(kind, got[b], ref, dc)
+        plain = oracle.rope(rows32[b, dc:], pos[b])
+        differs += np.abs(plain - ref[dc:]).max() > 0.1 * np.abs(ref[dc:]).max()
+    assert differs >= batch // 2   # (the YaRN frequencies are what the check sees)

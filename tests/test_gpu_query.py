@@ -35,7 +35,7 @@ def _round(x, kind):
     return ostore.bf16_bits_to_f64(ostore.f32_to_bf16_bits(x.astype(np.float32)))
 
 
-def _run(dims, batch, h_kind, w_kind, out_kind, seed, rope_base=10000.0, max_pos=None, sigma=None):
+def _run(dims, batch, h_kind, w_kind, out_kind, seed, rope_base=10000.0, max_pos=None, sigma=None, yarn=None):
     import torch
     import synth
     import mla_latent_kv_37_amd as mk
@@ -55,8 +55,9 @@ def _run(dims, batch, h_kind, w_kind, out_kind, seed, rope_base=10000.0, max_pos
     q_pe = torch.empty((batch, dims.n_heads, dims.d_rope), dtype=tdt[out_kind], device="cuda")
     print(f"case: query prep B={batch} d={dims.d_model} h {h_kind} w {w_kind} out {out_kind} "
           f"base {rope_base} scratch {nbytes}", flush=True)
+    rope = None if yarn is None else mk.rope(rope_base, *yarn)
     mk.query_prep(d, dev(h, h_kind), dev(W["W_DQ"], w_kind), dev(W["W_UQ"], w_kind), dev(W["W_QR"], w_kind),
-                  torch.from_numpy(pos).cuda(), q_nope, q_pe, scratch, rope_base)
+                  torch.from_numpy(pos).cuda(), q_nope, q_pe, scratch, rope_base, rope=rope)
     torch.cuda.synchronize()
     got_c = q_nope.float().cpu().numpy().astype(np.float64)
     got_r = q_pe.float().cpu().numpy().astype(np.float64)
@@ -67,6 +68,9 @@ def _run(dims, batch, h_kind, w_kind, out_kind, seed, rope_base=10000.0, max_pos
         ref_c[b] = qc
         # rope_base 0 means the device leaves q^R unrotated: position 0 in the oracle
         ref_r[b] = qr if rope_base > 0 else oracle.project_query(h[b], W, 0, dims.n_heads)[1]
+        if yarn is not None:
+            theta = oracle.yarn_theta(dims.d_rope, rope_base, *yarn)
+            ref_r[b] = oracle.rope_theta(oracle.project_query(h[b], W, 0, dims.n_heads)[1], int(pos[b]), theta)
     return got_c, got_r, ref_c, ref_r
 
 
@@ -205,3 +209,19 @@ def test_query_prep_tiny_uncompressed_f32():
     import synth
     got_c, got_r, ref_c, ref_r = _run_uncompressed(synth.TINY, 7, "f32", 11, 0.05)
     assert _rel(got_c, ref_c) <= TOL["f32"] and _rel(got_r, ref_r) <= TOL["f32"]
+
+
+YARN_V2 = (40.0, 1.0, 32.0, 4096)   # s, alpha, beta, original context ([V2-explainer] §3.1.3)
+
+
+def test_query_prep_yarn():
+    """q^R rotated with the YaRN frequencies (mla_query_prep_rope) at positions
+    up to 160K; the plain-RoPE reference differs there, so the check sees the
+    frequencies."""
+    import synth
+    got_c, got_r, ref_c, ref_r = _run(synth.V2, 24, "bf16", "bf16", "f32", seed=61, max_pos=163840, yarn=YARN_V2)
+    ec, er = _rel(got_c, ref_c), _rel(got_r, ref_r)
+    print(f"q^C rel err {ec:.3e}  q^R rel err {er:.3e}", flush=True)
+    assert ec <= TOL["bf16"] and er <= TOL["bf16"]
+    _, plain_r, _, _ = _run(synth.V2, 24, "bf16", "bf16", "f32", seed=61, max_pos=163840)
+    assert _rel(plain_r, ref_r) > 0.1
