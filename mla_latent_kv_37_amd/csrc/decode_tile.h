@@ -22,7 +22,6 @@ constexpr int kRowBytes = kV2Row * 2;                 // 1152
 constexpr int kPageBytes = kV2Page * kRowBytes;       // 73728
 constexpr int kTileTok = 32;
 constexpr int kTileBytes = kTileTok * kRowBytes;      // 36864
-constexpr int kQpeBytes = kV2Heads * kV2Rope * 2;     // RoPE part of the query, 16 KB
 constexpr uint32_t kBufferFlags = 0x00020000u;        // raw buffer, 32-bit data format
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -122,29 +121,6 @@ __device__ __forceinline__ void issue_query_pass(const uint16_t* src, uint32_t s
                  : : "s"(m0), "v"(voff), "s"(rsrc) : "memory", "m0");
   }
 }
-
-// The RoPE query of all 128 heads (16 KB) into its LDS area (head hd, chunk c at
-// hd*128 + ((c ^ (hd & 7)) * 16)): one-KB blocks 2w and 2w+1 by wavefront w.
-__device__ __forceinline__ void issue_query_pe(const uint16_t* src, uint32_t qpe, int wave) {
-  int ln = threadIdx.x & 63;
-  asm volatile("" : "+v"(ln));
-  const uint64_t base = reinterpret_cast<uint64_t>(src);
-  i32x4 rsrc;
-  rsrc[0] = uniform(int(uint32_t(base)));
-  rsrc[1] = uniform(int(uint32_t(base >> 32) & 0xFFFFu));
-  rsrc[2] = kQpeBytes;
-  rsrc[3] = int(kBufferFlags);
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int i = 2 * wave + j;
-    const int hd = 8 * i + (ln >> 3), c = (ln & 7) ^ (hd & 7);
-    const int voff = hd * (kV2Rope * 2) + c * 16;
-    const int m0 = uniform(int(qpe + uint32_t(i * 1024)));
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 : : "s"(m0), "v"(voff), "s"(rsrc) : "memory", "m0");
-  }
-}
-
 
 // ---------------------------------------------------------------------------
 // fp8 cache (OCP E4M3 codes, one fp32 scale per token per 128-channel group;

@@ -9,9 +9,9 @@
 //   O^T [512 x 32 heads]     += V^T [512 x 32] . P^T [32 x 32]    (32 MFMAs)
 // on v_mfma_f32_32x32x16_bf16, with nothing exchanged between wavefronts but
 // the tiles.  Alone on its SIMD, a wavefront has the whole 512-entry register
-// file: the 256 accumulator registers hold O^T, the VGPRs the latent query
-// (128), the scores and the fragment reads issued several MFMAs ahead of their
-// use.  Those reads are what hides the LDS latency: no second wavefront shares
+// file: the 256 accumulator registers hold O^T, the VGPRs the query of its
+// heads (128 latent + 16 RoPE), the scores and the fragment reads issued
+// several MFMAs ahead of their use.  Those reads are what hides the LDS latency: no second wavefront shares
 // the SIMD to switch to.
 //
 // Software pipeline of tile k (per wavefront):
@@ -22,8 +22,10 @@
 //            row block of tile k+3 between them
 //   wait for this wavefront's loads of tile k+2, barrier (tile k+2 complete;
 //     every wavefront is done with tile k, whose buffer takes tile k+4)
-// Four tile buffers (144 KB) and the RoPE query of all heads (16 KB) fill the
-// 160 KB of LDS.
+// Four tile buffers take 144 KB of the 160 KB of LDS.  (The RoPE query is held
+// in registers rather than read from LDS every tile: 4 KB less LDS reading per
+// wavefront and tile, the latent score steps' K reads being what the loop
+// waits for.)
 //
 // Softmax without rescaling.  The accumulators are written by MFMAs only:
 // multiplying them by a rescale factor anywhere in the segment loop makes the
@@ -52,10 +54,10 @@ constexpr int kStageBytes = kWideWaves * 32768;   // epilogue staging (bf16 outp
 constexpr int kFlagOffset = kStageBytes;          // redo flags, past the staging area
 // fp8 cache: three bf16 tile buffers (tiles k, k+1 and k+2, which is written
 // by the dequantisation during tile k's PV phase) and two staging buffers of
-// codes and scales; the RoPE query is held in registers instead of LDS
+// codes and scales
 constexpr int kWideF8Bufs = 3;
 constexpr int kWideF8Area = kWideF8Bufs * kTileBytes + 2 * kF8StageBytes;
-static_assert(kWideBufs * kTileBytes + kQpeBytes <= 160 * 1024, "LDS budget");
+static_assert(kWideBufs * kTileBytes <= 160 * 1024, "LDS budget");
 static_assert(kWideF8Area <= 160 * 1024, "LDS budget (fp8)");
 static_assert(kFlagOffset + 16 <= kWideBufs * kTileBytes && kFlagOffset + 16 <= kWideF8Area,
               "flags inside the tile area");
@@ -133,14 +135,12 @@ __global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(1,
 void decode_wide_kernel(V2DecodeArgs a) {
   constexpr int kTileArea = kF8 ? kWideF8Area : kWideBufs * kTileBytes;
   __shared__ __attribute__((aligned(2048))) char tiles_raw[kTileArea];
-  __shared__ __attribute__((aligned(1024))) char qpe_raw[kF8 ? 16 : kQpeBytes];
   // XCD-aware item order: block x runs on XCD x % 8
   const int n_items = a.n_items;
   const int item = (n_items & 7) == 0 ? int(blockIdx.x & 7) * (n_items >> 3) + int(blockIdx.x >> 3) : int(blockIdx.x);
   if (item >= n_items) return;
   const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63, h = lane >> 5;
   const uint32_t tiles_lds = uint32_t(reinterpret_cast<uintptr_t>(tiles_raw));
-  const uint32_t qpe_lds = uint32_t(reinterpret_cast<uintptr_t>(qpe_raw));
   // per-lane LDS bases are recomputed where they are used from an opaque copy
   // of the lane id, so that they hold no registers across the tile loop
   auto opaque_lane = [&]() { int ln = lane; asm volatile("" : "+v"(ln)); return ln; };
@@ -199,9 +199,8 @@ void decode_wide_kernel(V2DecodeArgs a) {
     // Query: this wavefront's 32 heads x 512 latent dims in four 128-dim passes
     // through a 16 KB staging area per wavefront (bf16: tile buffers 2-3, free
     // until tile 2 is issued; fp8: tile buffers 1-2, free until tile 1 is
-    // dequantised), two passes at a time; the RoPE query of all heads into its
-    // own area (blocks 2w, 2w+1, 2w+8, 2w+9 by wavefront w), or for fp8 this
-    // wavefront's heads into registers.
+    // dequantised), two passes at a time; the RoPE query of its heads straight
+    // into registers.
     const uint32_t qstage = tiles_lds + uint32_t((kF8 ? 1 : 2) * kTileBytes + wave * 16384);
     const uint16_t* const qsrc = a.q_lat + (int64_t(b) * kV2Heads + wave * 32) * kV2Lat;
     const uint16_t* const qpe_src = a.q_pe + int64_t(b) * kV2Heads * kV2Rope;
@@ -219,26 +218,26 @@ void decode_wide_kernel(V2DecodeArgs a) {
           qf[8 * (pass0 + p) + t] = lds_read_b128(qstage + uint32_t(p * 8192 + r * 256 + ((c ^ (r & 15)) * 16)));
         }
     };
-    // fp8: RoPE query slices of head 32w + (lane&31) (MFMA B operand of the last
+    // RoPE query slices of head 32w + (lane&31) (MFMA B operand of the last
     // four k-steps: dims 8(2j + (lane>>5)) .. +8)
     bf16x8 qpe_r[4];
     issue_query_pass(qsrc, qstage);
     issue_query_pass(qsrc + 128, qstage + 8192);
-    if constexpr (kF8) {
+    {
       const int ln = opaque_lane();
       const uint16_t* const qp = qpe_src + (wave * 32 + (ln & 31)) * kV2Rope + 8 * (ln >> 5);
 #pragma unroll
       for (int j = 0; j < 4; ++j) qpe_r[j] = *reinterpret_cast<const bf16x8*>(qp + 16 * j);
+    }
+    if constexpr (kF8) {
       issue_f8(0, page0);
       if (ntiles > 1) issue_f8(1, page0);
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     } else {
-      issue_query_pe(qpe_src, qpe_lds, wave);
-      issue_query_pe(qpe_src, qpe_lds, wave + 4);
       load_tile(0, page0);
       if (ntiles > 1) {
         load_tile(1, page0);
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(18));   // query passes 0-1 and RoPE query
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(18));   // query passes 0-1 and the RoPE query
       } else {
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(9));
       }
@@ -252,7 +251,7 @@ void decode_wide_kernel(V2DecodeArgs a) {
     // an explicit wait tells the compiler that the query registers are ready,
     // so that it puts no waits for them inside the tile loop
     __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
-    raw_barrier();   // tiles 0-1 and the RoPE query complete; staging areas free
+    raw_barrier();   // tiles 0-1 complete; staging areas free
     if constexpr (kF8) {
       // tiles 0-1 dequantised by all threads; then staging buffer 0 takes tile 2
       {
@@ -279,8 +278,8 @@ void decode_wide_kernel(V2DecodeArgs a) {
       if (ntiles > 2) load_tile(2, page1);
     }
 
-    // ---- score MFMAs of tile kt into sn, k-steps in order; the K fragments
-    // (and for the RoPE steps the query fragments) are read kKAhead steps ahead.
+    // ---- score MFMAs of tile kt into sn, k-steps in order; the K fragments are
+    // read kKAhead steps ahead.
     // `between(st)` runs after the MFMA of step st (VALU work of the previous
     // tile) and may issue reads for the phase that follows.
     auto score_phase = [&](int kt, f32x16& sn, auto&& between) {
@@ -288,13 +287,10 @@ void decode_wide_kernel(V2DecodeArgs a) {
       const int ln = opaque_lane();
       const int kb0 = kb0_of(ln);
       const uint32_t kl = tb + uint32_t(kb0), krp = tb + uint32_t(32768 + kb0);
-      const int hq = wave * 32 + (ln & 31);
-      const uint32_t qpl = qpe_lds + uint32_t(hq * 128);
       auto kaddr = [&](int st) -> uint32_t {
         return st < 32 ? (kl ^ uint32_t(32 * (st & 3))) + uint32_t((st >> 2) * 4096) : krp ^ uint32_t(32 * (st - 32));
       };
-      auto qaddr = [&](int j) -> uint32_t { return qpl + uint32_t(((2 * j + (ln >> 5)) ^ (hq & 7)) * 16); };
-      bf16x8 kr[kKAhead], qr[4];
+      bf16x8 kr[kKAhead];
 #pragma unroll
       for (int i = 0; i < kKAhead; ++i) kr[i] = lds_read_b128(kaddr(i));
 #pragma unroll
@@ -303,9 +299,8 @@ void decode_wide_kernel(V2DecodeArgs a) {
         const int nx = st + kKAhead;
         if (nx < kScoreSteps) {
           kr[st % kKAhead] = lds_read_b128(kaddr(nx));
-          if (!kF8 && nx >= 32) qr[nx - 32] = lds_read_b128(qaddr(nx - 32));
         }
-        score_mfma(sn, kc, st < 32 ? qf[st] : kF8 ? qpe_r[st - 32] : qr[st - 32], st == 0);
+        score_mfma(sn, kc, st < 32 ? qf[st] : qpe_r[st - 32], st == 0);
         between(st);
         __builtin_amdgcn_sched_barrier(0);   // keep each step's order
       }
