@@ -167,9 +167,10 @@ mla_status_t store_args(const mla_dims_t* dims, int32_t batch, const void* rows,
 // mla_query_prep scratch: stage-1 k slices (at most kQueryMaxSlices: d_model is
 // not an argument of the size query), c^Q (in the weights' dtype; its area is
 // sized for fp32), stage-2 k slices (as many as the bf16 plan for
-// [n_h (d_h + d_rope)] x d_qlatent uses; every other plan uses one).  One size
+// [n_h (d_h + d_rope)] x d_qlatent uses; every other plan uses one), and the
+// query epilogue's RoPE table (batch x d_rope/2 pairs of doubles).  One size
 // serves every dtype.
-struct QueryScratch { size_t s1, cq, s2, total; };
+struct QueryScratch { size_t s1, cq, s2, tab, total; };
 // d_qlatent = 0 (no query compression): no stage 1, and the single product's
 // k slices are sized for the largest plan (d_model is not an argument either).
 QueryScratch query_scratch(const mla_dims_t* d, int32_t d_qlatent, int32_t batch) {
@@ -180,7 +181,8 @@ QueryScratch query_scratch(const mla_dims_t* d, int32_t d_qlatent, int32_t batch
   q.cq = align256(kQueryMaxSlices * B * d_qlatent * sizeof(float));
   q.s2 = q.cq + align256(B * d_qlatent * sizeof(float));
   const size_t slices2 = d_qlatent > 0 ? size_t(gemm_ws_slices(n2, d_qlatent, int(B), kQueryMaxSlices)) : kQueryMaxSlices;
-  q.total = q.s2 + align256(slices2 * B * n2 * sizeof(float));
+  q.tab = q.s2 + align256(slices2 * B * n2 * sizeof(float));
+  q.total = q.tab + align256(B * size_t(d->d_rope / 2) * 2 * sizeof(double));
   return q;
 }
 
@@ -710,6 +712,35 @@ mla_status_t mla_query_prep_rope(const mla_dims_t* dims, int32_t d_model, int32_
   char* ws = static_cast<char*>(scratch);
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
+  // stage 2's plan first: with one k slice (the V2 shapes) its epilogue writes
+  // q^C and the rotated q^R itself, from a RoPE table that stage 1's reduction
+  // launch computes
+  const int nc = dims->n_heads * dims->d_head;
+  GemmArgs g2{};
+  g2.x = compressed ? static_cast<const void*>(ws + L.cq) : h;
+  g2.x_dt = compressed ? w_dt : h_dt;
+  g2.w0 = w_uq;
+  g2.w1 = w_qr;
+  g2.w_dt = w_dt;
+  g2.out = reinterpret_cast<float*>(ws + L.s2);
+  g2.batch = batch;
+  g2.K = compressed ? d_qlatent : d_model;
+  g2.N = dims->n_heads * (dims->d_head + dims->d_rope);
+  g2.n0 = nc;
+  gemm_ws_plan(g2, kQueryMaxSlices);
+  const bool fused = compressed && g2.use_mfma && g2.slices == 1 && nc % 4 == 0 && dims->d_rope % 4 == 0 &&
+                     aligned16(q_nope) && (dims->d_rope == 0 || aligned16(q_pe));
+  RopeTableArgs tab{positions, rp, batch, dims->d_rope, nullptr};
+  if (fused) {
+    g2.fin_nope = q_nope;
+    g2.fin_pe = q_pe;
+    g2.fin_dt = out_dt;
+    g2.fin_drope = dims->d_rope;
+    if (dims->d_rope > 0 && rp.base > 0.f) {
+      tab.table = reinterpret_cast<double*>(ws + L.tab);
+      g2.fin_rope = tab.table;
+    }
+  }
   if (compressed) {
   // stage 1: c^Q = W^DQ h
   GemmArgs g1{};
@@ -725,23 +756,13 @@ mla_status_t mla_query_prep_rope(const mla_dims_t* dims, int32_t d_model, int32_
   g1.n0 = d_qlatent;
   gemm_ws_plan(g1, kQueryMaxSlices);
   e = launch_gemm_ws(g1, st);
-  if (e == hipSuccess) e = launch_reduce_cast(g1.out, g1.slices, int64_t(batch) * d_qlatent, ws + L.cq, w_dt, st);
+  if (e == hipSuccess)
+    e = launch_reduce_cast(g1.out, g1.slices, int64_t(batch) * d_qlatent, ws + L.cq, w_dt, tab, st);
   }
   // stage 2: [q^C ; q^R before rotation] = [W^UQ ; W^QR] c^Q (or h when the
   // query is not compressed), then rotate and write
-  GemmArgs g2{};
-  g2.x = compressed ? static_cast<const void*>(ws + L.cq) : h;
-  g2.x_dt = compressed ? w_dt : h_dt;
-  g2.w0 = w_uq;
-  g2.w1 = w_qr;
-  g2.w_dt = w_dt;
-  g2.out = reinterpret_cast<float*>(ws + L.s2);
-  g2.batch = batch;
-  g2.K = compressed ? d_qlatent : d_model;
-  g2.N = dims->n_heads * (dims->d_head + dims->d_rope);
-  g2.n0 = dims->n_heads * dims->d_head;
-  gemm_ws_plan(g2, kQueryMaxSlices);
   if (e == hipSuccess) e = launch_gemm_ws(g2, st);
+  if (fused) return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
   QueryFinishArgs f{};
   f.slices = g2.out;
   f.n_slices = g2.slices;

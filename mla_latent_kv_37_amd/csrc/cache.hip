@@ -49,12 +49,23 @@ __global__ __launch_bounds__(640) void cache_store_kernel(CacheStoreArgs a) {
     x0 = load_any(a.rows, int64_t(b) * W + c0, a.rows_dt);
     x1 = load_any(a.rows, int64_t(b) * W + c0 + 1, a.rows_dt);
     if (a.n_partials > 1) {
-      // projection slices (fp32), summed in slice order; the sum replaces slice 0
+      // projection slices (fp32), summed in slice order; the sum replaces slice
+      // 0.  Every slice's load goes out before the first addition (the slices
+      // were just written: a chain of dependent cache round trips otherwise).
       const float* pr = static_cast<const float*>(a.rows) + int64_t(b) * W + c0;
-      for (int q = 1; q < a.n_partials; ++q) {
-        x0 += pr[int64_t(q) * a.batch * W];
-        x1 += pr[int64_t(q) * a.batch * W + 1];
-      }
+      float p0[kGemmMaxSlices], p1[kGemmMaxSlices];
+#pragma unroll
+      for (int q = 1; q < kGemmMaxSlices; ++q)
+        if (q < a.n_partials) {
+          p0[q] = pr[int64_t(q) * a.batch * W];
+          p1[q] = pr[int64_t(q) * a.batch * W + 1];
+        }
+#pragma unroll
+      for (int q = 1; q < kGemmMaxSlices; ++q)
+        if (q < a.n_partials) {
+          x0 += p0[q];
+          x1 += p1[q];
+        }
       float* r0 = static_cast<float*>(const_cast<void*>(a.rows)) + int64_t(b) * W + c0;
       r0[0] = x0;
       r0[1] = x1;

@@ -9,99 +9,128 @@
 // gemm_ws_mfma_kernel (bf16 x and W, N % 64 == 0, K % (64 * slices) == 0):
 // out^T [n x b] = W [n x k] . x^T [k x b] on v_mfma_f32_32x32x16_bf16.  A
 // workgroup owns a tile of 64 weight rows by 64 batch rows (one 32 x 32 MFMA
-// tile per wavefront) and one k slice, which it walks in chunks of 64.
-// Operands reach LDS by plain loads in which 8 consecutive lanes read one
-// row's 128-byte chunk (whole cache lines per instruction), kGemmDepth chunks
-// ahead of use in registers; the chunk is written to one of two LDS buffers
-// (row r's 16-byte piece p at r*128 + ((p ^ (r&7) ^ ((r>>3)&1)) * 16), so the
-// MFMA fragment reads, 16 rows of one piece per 16 lanes, hit 64 distinct
-// banks), then one barrier (no memory fence, so the loads in flight stay in
-// flight) publishes it.  Batch rows past the end are clamped to the last row
-// and not stored; batches above 64 take more workgroups along z, which read
-// the weights again (from the caches when they run together).
+// tile per wavefront) and one k slice, which it walks in chunks of 64.  The
+// product is bound by the weight stream, so what matters is how many bytes each
+// workgroup keeps in flight: the chunks go straight from global memory to LDS
+// (direct-to-LDS loads, no registers held), kStages - 1 chunks ahead of the one
+// being multiplied, 16 KB each (8 KB of weight rows, 8 KB of batch rows).  Each
+// one-KB load covers 8 whole rows (8 cache lines); a row's 16-byte piece p goes
+// to slot p ^ (r & 7) ^ ((r >> 3) & 1) of its row, so that the MFMA fragment
+// reads, 16 rows of one piece per 16 lanes, hit 64 distinct banks.  One
+// barrier per chunk publishes it (each wavefront first waits for its own loads
+// of the chunk) and frees the stage of the chunk before it.  Batch rows past
+// the end are clamped to the last row and not stored; batches above 64 take
+// more workgroups along z, which read the weights again (from the caches when
+// they run together).
 #include "kernels.h"
 
 namespace mla {
 
-// kGemmDepth: chunks in flight per thread beyond the one being stored
-// (registers).  Few chunks leave room for more resident workgroups: 8 chunks
-// held 172 VGPRs (2 wavefronts per SIMD), 2 hold 66 and 1 holds 49 (5).
-// Measured: query prep (384 workgroups) 59.6 us with 8, 52.9 with 2, 50.6
-// with 1; the cache append (72 workgroups) and the fused query product (1152
-// workgroups) are faster with 2 (16.1 vs 18.0 us; 97.9 vs 105.7 us).
-template <int kGemmDepth>
+constexpr int kGemmHalf = kGemmTile * kGemmChunk * 2;   // bytes of one operand's chunk (8 KB)
+constexpr int kGemmStageBytes = 2 * kGemmHalf;          // weight rows + batch rows
+constexpr int kGemmStages = 4;                          // 64 KB of LDS: two workgroups per compute unit
+
+// Four consecutive outputs of one row, in the output dtype (8 or 16 bytes)
+__device__ __forceinline__ void store4(void* base, int64_t i, const float (&v)[4], mla_dtype_t dt) {
+  if (dt == MLA_BF16) {
+    bf16x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = (__bf16)v[e];
+    *reinterpret_cast<bf16x4*>(static_cast<uint16_t*>(base) + i) = o;
+  } else {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(base) + i) = f32x4{v[0], v[1], v[2], v[3]};
+  }
+}
+
+template <int kStages, bool kFinish>
 __global__ __launch_bounds__(256) void gemm_ws_mfma_kernel(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t lw[2][kGemmTile * kGemmChunk];
-  __shared__ __attribute__((aligned(16))) uint16_t lx[2][kGemmTile * kGemmChunk];
+  static_assert(kStages >= 2 && 4 * (kStages - 2) <= 15, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) char stage_raw[kStages * kGemmStageBytes];
+  const uint32_t lds = uint32_t(reinterpret_cast<uintptr_t>(stage_raw));
   const int nt0 = blockIdx.x * kGemmTile, slice = blockIdx.y, bb = blockIdx.z * kGemmTile;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5;
   const int kslice = a.K / a.slices;
   const int k0 = slice * kslice;
   const int nch = kslice / kGemmChunk;
-  // loader: rows lr and 32 + lr of the tile, 16-byte piece lp of the chunk
-  const int lr = tid >> 3, lp = tid & 7;
-  auto wrow = [&](int r) {
+  // slot (16 bytes) s of an operand chunk holds row s >> 3, piece
+  // (s & 7) ^ (r & 7) ^ ((r >> 3) & 1); wavefront w loads slots 128w + 64j + lane
+  auto piece = [](int r, int q) { return q ^ (r & 7) ^ ((r >> 3) & 1); };
+  const char* wsrc[2];
+  const char* xsrc[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int sl = 128 * wave + 64 * j + lane, r = sl >> 3, p = piece(r, sl & 7);
     const int n = nt0 + r;
-    return static_cast<const uint16_t*>(n < a.n0 ? a.w0 : a.w1) + int64_t(n < a.n0 ? n : n - a.n0) * a.K;
+    const uint16_t* wr = static_cast<const uint16_t*>(n < a.n0 ? a.w0 : a.w1) + int64_t(n < a.n0 ? n : n - a.n0) * a.K;
+    const uint16_t* xr = static_cast<const uint16_t*>(a.x) + int64_t(min(bb + r, a.batch - 1)) * a.K;
+    wsrc[j] = reinterpret_cast<const char*>(wr + k0 + 8 * p);
+    xsrc[j] = reinterpret_cast<const char*>(xr + k0 + 8 * p);
+  }
+  auto issue = [&](int c) {
+    const uint32_t st = lds + uint32_t((c % kStages) * kGemmStageBytes + wave * 2048);
+    const int64_t off = int64_t(c) * (kGemmChunk * 2);
+    dma16(wsrc[0] + off, st);
+    dma16(wsrc[1] + off, st + 1024u);
+    dma16(xsrc[0] + off, st + uint32_t(kGemmHalf));
+    dma16(xsrc[1] + off, st + uint32_t(kGemmHalf + 1024));
   };
-  auto xrow = [&](int r) { return static_cast<const uint16_t*>(a.x) + int64_t(min(bb + r, a.batch - 1)) * a.K; };
-  const uint16_t* wp0 = wrow(lr) + k0 + lp * 8;
-  const uint16_t* wp1 = wrow(32 + lr) + k0 + lp * 8;
-  const uint16_t* xp0 = xrow(lr) + k0 + lp * 8;
-  const uint16_t* xp1 = xrow(32 + lr) + k0 + lp * 8;
-  auto sw = [](int r, int p) { return r * kGemmChunk + ((p ^ (r & 7) ^ ((r >> 3) & 1)) * 8); };
-  const int so0 = sw(lr, lp), so1 = sw(32 + lr, lp);
   // fragments: wavefront (n tile wave&1, batch tile wave>>1); lane row l&31, piece 2*kstep + h
   const int fr_w = 32 * (wave & 1) + (lane & 31), fr_x = 32 * (wave >> 1) + (lane & 31);
 
-  bf16x8 rw0[kGemmDepth], rw1[kGemmDepth], rx0[kGemmDepth], rx1[kGemmDepth];
-  auto load = [&](int d, int c) {
-    const int off = min(c, nch - 1) * kGemmChunk;
-    rw0[d] = *reinterpret_cast<const bf16x8*>(wp0 + off);
-    rw1[d] = *reinterpret_cast<const bf16x8*>(wp1 + off);
-    rx0[d] = *reinterpret_cast<const bf16x8*>(xp0 + off);
-    rx1[d] = *reinterpret_cast<const bf16x8*>(xp1 + off);
-  };
-  // prologue loads in the loop's order (chunk by chunk), so that the pending
-  // loads at the loop head are in the same order on entry and on every trip
 #pragma unroll
-  for (int d = 0; d < kGemmDepth; ++d) {
-    load(d, d);
-    __builtin_amdgcn_sched_barrier(0);
-  }
+  for (int c = 0; c < kStages - 1; ++c)
+    if (c < nch) issue(c);
   f32x16 acc = {};
-  // Every step of a group stores, reloads and synchronises unconditionally (steps
-  // past the last chunk store and reload copies of it), so the load queue looks
-  // the same on every trip and the compiler can wait for one chunk's loads at a
-  // time instead of draining all of them at the top of the loop.
-  for (int c0 = 0; c0 < nch; c0 += kGemmDepth) {
+  for (int c = 0; c < nch; ++c) {
+    // this wavefront's loads of chunk c are complete when at most the loads of
+    // the chunks issued after it remain; then chunk c is complete for everyone,
+    // and everyone is done with chunk c - 1, whose stage takes chunk c + kStages - 1
+    wait_vm(4 * min(kStages - 2, nch - 1 - c));
+    raw_barrier();
+    if (c + kStages - 1 < nch) issue(c + kStages - 1);
+    const uint32_t st = lds + uint32_t((c % kStages) * kGemmStageBytes);
+    // all of the chunk's fragments are read before its first MFMA
+    bf16x8 fw[kGemmChunk / 16], fx[kGemmChunk / 16];
 #pragma unroll
-    for (int d = 0; d < kGemmDepth; ++d) {
-      const int c = c0 + d;
-      // chunk c goes to buffer c & 1: the buffer it overwrites was last read
-      // for chunk c - 2, before the barrier of chunk c - 1
-      uint16_t MLA_LDS* bw = (uint16_t MLA_LDS*)lw[c & 1];
-      uint16_t MLA_LDS* bx = (uint16_t MLA_LDS*)lx[c & 1];
-      *reinterpret_cast<bf16x8 MLA_LDS*>(bw + so0) = rw0[d];
-      *reinterpret_cast<bf16x8 MLA_LDS*>(bw + so1) = rw1[d];
-      *reinterpret_cast<bf16x8 MLA_LDS*>(bx + so0) = rx0[d];
-      *reinterpret_cast<bf16x8 MLA_LDS*>(bx + so1) = rx1[d];
-      load(d, c + kGemmDepth);
-      __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
-      raw_barrier();
-      if (c < nch) {
-#pragma unroll
-        for (int ks = 0; ks < kGemmChunk / 16; ++ks) {
-          const bf16x8 fw = *reinterpret_cast<const bf16x8 MLA_LDS*>(bw + sw(fr_w, 2 * ks + h));
-          const bf16x8 fx = *reinterpret_cast<const bf16x8 MLA_LDS*>(bx + sw(fr_x, 2 * ks + h));
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw, fx, acc, 0, 0, 0);
-        }
-      }
+    for (int ks = 0; ks < kGemmChunk / 16; ++ks) {
+      fw[ks] = *reinterpret_cast<const bf16x8 MLA_LDS*>(
+          (const char MLA_LDS*)(uintptr_t)(st + uint32_t(fr_w * 128 + piece(fr_w, 2 * ks + h) * 16)));
+      fx[ks] = *reinterpret_cast<const bf16x8 MLA_LDS*>(
+          (const char MLA_LDS*)(uintptr_t)(st + uint32_t(kGemmHalf + fr_x * 128 + piece(fr_x, 2 * ks + h) * 16)));
     }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < kGemmChunk / 16; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[ks], fx[ks], acc, 0, 0, 0);
   }
   // D[n][b]: lane holds b = l&31, n = 8(r/4) + 4h + r%4 of the wavefront's tile
   const int b = bb + 32 * (wave >> 1) + (lane & 31);
-  if (b < a.batch) {
+  if (b >= a.batch) return;
+  if constexpr (kFinish) {
+    // the query's columns straight to q^C / q^R (no fp32 round trip): the
+    // rotation of the unfused finish, on the same fp32 sums and fp64 table
+    const int nr = a.N - a.n0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int n = nt0 + 32 * (wave & 1) + 8 * q + 4 * h;
+      float v[4] = {acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+      if (n < a.n0) {
+        store4(a.fin_nope, int64_t(b) * a.n0 + n, v, a.fin_dt);
+      } else {
+        const int r = n - a.n0;
+        if (a.fin_rope != nullptr) {
+          const double* t = a.fin_rope + 2 * (int64_t(b) * (a.fin_drope >> 1) + ((r % a.fin_drope) >> 1));
+#pragma unroll
+          for (int e = 0; e < 4; e += 2) {
+            const double cs = t[e], sn = t[e + 1];
+            const double y0 = double(v[e]) * cs - double(v[e + 1]) * sn, y1 = double(v[e]) * sn + double(v[e + 1]) * cs;
+            v[e] = float(y0);
+            v[e + 1] = float(y1);
+          }
+        }
+        store4(a.fin_pe, int64_t(b) * nr + r, v, a.fin_dt);
+      }
+    }
+  } else {
     float* o = a.out + (int64_t(slice) * a.batch + b) * a.N + nt0 + 32 * (wave & 1) + 4 * h;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -126,9 +155,8 @@ __global__ __launch_bounds__(256) void gemm_ws_generic_kernel(GemmArgs a) {
 hipError_t launch_gemm_ws(const GemmArgs& a, hipStream_t st) {
   if (a.use_mfma) {
     const dim3 grid(a.N / kGemmTile, a.slices, ceil_div(a.batch, kGemmTile));
-    const int64_t wgs = int64_t(grid.x) * grid.y * grid.z;
-    if (wgs >= 256 && wgs <= 512) gemm_ws_mfma_kernel<1><<<grid, 256, 0, st>>>(a);
-    else gemm_ws_mfma_kernel<2><<<grid, 256, 0, st>>>(a);
+    if (a.fin_nope != nullptr) gemm_ws_mfma_kernel<kGemmStages, true><<<grid, 256, 0, st>>>(a);
+    else gemm_ws_mfma_kernel<kGemmStages, false><<<grid, 256, 0, st>>>(a);
   } else {
     gemm_ws_generic_kernel<<<dim3(a.batch, ceil_div(a.N, 256)), 256, 0, st>>>(a);
   }

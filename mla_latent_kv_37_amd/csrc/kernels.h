@@ -90,6 +90,25 @@ struct GemmArgs {
   int batch, K, N, n0;
   int slices;              // set by gemm_ws_plan
   bool use_mfma;           // set by gemm_ws_plan
+  // Query epilogue (MFMA plan with one slice; n0 and fin_drope multiples of 4):
+  // when fin_nope is set, columns [0, n0) go to fin_nope [batch, n0] and columns
+  // [n0, N) to fin_pe [batch, N - n0], in fin_dt, instead of `out`; each q^R pair
+  // (2p, 2p+1) of a head is rotated by the (cos, sin) pair fin_rope[b][p]
+  // (doubles, [batch, fin_drope / 2]) unless fin_rope is null.
+  void* fin_nope;
+  void* fin_pe;
+  mla_dtype_t fin_dt;
+  int fin_drope;
+  const double* fin_rope;
+};
+
+// (cos, sin) of each sequence's RoPE angles for the query epilogue above:
+// table[b][p] = (cos, sin)(positions[b] * theta_p), angle in fp64
+struct RopeTableArgs {
+  const int32_t* positions;
+  RopeParams rope;
+  int batch, d_rope;
+  double* table;           // null: no table
 };
 
 // 128 heads, d_c = 512, d_rope = 64, page 64, bf16 queries, bf16 or fp8 cache:
@@ -148,6 +167,7 @@ int gemm_ws_slices(int N, int K, int batch, int max_slices);
 void gemm_ws_plan(GemmArgs& a, int max_slices);   // chooses slices (<= max_slices) and the kernel
 hipError_t launch_gemm_ws(const GemmArgs& a, hipStream_t st);
 hipError_t launch_reduce_cast(const float* slices, int n_slices, int64_t count, void* out, mla_dtype_t out_dt,
+                              const RopeTableArgs& tab,
                               hipStream_t st);
 hipError_t launch_query_finish(const QueryFinishArgs& a, hipStream_t st);
 hipError_t launch_merge(const MergeArgs& a, int batch, hipStream_t st);

@@ -134,6 +134,30 @@ __device__ __forceinline__ void raw_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// One direct-to-LDS load: 64 lanes x 16 bytes from per-lane global addresses
+// into 1 KB of LDS at `lds` (lane l's bytes at lds + 16 l).  Inline assembly,
+// so the compiler does not track it: its completion is waited for with an
+// explicit vmcnt before the barrier that publishes the data.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+  const int m0 = uniform(int(lds));
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(m0), "v"(src)
+               : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(n) for a wave-uniform n in [0, 15]
+__device__ __forceinline__ void wait_vm(int n) {
+  switch (n) {
+#define MLA_VM_CASE(i) case i: __builtin_amdgcn_s_waitcnt(waitcnt_vm(i)); break;
+    MLA_VM_CASE(1) MLA_VM_CASE(2) MLA_VM_CASE(3) MLA_VM_CASE(4) MLA_VM_CASE(5) MLA_VM_CASE(6) MLA_VM_CASE(7)
+    MLA_VM_CASE(8) MLA_VM_CASE(9) MLA_VM_CASE(10) MLA_VM_CASE(11) MLA_VM_CASE(12) MLA_VM_CASE(13) MLA_VM_CASE(14)
+    MLA_VM_CASE(15)
+#undef MLA_VM_CASE
+    default: __builtin_amdgcn_s_waitcnt(waitcnt_vm(0)); break;
+  }
+}
+
 __host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 // Balanced partition cost stream.  The pages of the non-empty sequences, in

@@ -114,18 +114,6 @@ __global__ __launch_bounds__(256) void prefill_gather_kernel(PrefillArgs a) {
   }
 }
 
-// One direct-to-LDS load: 64 lanes x 16 bytes from per-lane global addresses
-// into 1 KB of LDS at `lds` (lane l's bytes at lds + 16 l).  Inline assembly,
-// so the compiler does not track it: its completion is waited for with an
-// explicit vmcnt before the barrier that publishes the data.
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
-  const int m0 = uniform(int(lds));
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-               :
-               : "s"(m0), "v"(src)
-               : "memory", "m0");
-}
-
 // Output staging.  An MFMA accumulator tile holds, in lane (r, h) = (lane&31,
 // lane>>5), row r's columns 8j + 4h .. +3 in registers 4j .. 4j+3 of each
 // 32-column block: stored as they are, every global write would be 8 bytes
@@ -295,18 +283,6 @@ constexpr int kPaBufs = 6, kPaLead = kPaBufs - 1;
 constexpr int kPaKBytes = 3 * 4096, kPaVBytes = 2 * 4096, kPaTileBytes = kPaKBytes + kPaVBytes;
 constexpr float kPfSlack = 8.f;
 constexpr int kPaKAhead = 6;   // K fragment reads in flight ahead of the score MFMAs
-
-// s_waitcnt vmcnt(n) for a wave-uniform n in [0, 15]
-__device__ __forceinline__ void wait_vm(int n) {
-  switch (n) {
-#define MLA_VM_CASE(i) case i: __builtin_amdgcn_s_waitcnt(waitcnt_vm(i)); break;
-    MLA_VM_CASE(1) MLA_VM_CASE(2) MLA_VM_CASE(3) MLA_VM_CASE(4) MLA_VM_CASE(5) MLA_VM_CASE(6) MLA_VM_CASE(7)
-    MLA_VM_CASE(8) MLA_VM_CASE(9) MLA_VM_CASE(10) MLA_VM_CASE(11) MLA_VM_CASE(12) MLA_VM_CASE(13) MLA_VM_CASE(14)
-    MLA_VM_CASE(15)
-#undef MLA_VM_CASE
-    default: __builtin_amdgcn_s_waitcnt(waitcnt_vm(0)); break;
-  }
-}
 
 __global__ __launch_bounds__(64 * kPaWaves) void prefill_attn_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(2048))) char lds_raw[kPaBufs * kPaTileBytes];

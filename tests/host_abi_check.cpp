@@ -37,7 +37,7 @@ hipError_t launch_decode_lite(const V2DecodeArgs& a, hipStream_t) { ++g_launches
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t) { ++g_launches; g_pf = a; return hipSuccess; }
 hipError_t launch_cache_store(const CacheStoreArgs&, int, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_gemm_ws(const GemmArgs&, hipStream_t) { ++g_launches; return hipSuccess; }
-hipError_t launch_reduce_cast(const float*, int, int64_t, void*, mla_dtype_t, hipStream_t) { ++g_launches; return hipSuccess; }
+hipError_t launch_reduce_cast(const float*, int, int64_t, void*, mla_dtype_t, const RopeTableArgs&, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_query_finish(const QueryFinishArgs&, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_merge(const MergeArgs&, int, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_merge_proj(const MergeArgs&, const void*, void*, int, hipStream_t) { ++g_launches; return hipSuccess; }
