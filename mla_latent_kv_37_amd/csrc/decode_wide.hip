@@ -113,18 +113,20 @@ __device__ __forceinline__ F8Item f8_read(uint32_t stage, const F8Thread& p, int
   return x;
 }
 // code * scale in fp32, rounded to bf16; rows past the sequence end as zeros
+// (their codes read as zero bytes, the staged range ending at the last row's
+// codes, and their scale is taken as 0 here: the 16-byte rounding of the scale
+// range can reach a real scale past the end)
 __device__ __forceinline__ void f8_write(const F8Item& x, uint32_t buf, const F8Thread& p, bool row_ok, int r) {
   const auto f0 = __builtin_amdgcn_cvt_pk_f32_fp8(int(x.code[0]), false);
   const auto f1 = __builtin_amdgcn_cvt_pk_f32_fp8(int(x.code[0]), true);
   const auto f2 = __builtin_amdgcn_cvt_pk_f32_fp8(int(x.code[1]), false);
   const auto f3 = __builtin_amdgcn_cvt_pk_f32_fp8(int(x.code[1]), true);
-  const float sc = x.sc;
+  const float sc = row_ok ? x.sc : 0.f;
   bf16x8 v;
   v[0] = (__bf16)(f0[0] * sc); v[1] = (__bf16)(f0[1] * sc);
   v[2] = (__bf16)(f1[0] * sc); v[3] = (__bf16)(f1[1] * sc);
   v[4] = (__bf16)(f2[0] * sc); v[5] = (__bf16)(f2[1] * sc);
   v[6] = (__bf16)(f3[0] * sc); v[7] = (__bf16)(f3[1] * sc);
-  if (!row_ok) v = bf16x8{};
   *reinterpret_cast<bf16x8 MLA_LDS*>((char MLA_LDS*)(uintptr_t)(buf + p.write_off + uint32_t(4096 * r))) = v;
 }
 
