@@ -281,10 +281,11 @@ void decode_wide_kernel(V2DecodeArgs a) {
     }
 
     // ---- score MFMAs of tile kt into sn, k-steps in order; the K fragments are
-    // read kKAhead steps ahead.
-    // `between(st)` runs after the MFMA of step st (VALU work of the previous
-    // tile) and may issue reads for the phase that follows.
-    auto score_phase = [&](int kt, f32x16& sn, auto&& between) {
+    // read kKAhead steps ahead.  `before(st)` runs after step st's fragment read
+    // is issued and before its MFMA (VALU work of the previous tile, done while
+    // the wavefront would otherwise wait for the fragment), `between(st)` after
+    // the MFMA (reads for the phase that follows).
+    auto score_phase = [&](int kt, f32x16& sn, auto&& before, auto&& between) {
       const uint32_t tb = tile_buf(kt);
       const int ln = opaque_lane();
       const int kb0 = kb0_of(ln);
@@ -302,6 +303,8 @@ void decode_wide_kernel(V2DecodeArgs a) {
         if (nx < kScoreSteps) {
           kr[st % kKAhead] = lds_read_b128(kaddr(nx));
         }
+        before(st);   // VALU work while this step's fragment read is outstanding
+        __builtin_amdgcn_sched_barrier(0);
         score_mfma(sn, kc, st < 32 ? qf[st] : qpe_r[st - 32], st == 0);
         between(st);
         __builtin_amdgcn_sched_barrier(0);   // keep each step's order
@@ -309,7 +312,7 @@ void decode_wide_kernel(V2DecodeArgs a) {
     };
 
     f32x16 s;
-    score_phase(0, s, [](int) {});
+    score_phase(0, s, [](int) {}, [](int) {});
     score_settle();
 
     f32x16 acc[16];
@@ -350,9 +353,13 @@ void decode_wide_kernel(V2DecodeArgs a) {
       }
 
       bf16x8 pk0, pk1;
-      auto softmax_step = [&](int st) {
+      // pinned: the score passes through an empty asm where the step is placed,
+      // which keeps the compiler from hoisting the exponential out of the loop
+      auto softmax_step = [&](int st, bool pinned) {
         if (st < 16) {
-          s[st] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st], a.scale_log2, -m_ref));
+          float x = s[st];
+          if (pinned) asm volatile("" : "+v"(x));
+          s[st] = __builtin_amdgcn_exp2f(__builtin_fmaf(x, a.scale_log2, -m_ref));
         } else if (st == 16) {
           pk0 = pack_half(s, 0);
         } else if (st == 17) {
@@ -380,15 +387,14 @@ void decode_wide_kernel(V2DecodeArgs a) {
       // ======== phase A: scores of tile k+1 | softmax of tile k
       f32x16 sn;
       if (more) {
-        score_phase(k + 1, sn, [&](int st) {
-          softmax_step(st);
+        score_phase(k + 1, sn, [&](int st) { softmax_step(st, true); }, [&](int st) {
           const int i = st - (kScoreSteps - kVAhead);
           if (i == 0) v_start();
           if (i >= 0) vr[i] = vfrag(i);
         });
       } else {
 #pragma unroll
-        for (int st = 0; st < 19; ++st) softmax_step(st);
+        for (int st = 0; st < 19; ++st) softmax_step(st, false);
         v_start();
 #pragma unroll
         for (int i = 0; i < kVAhead; ++i) vr[i] = vfrag(i);
