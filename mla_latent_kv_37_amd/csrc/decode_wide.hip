@@ -15,9 +15,11 @@
 // the SIMD to switch to.
 //
 // Software pipeline of tile k (per wavefront):
-//   softmax max of S(k)
-//   phase A: the 36 score MFMAs of tile k+1, with the exponentials, the row
-//            sums and the bf16 packing of P(k) between them
+//   (first tile of a segment only: the max of S(k), which sets the reference)
+//   phase A: the 36 score MFMAs of tile k+1, with the exponentials of S(k)
+//            (each placed while a K fragment read is outstanding, the running
+//            max taken from the same scores), the row sums and the bf16
+//            packing of P(k) between them
 //   phase B: the 32 PV MFMAs of tile k, with the 9 loads of this wavefront's
 //            row block of tile k+3 between them
 //   wait for this wavefront's loads of tile k+2, barrier (tile k+2 complete;
@@ -321,8 +323,10 @@ void decode_wide_kernel(V2DecodeArgs a) {
     // Softmax of S(k): the lane holds head 32w + (lane&31) and 16 of the
     // tile's tokens (token 8(rr>>2) + 4h + (rr&3) in s[rr]); lane^32 the other
     // 16.  Scores are kept in the log2 domain (scale * log2 e folded into one
-    // FMA); m_ref is the reference max, m_seen the running true max.
-    float m_ref = m_preset, m_seen = -INFINITY, lsum = 0.f;
+    // FMA); m_ref is the reference max.  The running true max of the lane's
+    // raw scores, m_raw, is taken with the exponentials (the head's max, scaled,
+    // at the segment's end); only the first tile's max is needed before them.
+    float m_ref = m_preset, m_raw = -INFINITY, lsum = 0.f;
     int page3 = page1;   // page of tile k+3 (tiles 2j and 2j+1 share page j)
 
     for (int k = 0; k < ntiles; ++k) {
@@ -336,13 +340,14 @@ void decode_wide_kernel(V2DecodeArgs a) {
             s[rr] = tok < valid ? s[rr] : -INFINITY;
           }
         }
-        float mx = s[0];
+        if (k == 0) {
+          float mx = s[0];
 #pragma unroll
-        for (int rr = 1; rr < 16; ++rr) mx = fmaxf(mx, s[rr]);
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * a.scale_log2;
-        m_seen = fmaxf(m_seen, mx);
-        if (k == 0) m_ref = fmaxf(m_ref, mx);
+          for (int rr = 1; rr < 16; ++rr) mx = fmaxf(mx, s[rr]);
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+          mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * a.scale_log2;
+          m_ref = fmaxf(m_ref, mx);
+        }
       }
       const bool more = k + 1 < ntiles;
       const bool load3 = k + 3 < ntiles;
@@ -359,6 +364,7 @@ void decode_wide_kernel(V2DecodeArgs a) {
         if (st < 16) {
           float x = s[st];
           if (pinned) asm volatile("" : "+v"(x));
+          m_raw = fmaxf(m_raw, x);
           s[st] = __builtin_amdgcn_exp2f(__builtin_fmaf(x, a.scale_log2, -m_ref));
         } else if (st == 16) {
           pk0 = pack_half(s, 0);
@@ -466,7 +472,11 @@ void decode_wide_kernel(V2DecodeArgs a) {
     // each posts whether one of its heads' maxima outran its reference.
     __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
     raw_barrier();
+    float m_seen;
     {
+      // the head's true max over the segment (the scale is positive)
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(m_raw), __float_as_uint(m_raw), false, false);
+      m_seen = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * a.scale_log2;
       const bool bad = __any(m_seen > m_ref + kRefSlack);
       const uint32_t flags = tiles_lds + uint32_t(kFlagOffset);
       if (opaque_lane() == 0) *reinterpret_cast<int MLA_LDS*>((char MLA_LDS*)(uintptr_t)(flags + 4 * wave)) = bad;
