@@ -51,6 +51,16 @@ struct V2DecodeArgs {
   float* lse;
 };
 
+// Order of the merge's additions, shared by merge_kernel and the fused
+// merge_proj_kernel so that the two give the same bits: a row with more than
+// kMergeOneSplits splits is added in kMergeParts contiguous parts of
+// L = ceil(count / kMergeParts) splits (the last ones shorter), each summed in
+// split order from zero, the part sums then added in part order; a row with
+// fewer splits is one part.  (Several wavefronts can then share a long row.)
+constexpr int kMergeParts = 4;
+constexpr int kMergeOneSplits = 16;
+__host__ __device__ inline int merge_parts(int count) { return count > kMergeOneSplits ? kMergeParts : 1; }
+
 struct MergeArgs {
   const int32_t* seq_lens;
   PartParams pp;

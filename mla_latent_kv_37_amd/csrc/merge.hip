@@ -69,30 +69,43 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(MergeArgs a) {
         for (int e = 0; e < COLS; ++e) x[e] = load_any(a.o_part, src + e, a.o_dt);
       }
     };
-    // four partials per step: their loads are issued together
-    int s = 0;
-    for (; s + 4 <= count; s += 4) {
-      float l[4], x[4][COLS > 0 ? COLS : 1];
+    // the parts of merge_parts(count), each from zero, added in order
+    const int P = merge_parts(count), L = ceil_div(count, P);
+    for (int q = 0; q < P; ++q) {
+      const int s1 = min(count, (q + 1) * L);
+      float Zq = 0.f, accq[COLS > 0 ? COLS : 1];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        l[j] = a.lse_part[int64_t(first + s + j) * a.n_heads + head];
-        load_cols(s + j, x[j]);
+      for (int e = 0; e < COLS; ++e) accq[e] = 0.f;
+      // four partials per step: their loads are issued together
+      int s = q * L;
+      for (; s + 4 <= s1; s += 4) {
+        float l[4], x[4][COLS > 0 ? COLS : 1];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          l[j] = a.lse_part[int64_t(first + s + j) * a.n_heads + head];
+          load_cols(s + j, x[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float w = __expf(l[j] - M);
+          Zq += w;
+#pragma unroll
+          for (int e = 0; e < COLS; ++e) accq[e] += w * x[j][e];
+        }
       }
+      for (; s < s1; ++s) {
+        float x[COLS > 0 ? COLS : 1];
+        const float w = __expf(a.lse_part[int64_t(first + s) * a.n_heads + head] - M);
+        load_cols(s, x);
+        Zq += w;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float w = __expf(l[j] - M);
-        Z += w;
-#pragma unroll
-        for (int e = 0; e < COLS; ++e) acc[e] += w * x[j][e];
+        for (int e = 0; e < COLS; ++e) accq[e] += w * x[e];
       }
-    }
-    for (; s < count; ++s) {
-      float x[COLS > 0 ? COLS : 1];
-      const float w = __expf(a.lse_part[int64_t(first + s) * a.n_heads + head] - M);
-      load_cols(s, x);
-      Z += w;
+      // (the first part is taken as it is: adding it to zero could flip the
+      // sign of a zero)
+      Z = q == 0 ? Zq : Z + Zq;
 #pragma unroll
-      for (int e = 0; e < COLS; ++e) acc[e] += w * x[e];
+      for (int e = 0; e < COLS; ++e) acc[e] = q == 0 ? accq[e] : acc[e] + accq[e];
     }
     const float invZ = 1.f / Z;
     const int64_t base = out_row * a.d_latent + lane * COLS;

@@ -39,6 +39,7 @@ namespace mla {
 
 constexpr int kMPH = 128, kMPL = 512;   // d_h, d_c
 constexpr int kMPWaves = 16;
+constexpr int kXchRow = 64 * 8 * 4 + 64 * 4;   // part exchange slot of one row (bytes)
 
 __device__ __forceinline__ uint32_t mp_row_off(int r, int chunk) {
   return uint32_t(r * 1024 + ((chunk ^ (r & 15)) * 16));
@@ -83,72 +84,110 @@ __device__ __forceinline__ void mp_touch_row(const MergeArgs& a, int b, int head
   asm volatile("" : : "v"(sink));
 }
 
-// Merged (or single-split) row b of head `head`, 8 columns per lane; writes
-// o_lat / lse for sequences that were split or are empty, like merge_kernel.
-__device__ __forceinline__ bf16x8 mp_merge_row(const MergeArgs& a, int b, int head, int lane) {
-  const int64_t out_row = int64_t(b) * a.n_heads + head;
-  uint16_t* const orow = static_cast<uint16_t*>(a.o_lat) + out_row * kMPL + lane * 8;
-  bf16x8 o = {};
-  int first, count;
-  mp_splits(a, b, first, count);
-  if (count == 0) {
-    *reinterpret_cast<bf16x8*>(orow) = o;
-    if (lane == 0 && a.lse != nullptr) a.lse[out_row] = -INFINITY;
-    return o;
-  }
-  // one work item covered the sequence: mla_decode wrote the final row
-  if (count <= 1) return *reinterpret_cast<const bf16x8*>(orow);
-  // lse_s of split s sits in lane s (splits beyond 64 are read per split below);
-  // the maximum is exact in any order, so M is merge_kernel's M
+// Sums over the parts [q0, q1) of a row's splits (merge_parts of kernels.h),
+// 8 columns per lane: each part from zero in split order, the parts added in
+// order, the weight of split s being exp(lse_s - M).  The first chunk of 8
+// partials goes out with the lse loads; M, the maximum over all of the row's
+// splits, is exact in any order.
+struct MpPart {
+  float Z;
+  float acc[8];
+};
+
+__device__ __forceinline__ MpPart mp_sum(const MergeArgs& a, int head, int lane, int first, int count, int q0, int q1,
+                                         float& M_out) {
+  const int P = merge_parts(count), L = ceil_div(count, P);
   const float* const lsp = a.lse_part + int64_t(first) * a.n_heads + head;
+  // lse_s of split s sits in lane s (splits beyond 64 are read per split below)
   const float lv = lane < count ? lsp[int64_t(lane) * a.n_heads] : -INFINITY;
   const int64_t stride = int64_t(a.n_heads) * kMPL;
   const uint16_t* const src0 = static_cast<const uint16_t*>(a.o_part) + (int64_t(first) * a.n_heads + head) * kMPL + lane * 8;
-  // the first 8 partials go out with the lse loads
+  const int sb = q0 * L, se = min(count, q1 * L);
   bf16x8 x8[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j)
-    if (j < count) x8[j] = *reinterpret_cast<const bf16x8*>(src0 + j * stride);
+    if (sb + j < se) x8[j] = *reinterpret_cast<const bf16x8*>(src0 + (sb + j) * stride);
   float M = lv;
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
   for (int s = 64; s < count; ++s) M = fmaxf(M, lsp[int64_t(s) * a.n_heads]);
+  M_out = M;
   auto lse_of = [&](int s) {
     return s < 64 ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lv), s)) : lsp[int64_t(s) * a.n_heads];
   };
-  // accumulate in split order with merge_kernel's expressions
-  float Z = 0.f, acc[8];
+  MpPart tot;
+  for (int q = q0; q < q1; ++q) {
+    const int s0 = q * L, s1 = min(count, s0 + L);
+    float Zq = 0.f, accq[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    for (int e = 0; e < 8; ++e) accq[e] = 0.f;
+    for (int c0 = s0; c0 < s1; c0 += 8) {
+      if (c0 != sb) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    if (j < count) {
-      const float w = __expf(lse_of(j) - M);
-      Z += w;
+        for (int j = 0; j < 8; ++j)
+          if (c0 + j < s1) x8[j] = *reinterpret_cast<const bf16x8*>(src0 + (c0 + j) * stride);
+      }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += w * float(x8[j][e]);
-    }
-  }
-  for (int s0 = 8; s0 < count; s0 += 8) {
+      for (int j = 0; j < 8; ++j) {
+        if (c0 + j < s1) {
+          const float w = __expf(lse_of(c0 + j) - M);
+          Zq += w;
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (s0 + j < count) x8[j] = *reinterpret_cast<const bf16x8*>(src0 + (s0 + j) * stride);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (s0 + j < count) {
-        const float w = __expf(lse_of(s0 + j) - M);
-        Z += w;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] += w * float(x8[j][e]);
+          for (int e = 0; e < 8; ++e) accq[e] += w * float(x8[j][e]);
+        }
       }
     }
-  }
-  const float invZ = 1.f / Z;
+    // (the first part is taken as it is: adding it to zero could flip the sign of a zero)
+    tot.Z = q == q0 ? Zq : tot.Z + Zq;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) o[e] = (__bf16)(acc[e] * invZ);
-  *reinterpret_cast<bf16x8*>(orow) = o;
-  if (lane == 0 && a.lse != nullptr) a.lse[out_row] = M + __logf(Z);
+    for (int e = 0; e < 8; ++e) tot.acc[e] = q == q0 ? accq[e] : tot.acc[e] + accq[e];
+  }
+  return tot;
+}
+
+// The merged row from its sums: o_lat and lse written (for a split sequence),
+// the bf16 row returned
+__device__ __forceinline__ bf16x8 mp_finish(const MergeArgs& a, int b, int head, int lane, const MpPart& t, float M) {
+  const int64_t out_row = int64_t(b) * a.n_heads + head;
+  const float invZ = 1.f / t.Z;
+  bf16x8 o;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = (__bf16)(t.acc[e] * invZ);
+  *reinterpret_cast<bf16x8*>(static_cast<uint16_t*>(a.o_lat) + out_row * kMPL + lane * 8) = o;
+  if (lane == 0 && a.lse != nullptr) a.lse[out_row] = M + __logf(t.Z);
   return o;
+}
+
+// A row that needs no merge: an empty sequence (zeros, lse -inf, written as
+// merge_kernel does) or one that a single work item covered (mla_decode wrote
+// its final row).  false for a split row.
+__device__ __forceinline__ bool mp_plain_row(const MergeArgs& a, int b, int head, int lane, int count, bf16x8& o) {
+  const int64_t out_row = int64_t(b) * a.n_heads + head;
+  uint16_t* const orow = static_cast<uint16_t*>(a.o_lat) + out_row * kMPL + lane * 8;
+  if (count == 0) {
+    o = bf16x8{};
+    *reinterpret_cast<bf16x8*>(orow) = o;
+    if (lane == 0 && a.lse != nullptr) a.lse[out_row] = -INFINITY;
+    return true;
+  }
+  if (count == 1) {
+    o = *reinterpret_cast<const bf16x8*>(orow);
+    return true;
+  }
+  return false;
+}
+
+// Merged (or single-split) row b of head `head` by one wavefront, every part
+// in order; writes o_lat / lse for sequences that were split or are empty,
+// like merge_kernel.
+__device__ __forceinline__ bf16x8 mp_merge_row(const MergeArgs& a, int b, int head, int lane) {
+  int first, count;
+  mp_splits(a, b, first, count);
+  bf16x8 o;
+  if (mp_plain_row(a, b, head, lane, count, o)) return o;
+  float M;
+  const MpPart t = mp_sum(a, head, lane, first, count, 0, merge_parts(count), M);
+  return mp_finish(a, b, head, lane, t, M);
 }
 
 template <int R>
@@ -156,6 +195,10 @@ __global__ __launch_bounds__(64 * kMPWaves) void merge_proj_kernel(MergeArgs a, 
                                                                    uint16_t* __restrict__ out, int batch) {
   __shared__ __attribute__((aligned(1024))) char wl[kMPH * 1024];
   __shared__ __attribute__((aligned(1024))) char rows[R * 1024];
+  // part exchange (tiles of at most kMPWaves / kMergeParts rows): per row, 64
+  // lanes x 8 fp32 sums, then 64 lanes x Z
+  constexpr bool kParts = R <= 16;
+  __shared__ __attribute__((aligned(16))) char xch[kParts ? (kMPWaves / kMergeParts) * kXchRow : 16];
   float MLA_LDS* const red = (float MLA_LDS*)(uintptr_t)uint32_t(reinterpret_cast<uintptr_t>(wl));
   const int i = blockIdx.x, bt = blockIdx.y * R;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, h = lane >> 5;
@@ -186,19 +229,64 @@ __global__ __launch_bounds__(64 * kMPWaves) void merge_proj_kernel(MergeArgs a, 
     }
   }
   const uint32_t rows_lds = uint32_t(reinterpret_cast<uintptr_t>(rows));
-  {
-    const int nvalid = min(R, batch - bt);
+  const int nvalid = min(R, batch - bt);
+  if (kParts && nvalid * kMergeParts <= kMPWaves) {
+    // Few rows: wavefront w takes part w / nvalid of row w % nvalid (rows of
+    // more than kMergeOneSplits splits are added in kMergeParts parts), and
+    // parts 1.. reach the row's first wavefront through the exchange area one
+    // at a time, so that it adds them in order.  Every wavefront passes the
+    // same barriers.
+    const uint32_t xch_lds = uint32_t(reinterpret_cast<uintptr_t>(xch));
+    const int r = wave % nvalid, q = wave / nvalid, b = bt + r;
+    int first = 0, count = 0;
+    if (q < kMergeParts) mp_splits(a, b, first, count);
+    const bool mine = q < kMergeParts && count > 1 && q < merge_parts(count);
+    MpPart t{};
+    float M = 0.f;
+    if (mine) t = mp_sum(a, i, lane, first, count, q, q + 1, M);
+    const uint32_t xa = xch_lds + uint32_t(r * kXchRow + lane * 32), xz = xch_lds + uint32_t(r * kXchRow + 2048 + lane * 4);
+    for (int qq = 1; qq < kMergeParts; ++qq) {
+      if (mine && q == qq) {
+        *reinterpret_cast<f32x4 MLA_LDS*>((char MLA_LDS*)(uintptr_t)xa) = f32x4{t.acc[0], t.acc[1], t.acc[2], t.acc[3]};
+        *reinterpret_cast<f32x4 MLA_LDS*>((char MLA_LDS*)(uintptr_t)(xa + 16)) = f32x4{t.acc[4], t.acc[5], t.acc[6], t.acc[7]};
+        *reinterpret_cast<float MLA_LDS*>((char MLA_LDS*)(uintptr_t)xz) = t.Z;
+      }
+      __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
+      raw_barrier();
+      if (mine && q == 0 && qq < merge_parts(count)) {
+        const f32x4 u0 = *reinterpret_cast<const f32x4 MLA_LDS*>((const char MLA_LDS*)(uintptr_t)xa);
+        const f32x4 u1 = *reinterpret_cast<const f32x4 MLA_LDS*>((const char MLA_LDS*)(uintptr_t)(xa + 16));
+        t.Z += *reinterpret_cast<const float MLA_LDS*>((const char MLA_LDS*)(uintptr_t)xz);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          t.acc[e] += u0[e];
+          t.acc[4 + e] += u1[e];
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
+      raw_barrier();   // the slot is read before the next part overwrites it
+    }
+    if (q == 0) {
+      bf16x8 o;
+      if (!mp_plain_row(a, b, i, lane, count, o)) o = mp_finish(a, b, i, lane, t, M);
+      *reinterpret_cast<bf16x8 MLA_LDS*>((char MLA_LDS*)(uintptr_t)(rows_lds + mp_row_off(r, lane))) = o;
+    }
+#pragma unroll
+    for (int rz = wave; rz < R; rz += kMPWaves)
+      if (rz >= nvalid)
+        *reinterpret_cast<bf16x8 MLA_LDS*>((char MLA_LDS*)(uintptr_t)(rows_lds + mp_row_off(rz, lane))) = bf16x8{};
+  } else {
     if (nvalid < kMPWaves && wave >= nvalid) {
       const int hw = wave - nvalid, r = hw % nvalid;
       const int nh = (kMPWaves - nvalid - r + nvalid - 1) / nvalid;
       mp_touch_row(a, bt + r, i, lane, hw / nvalid, nh);
     }
-  }
 #pragma unroll
-  for (int r = wave; r < R; r += kMPWaves) {
-    const int b = bt + r;
-    const bf16x8 o = b < batch ? mp_merge_row(a, b, i, lane) : bf16x8{};
-    *reinterpret_cast<bf16x8 MLA_LDS*>((char MLA_LDS*)(uintptr_t)(rows_lds + mp_row_off(r, lane))) = o;
+    for (int r = wave; r < R; r += kMPWaves) {
+      const int b = bt + r;
+      const bf16x8 o = b < batch ? mp_merge_row(a, b, i, lane) : bf16x8{};
+      *reinterpret_cast<bf16x8 MLA_LDS*>((char MLA_LDS*)(uintptr_t)(rows_lds + mp_row_off(r, lane))) = o;
+    }
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   __syncthreads();

@@ -13,7 +13,7 @@ The fp32 cases take the fallback (the two calls in sequence): bit-identical.
 import numpy as np
 import pytest
 
-from _cases import TOL, direct_case, from_h_case, host, rel_err, to_device
+from _cases import TOL, Worst, compare_seq, direct_case, from_h_case, host, rel_err, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -105,6 +105,25 @@ def test_fused_more_than_64_splits():
     dev = to_device(case)
     print(f"case: V2 bf16 lens {lens}, split 64", flush=True)
     _check(*_both(case, dev, (64, 0)), exact_heads=False)
+
+
+def test_fused_one_sequence_64_splits_against_oracle():
+    """One sequence in 64 splits (the B = 1 decode): its row is added in four
+    parts by four wavefronts; fused against unfused, and against the oracle."""
+    lens = [4096]
+    case = direct_case(3, lens, max_pages=64, seed=88)
+    dev = to_device(case)
+    print(f"case: V2 bf16 lens {lens}, split 64", flush=True)
+    fused, unfused = _both(case, dev, (64, 0))
+    _check(fused, unfused, exact_heads=False)
+    o_lat, lse, o_heads = (host(t) for t in fused)
+    d = case.dims
+    heads = [0, 5, 64, 127]
+    worst = Worst()
+    compare_seq(case, 0, case.reference(0, heads=heads),
+                {"o_lat": o_lat[0], "lse": lse[0], "o_heads": o_heads[0].reshape(d.n_heads, d.d_head)},
+                TOL["bf16"], heads, worst)
+    worst.report(TOL["bf16"])
 
 
 def test_fused_v2lite_16_heads():

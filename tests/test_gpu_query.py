@@ -113,6 +113,15 @@ def test_query_prep_unrotated():
     assert _rel(got_r, ref_r) <= TOL["f32"]
 
 
+def test_query_prep_v2_unrotated():
+    """The V2 shapes (the second product writes q^C and q^R from its epilogue)
+    with the rotation off: q^R is the plain product."""
+    import synth
+    got_c, got_r, ref_c, ref_r = _run(synth.V2, 8, "bf16", "bf16", "bf16", seed=5, rope_base=0.0)
+    assert _rel(got_c, ref_c) <= TOL["bf16"]
+    assert _rel(got_r, ref_r) <= TOL["bf16"]
+
+
 def _fused_weights(W, n_heads, d_head):
     """The offline-fused query weight of the pages' absorption remark: head i's
     block is W^UK_i^T W^UQ_i, so W^UQK c^Q gives every head's q_lat directly."""
