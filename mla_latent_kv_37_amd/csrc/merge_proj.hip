@@ -12,10 +12,11 @@
 // ([DeepSeek-V2 explainer] §2.2.2: W^UV applied after attention), as
 // o^T [k x b] = W^UV_i [k x c] . o_lat^T [c x b] on v_mfma_f32_32x32x16_bf16.
 //
-// Workgroup of 16 wavefronts for R = 8, 16 or 32 sequences (the largest that
-// still gives about one workgroup per compute unit: the fewer workgroups read
-// each head's W^UV, the less traffic; 8 rows only for few heads, as in
-// V2-Lite, where it took the kernel from 9.4 to 8.8 us).  Wavefront w = 4q + kb owns
+// Workgroup of 16 wavefronts for R = 2, 4, 8, 16 or 32 sequences (the largest
+// that still gives a workgroup per compute unit: the fewer workgroups read each
+// head's W^UV, the less traffic; fewer rows for few heads, as in V2-Lite, where
+// 8 rows took the kernel from 9.4 to 8.8 us, or few sequences: 4 long ones in
+// 2-row tiles, 1.3% off their step).  Wavefront w = 4q + kb owns
 // output rows k = 32kb..32kb+31 and the contraction quarter c = 128q..128q+127.
 // Phase 0: the head's whole W^UV_i (128 rows x 1 KB) is copied into LDS by
 // direct-to-LDS loads issued before anything else (8 rows per wavefront; chunk
@@ -24,7 +25,9 @@
 // (measured: 8.7% less time than loading the fragments into registers after
 // the merge).  Phase 1: wavefront w merges tile rows w, w + 16 (lane = 8 columns): a row's
 // split lse values are loaded lane-parallel together with its first 8 partials
-// (two memory round trips for up to 8 splits), into an LDS copy of the R rows
+// (two memory round trips for up to 8 splits); in a tile of at most 4 rows each
+// row's parts (the association of kernels.h) go to four wavefronts and meet in
+// the first through LDS.  The merged rows go into an LDS copy of the R rows
 // (bf16, 16-byte chunk j of row r at slot j ^ (r & 15): conflict-free for the
 // row writes and the MFMA operand reads).  Phase 2: after the weight loads are
 // waited for, 8 MFMAs per wavefront (for
@@ -362,12 +365,14 @@ hipError_t launch_merge_proj(const MergeArgs& a, const void* w_uv, void* o_heads
     return hipErrorInvalidDevice;
   const uint16_t* w = static_cast<const uint16_t*>(w_uv);
   uint16_t* out = static_cast<uint16_t*>(o_heads);
-  if (int64_t(a.n_heads) * ceil_div(batch, 32) >= cus)
-    merge_proj_kernel<32><<<dim3(a.n_heads, ceil_div(batch, 32)), 64 * kMPWaves, 0, st>>>(a, w, out, batch);
-  else if (int64_t(a.n_heads) * ceil_div(batch, 16) >= cus / 2)
-    merge_proj_kernel<16><<<dim3(a.n_heads, ceil_div(batch, 16)), 64 * kMPWaves, 0, st>>>(a, w, out, batch);
-  else
-    merge_proj_kernel<8><<<dim3(a.n_heads, ceil_div(batch, 8)), 64 * kMPWaves, 0, st>>>(a, w, out, batch);
+  // the largest tile that still gives a workgroup per compute unit (fewer
+  // workgroups read each head's W^UV): 32, 16, 8, 4 or 2 rows
+  auto fits = [&](int r) { return int64_t(a.n_heads) * ceil_div(batch, r) >= cus; };
+  if (fits(32)) merge_proj_kernel<32><<<dim3(a.n_heads, ceil_div(batch, 32)), 64 * kMPWaves, 0, st>>>(a, w, out, batch);
+  else if (fits(16)) merge_proj_kernel<16><<<dim3(a.n_heads, ceil_div(batch, 16)), 64 * kMPWaves, 0, st>>>(a, w, out, batch);
+  else if (fits(8)) merge_proj_kernel<8><<<dim3(a.n_heads, ceil_div(batch, 8)), 64 * kMPWaves, 0, st>>>(a, w, out, batch);
+  else if (fits(4)) merge_proj_kernel<4><<<dim3(a.n_heads, ceil_div(batch, 4)), 64 * kMPWaves, 0, st>>>(a, w, out, batch);
+  else merge_proj_kernel<2><<<dim3(a.n_heads, ceil_div(batch, 2)), 64 * kMPWaves, 0, st>>>(a, w, out, batch);
   return hipGetLastError();
 }
 
