@@ -161,23 +161,73 @@ __device__ __forceinline__ bf16x8 mp_finish(const MergeArgs& a, int b, int head,
   return o;
 }
 
-// A row that needs no merge: an empty sequence (zeros, lse -inf, written as
-// merge_kernel does) or one that a single work item covered (mla_decode wrote
-// its final row).  false for a split row.
-__device__ __forceinline__ bool mp_plain_row(const MergeArgs& a, int b, int head, int lane, int count, bf16x8& o) {
+// A row of at most kMergeOneSplits splits (one part: the splits in order) by
+// one wavefront, 8 columns per lane; writes o_lat / lse for sequences that
+// were split or are empty, like merge_kernel.  (Kept apart from mp_sum: the
+// common short rows run measurably faster through this straight-line form.)
+__device__ __forceinline__ bf16x8 mp_merge_row_short(const MergeArgs& a, int b, int head, int lane, int first,
+                                                     int count) {
   const int64_t out_row = int64_t(b) * a.n_heads + head;
   uint16_t* const orow = static_cast<uint16_t*>(a.o_lat) + out_row * kMPL + lane * 8;
+  bf16x8 o = {};
   if (count == 0) {
-    o = bf16x8{};
     *reinterpret_cast<bf16x8*>(orow) = o;
     if (lane == 0 && a.lse != nullptr) a.lse[out_row] = -INFINITY;
-    return true;
+    return o;
   }
-  if (count == 1) {
-    o = *reinterpret_cast<const bf16x8*>(orow);
-    return true;
+  // one work item covered the sequence: mla_decode wrote the final row
+  if (count <= 1) return *reinterpret_cast<const bf16x8*>(orow);
+  // lse_s of split s sits in lane s (splits beyond 64 are read per split below);
+  // the maximum is exact in any order, so M is merge_kernel's M
+  const float* const lsp = a.lse_part + int64_t(first) * a.n_heads + head;
+  const float lv = lane < count ? lsp[int64_t(lane) * a.n_heads] : -INFINITY;
+  const int64_t stride = int64_t(a.n_heads) * kMPL;
+  const uint16_t* const src0 = static_cast<const uint16_t*>(a.o_part) + (int64_t(first) * a.n_heads + head) * kMPL + lane * 8;
+  // the first 8 partials go out with the lse loads
+  bf16x8 x8[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (j < count) x8[j] = *reinterpret_cast<const bf16x8*>(src0 + j * stride);
+  float M = lv;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+  for (int s = 64; s < count; ++s) M = fmaxf(M, lsp[int64_t(s) * a.n_heads]);
+  auto lse_of = [&](int s) {
+    return s < 64 ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lv), s)) : lsp[int64_t(s) * a.n_heads];
+  };
+  // accumulate in split order with merge_kernel's expressions
+  float Z = 0.f, acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j < count) {
+      const float w = __expf(lse_of(j) - M);
+      Z += w;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += w * float(x8[j][e]);
+    }
   }
-  return false;
+  for (int s0 = 8; s0 < count; s0 += 8) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (s0 + j < count) x8[j] = *reinterpret_cast<const bf16x8*>(src0 + (s0 + j) * stride);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (s0 + j < count) {
+        const float w = __expf(lse_of(s0 + j) - M);
+        Z += w;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += w * float(x8[j][e]);
+      }
+    }
+  }
+  const float invZ = 1.f / Z;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = (__bf16)(acc[e] * invZ);
+  *reinterpret_cast<bf16x8*>(orow) = o;
+  if (lane == 0 && a.lse != nullptr) a.lse[out_row] = M + __logf(Z);
+  return o;
 }
 
 // Merged (or single-split) row b of head `head` by one wavefront, every part
@@ -186,10 +236,9 @@ __device__ __forceinline__ bool mp_plain_row(const MergeArgs& a, int b, int head
 __device__ __forceinline__ bf16x8 mp_merge_row(const MergeArgs& a, int b, int head, int lane) {
   int first, count;
   mp_splits(a, b, first, count);
-  bf16x8 o;
-  if (mp_plain_row(a, b, head, lane, count, o)) return o;
+  if (count <= kMergeOneSplits) return mp_merge_row_short(a, b, head, lane, first, count);
   float M;
-  const MpPart t = mp_sum(a, head, lane, first, count, 0, merge_parts(count), M);
+  const MpPart t = mp_sum(a, head, lane, first, count, 0, kMergeParts, M);
   return mp_finish(a, b, head, lane, t, M);
 }
 
@@ -243,7 +292,7 @@ __global__ __launch_bounds__(64 * kMPWaves) void merge_proj_kernel(MergeArgs a, 
     const int r = wave % nvalid, q = wave / nvalid, b = bt + r;
     int first = 0, count = 0;
     if (q < kMergeParts) mp_splits(a, b, first, count);
-    const bool mine = q < kMergeParts && count > 1 && q < merge_parts(count);
+    const bool mine = q < kMergeParts && count > kMergeOneSplits;   // rows of several parts
     MpPart t{};
     float M = 0.f;
     if (mine) t = mp_sum(a, i, lane, first, count, q, q + 1, M);
@@ -256,7 +305,7 @@ __global__ __launch_bounds__(64 * kMPWaves) void merge_proj_kernel(MergeArgs a, 
       }
       __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
       raw_barrier();
-      if (mine && q == 0 && qq < merge_parts(count)) {
+      if (mine && q == 0) {
         const f32x4 u0 = *reinterpret_cast<const f32x4 MLA_LDS*>((const char MLA_LDS*)(uintptr_t)xa);
         const f32x4 u1 = *reinterpret_cast<const f32x4 MLA_LDS*>((const char MLA_LDS*)(uintptr_t)(xa + 16));
         t.Z += *reinterpret_cast<const float MLA_LDS*>((const char MLA_LDS*)(uintptr_t)xz);
@@ -270,8 +319,7 @@ __global__ __launch_bounds__(64 * kMPWaves) void merge_proj_kernel(MergeArgs a, 
       raw_barrier();   // the slot is read before the next part overwrites it
     }
     if (q == 0) {
-      bf16x8 o;
-      if (!mp_plain_row(a, b, i, lane, count, o)) o = mp_finish(a, b, i, lane, t, M);
+      const bf16x8 o = mine ? mp_finish(a, b, i, lane, t, M) : mp_merge_row_short(a, b, i, lane, first, count);
       *reinterpret_cast<bf16x8 MLA_LDS*>((char MLA_LDS*)(uintptr_t)(rows_lds + mp_row_off(r, lane))) = o;
     }
 #pragma unroll
