@@ -167,7 +167,11 @@ void decode_wide_kernel(V2DecodeArgs a) {
   while (redo || it.next(sg)) {
     const int b = uniform(sg.b);
     const int t0 = uniform(sg.t0), t1 = uniform(sg.t1);   // t0 is a multiple of the page size
-    const int32_t* bt = a.block_table + int64_t(b / a.bt_div) * a.max_pages + t0 / kV2Page;
+    // (the divisor passes through an empty asm: the division's reciprocal is
+    // then made here each segment instead of held, and spilled, across them)
+    int bt_div = a.bt_div;
+    asm volatile("" : "+s"(bt_div));
+    const int32_t* bt = a.block_table + int64_t(b / bt_div) * a.max_pages + t0 / kV2Page;
     const char* kv = static_cast<const char*>(a.kv);
     const int ntiles = ceil_div(t1 - t0, kTileTok);
     auto tile_valid = [&](int k) { return min(kTileTok, t1 - t0 - k * kTileTok); };
@@ -318,8 +322,22 @@ void decode_wide_kernel(V2DecodeArgs a) {
     score_settle();
 
     f32x16 acc[16];
+    if constexpr (kF8) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = f32x16{};
+      for (int i = 0; i < 16; ++i) acc[i] = f32x16{};
+    } else {
+      // O^T from zero, written by MFMAs of zero operands made here (a zeroed
+      // register tuple kept for the segment starts would be spilled)
+      uint32_t z0, z1, z2, z3;
+      asm volatile("v_mov_b32 %0, 0" : "=v"(z0));
+      asm volatile("v_mov_b32 %0, 0" : "=v"(z1));
+      asm volatile("v_mov_b32 %0, 0" : "=v"(z2));
+      asm volatile("v_mov_b32 %0, 0" : "=v"(z3));
+      typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+      const bf16x8 z = __builtin_bit_cast(bf16x8, u32x4_t{z0, z1, z2, z3});
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(z, z, f32x16{}, 0, 0, 0);
+    }
     // Softmax of S(k): the lane holds head 32w + (lane&31) and 16 of the
     // tile's tokens (token 8(rr>>2) + 4h + (rr&3) in s[rr]); lane^32 the other
     // 16.  Scores are kept in the log2 domain (scale * log2 e folded into one

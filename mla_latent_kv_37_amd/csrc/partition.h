@@ -137,8 +137,13 @@ struct SegmentIter {
         // caller's loop (where that register would be held, or spilled, throughout)
         int w = item;
         asm volatile("" : "+s"(w));
-        if (Sb >= p0) meta[bb] = w;
-        if (Sb + np <= p1) meta[B + bb] = w;
+        // (and so is the store's vector offset, which the compiler would
+        // otherwise make once and hold across the caller's loop)
+        int off0, off1;
+        asm volatile("v_mov_b32 %0, %1" : "=v"(off0) : "s"(bb * 4));
+        asm volatile("v_mov_b32 %0, %1" : "=v"(off1) : "s"((B + bb) * 4));
+        if (Sb >= p0) *reinterpret_cast<int32_t*>(reinterpret_cast<char*>(meta) + off0) = w;
+        if (Sb + np <= p1) *reinterpret_cast<int32_t*>(reinterpret_cast<char*>(meta) + off1) = w;
       }
       return true;
     }
