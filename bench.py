@@ -277,14 +277,14 @@ def run(args, workload=None, partition=None, cpu=True, copy_tbps=None):
             ev[1].record(stream)
         if q_len > 1:
             if args.unfused:
-                # expand + decode + merge in one call, then the projection
+                # decode + merge in one call, then the projection
                 mk.decode_multi(step.d, q_lat_m, s["q_pe"].view(B, q_len, N_H, D_R), s["cache"].desc, scale,
                                 step.part, multi_ws, o_lat_m, lse_m)
                 if ev is not None:
                     ev[2].record(stream)
                 step.project(s["W_UV"])
             else:
-                # expand + decode, then merge + projection in one launch
+                # decode, then merge + projection in one launch
                 mk.decode_multi_out_proj(step.d, q_lat_m, s["q_pe"].view(B, q_len, N_H, D_R), s["cache"].desc, scale,
                                          step.part, multi_ws, o_lat_m, s["W_UV"], step.o_heads, lse_m)
                 if ev is not None:
@@ -436,8 +436,8 @@ def run(args, workload=None, partition=None, cpu=True, copy_tbps=None):
                            "kernel": ("decode_wide_kernel<true> (fp8 cache, one wavefront per SIMD)" if cid == 5 else
                                       "decode_lite_kernel (16 heads, bf16 cache)" if n_h == 16 else
                                       "decode_wide_kernel<false> (bf16 cache, one wavefront per SIMD)") +
-                                     ((" + expand_kernel + merge_kernel (mla_decode_multi)" if args.unfused else
-                                       " + expand_kernel + merge_proj_kernel (mla_decode_multi_out_proj; the "
+                                     ((" + merge_kernel (mla_decode_multi)" if args.unfused else
+                                       " + merge_proj_kernel (mla_decode_multi_out_proj; the "
                                        "time includes the W^UV projection)") if q_len > 1 else ""),
                            "algorithmic_bytes_per_launch": alg["decode_bytes"],
                            "algorithmic_flops_per_launch": alg["decode_flops"],

@@ -205,10 +205,12 @@ mla_status_t mla_merge_splits(const mla_dims_t* dims, int32_t batch,
  *   o_lat: [batch, q_len, n_h, d_c] (o_dt), lse: [batch, q_len, n_h] or NULL.
  * One call runs the whole attention, merge included: each (sequence, new
  * token) pair is a virtual sequence of mla_decode's batch * q_len, with the
- * partition `part` applied to the virtual batch; the virtual lengths live in
- * the workspace, and virtual sequence b*q_len + t reads sequence b's
- * block-table row in place.  Same cache and dtype rules as mla_decode.
- *   workspace: mla_decode_multi_workspace_size(...) bytes, 16-B aligned (never 0).
+ * partition `part` applied to the virtual batch; the kernels derive virtual
+ * sequence b*q_len + t's length from seq_lens[b] and read sequence b's
+ * block-table row in place (no extra launch).  Same cache and dtype rules as
+ * mla_decode.
+ *   workspace: mla_decode_multi_workspace_size(...) bytes (those of mla_decode
+ *       over the virtual batch), 16-B aligned; may be NULL when that is 0.
  */
 mla_status_t mla_decode_multi_workspace_size(const mla_dims_t* dims, int32_t batch, int32_t q_len,
                                              int32_t max_pages_per_seq, int32_t page_size,

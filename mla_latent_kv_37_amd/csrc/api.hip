@@ -276,6 +276,7 @@ mla_status_t decode_impl(const mla_dims_t* dims, int32_t batch, const void* q_la
   int n_items = 0, n_slots = 0;
   if (mla_status_t s = resolve(dims, batch, cache->max_pages_per_seq, cache->page_size, part, &pp, &n_items, &n_slots))
     return s;
+  pp.q_len = bt_div;   // (a multi-token decode's virtual lengths come from seq_lens)
   const WsLayout L = ws_layout(dims, n_slots, batch, pp.mode == PART_BALANCED, o_elem);
   if (L.total > 0 && (workspace == nullptr || workspace_bytes < L.total)) return MLA_ERR_WORKSPACE;
   if (L.total > 0 && !aligned16(workspace)) return MLA_ERR_ALIGNMENT;
@@ -348,7 +349,7 @@ mla_status_t decode_impl(const mla_dims_t* dims, int32_t batch, const void* q_la
 mla_status_t merge_impl(const mla_dims_t* dims, int32_t batch, const int32_t* seq_lens, int32_t page_size,
                         int32_t max_pages_per_seq, const mla_partition_t* part, const void* workspace,
                         size_t workspace_bytes, void* o_lat, mla_dtype_t o_dt, float* lse, void* stream,
-                        size_t o_elem) {
+                        size_t o_elem, int q_len) {
   if (mla_status_t s = check_dims(dims)) return s;
   if (!seq_lens || !o_lat) return MLA_ERR_INVALID_ARG;
   if (o_dt != MLA_F32 && o_dt != MLA_BF16) return valid_dtype(o_dt) ? MLA_ERR_UNSUPPORTED : MLA_ERR_INVALID_ARG;
@@ -356,6 +357,7 @@ mla_status_t merge_impl(const mla_dims_t* dims, int32_t batch, const int32_t* se
   PartParams pp;
   int n_items = 0, n_slots = 0;
   if (mla_status_t s = resolve(dims, batch, max_pages_per_seq, page_size, part, &pp, &n_items, &n_slots)) return s;
+  pp.q_len = q_len;
   const WsLayout L = ws_layout(dims, n_slots, batch, pp.mode == PART_BALANCED, o_elem);
   if (L.total > 0 && (workspace == nullptr || workspace_bytes < L.total)) return MLA_ERR_WORKSPACE;
   if (batch == 0) return MLA_OK;
@@ -389,10 +391,10 @@ mla_status_t decode_workspace_layout(const mla_dims_t* dims, int32_t batch, int3
 
 namespace {
 
-// mla_decode_multi workspace: virtual lengths, virtual block table, then the
-// workspace of the decode over batch * q_len virtual sequences.
+// mla_decode_multi workspace: the workspace of the decode over batch * q_len
+// virtual sequences (whose lengths the kernels derive from seq_lens).
 struct MultiLayout {
-  size_t lens, dec, dec_bytes, total;
+  size_t dec, dec_bytes, total;
 };
 
 mla_status_t multi_layout(const mla_dims_t* dims, int32_t batch, int32_t q_len, int32_t max_pages,
@@ -405,8 +407,7 @@ mla_status_t multi_layout(const mla_dims_t* dims, int32_t batch, int32_t q_len, 
   int n_items = 0;
   if (mla_status_t s = resolve(dims, int(vb), max_pages, page_size, part, &pp, &n_items, n_slots)) return s;
   MultiLayout m{};
-  m.lens = 0;
-  m.dec = align256(size_t(vb) * sizeof(int32_t));
+  m.dec = 0;
   m.dec_bytes = ws_layout(dims, *n_slots, int(vb), pp.mode == PART_BALANCED).total;
   m.total = m.dec + m.dec_bytes;
   *M = m;
@@ -459,8 +460,17 @@ mla_status_t check_out_proj_args(const mla_dims_t* dims, mla_dtype_t o_dt, const
   return MLA_OK;
 }
 
-// expand + decode over the batch * q_len virtual sequences, then the merge
-// (w_uv == nullptr) or the merge + W^UV projection (mla_merge_out_proj).
+// Decode over the batch * q_len virtual sequences, then the merge (w_uv ==
+// nullptr) or the merge + W^UV projection (as mla_merge_out_proj).  Virtual
+// sequence b' = b*q_len + t is new token t of sequence b: the kernels read its
+// length from seq_lens[b] (seq_len_of in mla_common.h: the tokens up to its own
+// position, [deepseek(2) 關鍵技術] §1) and its pages from block-table row
+// b' / q_len, sequence b's row, in place.  A workgroup cannot hold more than
+// one token's 128 heads (their fp32 accumulators fill half a CU's register
+// file), so every virtual sequence streams the pages itself; the copies of one
+// sequence are adjacent in the work-item order, which puts them on the same XCD
+// at about the same time, so the repeated page reads are served from L2 and the
+// Infinity Cache rather than from HBM.
 mla_status_t decode_multi_impl(const mla_dims_t* dims, int32_t batch, int32_t q_len, const void* q_lat,
                                const void* q_pe, mla_dtype_t q_dt, const mla_paged_cache_t* cache,
                                float softmax_scale, const mla_partition_t* part, void* workspace,
@@ -472,31 +482,26 @@ mla_status_t decode_multi_impl(const mla_dims_t* dims, int32_t batch, int32_t q_
   if (mla_status_t s = multi_layout(dims, batch, q_len, cache->max_pages_per_seq, cache->page_size, part, &M, &n_slots))
     return s;
   if (!cache->block_table || !cache->seq_lens) return MLA_ERR_INVALID_ARG;
-  if (!workspace || workspace_bytes < M.total) return MLA_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return MLA_ERR_ALIGNMENT;
+  if (M.total > 0 && (!workspace || workspace_bytes < M.total)) return MLA_ERR_WORKSPACE;
+  if (M.total > 0 && !aligned16(workspace)) return MLA_ERR_ALIGNMENT;
   if (o_dt != MLA_F32 && o_dt != MLA_BF16) return valid_dtype(o_dt) ? MLA_ERR_UNSUPPORTED : MLA_ERR_INVALID_ARG;
   if (w_uv || o_heads)
     if (mla_status_t s = check_out_proj_args(dims, o_dt, w_uv, w_dt, o_heads, out_dt)) return s;
   char* ws = static_cast<char*>(workspace);
   const int vb = batch * q_len;
-  mla_paged_cache_t vc = *cache;
-  vc.seq_lens = reinterpret_cast<const int32_t*>(ws + M.lens);
   void* dec_ws = M.dec_bytes ? static_cast<void*>(ws + M.dec) : nullptr;
-  if (mla_status_t s = decode_impl(dims, vb, q_lat, q_pe, q_dt, &vc, softmax_scale, part, dec_ws, M.dec_bytes, o_lat,
-                                   o_dt, lse, stream, true, sizeof(float), q_len))
+  if (mla_status_t s = decode_impl(dims, vb, q_lat, q_pe, q_dt, cache, softmax_scale, part, dec_ws, M.dec_bytes,
+                                   o_lat, o_dt, lse, stream, true, sizeof(float), q_len))
     return s;
   if (batch == 0) return MLA_OK;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  if (launch_expand(cache->seq_lens, batch, q_len, reinterpret_cast<int32_t*>(ws + M.lens), st) != hipSuccess)
-    return MLA_ERR_HIP;
-  if (mla_status_t s = decode_impl(dims, vb, q_lat, q_pe, q_dt, &vc, softmax_scale, part, dec_ws, M.dec_bytes, o_lat,
-                                   o_dt, lse, stream, false, sizeof(float), q_len))
+  if (mla_status_t s = decode_impl(dims, vb, q_lat, q_pe, q_dt, cache, softmax_scale, part, dec_ws, M.dec_bytes,
+                                   o_lat, o_dt, lse, stream, false, sizeof(float), q_len))
     return s;
   if (!w_uv)
-    return mla_merge_splits(dims, vb, vc.seq_lens, cache->page_size, cache->max_pages_per_seq, part, dec_ws,
-                            M.dec_bytes, o_lat, o_dt, lse, stream);
-  return mla_merge_out_proj(dims, vb, vc.seq_lens, cache->page_size, cache->max_pages_per_seq, part, dec_ws,
-                            M.dec_bytes, o_lat, o_dt, lse, w_uv, w_dt, o_heads, out_dt, stream);
+    return merge_impl(dims, vb, cache->seq_lens, cache->page_size, cache->max_pages_per_seq, part, dec_ws,
+                      M.dec_bytes, o_lat, o_dt, lse, stream, sizeof(float), q_len);
+  return merge_out_proj_impl(dims, vb, cache->seq_lens, cache->page_size, cache->max_pages_per_seq, part, dec_ws,
+                             M.dec_bytes, o_lat, o_dt, lse, w_uv, w_dt, o_heads, out_dt, stream, q_len);
 }
 
 // mla_prefill workspace: sequence offsets, gathered rows, up-projected keys
@@ -570,6 +575,18 @@ mla_status_t mla_merge_out_proj(const mla_dims_t* dims, int32_t batch, const int
                                 int32_t max_pages_per_seq, const mla_partition_t* part, const void* workspace,
                                 size_t workspace_bytes, void* o_lat, mla_dtype_t o_dt, float* lse, const void* w_uv,
                                 mla_dtype_t w_dt, void* o_heads, mla_dtype_t out_dt, void* stream) {
+  return merge_out_proj_impl(dims, batch, seq_lens, page_size, max_pages_per_seq, part, workspace, workspace_bytes,
+                             o_lat, o_dt, lse, w_uv, w_dt, o_heads, out_dt, stream, 1);
+}
+
+}  // extern "C"
+
+namespace mla {
+
+mla_status_t merge_out_proj_impl(const mla_dims_t* dims, int32_t batch, const int32_t* seq_lens, int32_t page_size,
+                                 int32_t max_pages_per_seq, const mla_partition_t* part, const void* workspace,
+                                 size_t workspace_bytes, void* o_lat, mla_dtype_t o_dt, float* lse, const void* w_uv,
+                                 mla_dtype_t w_dt, void* o_heads, mla_dtype_t out_dt, void* stream, int q_len) {
   // validation of both calls before anything is enqueued
   if (mla_status_t s = check_dims(dims)) return s;
   if (batch < 0 || !seq_lens || !o_lat || !w_uv || !o_heads) return MLA_ERR_INVALID_ARG;
@@ -579,6 +596,7 @@ mla_status_t mla_merge_out_proj(const mla_dims_t* dims, int32_t batch, const int
   PartParams pp;
   int n_items = 0, n_slots = 0;
   if (mla_status_t s = resolve(dims, batch, max_pages_per_seq, page_size, part, &pp, &n_items, &n_slots)) return s;
+  pp.q_len = q_len;
   const WsLayout L = ws_layout(dims, n_slots, batch, pp.mode == PART_BALANCED);
   if (L.total > 0 && (workspace == nullptr || workspace_bytes < L.total)) return MLA_ERR_WORKSPACE;
   const bool fused = dims->d_head == 128 && dims->d_latent == 512 && o_dt == MLA_BF16 && w_dt == MLA_BF16 &&
@@ -588,8 +606,8 @@ mla_status_t mla_merge_out_proj(const mla_dims_t* dims, int32_t batch, const int
     return MLA_ERR_UNSUPPORTED;
   if (batch == 0) return MLA_OK;
   if (!fused) {
-    if (mla_status_t s = mla_merge_splits(dims, batch, seq_lens, page_size, max_pages_per_seq, part, workspace,
-                                          workspace_bytes, o_lat, o_dt, lse, stream))
+    if (mla_status_t s = merge_impl(dims, batch, seq_lens, page_size, max_pages_per_seq, part, workspace,
+                                    workspace_bytes, o_lat, o_dt, lse, stream, sizeof(float), q_len))
       return s;
     return mla_out_proj(dims, batch, o_lat, o_dt, w_uv, w_dt, o_heads, out_dt, stream);
   }
@@ -608,6 +626,10 @@ mla_status_t mla_merge_out_proj(const mla_dims_t* dims, int32_t batch, const int
   const hipError_t e = launch_merge_proj(a, w_uv, o_heads, batch, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
+
+}  // namespace mla
+
+extern "C" {
 
 mla_status_t mla_cache_store(const mla_dims_t* dims, int32_t batch, const void* rows, mla_dtype_t rows_dt,
                              const int32_t* positions, float rope_base, const mla_paged_cache_t* cache,

@@ -183,7 +183,6 @@ hipError_t launch_query_finish(const QueryFinishArgs& a, hipStream_t st);
 hipError_t launch_merge(const MergeArgs& a, int batch, hipStream_t st);
 // merge of split partials + W^UV projection (d_h 128, d_c 512, bf16)
 hipError_t launch_merge_proj(const MergeArgs& a, const void* w_uv, void* o_heads, int batch, hipStream_t st);
-hipError_t launch_expand(const int32_t* seq_lens, int batch, int q_len, int32_t* lens_out, hipStream_t st);
 hipError_t launch_absorb_generic(const void* q, mla_dtype_t q_dt, const void* w, mla_dtype_t w_dt, void* out,
                                  mla_dtype_t o_dt, int batch, int n_heads, int d_head, int d_latent, hipStream_t st);
 hipError_t launch_outproj_generic(const void* o, mla_dtype_t o_dt, const void* w, mla_dtype_t w_dt, void* out,

@@ -19,7 +19,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(MergeArgs a) {
   const int head = blockIdx.y * kMergeWaves + threadIdx.x / 64;
   const int lane = threadIdx.x % 64;
   if (head >= a.n_heads) return;
-  const int T = clamp_len(load_const(a.seq_lens, b), a.pp);
+  const int T = seq_len_of(load_const(a.seq_lens, seq_len_index(b, a.pp)), b, a.pp);
   const int64_t out_row = (int64_t(b) * a.n_heads + head);
   if (T <= 0) {
     for (int c = lane; c < a.d_latent; c += 64) store_any(a.o_lat, out_row * a.d_latent + c, 0.f, a.o_dt);

@@ -50,7 +50,7 @@ __device__ __forceinline__ uint32_t mp_row_off(int r, int chunk) {
 
 // Split slots of row b: [first, first + count); count 0 for an empty sequence.
 __device__ __forceinline__ void mp_splits(const MergeArgs& a, int b, int& first, int& count) {
-  const int T = clamp_len(load_const(a.seq_lens, b), a.pp);
+  const int T = seq_len_of(load_const(a.seq_lens, seq_len_index(b, a.pp)), b, a.pp);
   first = 0;
   count = T > 0 ? 1 : 0;
   if (T <= 0) return;

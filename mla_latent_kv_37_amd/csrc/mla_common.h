@@ -77,6 +77,7 @@ struct PartParams {
   int page_size;
   int batch;
   int max_tokens;     // max_pages_per_seq * page_size: longer lengths are read as this
+  int q_len = 1;      // > 1: sequence i is new token i % q_len of seq_lens[i / q_len] (multi-token decode)
 };
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
@@ -108,6 +109,20 @@ __device__ __forceinline__ double rope_theta(int k, int d, const RopeParams& r) 
 // reports them).
 __host__ __device__ __forceinline__ int clamp_len(int T, const PartParams& pp) {
   return T < 0 ? 0 : (T > pp.max_tokens ? pp.max_tokens : T);
+}
+
+// Lengths of the sequences of a multi-token decode (q_len > 1): sequence i is
+// new token t = i % q_len of cached sequence i / q_len, whose last q_len
+// tokens are the new ones; token t sits at position T - q_len + t and attends
+// to the T - q_len + t + 1 tokens up to it (none if that is not positive).
+// seq_len_index gives the seq_lens entry to read, seq_len_of the length from
+// that entry, clamped as clamp_len.  With q_len = 1 both are the identity.
+__host__ __device__ __forceinline__ int seq_len_index(int i, const PartParams& pp) {
+  return pp.q_len > 1 ? i / pp.q_len : i;
+}
+__host__ __device__ __forceinline__ int seq_len_of(int T, int i, const PartParams& pp) {
+  if (pp.q_len > 1) T = T < 0 ? 0 : T - pp.q_len + i % pp.q_len + 1;
+  return clamp_len(T, pp);
 }
 
 // Read-only int32 metadata (block table, lengths) through the constant address

@@ -59,7 +59,7 @@ struct SegmentIter {
     if (pp.mode != PART_BALANCED) return;
     const int B = pp.batch, page = pp.page_size;
     const int lane = threadIdx.x & 63;
-    auto pages_of = [&](int i) { return i < B ? ceil_div(clamp_len(seq_lens[i], pp), page) : 0; };
+    auto pages_of = [&](int i) { return i < B ? ceil_div(seq_len_of(seq_lens[seq_len_index(i, pp)], i, pp), page) : 0; };
     // total pages P and non-empty sequences m of the batch
     int P = 0, m = 0;
     for (int base = 0; base < B; base += 64) {
@@ -102,7 +102,7 @@ struct SegmentIter {
     if (pp.mode == PART_WHOLE) {
       done = true;
       if (item >= B) return false;
-      const int T = clamp_len(load_const(seq_lens, item), pp);
+      const int T = seq_len_of(load_const(seq_lens, seq_len_index(item, pp)), item, pp);
       if (T <= 0) return false;
       sg = Segment{item, 0, T, -1, true};
       return true;
@@ -111,14 +111,14 @@ struct SegmentIter {
       done = true;
       const int bb = item / pp.fixed_slots, sp = item % pp.fixed_slots;
       if (bb >= B) return false;
-      const int T = clamp_len(load_const(seq_lens, bb), pp);
+      const int T = seq_len_of(load_const(seq_lens, seq_len_index(bb, pp)), bb, pp);
       const int n = ceil_div(T, pp.split_tokens);
       if (sp >= n) return false;
       sg = Segment{bb, sp * pp.split_tokens, min(T, (sp + 1) * pp.split_tokens), item, n == 1};
       return true;
     }
     while (b < B && S < p1) {
-      const int T = clamp_len(load_const(seq_lens, b), pp);
+      const int T = seq_len_of(load_const(seq_lens, seq_len_index(b, pp)), b, pp);
       const int np = ceil_div(T, page);
       const int64_t Sb = S;
       const int bb = b;

@@ -41,10 +41,6 @@ hipError_t launch_reduce_cast(const float*, int, int64_t, void*, mla_dtype_t, co
 hipError_t launch_query_finish(const QueryFinishArgs&, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_merge(const MergeArgs&, int, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_merge_proj(const MergeArgs&, const void*, void*, int, hipStream_t) { ++g_launches; return hipSuccess; }
-hipError_t launch_expand(const int32_t*, int, int, int32_t*, hipStream_t) {
-  ++g_launches;
-  return hipSuccess;
-}
 hipError_t launch_absorb_generic(const void*, mla_dtype_t, const void*, mla_dtype_t, void*, mla_dtype_t, int, int, int,
                                  int, hipStream_t) {
   ++g_launches;

@@ -193,21 +193,21 @@ def test_prefill_workspace_and_validation(lib):
 
 
 def test_multi_decode_workspace_and_validation(lib):
-    """mla_decode_multi: the workspace holds the virtual lengths (B * q_len) before
-    the decode workspace of the virtual batch (virtual sequences read their
-    sequence's block-table row in place); checks fail before any device access."""
+    """mla_decode_multi: the workspace is the decode workspace of the virtual
+    batch (virtual lengths are derived from seq_lens in the kernels, and virtual
+    sequences read their sequence's block-table row in place); checks fail
+    before any device access."""
     L = _raw(lib)
     d = _v2(lib)
     fake = ctypes.c_void_p(0x10000)
     B, q, mp = 8, 3, 10
     nbytes, slots = lib.multi_workspace_size(d, B, q, mp, 64, lib.partition(0, 0))
-    align = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    assert slots == 0 and nbytes == align(B * q * 4)
+    assert slots == 0 and nbytes == 0
     dec, dslots = lib.workspace_size(d, B * q, mp, 64, lib.partition(0, 40))
     nbytes, slots = lib.multi_workspace_size(d, B, q, mp, 64, lib.partition(0, 40))
-    assert slots == dslots and nbytes == align(B * q * 4) + dec
+    assert slots == dslots and nbytes == dec > 0
     sz = ctypes.c_size_t(0)
-    part = lib.partition(0, 0)
+    part = lib.partition(0, 40)
     assert L.mla_decode_multi_workspace_size(ctypes.byref(d), B, 0, mp, 64, ctypes.byref(part), ctypes.byref(sz),
                                              None) == lib.MLA_ERR_INVALID_ARG
     cache = lib.PagedCache(0x10000, None, lib.MLA_BF16, 64, 100, 0x20000, mp, 0x30000)
