@@ -19,6 +19,7 @@
 static int g_launches = 0;
 static mla::V2DecodeArgs g_v2{};
 static mla::PrefillArgs g_pf{};
+static mla::MergeArgs g_mp{};
 static int g_fails = 0;
 
 #define CHECK(cond)                                                         \
@@ -40,7 +41,7 @@ hipError_t launch_gemm_ws(const GemmArgs&, hipStream_t) { ++g_launches; return h
 hipError_t launch_reduce_cast(const float*, int, int64_t, void*, mla_dtype_t, const RopeTableArgs&, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_query_finish(const QueryFinishArgs&, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_merge(const MergeArgs&, int, hipStream_t) { ++g_launches; return hipSuccess; }
-hipError_t launch_merge_proj(const MergeArgs&, const void*, void*, int, hipStream_t) { ++g_launches; return hipSuccess; }
+hipError_t launch_merge_proj(const MergeArgs& a, const void*, void*, int, hipStream_t) { ++g_launches; g_mp = a; return hipSuccess; }
 hipError_t launch_absorb_generic(const void*, mla_dtype_t, const void*, mla_dtype_t, void*, mla_dtype_t, int, int, int,
                                  int, hipStream_t) {
   ++g_launches;
@@ -186,6 +187,33 @@ static void check_decode_validation() {
   CHECK(mla_query_prep(&d, 5120, 1536, 8, dev(4), MLA_BF16, dev(5), dev(6), dev(7), MLA_BF16, idev(8), 1e4f, dev(9),
                        dev(10), MLA_BF16, nullptr, 0, nullptr) == MLA_ERR_WORKSPACE);
   CHECK(g_launches == before);
+  // a valid multi-token call: two launches (decode, merge + projection) over the
+  // virtual batch, both reading the caller's seq_lens with q_len set
+  {
+    const int b0 = g_launches;
+    CHECK(mla_decode_multi_out_proj(&d, 64, 3, dev(4), dev(5), MLA_BF16, &c, scale, &bal, dev(6), mws, dev(7),
+                                    MLA_BF16, nullptr, dev(8), MLA_BF16, dev(9), MLA_BF16, nullptr) == MLA_OK);
+    CHECK(g_launches == b0 + 2);
+    CHECK(g_v2.seq_lens == lens && g_v2.pp.q_len == 3 && g_v2.bt_div == 3 && g_v2.pp.batch == 192);
+    CHECK(g_mp.seq_lens == lens && g_mp.pp.q_len == 3 && g_mp.pp.batch == 192);
+    CHECK(mla_decode(&d, 64, dev(4), dev(5), MLA_BF16, &c, scale, &bal, dev(6), ws, dev(7), MLA_BF16, nullptr,
+                     nullptr) == MLA_OK);
+    CHECK(g_v2.pp.q_len == 1 && g_v2.bt_div == 1);
+  }
+  // virtual lengths: new token t of a sequence of T tokens (the last q_len of
+  // them new) attends to T - q_len + t + 1 tokens, at least 0, clamped
+  {
+    mla::PartParams pp{};
+    pp.max_tokens = 100;
+    pp.q_len = 3;
+    const int T10[3] = {mla::seq_len_of(10, 0, pp), mla::seq_len_of(10, 1, pp), mla::seq_len_of(10, 2, pp)};
+    CHECK(T10[0] == 8 && T10[1] == 9 && T10[2] == 10);
+    CHECK(mla::seq_len_of(1, 3, pp) == 0 && mla::seq_len_of(1, 4, pp) == 0 && mla::seq_len_of(1, 5, pp) == 1);
+    CHECK(mla::seq_len_of(-5, 2, pp) == 0 && mla::seq_len_of(500, 2, pp) == 100);
+    CHECK(mla::seq_len_index(7, pp) == 2 && mla::seq_len_index(8, pp) == 2 && mla::seq_len_index(9, pp) == 3);
+    pp.q_len = 1;
+    CHECK(mla::seq_len_of(10, 7, pp) == 10 && mla::seq_len_index(7, pp) == 7 && mla::seq_len_of(-1, 0, pp) == 0);
+  }
   // huge sizes: no overflow in the workspace arithmetic (sizes are size_t)
   CHECK(mla_decode_workspace_size(&d, 1 << 20, 1 << 10, 64, &fixed, &ws, &slots) == MLA_OK);
   CHECK(ws >= size_t(slots) * 128 * 512 * 4);
